@@ -1,0 +1,141 @@
+"""Oracle Qwen2 decoder: prefill and single-token greedy decode with a KV cache.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The layer sequence is the standard Qwen2 decoder, which the LLAISYS report
+runs and matches against Hugging Face token for token ("LLAISYS 训练营结项报告",
+sections 3.2 fourth layer and 3.5):
+
+  x = E[ids]
+  per layer:  h = rmsnorm(x, w_in)
+              q, k, v = h Wq^T + bq, h Wk^T + bk, h Wv^T + bv
+              q, k = rope(q, pos), rope(k, pos);  append k, v to the cache
+              o = causal GQA attention(q, K_cache, V_cache)
+              x = x + o Wo^T
+              h2 = rmsnorm(x, w_post)
+              x = x + (silu(h2 Wg^T) * (h2 Wu^T)) Wd^T
+  logits = rmsnorm(x_last, w_f) W_lm^T   (float32, last position of each sequence)
+  next = argmax(logits)
+
+Storage model ("bf16" mode): every operator output is rounded to bf16 before
+the next operator reads it, following section 3.3 item 3 of the report (low
+precision storage, float compute, low precision write-back).  The rounding
+points are: q/k/v after the bias add and again after RoPE, the attention
+output, o_proj output, each residual sum, each RMSNorm output, gate and up
+outputs, the SwiGLU output and the down output.  The logits stay float32 and
+argmax runs on them.  "fp32" mode performs no rounding (the tiny fp32 model).
+
+Pinned by: the operator pins, an fp64 brute-force forward on tiny shapes, the
+KV-cache decode equalling a full recompute of the prefix, batch independence,
+and the closed form when every o_proj and down weight is zero.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import ops
+
+F32 = np.float32
+
+
+class OracleModel:
+    """Holds float32 copies of the weights and a float32 KV cache.
+
+    ``weights`` maps (name, layer) -> array as produced by ``synth.make_weights``
+    (uint16 bf16 bit patterns or float32).  ``storage`` is "bf16" or "fp32".
+    """
+
+    def __init__(self, shape, weights, storage: str, batch: int, max_seq: int):
+        if storage not in ("bf16", "fp32"):
+            raise ValueError(storage)
+        self.shape = shape
+        self.storage = storage
+        self.batch = batch
+        self.max_seq = max_seq
+        self.w = {}
+        for key, arr in weights.items():
+            self.w[key] = ops.widen_bf16(arr) if arr.dtype == np.uint16 else np.asarray(arr, F32)
+        L, nkv, d = shape.nlayer, shape.nkv, shape.dh
+        self.k_cache = [np.zeros((batch, nkv, max_seq, d), F32) for _ in range(L)]
+        self.v_cache = [np.zeros((batch, nkv, max_seq, d), F32) for _ in range(L)]
+        self.length = 0
+
+    def reset(self):
+        self.length = 0
+
+    def _st(self, x):
+        return ops.bf16_round(x) if self.storage == "bf16" else np.asarray(x, F32)
+
+    def _weight(self, name, layer=-1):
+        return self.w[(name, layer)]
+
+    def forward(self, ids: np.ndarray, all_logits: bool = False):
+        """Process ids [B, T] at positions length .. length+T-1.
+
+        Returns (logits, next): logits [B, V] float32 of the last position (or
+        [B, T, V] when ``all_logits``), next [B] int64 greedy tokens.
+        """
+        ids = np.asarray(ids, np.int64)
+        if ids.ndim == 1:
+            ids = ids[:, None]
+        B, T = ids.shape
+        sh = self.shape
+        if B != self.batch:
+            raise ValueError("batch mismatch")
+        P = self.length
+        if P + T > self.max_seq:
+            raise ValueError("KV cache capacity exceeded")
+        H, nh, nkv, d = sh.hidden, sh.nh, sh.nkv, sh.dh
+        st = self._st
+        pos = np.arange(P, P + T)
+        scale = 1.0 / np.sqrt(d)
+
+        x = st(ops.embedding(ids.reshape(-1), self._weight("embed_tokens"))).reshape(B, T, H)
+        for l in range(sh.nlayer):
+            W = lambda n: self._weight(n, l)          # noqa: E731
+            h = st(ops.rms_norm(x, W("input_layernorm"), sh.eps))
+            q = st(ops.linear(h, W("q_proj.weight"), W("q_proj.bias"))).reshape(B, T, nh, d)
+            k = st(ops.linear(h, W("k_proj.weight"), W("k_proj.bias"))).reshape(B, T, nkv, d)
+            v = st(ops.linear(h, W("v_proj.weight"), W("v_proj.bias"))).reshape(B, T, nkv, d)
+            o = np.empty((B, T, nh, d), F32)
+            for b in range(B):
+                qb = st(ops.rope(q[b], pos, sh.theta))
+                kb = st(ops.rope(k[b], pos, sh.theta))
+                self.k_cache[l][b, :, P:P + T, :] = kb.transpose(1, 0, 2)
+                self.v_cache[l][b, :, P:P + T, :] = v[b].transpose(1, 0, 2)
+                kc = self.k_cache[l][b, :, :P + T, :].transpose(1, 0, 2)
+                vc = self.v_cache[l][b, :, :P + T, :].transpose(1, 0, 2)
+                o[b] = st(ops.attention(qb, kc, vc, scale))
+            a = st(ops.linear(o.reshape(B, T, nh * d), W("o_proj.weight")))
+            x = st(ops.add(x, a))
+            h2 = st(ops.rms_norm(x, W("post_attention_layernorm"), sh.eps))
+            g = st(ops.linear(h2, W("gate_proj.weight")))
+            u = st(ops.linear(h2, W("up_proj.weight")))
+            m = st(ops.swiglu(g, u))
+            dn = st(ops.linear(m, W("down_proj.weight")))
+            x = st(ops.add(x, dn))
+        self.length = P + T
+        xs = x if all_logits else x[:, -1, :]
+        hf = st(ops.rms_norm(xs, self._weight("norm"), sh.eps))
+        logits = ops.linear(hf, self._weight("lm_head"))
+        nxt, _ = ops.argmax(logits if not all_logits else logits[:, -1, :])
+        return logits, nxt
+
+    def generate(self, prompt: np.ndarray, steps: int, teacher=None):
+        """Prefill ``prompt``, then run ``steps`` single-token decode passes.
+
+        The prefill yields token 0; decode pass s (1-based) feeds token s-1 and
+        yields token s, so ``steps`` passes give steps + 1 tokens and the context
+        grows to prompt + steps.  With ``teacher`` [B, steps + 1] the decode
+        inputs come from it (teacher forcing) instead of the model's own argmax.
+        Returns (tokens [B, steps + 1], list of steps + 1 logits arrays [B, V]).
+        """
+        logits, nxt = self.forward(prompt)
+        toks = [nxt]
+        all_logits = [logits]
+        for s in range(1, steps + 1):
+            feed = teacher[:, s - 1] if teacher is not None else toks[-1]
+            logits, nxt = self.forward(np.asarray(feed)[:, None])
+            toks.append(nxt)
+            all_logits.append(logits)
+        return np.stack(toks, axis=1), all_logits

@@ -1,0 +1,316 @@
+"""Pin checks for the oracle operators, written against closed forms,
+invariants and brute force rather than against the oracle itself.
+
+Each ``check_*`` takes the implementation under test as an argument, so the
+same check pins the real oracle (tests/test_oracle_ops.py) and is shown to
+reject planted mistakes (tests/test_oracle_mutations.py).  Each raises
+AssertionError on failure.
+"""
+import math
+
+import numpy as np
+
+from tests import _brute
+
+
+def check_bf16_round(bf16_round):
+    one = np.float32(1.0)
+    # exact ties go to the even neighbour
+    assert bf16_round(np.array([1 + 2.0 ** -8], np.float32))[0] == one
+    assert bf16_round(np.array([1 + 3 * 2.0 ** -8], np.float32))[0] == np.float32(1 + 2.0 ** -6)
+    # just above a tie rounds up, just below rounds down
+    assert bf16_round(np.array([1 + 2.0 ** -8 + 2.0 ** -20], np.float32))[0] == np.float32(1 + 2.0 ** -7)
+    assert bf16_round(np.array([1 + 2.0 ** -8 - 2.0 ** -20], np.float32))[0] == one
+    # negative values round symmetrically
+    assert bf16_round(np.array([-(1 + 3 * 2.0 ** -8)], np.float32))[0] == np.float32(-(1 + 2.0 ** -6))
+    # representable values are fixed points, infinities are kept
+    rep = np.array([0.0, -0.0, 1.0, -2.0, 0.5, 3.0, 2.0 ** -100, np.inf, -np.inf], np.float32)
+    assert np.array_equal(bf16_round(rep), rep)
+    # random sample: low 16 bits cleared, result is the nearer of the two bf16 neighbours
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    r = bf16_round(x)
+    assert np.all(r.view(np.uint32) & 0xFFFF == 0)
+    x64 = x.astype(np.float64)
+    lo = (x.view(np.uint32) & 0xFFFF0000).view(np.float32).astype(np.float64)   # toward zero
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(lo))) - 7)
+    hi = lo + np.sign(lo) * ulp                                                # away from zero
+    r64 = r.astype(np.float64)
+    assert np.all((r64 == lo) | (r64 == hi))
+    other = np.where(r64 == lo, hi, lo)
+    assert np.all(np.abs(r64 - x64) <= np.abs(other - x64))
+
+
+def check_widen(widen):
+    bits = np.array([0x3F80, 0xC000, 0x7F80, 0x0000, 0x3F00], np.uint16)
+    assert widen(bits).tolist() == [1.0, -2.0, math.inf, 0.0, 0.5]
+
+
+def check_embedding(embedding):
+    V, H = 50, 12
+    table = np.zeros((V, H), np.float32)
+    table[:, 0] = np.arange(V)                     # each row encodes its own index
+    table[:, 1:] = (np.arange(V)[:, None] * 1000 + np.arange(1, H)[None, :])
+    ids = np.array([0, 49, 7, 7, 3, 49, 0], np.int64)
+    out = embedding(ids, table)
+    assert out.shape == (len(ids), H)
+    assert out[:, 0].astype(np.int64).tolist() == ids.tolist()
+    assert np.all(out[:, 1:] == ids[:, None] * 1000 + np.arange(1, H)[None, :])
+    for bad in ([-1], [V]):
+        try:
+            embedding(np.array(bad), table)
+        except IndexError:
+            pass
+        else:
+            raise AssertionError("out-of-range id accepted")
+
+
+def check_rms_norm(rms_norm):
+    eps = 1e-6
+    # closed form on a constant vector: y = c / sqrt(c^2 + eps) * w
+    H = 64
+    w = np.linspace(0.5, 1.5, H).astype(np.float32)
+    for c in (3.0, -0.25, 1e-4):
+        y = rms_norm(np.full((1, H), c, np.float32), w, eps)
+        ref = c / math.sqrt(c * c + eps) * w.astype(np.float64)
+        assert np.allclose(y[0], ref, rtol=2e-6, atol=0)
+    # output RMS with w = 1 is sqrt(ms / (ms + eps)) (epsilon inside the root)
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((8, H)) * 1e-3).astype(np.float32)
+    y = rms_norm(x, np.ones(H, np.float32), eps)
+    ms = np.mean(x.astype(np.float64) ** 2, axis=-1)
+    assert np.allclose(np.sqrt(np.mean(y.astype(np.float64) ** 2, axis=-1)), np.sqrt(ms / (ms + eps)), rtol=1e-5)
+    # scale invariance away from eps
+    x = rng.standard_normal((4, H)).astype(np.float32)
+    assert np.allclose(rms_norm(x * 8, w, eps), rms_norm(x, w, eps), rtol=1e-5, atol=1e-6)
+    # brute force
+    for r in range(4):
+        ref = _brute.rmsnorm(x[r].tolist(), w.tolist(), eps)
+        assert np.allclose(rms_norm(x[r:r + 1], w, eps)[0], ref, rtol=1e-5, atol=1e-6)
+
+
+def check_rope(rope, rope_cos_sin):
+    theta = 10000.0
+    rng = np.random.default_rng(2)
+    T, h, d = 6, 3, 16
+    x = rng.standard_normal((T, h, d)).astype(np.float32)
+    # position 0 is the identity
+    assert np.array_equal(rope(x[:1], np.array([0]), theta), x[:1])
+    # unit vector e_0 at position p lands on cos at index 0 and sin at index d/2 (rotate-half)
+    e0 = np.zeros((1, 1, d), np.float32)
+    e0[0, 0, 0] = 1
+    for p in (1, 5, 1000):
+        y = rope(e0, np.array([p]), theta)[0, 0]
+        ref = np.zeros(d)
+        ref[0], ref[d // 2] = math.cos(p), math.sin(p)
+        assert np.allclose(y, ref, atol=1e-6), (p, y)
+    # second frequency: e_1 rotates by p * theta^(-2/d) into index 1 + d/2
+    e1 = np.zeros((1, 1, d), np.float32)
+    e1[0, 0, 1] = 1
+    y = rope(e1, np.array([7]), theta)[0, 0]
+    ang = 7 * theta ** (-2.0 / d)
+    assert abs(y[1] - math.cos(ang)) < 1e-6 and abs(y[1 + d // 2] - math.sin(ang)) < 1e-6
+    assert abs(np.sum(np.abs(y)) - abs(math.cos(ang)) - abs(math.sin(ang))) < 1e-6
+    # pair norms preserved
+    pos = np.array([3, 17, 100, 4095, 0, 9])
+    y = rope(x, pos, theta)
+    n_in = x[..., :d // 2] ** 2 + x[..., d // 2:] ** 2
+    n_out = y[..., :d // 2] ** 2 + y[..., d // 2:] ** 2
+    assert np.allclose(n_in, n_out, rtol=1e-5, atol=1e-6)
+    # R(m) R(n) = R(m + n)
+    one = rope(rope(x[:1], np.array([13]), theta), np.array([29]), theta)
+    assert np.allclose(one, rope(x[:1], np.array([42]), theta), atol=2e-5)
+    # <R(m) q, R(n) k> depends on m - n only
+    q, k = x[0:1, 0:1], x[1:2, 0:1]
+    dots = [float(np.sum(rope(q, np.array([m]), theta) * rope(k, np.array([m - 5]), theta)))
+            for m in (5, 50, 700)]
+    assert max(dots) - min(dots) < 1e-4
+    # brute force (fp64 angles)
+    for t in range(T):
+        for hh in range(h):
+            ref = _brute.rope_head(x[t, hh].tolist(), int(pos[t]), theta)
+            assert np.allclose(y[t, hh], ref, atol=1e-5)
+    # table at position 0 and a hand value
+    c, s = rope_cos_sin(np.array([0, 2]), 4, 10000.0)
+    assert np.all(c[0] == 1) and np.all(s[0] == 0)
+    assert abs(c[1, 1] - math.cos(2 * 0.01)) < 1e-7 and abs(s[1, 1] - math.sin(0.02)) < 1e-7
+
+
+def check_linear(linear):
+    rng = np.random.default_rng(3)
+    M, K, N = 5, 7, 6
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    W = rng.standard_normal((N, K)).astype(np.float32)       # [out, in]
+    b = rng.standard_normal(N).astype(np.float32)
+    y = linear(x, W, b)
+    assert y.shape == (M, N)
+    for m in range(M):
+        assert np.allclose(y[m], _brute.matvec(W.tolist(), x[m].tolist(), b.tolist()), rtol=1e-5, atol=1e-5)
+    assert np.allclose(linear(x, W), y - b, atol=1e-5)
+    assert np.array_equal(linear(x, np.zeros_like(W), b), np.broadcast_to(b, (M, N)))
+    eye = np.eye(K, dtype=np.float32)
+    assert np.array_equal(linear(eye, W), W.T)                # one-hot input selects column k of W
+
+
+def check_attention(attention):
+    rng = np.random.default_rng(4)
+    # probabilities: V = identity over keys returns the probability rows
+    T, S, d = 5, 9, 16
+    q = rng.standard_normal((T, 2, d)).astype(np.float32)
+    k = rng.standard_normal((S, 1, d)).astype(np.float32)
+    v = np.zeros((S, 1, d), np.float32)
+    v[np.arange(S), 0, np.arange(S)] = 1
+    p = attention(q, k, v, 1 / math.sqrt(d))
+    past = S - T
+    for t in range(T):
+        for h in range(2):
+            row = p[t, h, :S]
+            assert abs(row.sum() - 1) < 1e-6
+            assert np.all(row[past + t + 1:] == 0)            # masked keys contribute exactly 0
+            assert np.all(row[:past + t + 1] > 0)
+            # softmax of the visible scores, computed in float64
+            sc = k[:past + t + 1, 0].astype(np.float64) @ q[t, h].astype(np.float64) / math.sqrt(d)
+            e = np.exp(sc - sc.max())
+            assert np.allclose(row[:past + t + 1], e / e.sum(), atol=1e-6)
+    # fresh sequence: query 0 returns v_0 exactly
+    T = S = 4
+    q = rng.standard_normal((T, 4, d)).astype(np.float32)
+    k = rng.standard_normal((S, 2, d)).astype(np.float32)
+    v = rng.standard_normal((S, 2, d)).astype(np.float32)
+    o = attention(q, k, v, 0.25)
+    assert np.array_equal(o[0, 0], v[0, 0]) and np.array_equal(o[0, 3], v[0, 1])
+    # future keys/values do not change earlier outputs
+    k2, v2 = k.copy(), v.copy()
+    k2[3] += 5
+    v2[3] -= 7
+    o2 = attention(q, k2, v2, 0.25)
+    assert np.array_equal(o2[:3], o[:3]) and not np.allclose(o2[3], o[3])
+    # GQA equals MHA with repeated KV heads (contiguous groups: head h reads h // 2)
+    krep = np.repeat(k, 2, axis=1)
+    vrep = np.repeat(v, 2, axis=1)
+    assert np.allclose(attention(q, krep, vrep, 0.25), o, atol=1e-6)
+    # brute force in fp64
+    for t in range(T):
+        for h in range(4):
+            g = h // 2
+            sc = [float(q[t, h] @ k[j, g]) * 0.25 for j in range(t + 1)]
+            m = max(sc)
+            e = [math.exp(s - m) for s in sc]
+            ref = sum(e[j] / sum(e) * v[j, g].astype(np.float64) for j in range(t + 1))
+            assert np.allclose(o[t, h], ref, atol=1e-5)
+
+
+def check_silu_swiglu(silu, swiglu):
+    assert silu(np.array([0.0], np.float32))[0] == 0
+    ref = {1.0: 1 / (1 + math.exp(-1)), -1.0: -1 / (1 + math.exp(1)), 2.0: 2 / (1 + math.exp(-2))}
+    for g, r in ref.items():
+        assert abs(silu(np.array([g], np.float32))[0] - r) < 1e-6
+    big = silu(np.array([30.0, -30.0, -200.0], np.float32))
+    assert abs(big[0] - 30) < 1e-5 and abs(big[1]) < 1e-10 and big[2] == 0
+    g = np.linspace(-6, 6, 25).astype(np.float32)
+    assert np.array_equal(swiglu(g, np.ones_like(g)), silu(g))
+    u = np.linspace(2, -3, 25).astype(np.float32)
+    assert np.allclose(swiglu(g, u), [_brute.silu(float(a)) * float(b) for a, b in zip(g, u)], atol=1e-6)
+
+
+def check_argmax(argmax):
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((6, 300)).astype(np.float32)
+    x[1, [10, 200]] = 9.0               # planted tie: lowest index wins
+    x[2, :] = 0.0                       # all equal: index 0
+    x[3, 299] = 50.0                    # maximum at the last index
+    idx, val = argmax(x)
+    for r in range(x.shape[0]):
+        best = 0
+        for j in range(1, x.shape[1]):
+            if x[r, j] > x[r, best]:
+                best = j
+        assert idx[r] == best and val[r] == x[r, best]
+    assert idx[1] == 10 and idx[2] == 0 and idx[3] == 299
+
+
+# ----------------------------------------------------------------------------- model
+
+def tiny_shape(nlayer=2, eps=1e-2):
+    """A small Qwen2-like shape.  The large epsilon makes its position visible
+    at model level (with 1e-6 it only shows at the operator level)."""
+    from synth import ModelShape
+    return ModelShape("pin-tiny", "f32", nlayer, 16, 4, 2, 4, 24, 40, 10000.0, eps)
+
+
+def check_model_vs_brute(model_cls, ops_module=None):
+    """fp32-mode oracle against the fp64 loop forward: prompt of 5, then 3 decode steps."""
+    import synth
+    sh = tiny_shape()
+    w = synth.make_weights(sh, seed=11)
+    # larger weights than N(0, 0.02) so that every term matters at fp32 tolerance
+    w = {k: (v * 20 if k[0] not in ("norm", "input_layernorm", "post_attention_layernorm") else v)
+         for k, v in w.items()}
+    prompt = np.array([[3, 17, 39, 0, 22]], np.int64)
+    m = model_cls(sh, w, "fp32", 1, 16)
+    logits, nxt = m.forward(prompt, all_logits=True)
+    brute = _brute.BruteModel(sh, w)
+    for t in range(prompt.shape[1]):
+        ref = brute.step(int(prompt[0, t]))
+        assert np.allclose(logits[0, t], ref, rtol=1e-4, atol=1e-4), t
+    assert nxt[0] == int(np.argmax(ref))
+    tok = int(nxt[0])
+    for _ in range(3):
+        lg, nx = m.forward(np.array([[tok]]))
+        ref = brute.step(tok)
+        assert np.allclose(lg[0], ref, rtol=1e-4, atol=1e-4)
+        tok = int(nx[0])
+
+
+def check_decode_equals_recompute(model_cls, storage):
+    import synth
+    sh = tiny_shape(3)
+    w = synth.make_weights(sh, seed=12)
+    if storage == "fp32":
+        w = {k: v for k, v in w.items()}
+    prompt = np.array([[5, 6, 7, 8, 9, 10]], np.int64)
+    m = model_cls(sh, w, storage, 1, 32)
+    toks, logits = m.generate(prompt, 6)
+    for s in range(1, 7):
+        full = np.concatenate([prompt, toks[:, :s]], axis=1)
+        r = model_cls(sh, w, storage, 1, 32)
+        lg, nx = r.forward(full)
+        tol = 1e-5 if storage == "fp32" else 2e-2
+        assert np.allclose(lg, logits[s], atol=tol, rtol=0), (s, np.abs(lg - logits[s]).max())
+
+
+def check_batch_independence(model_cls, storage):
+    import synth
+    sh = tiny_shape()
+    w = synth.make_weights(sh, seed=13)
+    a = np.array([[1, 2, 3, 4]], np.int64)
+    b = np.array([[30, 20, 10, 0]], np.int64)
+    mb = model_cls(sh, w, storage, 2, 16)
+    tb, lb = mb.generate(np.concatenate([a, b]), 3)
+    for i, p in enumerate((a, b)):
+        ms = model_cls(sh, w, storage, 1, 16)
+        ts, ls = ms.generate(p, 3)
+        assert np.array_equal(ts[0], tb[i])
+        for s in range(4):
+            assert np.allclose(ls[s][0], lb[s][i], atol=1e-5)
+
+
+def check_zero_mixers_closed_form(model_cls):
+    """With every o_proj and down weight zero the residual stream stays E[id],
+    so the logits reduce to rmsnorm(E[id], w_f) W_lm^T at every position."""
+    import synth
+    sh = tiny_shape()
+    w = synth.make_weights(sh, seed=14)
+    for l in range(sh.nlayer):
+        w[("o_proj.weight", l)] = np.zeros_like(w[("o_proj.weight", l)])
+        w[("down_proj.weight", l)] = np.zeros_like(w[("down_proj.weight", l)])
+    ids = np.array([[7, 0, 39, 12]], np.int64)
+    m = model_cls(sh, w, "fp32", 1, 8)
+    logits, _ = m.forward(ids, all_logits=True)
+    E = w[("embed_tokens", -1)].astype(np.float64)
+    wf = w[("norm", -1)].astype(np.float64)
+    Wl = w[("lm_head", -1)].astype(np.float64)
+    for t in range(ids.shape[1]):
+        e = E[ids[0, t]]
+        hf = e / np.sqrt(np.mean(e * e) + sh.eps) * wf
+        assert np.allclose(logits[0, t], Wl @ hf, rtol=1e-5, atol=1e-6)

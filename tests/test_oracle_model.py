@@ -1,0 +1,54 @@
+"""The oracle's whole-model forward against brute force and model invariants."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import pins
+
+
+def test_model_vs_brute_force():
+    pins.check_model_vs_brute(oracle.OracleModel)
+
+
+@pytest.mark.parametrize("storage", ["fp32", "bf16"])
+def test_decode_equals_recompute(storage):
+    pins.check_decode_equals_recompute(oracle.OracleModel, storage)
+
+
+@pytest.mark.parametrize("storage", ["fp32", "bf16"])
+def test_batch_independence(storage):
+    pins.check_batch_independence(oracle.OracleModel, storage)
+
+
+def test_zero_mixers_closed_form():
+    pins.check_zero_mixers_closed_form(oracle.OracleModel)
+
+
+def test_bf16_storage_close_to_fp32():
+    """bf16 storage changes the logits by roughly the bf16 rounding level only."""
+    sh = pins.tiny_shape(4)
+    w = synth.make_weights(sh, seed=21)
+    ids = np.array([[1, 5, 9, 13, 17, 21]], np.int64)
+    a, _ = oracle.OracleModel(sh, w, "fp32", 1, 8).forward(ids)
+    b, _ = oracle.OracleModel(sh, w, "bf16", 1, 8).forward(ids)
+    rel = np.abs(a - b).max() / np.abs(a).max()
+    assert 0 < rel < 3e-2
+
+
+def test_capacity_exceeded_raises():
+    sh = pins.tiny_shape()
+    w = synth.make_weights(sh, seed=1)
+    m = oracle.OracleModel(sh, w, "fp32", 1, 4)
+    m.forward(np.array([[1, 2, 3]]))
+    with pytest.raises(ValueError):
+        m.forward(np.array([[1, 2]]))
+
+
+def test_workload_a_runs():
+    wl = synth.WORKLOADS["A"]
+    w = synth.make_weights(wl)
+    m = oracle.OracleModel(wl.shape, w, "fp32", wl.batch, wl.max_seq)
+    toks, logits = m.generate(synth.make_prompt(wl), wl.steps)
+    assert toks.shape == (1, wl.steps + 1) and len(logits) == wl.steps + 1
+    assert m.length == wl.max_seq

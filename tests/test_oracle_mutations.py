@@ -1,0 +1,183 @@
+"""Planted mistakes in the oracle must be caught by the pins.
+
+Each case builds a plausible wrong variant of one oracle operator (a dropped
+term, a wrong sign or index, a transposed operand, the other RoPE pairing, the
+epsilon outside the root, ...) and checks that the corresponding pin check
+rejects it.  Model-level mutations are planted by patching ``oracle.ops`` on
+the CPU, so the whole-model pins see them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import ops
+from tests import pins
+
+F32 = np.float32
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except Exception:      # AssertionError or a shape error from the wrong variant
+        return True
+    return False
+
+
+def rope_interleaved(x, pos, theta):
+    x = np.asarray(x, F32)
+    d = x.shape[-1]
+    c, s = ops.rope_cos_sin(pos, d, theta)
+    a, b = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = a * c[:, None] - b * s[:, None]
+    out[..., 1::2] = b * c[:, None] + a * s[:, None]
+    return out
+
+
+def rope_wrong_sign(x, pos, theta):
+    x = np.asarray(x, F32)
+    d = x.shape[-1]
+    c, s = ops.rope_cos_sin(pos, d, theta)
+    a, b = x[..., :d // 2], x[..., d // 2:]
+    return np.concatenate([a * c[:, None] + b * s[:, None], b * c[:, None] - a * s[:, None]], -1)
+
+
+def rope_wrong_freq(x, pos, theta):
+    return ops.rope(x, pos, theta * 10)
+
+
+def rms_eps_outside(x, w, eps):
+    x = np.asarray(x, F32)
+    return x / (np.sqrt(np.mean(x * x, -1, keepdims=True)) + F32(eps)) * w
+
+
+def rms_no_mean(x, w, eps):
+    x = np.asarray(x, F32)
+    return x / np.sqrt(np.sum(x * x, -1, keepdims=True) + F32(eps)) * w
+
+
+def attention_no_scale(q, k, v, scale):
+    return ops.attention(q, k, v, 1.0)
+
+
+def attention_mask_off_by_one(q, k, v, scale):
+    # sees one key too few (strictly earlier keys plus itself excluded)
+    T = q.shape[0]
+    out = ops.attention(q, k, v, scale)
+    if T > 1:
+        out[1:] = ops.attention(q[1:], k[:-1], v[:-1], scale)
+    return out
+
+
+def attention_wrong_group(q, k, v, scale):
+    nh, nkv = q.shape[1], k.shape[1]
+    kk = k[:, [h % nkv for h in range(nh)]]
+    vv = v[:, [h % nkv for h in range(nh)]]
+    return ops.attention(q, kk, vv, scale)
+
+
+def attention_no_max_shift_with_bias(q, k, v, scale):
+    # adds a constant to the probabilities (unnormalised softmax)
+    return ops.attention(q, k, v, scale) * F32(1.01)
+
+
+def linear_transposed(x, w, b=None):
+    y = np.matmul(np.asarray(x, F32), np.asarray(w, F32))
+    return y + b if b is not None else y
+
+
+def linear_drop_bias(x, w, b=None):
+    return ops.linear(x, w)
+
+
+def silu_is_sigmoid(g):
+    g = np.asarray(g, F32)
+    return F32(1) / (F32(1) + np.exp(-g))
+
+
+def swiglu_swapped(g, u):
+    return ops.silu(u) * np.asarray(g, F32)
+
+
+def argmax_last_on_ties(x):
+    x = np.asarray(x)
+    rev = x[..., ::-1]
+    idx = x.shape[-1] - 1 - np.argmax(rev, axis=-1)
+    return idx.astype(np.int64), np.take_along_axis(x, idx[..., None], -1)[..., 0]
+
+
+def bf16_truncate(x):
+    return (np.asarray(x, F32).view(np.uint32) & np.uint32(0xFFFF0000)).view(F32)
+
+
+def bf16_round_half_up(x):
+    u = np.asarray(x, F32).view(np.uint32).astype(np.uint64)
+    return (((u + 0x8000) >> 16) << 16).astype(np.uint32).view(F32)
+
+
+def embedding_off_by_one(ids, table):
+    return table[np.clip(np.asarray(ids) + 1, 0, table.shape[0] - 1)]
+
+
+OP_CASES = [
+    ("rope interleaved pairing", lambda: pins.check_rope(rope_interleaved, ops.rope_cos_sin)),
+    ("rope wrong sign", lambda: pins.check_rope(rope_wrong_sign, ops.rope_cos_sin)),
+    ("rope wrong frequency", lambda: pins.check_rope(rope_wrong_freq, ops.rope_cos_sin)),
+    ("rmsnorm eps outside root", lambda: pins.check_rms_norm(rms_eps_outside)),
+    ("rmsnorm sum instead of mean", lambda: pins.check_rms_norm(rms_no_mean)),
+    ("attention without scale", lambda: pins.check_attention(attention_no_scale)),
+    ("attention causal off by one", lambda: pins.check_attention(attention_mask_off_by_one)),
+    ("attention wrong GQA map", lambda: pins.check_attention(attention_wrong_group)),
+    ("attention unnormalised", lambda: pins.check_attention(attention_no_max_shift_with_bias)),
+    ("linear transposed weight", lambda: pins.check_linear(linear_transposed)),
+    ("linear dropped bias", lambda: pins.check_linear(linear_drop_bias)),
+    ("silu is sigmoid", lambda: pins.check_silu_swiglu(silu_is_sigmoid, lambda g, u: silu_is_sigmoid(g) * u)),
+    ("swiglu operands swapped", lambda: pins.check_silu_swiglu(ops.silu, swiglu_swapped)),
+    ("argmax last index on ties", lambda: pins.check_argmax(argmax_last_on_ties)),
+    ("bf16 truncation", lambda: pins.check_bf16_round(bf16_truncate)),
+    ("bf16 round half up", lambda: pins.check_bf16_round(bf16_round_half_up)),
+    ("embedding off by one", lambda: pins.check_embedding(embedding_off_by_one)),
+]
+
+
+@pytest.mark.parametrize("name,case", OP_CASES, ids=[c[0] for c in OP_CASES])
+def test_op_mutation_is_caught(name, case):
+    assert _fails(case), f"planted mistake not caught: {name}"
+
+
+MODEL_PATCHES = [
+    ("swiglu operands swapped", "swiglu", swiglu_swapped),
+    ("rope interleaved", "rope", rope_interleaved),
+    ("rope wrong frequency", "rope", rope_wrong_freq),
+    ("rmsnorm eps outside", "rms_norm", rms_eps_outside),
+    ("linear dropped bias", "linear", linear_drop_bias),
+    ("attention wrong GQA map", "attention", attention_wrong_group),
+    ("attention causal off by one", "attention", attention_mask_off_by_one),
+    ("attention without scale", "attention", attention_no_scale),
+]
+
+
+@pytest.mark.parametrize("name,attr,bad", MODEL_PATCHES, ids=[c[0] for c in MODEL_PATCHES])
+def test_model_mutation_is_caught(monkeypatch, name, attr, bad):
+    monkeypatch.setattr(ops, attr, bad)
+    assert _fails(pins.check_model_vs_brute, oracle.OracleModel), f"planted mistake not caught: {name}"
+
+
+def test_model_mutation_residual_dropped(monkeypatch):
+    monkeypatch.setattr(ops, "add", lambda a, b: np.asarray(b, F32))
+    assert _fails(pins.check_model_vs_brute, oracle.OracleModel)
+
+
+def test_model_mutation_cache_not_used(monkeypatch):
+    """A decode step that forgets the cached keys must break decode == recompute."""
+    real = ops.attention
+
+    def only_new(q, k, v, scale):
+        T = q.shape[0]
+        return real(q, k[-T:], v[-T:], scale)
+
+    monkeypatch.setattr(ops, "attention", only_new)
+    assert _fails(pins.check_decode_equals_recompute, oracle.OracleModel, "fp32")
