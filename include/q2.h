@@ -1,0 +1,228 @@
+/*
+ * q2.h -- C ABI of a Qwen2 decoder forward for AMD Instinct MI355X (gfx950).
+ *
+ * The library exports one call per operator of the decoder and a model driver
+ * that owns the weights, the activation buffers and the KV cache.  The
+ * operator set follows "LLAISYS 训练营结项报告" (section 3.2, third layer:
+ * add, argmax, embedding, linear, rms_norm, rope, self_attention, swiglu,
+ * rearrange) and the model follows its fourth layer (weights, intermediate
+ * buffers and KV cache resident on the device, KV cache written with
+ * rearrange).  Every operator is a hand-written HIP kernel.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are passed as q2_tensor descriptors: a device pointer, a dtype,
+ *    the rank and per-dimension sizes and strides (in elements, not bytes).
+ *    The caller owns every tensor; no call allocates or frees caller memory.
+ *  - Unless a call says otherwise the last dimension must have stride 1 and
+ *    the outer dimensions may have any non-negative strides.
+ *  - Arithmetic is float32 whatever the storage type ("low precision storage,
+ *    float compute, low precision write-back", section 3.3 item 3 of the same
+ *    report).  bf16 results are rounded to nearest, ties to even.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call is
+ *    asynchronous on that stream; the caller synchronises.
+ *  - Every call returns a q2_status.  Arguments are validated on the host
+ *    before anything is launched; a call that fails validation launches
+ *    nothing and leaves its outputs untouched.  There is no fallback path:
+ *    unsupported shapes, dtypes or strides are errors.  q2_last_error()
+ *    returns a message describing the last failure on the calling thread.
+ *  - Inputs are assumed finite.  Results for NaN inputs are unspecified.
+ */
+#ifndef Q2_H
+#define Q2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  Q2_OK = 0,
+  Q2_EINVAL = -1,  /* null pointer, bad count, bad name */
+  Q2_EDTYPE = -2,  /* dtype not supported by the call or mismatched */
+  Q2_ESHAPE = -3,  /* sizes inconsistent with each other or with the model */
+  Q2_ESTRIDE = -4, /* layout not supported (e.g. last dim not contiguous) */
+  Q2_ENOMEM = -5,  /* device allocation failed (model creation only) */
+  Q2_EHIP = -6,    /* a HIP runtime call failed; see q2_last_error() */
+  Q2_ESTATE = -7   /* model state does not allow the call (capacity, batch) */
+} q2_status;
+
+typedef enum { Q2_F32 = 0, Q2_BF16 = 1, Q2_I64 = 2 } q2_dtype;
+
+#define Q2_MAX_DIMS 5
+
+typedef struct {
+  void* data;                    /* device pointer */
+  int32_t dtype;                 /* q2_dtype */
+  int32_t ndim;                  /* 1 .. Q2_MAX_DIMS */
+  int64_t shape[Q2_MAX_DIMS];
+  int64_t stride[Q2_MAX_DIMS];   /* in elements */
+} q2_tensor;
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* q2_last_error(void);
+
+/* Library version string. */
+const char* q2_version(void);
+
+/* ------------------------------------------------------------------------
+ * Operators
+ * ---------------------------------------------------------------------- */
+
+/* out[n, :] = weight[ids[n], :]  (section 3.2, embedding).
+ * ids: [N] int64.  weight: [V, H] f32/bf16.  out: [N, H], same dtype.
+ * Bit-exact copy.  Ids outside [0, V) produce a zero row (no fault). */
+q2_status q2_embedding(const q2_tensor* out, const q2_tensor* ids, const q2_tensor* weight,
+                       void* stream);
+
+/* out = in W^T (+ bias)  (section 3.2, linear; bias optional).
+ * in: [M, K] or [B, T, K] (flattened to M rows); weight: [N, K] row-major
+ * ([out features, in features]); bias: [N] or NULL; out: [M, N] / [B, T, N].
+ * dtype: all f32, or in/weight/bias bf16 with out bf16 or f32.  bf16 path:
+ * MFMA with float32 accumulation; K must be a multiple of 8 and rows and
+ * pointers 16-byte aligned.  Rows of `in` and `out` may be strided. */
+q2_status q2_linear(const q2_tensor* out, const q2_tensor* in, const q2_tensor* weight,
+                    const q2_tensor* bias, void* stream);
+
+/* out = in / sqrt(mean(in^2) + eps) * weight over the last dimension
+ * (section 3.2, rms_norm; epsilon inside the root).  in/out: [..., H];
+ * weight: [H]; all the same dtype (f32 or bf16).  The output is rounded once. */
+q2_status q2_rms_norm(const q2_tensor* out, const q2_tensor* in, const q2_tensor* weight,
+                      float eps, void* stream);
+
+/* Rotary position embedding, rotate-half pairing (section 3.2, rope):
+ * for j < d/2, a = in[t,h,j], b = in[t,h,j+d/2], angle = pos[t] * theta^(-2j/d),
+ * out[t,h,j] = a cos - b sin, out[t,h,j+d/2] = b cos + a sin.
+ * in/out: [T, nh, d] (or [B, T, nh, d] with pos [B, T] or [T]); pos int64.
+ * cos/sin are evaluated from a float64 angle and rounded to float32.
+ * out may alias in. */
+q2_status q2_rope(const q2_tensor* out, const q2_tensor* in, const q2_tensor* pos, float theta,
+                  void* stream);
+
+/* Causal grouped-query attention (section 3.2, self_attention; the scaled
+ * Q K^T -> causal mask -> stable softmax -> times V sequence of the Day-0
+ * adaptation article, step 5).
+ * q: [T, nh, d] or [B, T, nh, d]; k, v: [S, nkv, d] or [B, S, nkv, d] with
+ * S >= T; out: same shape as q.  Query t (absolute position S - T + t) sees
+ * keys j <= S - T + t.  Query head h reads KV head h / (nh / nkv).
+ * scores = (q . k) * scale, softmax in float32.  k and v may be strided views
+ * (e.g. of a KV cache laid out [B, nkv, S_max, d]); their last dim must be
+ * contiguous.  dtype f32 (any d <= 256) or bf16 (d = 128 only).
+ * The library keeps a per-device scratch buffer (allocated on first use) for
+ * split-KV partial results. */
+q2_status q2_self_attention(const q2_tensor* out, const q2_tensor* q, const q2_tensor* k,
+                            const q2_tensor* v, float scale, void* stream);
+
+/* out = silu(gate) * up, silu(g) = g / (1 + exp(-g))  (section 3.2, swiglu).
+ * Same shape [..., I] and dtype for all three. */
+q2_status q2_swiglu(const q2_tensor* out, const q2_tensor* gate, const q2_tensor* up,
+                    void* stream);
+
+/* c = a + b element-wise (section 3.2, add).  Same shape and dtype. c may alias a or b. */
+q2_status q2_add(const q2_tensor* c, const q2_tensor* a, const q2_tensor* b, void* stream);
+
+/* Row-wise maximum and its index, lowest index on ties (section 3.2 argmax;
+ * section 4.3 item 4: the best score travels with its token id).
+ * vals: [V] or [B, V] f32/bf16; max_idx: [] / [B] int64 (shape [1] accepted for
+ * a single row); max_val: same count, f32.  max_idx is used as the reduction
+ * accumulator, so it must not alias vals.  Bit-exact. */
+q2_status q2_argmax(const q2_tensor* max_idx, const q2_tensor* max_val, const q2_tensor* vals,
+                    void* stream);
+
+/* out[...] = in[...] for two tensors of the same shape and dtype with any
+ * strides (section 3.2 rearrange: contiguous fast path plus a general
+ * stride-aware copy).  Bit-exact.  Any dtype, up to 5 dims, strides >= 0;
+ * overlapping in/out is undefined. */
+q2_status q2_rearrange(const q2_tensor* out, const q2_tensor* in, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Model driver (section 3.2, fourth layer; section 3.3 item 4: per-device
+ * handles and intermediate buffers are created once and reused).
+ * ---------------------------------------------------------------------- */
+
+typedef struct q2_model q2_model;
+
+typedef struct {
+  int32_t dtype;        /* Q2_F32 or Q2_BF16 (weights, activations, KV cache) */
+  int32_t nlayer;
+  int32_t hidden;       /* H */
+  int32_t nh;           /* query heads */
+  int32_t nkv;          /* key/value heads, divides nh */
+  int32_t dh;           /* head dim (bf16: 128; f32: even, <= 256) */
+  int32_t inter;        /* SwiGLU intermediate size */
+  int32_t vocab;
+  int32_t max_seq;      /* KV-cache capacity per sequence */
+  int32_t max_batch;    /* sequences per call, at most */
+  float eps;            /* RMSNorm epsilon */
+  float theta;          /* RoPE base */
+} q2_config;
+
+/* Create a model on `device`: allocates the packed weights, the KV cache
+ * (K and V each [nlayer][max_batch][nkv][max_seq][dh]), the RoPE cos/sin
+ * table and the activation arena, sized for max_batch x max_seq.  Weights
+ * start zeroed.  Returns Q2_ENOMEM if the device cannot hold it. */
+q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_model** out);
+
+/* Bytes of device memory the model holds. */
+q2_status q2_model_device_bytes(const q2_model* m, size_t* bytes);
+
+/* Copy one weight tensor (device memory, the model's dtype, contiguous) into
+ * the model's packed layout.  Names and shapes (Hugging Face Qwen2 naming,
+ * layer = -1 for the global tensors):
+ *   embed_tokens [V,H], lm_head [V,H], norm [H]                  (layer -1)
+ *   input_layernorm [H], post_attention_layernorm [H],
+ *   q_proj.weight [nh*d,H], q_proj.bias [nh*d], k_proj.weight [nkv*d,H],
+ *   k_proj.bias [nkv*d], v_proj.weight [nkv*d,H], v_proj.bias [nkv*d],
+ *   o_proj.weight [H,nh*d], gate_proj.weight [I,H], up_proj.weight [I,H],
+ *   down_proj.weight [H,I]                                      (layer 0..L-1)
+ * The source may be freed once the stream has passed this call. */
+q2_status q2_model_load_weight(q2_model* m, const char* name, int32_t layer, const q2_tensor* src,
+                               void* stream);
+
+/* Run ids [B, T] (int64) at positions len .. len+T-1 of every sequence, where
+ * len is the current cached length (0 after create/reset), then len += T.
+ * next: [B] int64 greedy tokens of the last position.  logits: NULL or
+ * [B, V] f32 (last position).  B must not exceed max_batch and must equal
+ * the batch of earlier calls since the last reset; len + T must not exceed
+ * max_seq (else Q2_ESTATE and nothing changes). */
+q2_status q2_model_prefill(q2_model* m, const q2_tensor* ids, const q2_tensor* next,
+                           const q2_tensor* logits, void* stream);
+
+/* One decode step: ids [B] int64 at position len; same outputs as prefill.
+ * Replays a HIP graph captured once per batch size. */
+q2_status q2_model_decode(q2_model* m, const q2_tensor* ids, const q2_tensor* next,
+                          const q2_tensor* logits, void* stream);
+
+/* Greedy generation: prefill prompt [B, T], then `steps` decode steps fed
+ * on the device with the previous step's argmax.  out_ids: [B, steps + 1]
+ * int64; column 0 is the prefill's token, column s the token of decode step s.
+ * Needs len + T + steps <= max_seq. */
+q2_status q2_model_generate(q2_model* m, const q2_tensor* prompt, int32_t steps,
+                            const q2_tensor* out_ids, void* stream);
+
+/* Continue greedy generation from the current state: `steps` decode steps,
+ * each fed on the device with the previous step's token (the token the last
+ * prefill, decode or continue call produced).  out_ids: NULL or [B, steps]
+ * int64, column s - 1 holding the token of step s.  Needs len >= 1 and
+ * len + steps <= max_seq. */
+q2_status q2_model_continue(q2_model* m, int32_t steps, const q2_tensor* out_ids, void* stream);
+
+/* Describe layer `layer`'s cache as tensors k, v of shape
+ * [max_batch, max_seq, nkv, dh] (strided views of the [B][nkv][S][d] layout). */
+q2_status q2_model_kv_view(q2_model* m, int32_t layer, q2_tensor* k, q2_tensor* v);
+
+/* Cached length (positions per sequence). */
+q2_status q2_model_length(const q2_model* m, int32_t* len);
+
+/* Forget the cached sequences (len = 0).  Does not touch device memory. */
+q2_status q2_model_reset(q2_model* m);
+
+/* Free everything the model holds.  Synchronises the device first. */
+void q2_model_destroy(q2_model* m);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q2_H */

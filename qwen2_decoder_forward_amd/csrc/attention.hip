@@ -1,0 +1,484 @@
+// Causal grouped-query attention: scores = (q . k) * scale, causal mask,
+// max-subtracted softmax in float32, probabilities times v.
+//
+// bf16, d = 128, two kernels:
+//  * attn_decode  few query rows per KV head (T * group <= 16, the decode
+//                 step): one workgroup per (sequence, KV head, key chunk).  All
+//                 query heads of the group share each K/V load.  Q K^T runs
+//                 on MFMA with K rows streamed straight from memory as the A
+//                 operand; P V runs on MFMA with V transposed through LDS.
+//                 Chunks beyond one are merged by attn_combine (split-KV).
+//  * attn_prefill 64 queries of one head per workgroup (16 per wave), K and
+//                 V^T tiles of 64 keys staged in LDS, online softmax.
+// float32, any d <= 256: attn_f32, one wave per (query, head).
+//
+// MFMA layout facts used below (16x16 tiles): the A operand lane l holds row
+// l%16, the B operand lane l holds column l%16, both with the reduction
+// index block l/16; the result lane l holds rows 4*(l/16)+i, column l%16.
+// Q K^T is computed transposed (S^T = K Q^T), so a lane's four results are
+// four consecutive keys of one query: exactly the B-operand layout of the
+// 16x16x16 MFMA that computes O^T = V^T P^T.  No shuffles are needed between
+// the two products.
+#include "attention.hpp"
+
+namespace q2 {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int VT_DEC = 20;    // bf16 per V^T LDS row in attn_decode: 16 keys + pad (40 B rows)
+constexpr int K_ROW = D + 8;  // bf16 per K LDS row in attn_prefill (272 B: conflict-free b128 reads)
+constexpr int VT_PRE = 72;    // bf16 per V^T LDS row in attn_prefill: 64 keys + pad
+constexpr float NEG_INF = -__builtin_huge_valf();
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
+  bf16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+__device__ __forceinline__ short4_t as_short4(uint2 v) {
+  short4_t r;
+  __builtin_memcpy(&r, &v, 8);
+  return r;
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Order the wave's own LDS writes before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Element i (0..7) of a 16-byte vector of bf16.
+__device__ __forceinline__ uint32_t elem16(const uint4& v, int i) {
+  const uint32_t w = (&v.x)[i >> 1];
+  return (i & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// Write four keys' 8-element d-chunks transposed: row (d0 + i) gets the 4 keys
+// at column `col` (4 consecutive bf16 = 8 bytes).
+__device__ __forceinline__ void store_vt4(uint16_t* base, int row_stride, int d0, int col, const uint4 (&v)[4]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint2 w;
+    w.x = elem16(v[0], i) | (elem16(v[1], i) << 16);
+    w.y = elem16(v[2], i) | (elem16(v[3], i) << 16);
+    *reinterpret_cast<uint2*>(base + (d0 + i) * row_stride + col) = w;
+  }
+}
+
+// Online-softmax update of one column held by 4 lane groups x 4 values.
+// s[] are masked (-inf) scaled scores; returns alpha and writes probabilities.
+__device__ __forceinline__ float softmax_step(float* s, int n, float& m_run, float& l_run) {
+  float mt = NEG_INF;
+  for (int i = 0; i < n; ++i) mt = fmaxf(mt, s[i]);
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float m_new = fmaxf(m_run, mt);
+  const float base = (m_new == NEG_INF) ? 0.f : m_new;
+  const float alpha = (m_run == NEG_INF) ? 0.f : __expf(m_run - base);
+  float ps = 0.f;
+  for (int i = 0; i < n; ++i) {
+    const float p = (s[i] == NEG_INF) ? 0.f : __expf(s[i] - base);
+    s[i] = p;
+    ps += p;
+  }
+  ps += __shfl_xor(ps, 16, 64);
+  ps += __shfl_xor(ps, 32, 64);
+  l_run = l_run * alpha + ps;
+  m_run = m_new;
+  return alpha;
+}
+
+// ------------------------------------------------------------------ decode (split-KV)
+
+__global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk, int nsplit,
+                                                          float* __restrict__ part_o, float2* __restrict__ part_ml) {
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[4][D * VT_DEC];
+  __shared__ float sO[4][D][17];
+  __shared__ float sM[4][16], sL[4][16];
+
+  const int split = blockIdx.x;
+  const int bg = blockIdx.y;
+  const int b = bg / a.nkv;
+  const int g = bg - b * a.nkv;
+  const int group = a.nh / a.nkv;
+  const int R = a.T * group;
+  const int S = a.d_len ? (*a.d_len + a.T) : a.S;
+  const int P = S - a.T;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int G = lane >> 4;
+  const int j_begin = split * chunk;
+  const int j_end = min(j_begin + chunk, S);
+
+  // query row `col` of this KV head's group: token t, head g*group + hh
+  const bool rvalid = col < R;
+  const int t = rvalid ? col / group : 0;
+  const int head = g * group + (rvalid ? col - t * group : 0);
+  const int lim = rvalid ? P + t : S - 1;
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_bs + t * a.q_ts + head * a.q_hs;
+  uint4 qf[4];
+  const uint4 z = {0, 0, 0, 0};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) qf[kk] = rvalid ? ld16(qp + 32 * kk + 8 * G) : z;
+
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_bs + g * a.k_hs;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.v_bs + g * a.v_hs;
+  uint16_t* vt = sVt[wave];
+
+  float m_run = NEG_INF, l_run = 0.f;
+  floatx4_t oacc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) oacc[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int j0 = j_begin + 16 * wave; j0 < j_end; j0 += 64) {
+    // K rows j0 + col: 4 x 16 B (d = 32kk + 8G .. +8); V rows j0 + 4G + s, d-chunk 8*col
+    const int key = j0 + col;
+    uint4 kf[4], vf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kf[kk] = key < j_end ? ld16(kbase + static_cast<int64_t>(key) * a.k_ss + 32 * kk + 8 * G) : z;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int vk = j0 + 4 * G + s;
+      vf[s] = vk < j_end ? ld16(vbase + static_cast<int64_t>(vk) * a.v_ss + 8 * col) : z;
+    }
+    floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kk]), as_bf16x8(qf[kk]), sacc, 0, 0, 0);
+    store_vt4(vt, VT_DEC, 8 * col, 4 * G, vf);
+
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kj = j0 + 4 * G + i;
+      s[i] = (kj < j_end && kj <= lim) ? sacc[i] * a.scale : NEG_INF;
+    }
+    const float alpha = softmax_step(s, 4, m_run, l_run);
+    uint2 pw;
+    pw.x = pack_bf2(s[0], s[1]);
+    pw.y = pack_bf2(s[2], s[3]);
+    const short4_t pf = as_short4(pw);
+    wave_lds_sync();
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      oacc[dt][0] *= alpha; oacc[dt][1] *= alpha; oacc[dt][2] *= alpha; oacc[dt][3] *= alpha;
+      const uint2 vv = *reinterpret_cast<const uint2*>(vt + (16 * dt + col) * VT_DEC + 4 * G);
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(vv), pf, oacc[dt], 0, 0, 0);
+    }
+    wave_lds_sync();
+  }
+
+  // merge the four waves
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sO[wave][16 * dt + 4 * G + i][col] = oacc[dt][i];
+  if (G == 0) {
+    sM[wave][col] = m_run;
+    sL[wave][col] = l_run;
+  }
+  __syncthreads();
+  const int r = threadIdx.x >> 4;          // row 0..15
+  const int d0 = (threadIdx.x & 15) * 8;   // 8 consecutive d
+  float mw[4];
+  float M = NEG_INF;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    mw[w] = sM[w][r];
+    M = fmaxf(M, mw[w]);
+  }
+  const float base = (M == NEG_INF) ? 0.f : M;
+  float L = 0.f, o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float f = (mw[w] == NEG_INF) ? 0.f : __expf(mw[w] - base);
+    L += f * sL[w][r];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] += f * sO[w][d0 + i][r];
+  }
+  if (nsplit == 1) {
+    if (r < R) {
+      const int tt = r / group;
+      const int hh = g * group + (r - tt * group);
+      uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.o_bs + tt * a.o_ts + hh * a.o_hs + d0;
+      const float inv = 1.f / L;
+      uint4 w;
+      w.x = pack_bf2(o[0] * inv, o[1] * inv);
+      w.y = pack_bf2(o[2] * inv, o[3] * inv);
+      w.z = pack_bf2(o[4] * inv, o[5] * inv);
+      w.w = pack_bf2(o[6] * inv, o[7] * inv);
+      *reinterpret_cast<uint4*>(op) = w;
+    }
+    return;
+  }
+  const int64_t slot = (static_cast<int64_t>(bg) * nsplit + split) * 16 + r;
+  float* po = part_o + slot * D + d0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) po[i] = o[i];
+  if ((threadIdx.x & 15) == 0) part_ml[slot] = make_float2(M, L);
+}
+
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nsplit, const float* __restrict__ part_o,
+                                                           const float2* __restrict__ part_ml) {
+  const int bg = blockIdx.x;
+  const int b = bg / a.nkv;
+  const int g = bg - b * a.nkv;
+  const int group = a.nh / a.nkv;
+  const int R = a.T * group;
+  const int r = threadIdx.x >> 4;
+  const int d0 = (threadIdx.x & 15) * 8;
+  if (r >= R) return;
+  const int64_t base_slot = static_cast<int64_t>(bg) * nsplit * 16 + r;
+  float M = NEG_INF;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[base_slot + s * 16].x);
+  const float base = (M == NEG_INF) ? 0.f : M;
+  float L = 0.f, o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float2 ml = part_ml[base_slot + s * 16];
+    if (ml.x == NEG_INF) continue;
+    const float f = __expf(ml.x - base);
+    L += f * ml.y;
+    const float* po = part_o + (base_slot + s * 16) * D + d0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] += f * po[i];
+  }
+  const int tt = r / group;
+  const int hh = g * group + (r - tt * group);
+  uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.o_bs + tt * a.o_ts + hh * a.o_hs + d0;
+  const float inv = 1.f / L;
+  uint4 w;
+  w.x = pack_bf2(o[0] * inv, o[1] * inv);
+  w.y = pack_bf2(o[2] * inv, o[3] * inv);
+  w.z = pack_bf2(o[4] * inv, o[5] * inv);
+  w.w = pack_bf2(o[6] * inv, o[7] * inv);
+  *reinterpret_cast<uint4*>(op) = w;
+}
+
+// ------------------------------------------------------------------ prefill (flash)
+
+__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[64 * K_ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * VT_PRE];
+
+  const int nqb = (a.T + 63) / 64;
+  const int qb = nqb - 1 - static_cast<int>(blockIdx.x);  // longest rows first
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int group = a.nh / a.nkv;
+  const int g = h / group;
+  const int S = a.d_len ? (*a.d_len + a.T) : a.S;
+  const int P = S - a.T;
+  const int q0 = qb * 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;
+  const int G = lane >> 4;
+
+  const int tq = q0 + 16 * wave + col;
+  const bool qvalid = tq < a.T;
+  const int lim = qvalid ? P + tq : S - 1;
+  const uint4 z = {0, 0, 0, 0};
+  uint4 qf[4];
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_bs + static_cast<int64_t>(qvalid ? tq : 0) * a.q_ts + h * a.q_hs;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) qf[kk] = qvalid ? ld16(qp + 32 * kk + 8 * G) : z;
+
+  const int kv_end = min(S, P + min(q0 + 64, a.T));
+  const int wave_first = q0 + 16 * wave;
+  const bool wave_active = wave_first < a.T;
+  const int wave_lim = P + min(wave_first + 15, a.T - 1);
+
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_bs + g * a.k_hs;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.v_bs + g * a.v_hs;
+
+  float m_run = NEG_INF, l_run = 0.f;
+  floatx4_t oacc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) oacc[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int j0 = 0; j0 < kv_end; j0 += 64) {
+    __syncthreads();  // the previous tile is consumed
+    {
+      const int r = tid >> 4;
+      const int c8 = (tid & 15) * 8;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int key = j0 + r + 16 * s;
+        const uint4 kv = key < kv_end ? ld16(kbase + static_cast<int64_t>(key) * a.k_ss + c8) : z;
+        *reinterpret_cast<uint4*>(&sK[(r + 16 * s) * K_ROW + c8]) = kv;
+      }
+      uint4 vf[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int key = j0 + 4 * r + s;
+        vf[s] = key < kv_end ? ld16(vbase + static_cast<int64_t>(key) * a.v_ss + c8) : z;
+      }
+      store_vt4(sVt, VT_PRE, c8, 4 * r, vf);
+    }
+    __syncthreads();
+    if (!wave_active || wave_lim < j0) continue;
+
+    floatx4_t sacc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      sacc[kt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint4 kfr = *reinterpret_cast<const uint4*>(&sK[(kt * 16 + col) * K_ROW + 32 * kk + 8 * G]);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kfr), as_bf16x8(qf[kk]), sacc[kt], 0, 0, 0);
+      }
+    }
+    float s[16];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kj = j0 + kt * 16 + 4 * G + i;
+        s[kt * 4 + i] = (kj < kv_end && kj <= lim) ? sacc[kt][i] * a.scale : NEG_INF;
+      }
+    const float alpha = softmax_step(s, 16, m_run, l_run);
+    short4_t pf[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      uint2 pw;
+      pw.x = pack_bf2(s[kt * 4 + 0], s[kt * 4 + 1]);
+      pw.y = pack_bf2(s[kt * 4 + 2], s[kt * 4 + 3]);
+      pf[kt] = as_short4(pw);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      oacc[dt][0] *= alpha; oacc[dt][1] *= alpha; oacc[dt][2] *= alpha; oacc[dt][3] *= alpha;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const uint2 vv = *reinterpret_cast<const uint2*>(&sVt[(16 * dt + col) * VT_PRE + kt * 16 + 4 * G]);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(vv), pf[kt], oacc[dt], 0, 0, 0);
+      }
+    }
+  }
+  if (!qvalid) return;
+  const float inv = 1.f / l_run;
+  uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.o_bs + static_cast<int64_t>(tq) * a.o_ts + h * a.o_hs;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    uint2 w;
+    w.x = pack_bf2(oacc[dt][0] * inv, oacc[dt][1] * inv);
+    w.y = pack_bf2(oacc[dt][2] * inv, oacc[dt][3] * inv);
+    *reinterpret_cast<uint2*>(op + 16 * dt + 4 * G) = w;
+  }
+}
+
+// ------------------------------------------------------------------ float32
+
+__global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
+  extern __shared__ float sp[];
+  const int t = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int group = a.nh / a.nkv;
+  const int g = h / group;
+  const int S = a.d_len ? (*a.d_len + a.T) : a.S;
+  const int vis = S - a.T + t + 1;
+  const float* q = static_cast<const float*>(a.q) + b * a.q_bs + static_cast<int64_t>(t) * a.q_ts + h * a.q_hs;
+  const float* kb = static_cast<const float*>(a.k) + b * a.k_bs + g * a.k_hs;
+  const float* vb = static_cast<const float*>(a.v) + b * a.v_bs + g * a.v_hs;
+  float mx = NEG_INF;
+  for (int j = lane; j < vis; j += 64) {
+    const float* k = kb + static_cast<int64_t>(j) * a.k_ss;
+    float s = 0.f;
+    for (int i = 0; i < a.d; ++i) s = fmaf(q[i], k[i], s);
+    s *= a.scale;
+    sp[j] = s;
+    mx = fmaxf(mx, s);
+  }
+  mx = wave_max(mx);
+  float sum = 0.f;
+  for (int j = lane; j < vis; j += 64) {
+    const float p = __expf(sp[j] - mx);
+    sp[j] = p;
+    sum += p;
+  }
+  sum = wave_sum(sum);
+  __syncthreads();
+  float* o = static_cast<float*>(a.o) + b * a.o_bs + static_cast<int64_t>(t) * a.o_ts + h * a.o_hs;
+  for (int i = lane; i < a.d; i += 64) {
+    float acc = 0.f;
+    for (int j = 0; j < vis; ++j) acc = fmaf(sp[j], vb[static_cast<int64_t>(j) * a.v_ss + i], acc);
+    o[i] = acc / sum;
+  }
+}
+
+struct DecodePlan {
+  int chunk, nsplit;
+};
+
+DecodePlan plan_decode(int B, int s_max, int nkv) {
+  DecodePlan p;
+  const int64_t heads = static_cast<int64_t>(B) * nkv;
+  int chunk = 64;
+  while (chunk < 1024 && heads * cdiv(s_max, chunk) > 1024) chunk *= 2;
+  p.chunk = chunk;
+  p.nsplit = cdiv(s_max, chunk);
+  if (p.nsplit < 1) p.nsplit = 1;
+  return p;
+}
+
+}  // namespace
+
+size_t attention_scratch_bytes(int B, int T, int s_max, int nh, int nkv, int d) {
+  if (d != D || T * (nh / nkv) > 16) return 0;
+  DecodePlan p = plan_decode(B, s_max, nkv);
+  if (p.nsplit == 1) return 0;
+  const size_t slots = static_cast<size_t>(B) * nkv * p.nsplit * 16;
+  return slots * (D * sizeof(float) + sizeof(float2));
+}
+
+q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
+  Q2_CHECK(a.d == D, Q2_ESHAPE, "bf16 attention supports head_dim 128 only (got %d)", a.d);
+  if (a.B == 0 || a.T == 0) return Q2_OK;
+  const int group = a.nh / a.nkv;
+  if (a.T * group <= 16) {
+    const int s_max = a.d_len ? a.s_max : a.S;
+    DecodePlan p = plan_decode(a.B, s_max, a.nkv);
+    float* part_o = nullptr;
+    float2* part_ml = nullptr;
+    if (p.nsplit > 1) {
+      const size_t slots = static_cast<size_t>(a.B) * a.nkv * p.nsplit * 16;
+      const size_t need = slots * (D * sizeof(float) + sizeof(float2));
+      Q2_CHECK(a.scratch && a.scratch_bytes >= need, Q2_EINVAL, "attention: split-KV scratch too small");
+      part_o = static_cast<float*>(a.scratch);
+      part_ml = reinterpret_cast<float2*>(part_o + slots * D);
+    }
+    hipLaunchKernelGGL(attn_decode_kernel, dim3(p.nsplit, a.B * a.nkv), dim3(256), 0, s, a, p.chunk, p.nsplit,
+                       part_o, part_ml);
+    Q2_TRY(check_launch("attn_decode"));
+    if (p.nsplit > 1) {
+      hipLaunchKernelGGL(attn_combine_kernel, dim3(a.B * a.nkv), dim3(256), 0, s, a, p.nsplit, part_o, part_ml);
+      Q2_TRY(check_launch("attn_combine"));
+    }
+    return Q2_OK;
+  }
+  hipLaunchKernelGGL(attn_prefill_kernel, dim3(cdiv(a.T, 64), a.nh, a.B), dim3(256), 0, s, a);
+  return check_launch("attn_prefill");
+}
+
+q2_status attention_f32(const AttnArgs& a, hipStream_t s) {
+  Q2_CHECK(a.d <= 256, Q2_ESHAPE, "fp32 attention supports head_dim <= 256");
+  if (a.B == 0 || a.T == 0) return Q2_OK;
+  const int s_max = a.d_len ? a.s_max : a.S;
+  Q2_CHECK(s_max <= 16384, Q2_ESHAPE, "fp32 attention supports at most 16384 keys");
+  hipLaunchKernelGGL(attn_f32_kernel, dim3(a.T, a.nh, a.B), dim3(64), s_max * sizeof(float), s, a);
+  return check_launch("attn_f32");
+}
+
+}  // namespace q2

@@ -1,0 +1,36 @@
+// Causal grouped-query attention kernels (attention.hip).
+#pragma once
+
+#include "common.hpp"
+
+namespace q2 {
+
+// Strides are in elements; the head dimension is contiguous everywhere.
+// Sequence b, query t, head h:     q + b*q_bs + t*q_ts + h*q_hs
+// Sequence b, key j, kv head g:    k + b*k_bs + j*k_ss + g*k_hs   (same for v)
+// Query t sits at absolute position S - T + t and sees keys j <= S - T + t.
+// When d_len is set, S = *d_len + T is read on the device (graph replay);
+// s_max bounds it and sizes the split-KV grid.
+struct AttnArgs {
+  const void* q;
+  int64_t q_bs, q_ts, q_hs;
+  const void* k;
+  int64_t k_bs, k_ss, k_hs;
+  const void* v;
+  int64_t v_bs, v_ss, v_hs;
+  void* o;
+  int64_t o_bs, o_ts, o_hs;
+  int B, T, S, nh, nkv, d;
+  float scale;
+  const int* d_len;
+  int s_max;
+  void* scratch;
+  size_t scratch_bytes;
+};
+
+q2_status attention_bf16(const AttnArgs& a, hipStream_t s);
+q2_status attention_f32(const AttnArgs& a, hipStream_t s);
+// Scratch (bytes) the bf16 split-KV decode path needs for these sizes.
+size_t attention_scratch_bytes(int B, int T, int s_max, int nh, int nkv, int d);
+
+}  // namespace q2

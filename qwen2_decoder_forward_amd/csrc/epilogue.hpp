@@ -1,0 +1,136 @@
+// Fused GEMM epilogues.  Every GEMM kernel of the library hands its float32
+// accumulators to one of these, two adjacent output features at a time.
+//
+// Rounding points follow the operator sequence they replace, so that a fused
+// kernel stores exactly what the unfused chain of operators would store:
+//   STORE   out = rnd(acc + bias)                          (linear)
+//   RESID   x   = rnd(x + rnd(acc))                        (linear, then add)
+//   SWIGLU  a   = rnd(silu(rnd(g)) * rnd(u))               (two linears, then swiglu)
+//   QKV     q/k = rnd(rope(rnd(acc + bias))), v = rnd(acc + bias), with k and
+//           v written straight into the KV cache           (linear, rope, rearrange)
+//   ARGMAX  logits (float32, optional) and a per-row packed (value, index) key
+//           combined with atomicMax                        (linear, argmax)
+//
+// Packed weight layouts the epilogues rely on (built by the model loader):
+//   QKV rows: q heads, then k heads, then v heads, d rows each.  Inside a q
+//   or k head, row 2p holds original row p and row 2p+1 original row p + d/2,
+//   so the two halves of a rotate-half pair are adjacent.  v heads keep the
+//   original order.
+//   gate/up rows: row 2f is gate row f, row 2f+1 is up row f.
+#pragma once
+
+#include "common.hpp"
+
+namespace q2 {
+
+enum EpiKind : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_ARGMAX = 4 };
+
+struct Epi {
+  int kind;
+  int out_f32;            // STORE: output is float32 instead of the storage type
+  void* out;              // STORE / RESID / SWIGLU / QKV(q) / ARGMAX(logits, may be null)
+  int64_t ldo;            // row stride of out, elements
+  const void* bias;       // STORE / QKV: [N] storage type, or null
+  // QKV
+  void* kc;               // K cache of this layer, [B][nkv][S_max][d]
+  void* vc;               // V cache of this layer, same layout
+  int64_t kv_bstride;     // elements between batches
+  int64_t kv_hstride;     // elements between kv heads (= S_max * d)
+  int nh, nkv, dh;
+  int T;                  // tokens per sequence in this call (row m = b * T + t)
+  const int* d_len;       // device cached length (position of t = 0) or null
+  int len0;               // host cached length, used when d_len is null
+  const float2* rope;     // [S_max][d/2] (cos, sin)
+  // ARGMAX
+  unsigned long long* keys;  // [M] packed keys, reset to 0 before the GEMM
+};
+
+template <typename T, int EK>
+__device__ __forceinline__ void epi_pair(const Epi& e, int m, int n, float v0, float v1, bool has1) {
+  using S = St<T>;
+  switch (EK) {
+    case EPI_STORE: {
+      if (e.bias) {
+        v0 += S::ld(static_cast<const T*>(e.bias) + n);
+        if (has1) v1 += S::ld(static_cast<const T*>(e.bias) + n + 1);
+      }
+      if (e.out_f32) {
+        float* o = static_cast<float*>(e.out) + static_cast<int64_t>(m) * e.ldo + n;
+        o[0] = v0;
+        if (has1) o[1] = v1;
+      } else {
+        T* o = static_cast<T*>(e.out) + static_cast<int64_t>(m) * e.ldo + n;
+        S::st(o, v0);
+        if (has1) S::st(o + 1, v1);
+      }
+      break;
+    }
+    case EPI_RESID: {
+      T* o = static_cast<T*>(e.out) + static_cast<int64_t>(m) * e.ldo + n;
+      S::st(o, S::ld(o) + S::rnd(v0));
+      if (has1) S::st(o + 1, S::ld(o + 1) + S::rnd(v1));
+      break;
+    }
+    case EPI_SWIGLU: {
+      T* o = static_cast<T*>(e.out) + static_cast<int64_t>(m) * e.ldo + (n >> 1);
+      S::st(o, silu_f(S::rnd(v0)) * S::rnd(v1));
+      break;
+    }
+    case EPI_QKV: {
+      const T* b = static_cast<const T*>(e.bias);
+      float a = S::rnd(v0 + S::ld(b + n));
+      float c = S::rnd(v1 + S::ld(b + n + 1));
+      const int d = e.dh;
+      const int head = n / d;
+      const int r = n - head * d;
+      const int bt = m / e.T;
+      const int t = m - bt * e.T;
+      const int pos = (e.d_len ? *e.d_len : e.len0) + t;
+      if (head < e.nh + e.nkv) {
+        const int p = r >> 1;
+        const float2 cs = e.rope[static_cast<int64_t>(pos) * (d >> 1) + p];
+        const float ra = S::rnd(a * cs.x - c * cs.y);
+        const float rb = S::rnd(c * cs.x + a * cs.y);
+        T* dst;
+        if (head < e.nh) {
+          dst = static_cast<T*>(e.out) + static_cast<int64_t>(m) * e.ldo + head * d;
+        } else {
+          dst = static_cast<T*>(e.kc) + bt * e.kv_bstride + (head - e.nh) * e.kv_hstride +
+                static_cast<int64_t>(pos) * d;
+        }
+        S::st(dst + p, ra);
+        S::st(dst + p + (d >> 1), rb);
+      } else {
+        T* dst = static_cast<T*>(e.vc) + bt * e.kv_bstride + (head - e.nh - e.nkv) * e.kv_hstride +
+                 static_cast<int64_t>(pos) * d + r;
+        S::st(dst, a);
+        S::st(dst + 1, c);
+      }
+      break;
+    }
+    default:
+      break;
+  }
+}
+
+// Host-side launch descriptors for the GEMM family (gemm.hip).
+// Y[m, n] = sum_k X[m, k] W[n, k], epilogue `epi`; W [N, K], X [M, K] with
+// row strides ldw, ldx.  `scratch` (float32) is needed for split-K runs of
+// the skinny kernel; `scratch_bytes` bounds it.
+struct GemmArgs {
+  const void* W;
+  int64_t ldw;
+  const void* X;
+  int64_t ldx;
+  int M, N, K;
+  Epi epi;
+  void* scratch;
+  size_t scratch_bytes;
+};
+
+q2_status gemm_bf16(const GemmArgs& a, hipStream_t s);
+q2_status gemm_f32(const GemmArgs& a, hipStream_t s);
+// Split-K scratch the skinny path wants for this shape (0 if none).
+size_t gemm_scratch_bytes(int M, int N, int K);
+
+}  // namespace q2

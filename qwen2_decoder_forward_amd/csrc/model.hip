@@ -1,0 +1,725 @@
+// Qwen2 decoder model driver: packed weights, KV cache, activation arena,
+// prefill in token chunks, single-token decode replayed from a HIP graph,
+// and greedy generation with the next token fed back on the device.
+//
+// Per layer (x is the residual stream, stored in the model dtype):
+//   h = rmsnorm(x, w_in)                         rmsnorm kernel
+//   q, K/V cache <- rope(h Wqkv^T + b)           GEMM, QKV epilogue
+//   att = attention(q, K, V)                     attention kernels
+//   x = x + att Wo^T                             GEMM, residual epilogue
+//   h = rmsnorm(x, w_post)                       rmsnorm kernel
+//   act = silu(h Wg^T) * (h Wu^T)                GEMM, SwiGLU epilogue
+//   x = x + act Wd^T                             GEMM, residual epilogue
+// then rmsnorm of each sequence's last row, the LM head GEMM with a fused
+// argmax epilogue, and a finalize kernel that turns the packed argmax keys
+// into token ids, stores them for the next step and resets the keys.
+#include <math.h>
+#include <string.h>
+
+#include <map>
+#include <new>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "attention.hpp"
+#include "epilogue.hpp"
+#include "simple.hpp"
+
+using namespace q2;
+
+struct q2_model {
+  q2_config cfg{};
+  int device = 0;
+  int esize = 2;
+  int qkv_out = 0;
+  int max_tok = 0;   // tokens per forward chunk
+  // device memory
+  char* wmem = nullptr;
+  char* kvmem = nullptr;
+  char* amem = nullptr;
+  size_t wbytes = 0, kvbytes = 0, abytes = 0;
+  // weights
+  void* embed = nullptr;
+  void* lm_head = nullptr;
+  void* w_final = nullptr;
+  struct Layer {
+    void *w_in, *w_post, *w_qkv, *b_qkv, *w_o, *w_gu, *w_d;
+  };
+  std::vector<Layer> layers;
+  // KV cache [L][Bmax][nkv][S][d]
+  void* kc = nullptr;
+  void* vc = nullptr;
+  int64_t kv_lstride = 0, kv_bstride = 0, kv_hstride = 0;
+  float2* rope = nullptr;
+  // arena
+  void *x = nullptr, *h = nullptr, *q = nullptr, *att = nullptr, *act = nullptr, *xl = nullptr;
+  float* logits_buf = nullptr;
+  unsigned long long* keys = nullptr;
+  int64_t* ids_buf = nullptr;
+  int64_t* hist = nullptr;
+  int* d_len = nullptr;
+  void* gscratch = nullptr;
+  size_t gscratch_bytes = 0;
+  void* ascratch = nullptr;
+  size_t ascratch_bytes = 0;
+  // host state
+  int len = 0;
+  int cur_batch = 0;
+  bool len_dirty = true;
+  hipStream_t cap = nullptr;
+  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+};
+
+namespace {
+
+__global__ void set_len_kernel(int* d_len, int v) { *d_len = v; }
+__global__ void advance_len_kernel(int* d_len, int t) { *d_len += t; }
+
+__global__ void copy_ids_kernel(int64_t* dst, int64_t dst_stride, const int64_t* src, int64_t src_stride, int B) {
+  const int b = blockIdx.x * 64 + threadIdx.x;
+  if (b < B) dst[b * dst_stride] = src[b * src_stride];
+}
+
+// next token of each sequence from the packed argmax keys; stores it for the
+// next step (ids_buf), in the history at its position, optionally in `next`;
+// resets the keys for the next LM-head pass.
+__global__ void finalize_kernel(unsigned long long* keys, int64_t* ids_buf, int64_t* hist, int64_t hist_ld,
+                                const int* d_len, int64_t* next, int64_t next_stride, int B) {
+  const int b = threadIdx.x;
+  if (b >= B) return;
+  const int pos = *d_len;
+  const int64_t id = static_cast<int64_t>(argmax_key_index(keys[b]));
+  keys[b] = 0ull;
+  ids_buf[b] = id;
+  hist[b * hist_ld + pos] = id;
+  if (next) next[b * next_stride] = id;
+}
+
+__global__ void copy_hist_kernel(int64_t* out, int64_t ld_out, const int64_t* hist, int64_t hist_ld, int start, int n,
+                                 int B) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n * B) return;
+  const int b = i / n;
+  const int c = i - b * n;
+  out[b * ld_out + c] = hist[b * hist_ld + start + c];
+}
+
+__global__ void copy_logits_kernel(float* out, int64_t ld_out, const float* src, int64_t ld_src, int V, int B) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(V) * B) return;
+  const int b = static_cast<int>(i / V);
+  const int v = static_cast<int>(i - static_cast<int64_t>(b) * V);
+  out[b * ld_out + v] = src[b * ld_src + v];
+}
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+q2_status gemm(const q2_model* m, const GemmArgs& a, hipStream_t s) {
+  return m->cfg.dtype == Q2_BF16 ? gemm_bf16(a, s) : gemm_f32(a, s);
+}
+
+GemmArgs gemm_args(const q2_model* m, const void* W, int64_t ldw, const void* X, int64_t ldx, int M, int N, int K) {
+  GemmArgs a{};
+  a.W = W;
+  a.ldw = ldw;
+  a.X = X;
+  a.ldx = ldx;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.scratch = m->gscratch;
+  a.scratch_bytes = m->gscratch_bytes;
+  return a;
+}
+
+// Transformer layers for B sequences x Tc new tokens whose ids are already
+// embedded in x.  Positions start at the device length.
+template <typename T>
+q2_status run_layers(q2_model* m, int B, int Tc, hipStream_t s) {
+  const q2_config& c = m->cfg;
+  const int M = B * Tc;
+  const int H = c.hidden, d = c.dh, qd = c.nh * c.dh;
+  for (int l = 0; l < c.nlayer; ++l) {
+    const q2_model::Layer& L = m->layers[l];
+    void* kc = static_cast<char*>(m->kc) + l * m->kv_lstride * m->esize;
+    void* vc = static_cast<char*>(m->vc) + l * m->kv_lstride * m->esize;
+    Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->h), H, static_cast<const T*>(m->x), H, static_cast<const T*>(L.w_in),
+                             M, H, c.eps, s));
+    {
+      GemmArgs a = gemm_args(m, L.w_qkv, H, m->h, H, M, m->qkv_out, H);
+      a.epi.kind = EPI_QKV;
+      a.epi.out = m->q;
+      a.epi.ldo = qd;
+      a.epi.bias = L.b_qkv;
+      a.epi.kc = kc;
+      a.epi.vc = vc;
+      a.epi.kv_bstride = m->kv_bstride;
+      a.epi.kv_hstride = m->kv_hstride;
+      a.epi.nh = c.nh;
+      a.epi.nkv = c.nkv;
+      a.epi.dh = d;
+      a.epi.T = Tc;
+      a.epi.d_len = m->d_len;
+      a.epi.rope = m->rope;
+      Q2_TRY(gemm(m, a, s));
+    }
+    {
+      AttnArgs a{};
+      a.q = m->q;
+      a.q_bs = static_cast<int64_t>(Tc) * qd;
+      a.q_ts = qd;
+      a.q_hs = d;
+      a.o = m->att;
+      a.o_bs = a.q_bs;
+      a.o_ts = a.q_ts;
+      a.o_hs = a.q_hs;
+      a.k = kc;
+      a.v = vc;
+      a.k_bs = a.v_bs = m->kv_bstride;
+      a.k_ss = a.v_ss = d;
+      a.k_hs = a.v_hs = m->kv_hstride;
+      a.B = B;
+      a.T = Tc;
+      a.S = m->len + Tc;  // unused when d_len is set
+      a.nh = c.nh;
+      a.nkv = c.nkv;
+      a.d = d;
+      a.scale = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
+      a.d_len = m->d_len;
+      a.s_max = c.max_seq;
+      a.scratch = m->ascratch;
+      a.scratch_bytes = m->ascratch_bytes;
+      Q2_TRY(c.dtype == Q2_BF16 ? attention_bf16(a, s) : attention_f32(a, s));
+    }
+    {
+      GemmArgs a = gemm_args(m, L.w_o, qd, m->att, qd, M, H, qd);
+      a.epi.kind = EPI_RESID;
+      a.epi.out = m->x;
+      a.epi.ldo = H;
+      Q2_TRY(gemm(m, a, s));
+    }
+    Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->h), H, static_cast<const T*>(m->x), H,
+                             static_cast<const T*>(L.w_post), M, H, c.eps, s));
+    {
+      GemmArgs a = gemm_args(m, L.w_gu, H, m->h, H, M, 2 * c.inter, H);
+      a.epi.kind = EPI_SWIGLU;
+      a.epi.out = m->act;
+      a.epi.ldo = c.inter;
+      Q2_TRY(gemm(m, a, s));
+    }
+    {
+      GemmArgs a = gemm_args(m, L.w_d, c.inter, m->act, c.inter, M, H, c.inter);
+      a.epi.kind = EPI_RESID;
+      a.epi.out = m->x;
+      a.epi.ldo = H;
+      Q2_TRY(gemm(m, a, s));
+    }
+  }
+  hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(1), 0, s, m->d_len, Tc);
+  return check_launch("advance_len");
+}
+
+// Final norm of each sequence's last row, LM head with argmax, finalize.
+template <typename T>
+q2_status run_head(q2_model* m, int B, int Tc, float* logits, int64_t ld_logits, int64_t* next, int64_t next_stride,
+                   hipStream_t s) {
+  const q2_config& c = m->cfg;
+  const int H = c.hidden;
+  Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->xl), H, static_cast<const T*>(m->x) + static_cast<int64_t>(Tc - 1) * H,
+                           static_cast<int64_t>(Tc) * H, static_cast<const T*>(m->w_final), B, H, c.eps, s));
+  GemmArgs a = gemm_args(m, m->lm_head, H, m->xl, H, B, c.vocab, H);
+  a.epi.kind = EPI_ARGMAX;
+  a.epi.out = logits;
+  a.epi.ldo = ld_logits;
+  a.epi.keys = m->keys;
+  Q2_TRY(gemm(m, a, s));
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(64), 0, s, m->keys, m->ids_buf, m->hist,
+                     static_cast<int64_t>(c.max_seq) + 1, m->d_len, next, next_stride, B);
+  return check_launch("finalize");
+}
+
+template <typename T>
+q2_status prefill_impl(q2_model* m, const int64_t* ids, int64_t ids_bs, int64_t ids_ts, int B, int Tn, float* logits,
+                       int64_t ld_logits, int64_t* next, int64_t next_stride, hipStream_t s) {
+  const int Tc_max = m->max_tok / B > 0 ? m->max_tok / B : 1;
+  int tc = 0;
+  for (int t0 = 0; t0 < Tn; t0 += tc) {
+    tc = Tn - t0 < Tc_max ? Tn - t0 : Tc_max;
+    Q2_TRY(launch_embedding<T>(static_cast<T*>(m->x), m->cfg.hidden, ids + t0 * ids_ts, ids_bs, ids_ts, B, tc,
+                               static_cast<const T*>(m->embed), m->cfg.hidden, m->cfg.vocab, m->cfg.hidden, s));
+    Q2_TRY(run_layers<T>(m, B, tc, s));
+    m->len += tc;
+  }
+  return run_head<T>(m, B, tc, logits, ld_logits, next, next_stride, s);
+}
+
+// One decode step from ids_buf (the graph body).
+template <typename T>
+q2_status decode_body(q2_model* m, int B, bool want_logits, hipStream_t s) {
+  Q2_TRY(launch_embedding<T>(static_cast<T*>(m->x), m->cfg.hidden, m->ids_buf, 1, 0, B, 1,
+                             static_cast<const T*>(m->embed), m->cfg.hidden, m->cfg.vocab, m->cfg.hidden, s));
+  Q2_TRY(run_layers<T>(m, B, 1, s));
+  return run_head<T>(m, B, 1, want_logits ? m->logits_buf : nullptr, m->cfg.vocab, nullptr, 0, s);
+}
+
+q2_status get_graph(q2_model* m, int B, bool want_logits, hipGraphExec_t* out) {
+  auto key = std::make_pair(B, want_logits ? 1 : 0);
+  auto it = m->graphs.find(key);
+  if (it != m->graphs.end()) {
+    *out = it->second;
+    return Q2_OK;
+  }
+  Q2_HIP(hipStreamBeginCapture(m->cap, hipStreamCaptureModeThreadLocal));
+  const int saved_len = m->len;
+  q2_status st = m->cfg.dtype == Q2_BF16 ? decode_body<uint16_t>(m, B, want_logits, m->cap)
+                                         : decode_body<float>(m, B, want_logits, m->cap);
+  m->len = saved_len;
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamEndCapture(m->cap, &graph);
+  if (st != Q2_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return st;
+  }
+  if (e != hipSuccess) return fail(Q2_EHIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (e != hipSuccess) return fail(Q2_EHIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
+  m->graphs[key] = exec;
+  *out = exec;
+  return Q2_OK;
+}
+
+q2_status sync_len(q2_model* m, hipStream_t s) {
+  if (!m->len_dirty) return Q2_OK;
+  hipLaunchKernelGGL(set_len_kernel, dim3(1), dim3(1), 0, s, m->d_len, m->len);
+  Q2_TRY(check_launch("set_len"));
+  m->len_dirty = false;
+  return Q2_OK;
+}
+
+q2_status check_batch(q2_model* m, int B, int add) {
+  Q2_CHECK(B >= 1 && B <= m->cfg.max_batch, Q2_ESHAPE, "batch %d not in [1, %d]", B, m->cfg.max_batch);
+  Q2_CHECK(m->len == 0 || B == m->cur_batch, Q2_ESTATE, "batch %d differs from the cached batch %d (reset first)", B,
+           m->cur_batch);
+  Q2_CHECK(static_cast<int64_t>(m->len) + add <= m->cfg.max_seq, Q2_ESTATE,
+           "KV cache capacity exceeded: %d cached + %d new > %d", m->len, add, m->cfg.max_seq);
+  return Q2_OK;
+}
+
+q2_status check_ids_2d(const q2_tensor* ids, int* B, int* Tn, int64_t* bs, int64_t* ts) {
+  Q2_TRY(check_desc(ids, "ids"));
+  Q2_CHECK(ids->dtype == Q2_I64, Q2_EDTYPE, "ids must be int64");
+  Q2_CHECK(ids->ndim == 1 || ids->ndim == 2, Q2_ESHAPE, "ids must be [T] or [B, T]");
+  *B = ids->ndim == 2 ? static_cast<int>(ids->shape[0]) : 1;
+  *Tn = static_cast<int>(ids->shape[ids->ndim - 1]);
+  *bs = ids->ndim == 2 ? ids->stride[0] : 0;
+  *ts = ids->stride[ids->ndim - 1];
+  return Q2_OK;
+}
+
+q2_status check_next(const q2_tensor* next, int B, int64_t* stride) {
+  *stride = 0;
+  if (!next) return Q2_OK;
+  Q2_TRY(check_desc(next, "next"));
+  Q2_CHECK(next->dtype == Q2_I64, Q2_EDTYPE, "next must be int64");
+  Q2_CHECK(numel(*next) == B && next->ndim == 1, Q2_ESHAPE, "next must be [B]");
+  *stride = next->stride[0];
+  return Q2_OK;
+}
+
+q2_status check_logits(const q2_model* m, const q2_tensor* logits, int B, Rows* r) {
+  if (!logits) return Q2_OK;
+  Q2_TRY(as_rows(logits, "logits", r));
+  Q2_CHECK(r->dtype == Q2_F32, Q2_EDTYPE, "logits must be f32");
+  Q2_CHECK(r->rows == B && r->cols == m->cfg.vocab, Q2_ESHAPE, "logits must be [B, V]");
+  return Q2_OK;
+}
+
+struct WeightSlot {
+  void* dst;
+  int64_t rows, cols;   // source shape ([rows] for vectors: cols = 1)
+  int mode;             // pack_rows mode
+  int64_t off;          // destination row offset
+  int64_t dst_ld;       // destination row stride (elements)
+};
+
+q2_status find_slot(q2_model* m, const std::string& name, int layer, WeightSlot* w) {
+  const q2_config& c = m->cfg;
+  const int64_t H = c.hidden, d = c.dh, qd = int64_t(c.nh) * c.dh, kd = int64_t(c.nkv) * c.dh, I = c.inter;
+  if (layer < 0) {
+    Q2_CHECK(layer == -1, Q2_EINVAL, "layer must be -1 for global tensors");
+    if (name == "embed_tokens") *w = {m->embed, c.vocab, H, 0, 0, H};
+    else if (name == "lm_head") *w = {m->lm_head, c.vocab, H, 0, 0, H};
+    else if (name == "norm") *w = {m->w_final, H, 1, 0, 0, 1};
+    else return fail(Q2_EINVAL, "unknown global weight '%s'", name.c_str());
+    return Q2_OK;
+  }
+  Q2_CHECK(layer < c.nlayer, Q2_EINVAL, "layer %d out of range", layer);
+  const q2_model::Layer& L = m->layers[layer];
+  if (name == "input_layernorm") *w = {L.w_in, H, 1, 0, 0, 1};
+  else if (name == "post_attention_layernorm") *w = {L.w_post, H, 1, 0, 0, 1};
+  else if (name == "q_proj.weight") *w = {L.w_qkv, qd, H, 1, 0, H};
+  else if (name == "k_proj.weight") *w = {L.w_qkv, kd, H, 1, qd, H};
+  else if (name == "v_proj.weight") *w = {L.w_qkv, kd, H, 0, qd + kd, H};
+  else if (name == "q_proj.bias") *w = {L.b_qkv, qd, 1, 1, 0, 1};
+  else if (name == "k_proj.bias") *w = {L.b_qkv, kd, 1, 1, qd, 1};
+  else if (name == "v_proj.bias") *w = {L.b_qkv, kd, 1, 0, qd + kd, 1};
+  else if (name == "o_proj.weight") *w = {L.w_o, H, qd, 0, 0, qd};
+  else if (name == "gate_proj.weight") *w = {L.w_gu, I, H, 2, 0, H};
+  else if (name == "up_proj.weight") *w = {L.w_gu, I, H, 2, 1, H};
+  else if (name == "down_proj.weight") *w = {L.w_d, H, I, 0, 0, I};
+  else return fail(Q2_EINVAL, "unknown layer weight '%s'", name.c_str());
+  (void)d;
+  return Q2_OK;
+}
+
+}  // namespace
+
+// ==================================================================== C ABI
+
+extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_model** out) {
+  clear_error();
+  Q2_CHECK(cfg && out, Q2_EINVAL, "null argument");
+  *out = nullptr;
+  const q2_config c = *cfg;
+  Q2_CHECK(c.dtype == Q2_F32 || c.dtype == Q2_BF16, Q2_EDTYPE, "model dtype must be f32 or bf16");
+  Q2_CHECK(c.nlayer >= 1 && c.hidden >= 1 && c.nh >= 1 && c.nkv >= 1 && c.dh >= 2 && c.inter >= 1 && c.vocab >= 1 &&
+               c.max_seq >= 1 && c.max_batch >= 1,
+           Q2_ESHAPE, "all sizes must be positive");
+  Q2_CHECK(c.nh % c.nkv == 0, Q2_ESHAPE, "nh must be a multiple of nkv");
+  Q2_CHECK(c.dh % 2 == 0, Q2_ESHAPE, "head dim must be even");
+  Q2_CHECK(c.max_batch <= 64, Q2_ESHAPE, "max_batch must be <= 64");
+  Q2_CHECK(c.eps >= 0.f && c.theta > 0.f, Q2_EINVAL, "bad eps / theta");
+  if (c.dtype == Q2_BF16) {
+    Q2_CHECK(c.dh == 128, Q2_ESHAPE, "bf16 model needs head_dim 128");
+    Q2_CHECK(c.hidden % 32 == 0 && c.inter % 32 == 0, Q2_ESHAPE, "bf16 model needs hidden and inter multiples of 32");
+  } else {
+    Q2_CHECK(c.dh <= 256 && c.max_seq <= 16384, Q2_ESHAPE, "f32 model: head_dim <= 256, max_seq <= 16384");
+  }
+  int ndev = 0;
+  Q2_HIP(hipGetDeviceCount(&ndev));
+  Q2_CHECK(device >= 0 && device < ndev, Q2_EINVAL, "device %d not present", device);
+  Q2_HIP(hipSetDevice(device));
+
+  q2_model* m = new (std::nothrow) q2_model();
+  Q2_CHECK(m, Q2_ENOMEM, "host allocation failed");
+  m->cfg = c;
+  m->device = device;
+  m->esize = c.dtype == Q2_BF16 ? 2 : 4;
+  m->qkv_out = (c.nh + 2 * c.nkv) * c.dh;
+  const size_t es = m->esize;
+  const size_t H = c.hidden, I = c.inter, V = c.vocab, qd = size_t(c.nh) * c.dh;
+
+  // weights
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t o_embed = take(V * H * es), o_lm = take(V * H * es), o_final = take(H * es);
+  std::vector<size_t> lo(size_t(c.nlayer) * 7);
+  for (int l = 0; l < c.nlayer; ++l) {
+    size_t* p = &lo[size_t(l) * 7];
+    p[0] = take(H * es);
+    p[1] = take(H * es);
+    p[2] = take(size_t(m->qkv_out) * H * es);
+    p[3] = take(size_t(m->qkv_out) * es);
+    p[4] = take(H * qd * es);
+    p[5] = take(2 * I * H * es);
+    p[6] = take(H * I * es);
+  }
+  m->wbytes = off;
+
+  // KV cache
+  m->kv_hstride = int64_t(c.max_seq) * c.dh;
+  m->kv_bstride = m->kv_hstride * c.nkv;
+  m->kv_lstride = m->kv_bstride * c.max_batch;
+  const size_t kv_one = size_t(m->kv_lstride) * c.nlayer * es;
+  m->kvbytes = 2 * align256(kv_one);
+
+  // arena
+  const int64_t bs = int64_t(c.max_batch) * c.max_seq;
+  m->max_tok = static_cast<int>(bs < 16384 ? bs : 16384);
+  if (m->max_tok < c.max_batch) m->max_tok = c.max_batch;
+  const size_t mt = m->max_tok;
+  off = 0;
+  const size_t a_rope = take(size_t(c.max_seq) * (c.dh / 2) * sizeof(float2));
+  const size_t a_x = take(mt * H * es), a_h = take(mt * H * es), a_q = take(mt * qd * es), a_att = take(mt * qd * es);
+  const size_t a_act = take(mt * I * es), a_xl = take(size_t(c.max_batch) * H * es);
+  const size_t a_logits = take(size_t(c.max_batch) * V * sizeof(float));
+  const size_t a_keys = take(size_t(c.max_batch) * 8), a_ids = take(size_t(c.max_batch) * 8);
+  const size_t a_hist = take(size_t(c.max_batch) * (c.max_seq + 1) * 8), a_len = take(sizeof(int));
+  size_t gs = 0;
+  {
+    const int mm = c.max_batch < 16 ? c.max_batch : 16;
+    const int shapes[4][2] = {{m->qkv_out, c.hidden}, {c.hidden, int(qd)}, {2 * c.inter, c.hidden}, {c.hidden, c.inter}};
+    for (int i = 0; i < 4; ++i)
+      for (int mm2 = 1; mm2 <= mm; ++mm2) {
+        size_t b = gemm_scratch_bytes(mm2, shapes[i][0], shapes[i][1]);
+        gs = b > gs ? b : gs;
+      }
+  }
+  m->gscratch_bytes = gs;
+  const size_t a_gs = take(gs);
+  size_t as = 0;
+  if (c.dtype == Q2_BF16)
+    for (int b = 1; b <= c.max_batch; ++b) {
+      const int group = c.nh / c.nkv;
+      for (int t = 1; t * group <= 16; ++t) {
+        size_t x = attention_scratch_bytes(b, t, c.max_seq, c.nh, c.nkv, c.dh);
+        as = x > as ? x : as;
+      }
+    }
+  m->ascratch_bytes = as;
+  const size_t a_as = take(as);
+  m->abytes = off;
+
+  auto cleanup = [&](q2_status st) {
+    q2_model_destroy(m);
+    return st;
+  };
+  if (hipMalloc(&m->wmem, m->wbytes) != hipSuccess || hipMalloc(&m->kvmem, m->kvbytes) != hipSuccess ||
+      hipMalloc(&m->amem, m->abytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return cleanup(fail(Q2_ENOMEM, "device allocation of %.2f GB failed",
+                        double(m->wbytes + m->kvbytes + m->abytes) / 1e9));
+  }
+  if (hipMemset(m->wmem, 0, m->wbytes) != hipSuccess || hipMemset(m->kvmem, 0, m->kvbytes) != hipSuccess ||
+      hipMemset(m->amem, 0, m->abytes) != hipSuccess)
+    return cleanup(fail(Q2_EHIP, "hipMemset failed"));
+  m->embed = m->wmem + o_embed;
+  m->lm_head = m->wmem + o_lm;
+  m->w_final = m->wmem + o_final;
+  m->layers.resize(c.nlayer);
+  for (int l = 0; l < c.nlayer; ++l) {
+    const size_t* p = &lo[size_t(l) * 7];
+    m->layers[l] = {m->wmem + p[0], m->wmem + p[1], m->wmem + p[2], m->wmem + p[3],
+                    m->wmem + p[4], m->wmem + p[5], m->wmem + p[6]};
+  }
+  m->kc = m->kvmem;
+  m->vc = m->kvmem + align256(kv_one);
+  m->rope = reinterpret_cast<float2*>(m->amem + a_rope);
+  m->x = m->amem + a_x;
+  m->h = m->amem + a_h;
+  m->q = m->amem + a_q;
+  m->att = m->amem + a_att;
+  m->act = m->amem + a_act;
+  m->xl = m->amem + a_xl;
+  m->logits_buf = reinterpret_cast<float*>(m->amem + a_logits);
+  m->keys = reinterpret_cast<unsigned long long*>(m->amem + a_keys);
+  m->ids_buf = reinterpret_cast<int64_t*>(m->amem + a_ids);
+  m->hist = reinterpret_cast<int64_t*>(m->amem + a_hist);
+  m->d_len = reinterpret_cast<int*>(m->amem + a_len);
+  m->gscratch = gs ? m->amem + a_gs : nullptr;
+  m->ascratch = as ? m->amem + a_as : nullptr;
+  if (hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking) != hipSuccess)
+    return cleanup(fail(Q2_EHIP, "stream creation failed"));
+  q2_status st = launch_rope_table(m->rope, c.max_seq, c.dh, c.theta, nullptr);
+  if (st != Q2_OK) return cleanup(st);
+  if (hipDeviceSynchronize() != hipSuccess) return cleanup(fail(Q2_EHIP, "device synchronize failed"));
+  *out = m;
+  return Q2_OK;
+}
+
+extern "C" q2_status q2_model_device_bytes(const q2_model* m, size_t* bytes) {
+  clear_error();
+  Q2_CHECK(m && bytes, Q2_EINVAL, "null argument");
+  *bytes = m->wbytes + m->kvbytes + m->abytes;
+  return Q2_OK;
+}
+
+extern "C" q2_status q2_model_load_weight(q2_model* m, const char* name, int32_t layer, const q2_tensor* src,
+                                          void* stream) {
+  clear_error();
+  Q2_CHECK(m && name, Q2_EINVAL, "null argument");
+  Q2_TRY(check_desc(src, "src"));
+  WeightSlot w{};
+  Q2_TRY(find_slot(m, name, layer, &w));
+  Q2_CHECK(src->dtype == m->cfg.dtype, Q2_EDTYPE, "weight '%s' dtype differs from the model dtype", name);
+  Q2_CHECK(is_contiguous(*src), Q2_ESTRIDE, "weight '%s' must be contiguous", name);
+  const bool vec = w.cols == 1;
+  if (vec) {
+    Q2_CHECK(src->ndim == 1 && src->shape[0] == w.rows, Q2_ESHAPE, "weight '%s' must be [%lld]", name,
+             (long long)w.rows);
+  } else {
+    Q2_CHECK(src->ndim == 2 && src->shape[0] == w.rows && src->shape[1] == w.cols, Q2_ESHAPE,
+             "weight '%s' must be [%lld, %lld]", name, (long long)w.rows, (long long)w.cols);
+  }
+  return launch_pack_rows(w.dst, w.dst_ld, src->data, vec ? 1 : w.cols, w.rows, w.cols, m->esize, w.mode, m->cfg.dh,
+                          w.off, static_cast<hipStream_t>(stream));
+}
+
+extern "C" q2_status q2_model_prefill(q2_model* m, const q2_tensor* ids, const q2_tensor* next,
+                                      const q2_tensor* logits, void* stream) {
+  clear_error();
+  Q2_CHECK(m, Q2_EINVAL, "null model");
+  int B = 0, Tn = 0;
+  int64_t bs = 0, ts = 0, ns = 0;
+  Q2_TRY(check_ids_2d(ids, &B, &Tn, &bs, &ts));
+  Q2_CHECK(Tn >= 1, Q2_ESHAPE, "prefill needs at least one token");
+  Q2_TRY(check_batch(m, B, Tn));
+  Q2_TRY(check_next(next, B, &ns));
+  Rows lg{};
+  Q2_TRY(check_logits(m, logits, B, &lg));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Q2_TRY(sync_len(m, s));
+  m->cur_batch = B;
+  const int64_t* ip = static_cast<const int64_t*>(ids->data);
+  int64_t* np = next ? static_cast<int64_t*>(next->data) : nullptr;
+  float* lp = logits ? reinterpret_cast<float*>(lg.data) : nullptr;
+  return m->cfg.dtype == Q2_BF16 ? prefill_impl<uint16_t>(m, ip, bs, ts, B, Tn, lp, lg.ld, np, ns, s)
+                                 : prefill_impl<float>(m, ip, bs, ts, B, Tn, lp, lg.ld, np, ns, s);
+}
+
+extern "C" q2_status q2_model_decode(q2_model* m, const q2_tensor* ids, const q2_tensor* next,
+                                     const q2_tensor* logits, void* stream) {
+  clear_error();
+  Q2_CHECK(m, Q2_EINVAL, "null model");
+  Q2_TRY(check_desc(ids, "ids"));
+  Q2_CHECK(ids->dtype == Q2_I64, Q2_EDTYPE, "ids must be int64");
+  Q2_CHECK(ids->ndim == 1 || (ids->ndim == 2 && ids->shape[1] == 1), Q2_ESHAPE, "ids must be [B] or [B, 1]");
+  const int B = static_cast<int>(ids->shape[0]);
+  Q2_TRY(check_batch(m, B, 1));
+  int64_t ns = 0;
+  Q2_TRY(check_next(next, B, &ns));
+  Rows lg{};
+  Q2_TRY(check_logits(m, logits, B, &lg));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Q2_TRY(sync_len(m, s));
+  hipGraphExec_t g = nullptr;
+  Q2_TRY(get_graph(m, B, logits != nullptr, &g));
+  m->cur_batch = B;
+  hipLaunchKernelGGL(copy_ids_kernel, dim3(1), dim3(64), 0, s, m->ids_buf, int64_t(1),
+                     static_cast<const int64_t*>(ids->data), ids->stride[0], B);
+  Q2_TRY(check_launch("copy_ids"));
+  Q2_HIP(hipGraphLaunch(g, s));
+  m->len += 1;
+  if (next) {
+    hipLaunchKernelGGL(copy_ids_kernel, dim3(1), dim3(64), 0, s, static_cast<int64_t*>(next->data), ns, m->ids_buf,
+                       int64_t(1), B);
+    Q2_TRY(check_launch("copy_next"));
+  }
+  if (logits) {
+    const int64_t n = int64_t(B) * m->cfg.vocab;
+    hipLaunchKernelGGL(copy_logits_kernel, dim3(cdiv(n, 256)), dim3(256), 0, s, reinterpret_cast<float*>(lg.data),
+                       lg.ld, m->logits_buf, m->cfg.vocab, m->cfg.vocab, B);
+    Q2_TRY(check_launch("copy_logits"));
+  }
+  return Q2_OK;
+}
+
+static q2_status run_steps(q2_model* m, int steps, const q2_tensor* out_ids, int first_col, hipStream_t s) {
+  const int B = m->cur_batch;
+  hipGraphExec_t g = nullptr;
+  if (steps > 0) Q2_TRY(get_graph(m, B, false, &g));
+  const int start = m->len;  // the token produced last sits at position `start`
+  for (int i = 0; i < steps; ++i) Q2_HIP(hipGraphLaunch(g, s));
+  m->len += steps;
+  if (out_ids) {
+    const int n = static_cast<int>(out_ids->shape[1]);
+    hipLaunchKernelGGL(copy_hist_kernel, dim3(cdiv(int64_t(n) * B, 256)), dim3(256), 0, s,
+                       static_cast<int64_t*>(out_ids->data), out_ids->stride[0], m->hist,
+                       static_cast<int64_t>(m->cfg.max_seq) + 1, start + 1 - first_col, n, B);
+    Q2_TRY(check_launch("copy_hist"));
+  }
+  return Q2_OK;
+}
+
+static q2_status check_out_ids(const q2_tensor* out_ids, int B, int cols) {
+  Q2_TRY(check_desc(out_ids, "out_ids"));
+  Q2_CHECK(out_ids->dtype == Q2_I64, Q2_EDTYPE, "out_ids must be int64");
+  Q2_CHECK(out_ids->ndim == 2 && out_ids->shape[0] == B && out_ids->shape[1] == cols, Q2_ESHAPE,
+           "out_ids must be [%d, %d]", B, cols);
+  Q2_CHECK(out_ids->stride[1] == 1 || cols <= 1, Q2_ESTRIDE, "out_ids rows must be contiguous");
+  return Q2_OK;
+}
+
+extern "C" q2_status q2_model_generate(q2_model* m, const q2_tensor* prompt, int32_t steps, const q2_tensor* out_ids,
+                                       void* stream) {
+  clear_error();
+  Q2_CHECK(m, Q2_EINVAL, "null model");
+  Q2_CHECK(steps >= 0, Q2_EINVAL, "steps must be >= 0");
+  int B = 0, Tn = 0;
+  int64_t bs = 0, ts = 0;
+  Q2_TRY(check_ids_2d(prompt, &B, &Tn, &bs, &ts));
+  Q2_CHECK(Tn >= 1, Q2_ESHAPE, "prompt needs at least one token");
+  Q2_TRY(check_batch(m, B, Tn + steps));
+  Q2_TRY(check_out_ids(out_ids, B, steps + 1));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Q2_TRY(sync_len(m, s));
+  if (steps > 0) {
+    hipGraphExec_t g = nullptr;
+    Q2_TRY(get_graph(m, B, false, &g));  // capture before any state changes
+  }
+  m->cur_batch = B;
+  const int64_t* ip = static_cast<const int64_t*>(prompt->data);
+  Q2_TRY(m->cfg.dtype == Q2_BF16 ? prefill_impl<uint16_t>(m, ip, bs, ts, B, Tn, nullptr, 0, nullptr, 0, s)
+                                 : prefill_impl<float>(m, ip, bs, ts, B, Tn, nullptr, 0, nullptr, 0, s));
+  // out column 0 is the prefill's token (position len), then one per step
+  return run_steps(m, steps, out_ids, 1, s);
+}
+
+extern "C" q2_status q2_model_continue(q2_model* m, int32_t steps, const q2_tensor* out_ids, void* stream) {
+  clear_error();
+  Q2_CHECK(m, Q2_EINVAL, "null model");
+  Q2_CHECK(steps >= 0, Q2_EINVAL, "steps must be >= 0");
+  Q2_CHECK(m->len >= 1 && m->cur_batch >= 1, Q2_ESTATE, "continue needs a prefill first");
+  Q2_TRY(check_batch(m, m->cur_batch, steps));
+  if (out_ids) Q2_TRY(check_out_ids(out_ids, m->cur_batch, steps));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Q2_TRY(sync_len(m, s));
+  return run_steps(m, steps, out_ids, 0, s);
+}
+
+extern "C" q2_status q2_model_kv_view(q2_model* m, int32_t layer, q2_tensor* k, q2_tensor* v) {
+  clear_error();
+  Q2_CHECK(m && k && v, Q2_EINVAL, "null argument");
+  Q2_CHECK(layer >= 0 && layer < m->cfg.nlayer, Q2_EINVAL, "layer out of range");
+  for (int i = 0; i < 2; ++i) {
+    q2_tensor* t = i ? v : k;
+    memset(t, 0, sizeof *t);
+    t->data = static_cast<char*>(i ? m->vc : m->kc) + int64_t(layer) * m->kv_lstride * m->esize;
+    t->dtype = m->cfg.dtype;
+    t->ndim = 4;
+    t->shape[0] = m->cfg.max_batch;
+    t->shape[1] = m->cfg.max_seq;
+    t->shape[2] = m->cfg.nkv;
+    t->shape[3] = m->cfg.dh;
+    t->stride[0] = m->kv_bstride;
+    t->stride[1] = m->cfg.dh;
+    t->stride[2] = m->kv_hstride;
+    t->stride[3] = 1;
+  }
+  return Q2_OK;
+}
+
+extern "C" q2_status q2_model_length(const q2_model* m, int32_t* len) {
+  clear_error();
+  Q2_CHECK(m && len, Q2_EINVAL, "null argument");
+  *len = m->len;
+  return Q2_OK;
+}
+
+extern "C" q2_status q2_model_reset(q2_model* m) {
+  clear_error();
+  Q2_CHECK(m, Q2_EINVAL, "null model");
+  m->len = 0;
+  m->cur_batch = 0;
+  m->len_dirty = true;
+  return Q2_OK;
+}
+
+extern "C" void q2_model_destroy(q2_model* m) {
+  if (!m) return;
+  (void)hipSetDevice(m->device);
+  (void)hipDeviceSynchronize();
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  if (m->cap) (void)hipStreamDestroy(m->cap);
+  if (m->wmem) (void)hipFree(m->wmem);
+  if (m->kvmem) (void)hipFree(m->kvmem);
+  if (m->amem) (void)hipFree(m->amem);
+  delete m;
+}

@@ -1,0 +1,85 @@
+"""Python handle around the q2 model driver (argument marshalling only)."""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import Q2Config, Q2_BF16, Q2_F32
+
+
+def make_config(shape, max_seq: int, max_batch: int) -> Q2Config:
+    """q2_config from any object with the Qwen2 shape attributes
+    (dtype "f32"/"bf16", nlayer, hidden, nh, nkv, dh, inter, vocab, eps, theta)."""
+    c = Q2Config()
+    c.dtype = Q2_BF16 if shape.dtype == "bf16" else Q2_F32
+    c.nlayer, c.hidden, c.nh, c.nkv = shape.nlayer, shape.hidden, shape.nh, shape.nkv
+    c.dh, c.inter, c.vocab = shape.dh, shape.inter, shape.vocab
+    c.max_seq, c.max_batch = max_seq, max_batch
+    c.eps, c.theta = shape.eps, shape.theta
+    return c
+
+
+class Model:
+    """Owns one q2_model.  Weights are loaded from device tensors with
+    `load_weight(name, layer, tensor)`; all calls run on the current stream."""
+
+    def __init__(self, shape, max_seq: int, max_batch: int, device: int = 0):
+        self.shape = shape
+        self.max_seq = max_seq
+        self.max_batch = max_batch
+        self.device = device
+        self.torch_dtype = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+        self.handle = _lib.q2_model_create(make_config(shape, max_seq, max_batch), device)
+
+    def close(self):
+        if self.handle:
+            _lib.q2_model_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def device_bytes(self) -> int:
+        return _lib.q2_model_device_bytes(self.handle)
+
+    def load_weight(self, name: str, layer: int, tensor):
+        _lib.q2_model_load_weight(self.handle, name, layer, tensor)
+
+    def prefill(self, ids, logits: bool = False):
+        B = ids.shape[0] if ids.dim() == 2 else 1
+        nxt = torch.empty(B, dtype=torch.int64, device=ids.device)
+        lg = torch.empty(B, self.shape.vocab, dtype=torch.float32, device=ids.device) if logits else None
+        _lib.q2_model_prefill(self.handle, ids, nxt, lg)
+        return (nxt, lg) if logits else nxt
+
+    def decode(self, ids, logits: bool = False):
+        B = ids.shape[0]
+        nxt = torch.empty(B, dtype=torch.int64, device=ids.device)
+        lg = torch.empty(B, self.shape.vocab, dtype=torch.float32, device=ids.device) if logits else None
+        _lib.q2_model_decode(self.handle, ids, nxt, lg)
+        return (nxt, lg) if logits else nxt
+
+    def generate(self, prompt, steps: int, out=None):
+        B = prompt.shape[0]
+        if out is None:
+            out = torch.empty(B, steps + 1, dtype=torch.int64, device=prompt.device)
+        _lib.q2_model_generate(self.handle, prompt, steps, out)
+        return out
+
+    def continue_(self, steps: int, out=None):
+        """Greedy decode `steps` more tokens from the device-resident state."""
+        _lib.q2_model_continue(self.handle, steps, out)
+        return out
+
+    def kv_view(self, layer: int):
+        """q2_tensor descriptors (k, v) of layer `layer`'s cache, [max_batch, max_seq, nkv, dh]."""
+        return _lib.q2_model_kv_view(self.handle, layer)
+
+    def length(self) -> int:
+        return _lib.q2_model_length(self.handle)
+
+    def reset(self):
+        _lib.q2_model_reset(self.handle)

@@ -1,0 +1,74 @@
+"""Helpers for model-level GPU tests and the benchmark: build a q2 model on
+the GPU from the seeded synthetic weights, and compare it with the oracle
+under teacher forcing."""
+import dataclasses
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+from qwen2_decoder_forward_amd import Model
+
+DEV = "cuda:0"
+
+
+def to_device(arr: np.ndarray) -> torch.Tensor:
+    """Upload a synthetic weight (uint16 bf16 bits or float32) bit-for-bit."""
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(DEV)
+
+
+def build_model(shape, weights, max_seq, max_batch) -> Model:
+    m = Model(shape, max_seq, max_batch)
+    for (name, layer), arr in weights.items():
+        t = to_device(arr)
+        m.load_weight(name, layer, t)
+        torch.cuda.synchronize()
+        del t
+    return m
+
+
+def reduced_shape(shape, **kw):
+    return dataclasses.replace(shape, **kw)
+
+
+@dataclasses.dataclass
+class TFResult:
+    steps: int
+    max_abs_err: float          # over all compared logits, after rounding both to bf16 (bf16 models)
+    max_rel_err: float          # max |d| / max |ref| per step, worst step
+    agreement: float            # fraction of positions whose argmax matches, all sequences
+    cosine_min: float
+    gpu_tokens: np.ndarray
+    ref_tokens: np.ndarray
+
+
+def teacher_forced(model: Model, orc: oracle.OracleModel, prompt: np.ndarray, steps: int) -> TFResult:
+    """Oracle runs greedily; the GPU is fed the oracle's tokens; logits of the
+    prefill and of every decode step are compared."""
+    ref_toks, ref_logits = orc.generate(prompt, steps)
+    bf = orc.storage == "bf16"
+    nxt, lg = model.prefill(torch.from_numpy(prompt).to(DEV), logits=True)
+    gpu_logits = [lg.cpu().numpy()]
+    gpu_toks = [nxt.cpu().numpy()]
+    for s in range(1, steps + 1):
+        feed = torch.from_numpy(np.ascontiguousarray(ref_toks[:, s - 1])).to(DEV)
+        nxt, lg = model.decode(feed, logits=True)
+        gpu_logits.append(lg.cpu().numpy())
+        gpu_toks.append(nxt.cpu().numpy())
+    max_abs = max_rel = 0.0
+    cos_min = 1.0
+    for g, r in zip(gpu_logits, ref_logits):
+        if bf:
+            g, r = oracle.bf16_round(g), oracle.bf16_round(r)
+        d = np.abs(g.astype(np.float64) - r)
+        max_abs = max(max_abs, float(d.max()))
+        max_rel = max(max_rel, float(d.max() / np.abs(r).max()))
+        for b in range(g.shape[0]):
+            c = float(np.dot(g[b], r[b]) / (np.linalg.norm(g[b]) * np.linalg.norm(r[b])))
+            cos_min = min(cos_min, c)
+    gt = np.stack(gpu_toks, axis=1)
+    agree = float(np.mean(gt == ref_toks))
+    return TFResult(steps, max_abs, max_rel, agree, cos_min, gt, ref_toks)

@@ -1,0 +1,243 @@
+"""Model-level parity on the GPU: the q2 model driver against the oracle under
+teacher forcing, plus invariants that hold at any size.
+
+Bars (from the arithmetic and the workload definitions):
+  * fp32 model (workload A): logits within 1e-4 of the oracle relative to the
+    largest logit, every greedy token equal.
+  * bf16 models: max abs error <= 2e-2 on logits rounded to bf16 (float32
+    accumulation on both sides) and >= 99 % top-1 agreement per position.
+Where the oracle cannot run a workload at full size in seconds (the 4096-token
+prefill, the 64 x 4096 batched decode, the 7B shape) the same kernels are
+checked on the full shape with fewer layers or a shorter context against the
+oracle, and at full size through invariants (decode equals recompute,
+chunked prefill equals one-shot prefill, batch independence).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qwen2_decoder_forward_amd as q2
+import synth
+from tests.model_util import DEV, build_model, reduced_shape, teacher_forced
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BF16 = synth.ModelShape("small-bf16", "bf16", 3, 256, 4, 2, 128, 512, 1000, 10000.0)
+
+
+def _run(shape, batch, prompt_len, steps, seed=1234, prompt_seed=5678):
+    wl = synth.Workload("t", shape, batch, prompt_len, steps, seed, prompt_seed)
+    w = synth.make_weights(wl)
+    prompt = synth.make_prompt(wl)
+    model = build_model(shape, w, wl.max_seq, batch)
+    orc = oracle.OracleModel(shape, w, "bf16" if shape.dtype == "bf16" else "fp32", batch, wl.max_seq)
+    res = teacher_forced(model, orc, prompt, steps)
+    model.close()
+    return res
+
+
+def _print(name, r):
+    print(f"\n[{name}] steps={r.steps} max_abs_err={r.max_abs_err:.3e} max_rel_err={r.max_rel_err:.3e} "
+          f"agreement={r.agreement:.4f} cos_min={r.cosine_min:.6f}", flush=True)
+
+
+def test_workload_a_fp32_full():
+    wl = synth.WORKLOADS["A"]
+    r = _run(wl.shape, wl.batch, wl.prompt, wl.steps)
+    _print("A", r)
+    assert r.max_rel_err <= 1e-4
+    assert np.array_equal(r.gpu_tokens, r.ref_tokens)
+
+
+def test_workload_a_generate_matches_oracle_greedy():
+    wl = synth.WORKLOADS["A"]
+    w = synth.make_weights(wl)
+    prompt = synth.make_prompt(wl)
+    model = build_model(wl.shape, w, wl.max_seq, 1)
+    out = model.generate(torch.from_numpy(prompt).to(DEV), wl.steps).cpu().numpy()
+    ref, _ = oracle.OracleModel(wl.shape, w, "fp32", 1, wl.max_seq).generate(prompt, wl.steps)
+    assert model.length() == wl.max_seq
+    model.close()
+    assert np.array_equal(out, ref)
+
+
+def test_workload_b_full_teacher_forced():
+    """Qwen2-1.5B shape, batch 1, prompt 64, 128 decode steps (the full workload)."""
+    wl = synth.WORKLOADS["B"]
+    r = _run(wl.shape, wl.batch, wl.prompt, wl.steps)
+    _print("B", r)
+    assert r.max_abs_err <= 2e-2
+    assert r.agreement >= 0.99
+
+
+def test_small_bf16_teacher_forced():
+    r = _run(SMALL_BF16, 3, 40, 12)
+    _print("small-bf16", r)
+    assert r.max_abs_err <= 2e-2 and r.agreement >= 0.99
+
+
+def test_c_shape_4_layers_prefill_4096():
+    """1.5B shape with 4 layers, one 4096-token prefill (multi-block flash attention)."""
+    sh = reduced_shape(synth.SHAPES["1.5b"], nlayer=4)
+    r = _run(sh, 1, 4096, 2)
+    _print("C-4layers", r)
+    assert r.max_abs_err <= 2e-2 and r.agreement >= 0.99
+
+
+def test_d_shape_batch64_short_context():
+    """1.5B shape (4 layers), 64 sequences, 96-token prompts, 4 batched decode steps."""
+    sh = reduced_shape(synth.SHAPES["1.5b"], nlayer=4)
+    r = _run(sh, 64, 96, 4)
+    _print("D-short", r)
+    assert r.max_abs_err <= 2e-2 and r.agreement >= 0.99
+
+
+def test_e_shape_2_layers_batch8():
+    """7B shape (hidden 3584, 28/4 heads, theta 1e6) with 2 layers, batch 8, prompt 64, 6 steps."""
+    sh = reduced_shape(synth.SHAPES["7b"], nlayer=2)
+    r = _run(sh, 8, 64, 6)
+    _print("E-2layers", r)
+    assert r.max_abs_err <= 2e-2 and r.agreement >= 0.99
+
+
+# ------------------------------------------------------------------ invariants
+
+def _logits_of(model, ids):
+    return model.prefill(torch.from_numpy(ids).to(DEV), logits=True)[1].cpu().numpy()
+
+
+def test_decode_equals_recompute_small_bf16():
+    sh = SMALL_BF16
+    w = synth.make_weights(sh, seed=3)
+    prompt = np.array([[5, 17, 900, 3, 44, 2, 8, 600, 31, 7]], np.int64)
+    m = build_model(sh, w, 32, 1)
+    toks = m.generate(torch.from_numpy(prompt).to(DEV), 8).cpu().numpy()
+    m.reset()
+    nxt, lg = m.prefill(torch.from_numpy(prompt).to(DEV), logits=True)
+    step_logits = [lg.cpu().numpy()]
+    for s in range(1, 9):
+        nxt, lg = m.decode(torch.from_numpy(toks[:, s - 1]).to(DEV), logits=True)
+        step_logits.append(lg.cpu().numpy())
+    for s in range(1, 9):
+        m.reset()
+        full = np.concatenate([prompt, toks[:, :s]], axis=1)
+        ref = _logits_of(m, full)
+        assert np.abs(ref - step_logits[s]).max() <= 2e-2, s
+    m.close()
+
+
+def test_batch_independence_small_bf16():
+    sh = SMALL_BF16
+    w = synth.make_weights(sh, seed=4)
+    rng = np.random.default_rng(0)
+    prompts = rng.integers(0, sh.vocab, (5, 12)).astype(np.int64)
+    m = build_model(sh, w, 40, 5)
+    batched = m.generate(torch.from_numpy(prompts).to(DEV), 10).cpu().numpy()
+    for b in (0, 4):
+        m.reset()
+        single = m.generate(torch.from_numpy(prompts[b:b + 1]).to(DEV), 10).cpu().numpy()
+        assert np.array_equal(single[0], batched[b])
+    m.close()
+
+
+def test_chunked_prefill_equals_one_shot_small_bf16():
+    sh = SMALL_BF16
+    w = synth.make_weights(sh, seed=5)
+    ids = np.random.default_rng(1).integers(0, sh.vocab, (2, 150)).astype(np.int64)
+    m = build_model(sh, w, 160, 2)
+    one = _logits_of(m, ids)
+    m.reset()
+    m.prefill(torch.from_numpy(ids[:, :64]).to(DEV))
+    m.prefill(torch.from_numpy(ids[:, 64:149]).to(DEV))
+    two = m.prefill(torch.from_numpy(ids[:, 149:]).to(DEV), logits=True)[1].cpu().numpy()
+    m.close()
+    assert np.abs(one - two).max() <= 2e-2
+
+
+def test_fused_model_equals_unfused_operator_chain():
+    """The model's fused kernels store what the chain of standalone operators
+    (embedding, rms_norm, linear, rope, rearrange into the KV cache,
+    self_attention, linear, add, swiglu, argmax) stores."""
+    sh = SMALL_BF16
+    w = synth.make_weights(sh, seed=6)
+    ids = np.array([[1, 2, 3, 500, 999, 0, 42]], np.int64)
+    T, H, nh, nkv, d, I = ids.shape[1], sh.hidden, sh.nh, sh.nkv, sh.dh, sh.inter
+    m = build_model(sh, w, 16, 1)
+    nxt_model, lg_model = m.prefill(torch.from_numpy(ids).to(DEV), logits=True)
+    from tests.model_util import to_device
+    W = {k: to_device(v) for k, v in w.items()}
+    bf = torch.bfloat16
+    tid = torch.from_numpy(ids[0]).to(DEV)
+    pos = torch.arange(T, dtype=torch.int64, device=DEV)
+    x = torch.empty(T, H, dtype=bf, device=DEV)
+    q2.q2_embedding(x, tid, W[("embed_tokens", -1)])
+    kc = torch.zeros(nkv, 16, d, dtype=bf, device=DEV)
+    vc = torch.zeros(nkv, 16, d, dtype=bf, device=DEV)
+    for l in range(sh.nlayer):
+        h = torch.empty_like(x)
+        q2.q2_rms_norm(h, x, W[("input_layernorm", l)], sh.eps)
+        q = torch.empty(T, nh * d, dtype=bf, device=DEV)
+        k = torch.empty(T, nkv * d, dtype=bf, device=DEV)
+        v = torch.empty(T, nkv * d, dtype=bf, device=DEV)
+        q2.q2_linear(q, h, W[("q_proj.weight", l)], W[("q_proj.bias", l)])
+        q2.q2_linear(k, h, W[("k_proj.weight", l)], W[("k_proj.bias", l)])
+        q2.q2_linear(v, h, W[("v_proj.weight", l)], W[("v_proj.bias", l)])
+        q3, k3 = q.view(T, nh, d), k.view(T, nkv, d)
+        q2.q2_rope(q3, q3, pos, sh.theta)
+        q2.q2_rope(k3, k3, pos, sh.theta)
+        q2.q2_rearrange(kc.permute(1, 0, 2)[:T], k3)
+        q2.q2_rearrange(vc.permute(1, 0, 2)[:T], v.view(T, nkv, d))
+        att = torch.empty(T, nh, d, dtype=bf, device=DEV)
+        q2.q2_self_attention(att, q3, kc.permute(1, 0, 2)[:T], vc.permute(1, 0, 2)[:T], 1 / math.sqrt(d))
+        # the model's cache for this layer holds the same keys and values
+        kv_k, kv_v = m.kv_view(l)
+        got_k = torch.empty(1, T, nkv, d, dtype=bf, device=DEV)
+        fake = q2.Q2Tensor.from_buffer_copy(kv_k)
+        fake.shape[1] = T
+        q2.q2_rearrange(got_k, fake)
+        assert torch.equal(got_k[0], kc.permute(1, 0, 2)[:T]), l
+        a = torch.empty(T, H, dtype=bf, device=DEV)
+        q2.q2_linear(a, att.view(T, nh * d), W[("o_proj.weight", l)])
+        q2.q2_add(x, x, a)
+        q2.q2_rms_norm(h, x, W[("post_attention_layernorm", l)], sh.eps)
+        g = torch.empty(T, I, dtype=bf, device=DEV)
+        u = torch.empty(T, I, dtype=bf, device=DEV)
+        q2.q2_linear(g, h, W[("gate_proj.weight", l)])
+        q2.q2_linear(u, h, W[("up_proj.weight", l)])
+        act = torch.empty_like(g)
+        q2.q2_swiglu(act, g, u)
+        dn = torch.empty(T, H, dtype=bf, device=DEV)
+        q2.q2_linear(dn, act, W[("down_proj.weight", l)])
+        q2.q2_add(x, x, dn)
+    hf = torch.empty(1, H, dtype=bf, device=DEV)
+    q2.q2_rms_norm(hf, x[T - 1:], W[("norm", -1)], sh.eps)
+    logits = torch.empty(1, sh.vocab, dtype=torch.float32, device=DEV)
+    q2.q2_linear(logits, hf, W[("lm_head", -1)])
+    idx = torch.empty(1, dtype=torch.int64, device=DEV)
+    val = torch.empty(1, dtype=torch.float32, device=DEV)
+    q2.q2_argmax(idx, val, logits)
+    m.close()
+    assert torch.allclose(logits, lg_model, atol=1e-2, rtol=0)
+    assert int(idx[0]) == int(nxt_model[0])
+
+
+def test_capacity_exceeded_is_state_error_and_changes_nothing():
+    sh = SMALL_BF16
+    w = synth.make_weights(sh, seed=7)
+    m = build_model(sh, w, 8, 1)
+    ids = torch.arange(6, dtype=torch.int64, device=DEV).view(1, 6)
+    m.prefill(ids)
+    with pytest.raises(q2.Q2Error) as e:
+        m.prefill(torch.zeros(1, 3, dtype=torch.int64, device=DEV))
+    assert e.value.name == "Q2_ESTATE" and m.length() == 6
+    with pytest.raises(q2.Q2Error):
+        m.generate(torch.zeros(1, 1, dtype=torch.int64, device=DEV), 2)
+    m.decode(torch.zeros(1, dtype=torch.int64, device=DEV))
+    m.decode(torch.zeros(1, dtype=torch.int64, device=DEV))
+    assert m.length() == 8
+    with pytest.raises(q2.Q2Error):
+        m.decode(torch.zeros(1, dtype=torch.int64, device=DEV))
+    m.close()

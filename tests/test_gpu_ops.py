@@ -1,0 +1,268 @@
+"""Per-operator parity: each HIP operator, called through the C ABI, against
+the oracle on identical seeded inputs.
+
+Tolerances (derived from the arithmetic, both sides compute in float32):
+  * embedding, rearrange, add, argmax: bit-exact.
+  * rms_norm, rope, swiglu (bf16 out): both sides round the same float32
+    formula once, so they differ by at most one bf16 ulp (rtol 2^-7) plus a
+    float32-level absolute slack where cancellation makes the value small.
+  * linear: float32 accumulation in a different order; bf16 output within one
+    bf16 ulp plus 1e-6 * sum_k |x_k w_k|; float32 output within 1e-5 * that sum.
+  * attention bf16: the P V product takes P in bf16 on the MFMA (the oracle
+    keeps it float32), worth up to 2^-9 relative per probability, so
+    rtol 2^-7 plus atol 4e-3 * max|v|.  float32 attention: rtol 1e-5.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qwen2_decoder_forward_amd as q2
+from tests.gpu_util import DEV, assert_close, bf16_vals, down, up
+
+pytestmark = pytest.mark.gpu
+BF = torch.bfloat16
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------------------ embedding
+
+@pytest.mark.parametrize("dtype", [BF, torch.float32])
+def test_embedding_bit_exact(dtype):
+    r = rng(1)
+    V, H = 1000, 1536
+    table = bf16_vals(r, (V, H), 0.02)
+    ids = np.array([0, V - 1, 5, 5, 999, 17, 0, 400], np.int64)
+    out = torch.empty(len(ids), H, dtype=dtype, device=DEV)
+    q2.q2_embedding(out, up(ids), up(table, dtype))
+    assert np.array_equal(down(out), oracle.embedding(ids, table))
+    # [B, T] ids and an out-of-range id (zero row, documented)
+    ids2 = np.array([[3, V], [7, -1]], np.int64)
+    out2 = torch.full((4, H), 7.0, dtype=dtype, device=DEV)
+    q2.q2_embedding(out2, up(ids2), up(table, dtype))
+    o = down(out2)
+    assert np.array_equal(o[0], table[3]) and np.array_equal(o[2], table[7])
+    assert np.all(o[1] == 0) and np.all(o[3] == 0)
+
+
+# ------------------------------------------------------------------ rms_norm
+
+@pytest.mark.parametrize("rows,H", [(1, 1536), (7, 3584), (130, 128), (5, 100)])
+def test_rms_norm_bf16(rows, H):
+    r = rng(2)
+    x = bf16_vals(r, (rows, H))
+    w = bf16_vals(r, (H,), 0.02) + 1
+    w = oracle.bf16_round(w)
+    out = torch.empty(rows, H, dtype=BF, device=DEV)
+    q2.q2_rms_norm(out, up(x, BF), up(w, BF), 1e-6)
+    ref = oracle.bf16_round(oracle.rms_norm(x, w, 1e-6))
+    assert_close(down(out), ref, 1e-6, 2 ** -7, "rms_norm bf16")
+
+
+def test_rms_norm_f32_strided_rows():
+    r = rng(3)
+    base = r.standard_normal((9, 200)).astype(np.float32)
+    w = r.standard_normal(128).astype(np.float32)
+    xin = up(base)[:, 10:138]                 # rows with stride 200
+    out = torch.empty(9, 128, device=DEV)
+    q2.q2_rms_norm(out, xin, up(w), 1e-6)
+    assert_close(down(out), oracle.rms_norm(base[:, 10:138], w, 1e-6), 1e-6, 1e-5, "rms_norm f32")
+
+
+# ------------------------------------------------------------------ rope
+
+@pytest.mark.parametrize("T,nh,d,dtype", [(1, 12, 128, BF), (17, 2, 128, BF), (9, 4, 32, torch.float32)])
+def test_rope(T, nh, d, dtype):
+    r = rng(4)
+    x = bf16_vals(r, (T, nh, d))
+    pos = r.integers(0, 4096, T).astype(np.int64)
+    pos[0] = 0
+    out = torch.empty(T, nh, d, dtype=dtype, device=DEV)
+    q2.q2_rope(out, up(x, dtype), up(pos), 10000.0)
+    ref = oracle.rope(x, pos, 10000.0)
+    if dtype == BF:
+        assert_close(down(out), oracle.bf16_round(ref), 1e-6 * np.abs(x).max(), 2 ** -7, "rope bf16")
+    else:
+        assert_close(down(out), ref, 1e-6, 1e-5, "rope f32")
+
+
+def test_rope_batched_in_place_large_theta():
+    r = rng(5)
+    B, T, nh, d = 3, 5, 4, 128
+    x = bf16_vals(r, (B, T, nh, d))
+    pos = r.integers(0, 100000, (B, T)).astype(np.int64)
+    t = up(x, BF)
+    q2.q2_rope(t, t, up(pos), 1e6)
+    got = down(t)
+    for b in range(B):
+        ref = oracle.bf16_round(oracle.rope(x[b], pos[b], 1e6))
+        assert_close(got[b], ref, 1e-6 * np.abs(x).max(), 2 ** -7, "rope batched")
+
+
+# ------------------------------------------------------------------ linear
+
+@pytest.mark.parametrize("M,N,K", [(1, 300, 1536), (5, 2048, 1536), (16, 96, 8960), (33, 300, 200), (64, 130, 64),
+                                   (65, 300, 200), (200, 2048, 1536), (300, 260, 136)])
+@pytest.mark.parametrize("bias,out_f32", [(True, False), (False, True)])
+def test_linear_bf16(M, N, K, bias, out_f32):
+    r = rng(M * 1000 + N + K)
+    x = bf16_vals(r, (M, K))
+    w = bf16_vals(r, (N, K), 0.05)
+    b = bf16_vals(r, (N,), 0.1) if bias else None
+    out = torch.empty(M, N, dtype=torch.float32 if out_f32 else BF, device=DEV)
+    q2.q2_linear(out, up(x, BF), up(w, BF), up(b, BF) if bias else None)
+    ref = oracle.linear(x, w, b)
+    absprod = np.abs(x) @ np.abs(w).T
+    if out_f32:
+        assert_close(down(out), ref, 1e-5 * absprod + 1e-30, 0, "linear bf16->f32")
+    else:
+        assert_close(down(out), oracle.bf16_round(ref), 1e-6 * absprod + 1e-30, 2 ** -7, "linear bf16")
+
+
+def test_linear_bf16_strided_rows_and_batch_dims():
+    r = rng(6)
+    x = bf16_vals(r, (2, 3, 264))
+    w = bf16_vals(r, (40, 256), 0.05)
+    xin = up(x, BF)[..., :256]                      # row stride 264
+    out = torch.empty(2, 3, 40, dtype=BF, device=DEV)
+    q2.q2_linear(out, xin, up(w, BF))
+    ref = oracle.bf16_round(oracle.linear(x[..., :256].reshape(6, 256), w)).reshape(2, 3, 40)
+    assert_close(down(out), ref, 1e-6 * (np.abs(x[..., :256]) @ np.abs(w).T), 2 ** -7, "linear strided")
+
+
+def test_linear_f32():
+    r = rng(7)
+    x = r.standard_normal((7, 33)).astype(np.float32)
+    w = r.standard_normal((50, 33)).astype(np.float32)
+    b = r.standard_normal(50).astype(np.float32)
+    out = torch.empty(7, 50, device=DEV)
+    q2.q2_linear(out, up(x), up(w), up(b))
+    assert_close(down(out), oracle.linear(x, w, b), 1e-5, 1e-5, "linear f32")
+
+
+# ------------------------------------------------------------------ attention
+
+def _attn_case(seed, B, T, S, nh, nkv, d, dtype, cache_layout=False, smax=None):
+    r = rng(seed)
+    q = bf16_vals(r, (B, T, nh, d))
+    k = bf16_vals(r, (B, S, nkv, d))
+    v = bf16_vals(r, (B, S, nkv, d))
+    scale = 1 / math.sqrt(d)
+    if cache_layout:
+        smax = smax or S + 7
+        kc = torch.zeros(B, nkv, smax, d, dtype=dtype, device=DEV)
+        vc = torch.zeros(B, nkv, smax, d, dtype=dtype, device=DEV)
+        kc[:, :, :S] = up(k, dtype).permute(0, 2, 1, 3)
+        vc[:, :, :S] = up(v, dtype).permute(0, 2, 1, 3)
+        kt = kc.permute(0, 2, 1, 3)[:, :S]
+        vt = vc.permute(0, 2, 1, 3)[:, :S]
+    else:
+        kt, vt = up(k, dtype), up(v, dtype)
+    out = torch.empty(B, T, nh, d, dtype=dtype, device=DEV)
+    q2.q2_self_attention(out, up(q, dtype), kt, vt, scale)
+    got = down(out)
+    for b in range(B):
+        ref = oracle.attention(q[b], k[b], v[b], scale)
+        if dtype == BF:
+            assert_close(got[b], oracle.bf16_round(ref), 4e-3 * np.abs(v).max(), 2 ** -7, f"attention b={b}")
+        else:
+            assert_close(got[b], ref, 1e-6, 1e-5, f"attention f32 b={b}")
+
+
+@pytest.mark.parametrize("B,T,S,nh,nkv", [
+    (1, 1, 1, 12, 2),        # first token: output = v_0
+    (1, 1, 192, 12, 2),      # decode, several 16-key tiles, split-KV
+    (2, 1, 4097, 12, 2),     # long context, many splits, ragged tail
+    (1, 2, 50, 12, 2),       # two queries per head group (12 rows) in the decode kernel
+    (8, 1, 300, 28, 4),      # 7B-shaped group of 7
+    (1, 64, 64, 12, 2),      # one full prefill block
+    (1, 100, 300, 12, 2),    # prefill with a cached past, ragged
+    (2, 130, 130, 28, 4),    # several query blocks, batch 2
+])
+def test_attention_bf16(B, T, S, nh, nkv):
+    _attn_case(B * 7 + T * 13 + S, B, T, S, nh, nkv, 128, BF)
+
+
+@pytest.mark.parametrize("T,S", [(1, 33), (70, 200)])
+def test_attention_bf16_kv_cache_layout(T, S):
+    _attn_case(T + S, 2, T, S, 12, 2, 128, BF, cache_layout=True)
+
+
+@pytest.mark.parametrize("B,T,S,nh,nkv,d", [(1, 16, 16, 4, 2, 32), (2, 1, 40, 4, 2, 32), (1, 5, 9, 3, 1, 48)])
+def test_attention_f32(B, T, S, nh, nkv, d):
+    _attn_case(T * 3 + S, B, T, S, nh, nkv, d, torch.float32)
+
+
+# ------------------------------------------------------------------ swiglu / add
+
+@pytest.mark.parametrize("dtype", [BF, torch.float32])
+def test_swiglu_and_add(dtype):
+    r = rng(8)
+    g = bf16_vals(r, (33, 8960), 2.0)
+    u = bf16_vals(r, (33, 8960))
+    out = torch.empty(33, 8960, dtype=dtype, device=DEV)
+    q2.q2_swiglu(out, up(g, dtype), up(u, dtype))
+    ref = oracle.swiglu(g, u)
+    if dtype == BF:
+        assert_close(down(out), oracle.bf16_round(ref), 1e-6, 2 ** -7, "swiglu bf16")
+    else:
+        assert_close(down(out), ref, 1e-6, 1e-5, "swiglu f32")
+    c = torch.empty(33, 8960, dtype=dtype, device=DEV)
+    q2.q2_add(c, up(g, dtype), up(u, dtype))
+    ref = oracle.add(g, u)
+    if dtype == BF:
+        ref = oracle.bf16_round(ref)
+    assert np.array_equal(down(c), ref)
+
+
+def test_add_in_place_strided():
+    r = rng(9)
+    a = bf16_vals(r, (6, 300))
+    b = bf16_vals(r, (6, 256))
+    ta = up(a, BF)
+    view = ta[:, 20:276]
+    q2.q2_add(view, view, up(b, BF))
+    got = down(ta)
+    assert np.array_equal(got[:, 20:276], oracle.bf16_round(oracle.add(a[:, 20:276], b)))
+    assert np.array_equal(got[:, :20], a[:, :20]) and np.array_equal(got[:, 276:], a[:, 276:])
+
+
+# ------------------------------------------------------------------ argmax
+
+@pytest.mark.parametrize("dtype", [torch.float32, BF])
+def test_argmax_bit_exact(dtype):
+    r = rng(10)
+    V = 151936
+    x = oracle.bf16_round(r.standard_normal((4, V)).astype(np.float32))
+    x[1, [5, 150000]] = 9.0          # tie: lowest index
+    x[2, V - 1] = 20.0               # last index
+    x[3, :] = -1.0                   # all equal
+    idx = torch.empty(4, dtype=torch.int64, device=DEV)
+    val = torch.empty(4, dtype=torch.float32, device=DEV)
+    q2.q2_argmax(idx, val, up(x, dtype))
+    ri, rv = oracle.argmax(x)
+    assert np.array_equal(down(idx), ri) and np.array_equal(down(val), rv)
+    assert down(idx).tolist()[1:] == [5, V - 1, 0]
+
+
+# ------------------------------------------------------------------ rearrange
+
+@pytest.mark.parametrize("dtype", [BF, torch.float32, torch.int64])
+def test_rearrange_bit_exact(dtype):
+    r = rng(11)
+    src = torch.from_numpy(r.integers(-1000, 1000, (3, 4, 5, 6, 8))).to(dtype).to(DEV)
+    view = src.permute(4, 2, 0, 3, 1)
+    out = torch.empty(view.shape, dtype=dtype, device=DEV)
+    q2.q2_rearrange(out, view)
+    assert torch.equal(out.cpu(), view.cpu().contiguous())
+    # contiguous fast path and KV-cache style writeback into a strided destination
+    cache = torch.zeros(2, 4, 64, 128, dtype=dtype, device=DEV)
+    new = torch.from_numpy(r.integers(-9, 9, (2, 3, 4, 128))).to(dtype).to(DEV)
+    q2.q2_rearrange(cache.permute(0, 2, 1, 3)[:, 10:13], new)
+    assert torch.equal(cache.permute(0, 2, 1, 3)[:, 10:13].cpu(), new.cpu())
+    assert int((cache != 0).sum()) == int((new != 0).sum())
