@@ -190,6 +190,19 @@ q2_status q2_model_load_weight(q2_model* m, const char* name, int32_t layer, con
 q2_status q2_model_prefill(q2_model* m, const q2_tensor* ids, const q2_tensor* next,
                            const q2_tensor* logits, void* stream);
 
+/* Same as q2_model_prefill, but the first layer reads the hidden states
+ * `embeds` [B, T, H] (model dtype, rows contiguous) instead of looking token
+ * ids up in embed_tokens.  Used to check the layer stack on given inputs
+ * (layer-by-layer comparison) and for callers that bring their own embeddings. */
+q2_status q2_model_prefill_embeds(q2_model* m, const q2_tensor* embeds, const q2_tensor* next,
+                                  const q2_tensor* logits, void* stream);
+
+/* Describe the residual stream (the hidden states after the last layer, before
+ * the final norm) of the last prefill chunk or decode step: [rows, H] in the
+ * model dtype, row b * T + t for sequence b and token t of that chunk.  Valid
+ * until the next call on the model. */
+q2_status q2_model_hidden_view(q2_model* m, q2_tensor* x);
+
 /* One decode step: ids [B] int64 at position len; same outputs as prefill.
  * Replays a HIP graph captured once per batch size. */
 q2_status q2_model_decode(q2_model* m, const q2_tensor* ids, const q2_tensor* next,

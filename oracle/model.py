@@ -43,13 +43,19 @@ class OracleModel:
 
     ``weights`` maps (name, layer) -> array as produced by ``synth.make_weights``
     (uint16 bf16 bit patterns or float32).  ``storage`` is "bf16" or "fp32".
+    ``accum`` selects the accumulation precision of the linear layers: "f32"
+    (the pages' float compute) or "f64" (the same products summed in float64,
+    then rounded to float32).  Both are correct readings of the forward; the
+    distance between them measures how far two exact implementations that
+    differ only in summation rounding drift apart after bf16 storage rounding.
     """
 
-    def __init__(self, shape, weights, storage: str, batch: int, max_seq: int):
-        if storage not in ("bf16", "fp32"):
-            raise ValueError(storage)
+    def __init__(self, shape, weights, storage: str, batch: int, max_seq: int, accum: str = "f32"):
+        if storage not in ("bf16", "fp32") or accum not in ("f32", "f64"):
+            raise ValueError((storage, accum))
         self.shape = shape
         self.storage = storage
+        self.accum = accum
         self.batch = batch
         self.max_seq = max_seq
         self.w = {}
@@ -69,12 +75,27 @@ class OracleModel:
     def _weight(self, name, layer=-1):
         return self.w[(name, layer)]
 
-    def forward(self, ids: np.ndarray, all_logits: bool = False):
+    def _linear(self, x, w, b=None):
+        if self.accum == "f32":
+            return ops.linear(x, w, b)
+        y = np.matmul(np.asarray(x, np.float64), np.asarray(w, np.float64).T)
+        if b is not None:
+            y = y + np.asarray(b, np.float64)
+        return y.astype(F32)
+
+    def forward(self, ids: np.ndarray, all_logits: bool = False, embeds: np.ndarray | None = None,
+                layers: range | None = None, hidden: list | None = None):
         """Process ids [B, T] at positions length .. length+T-1.
 
         Returns (logits, next): logits [B, V] float32 of the last position (or
         [B, T, V] when ``all_logits``), next [B] int64 greedy tokens.
+        ``embeds`` [B, T, H] replaces the embedding lookup (ids then only give
+        the shape); ``layers`` restricts the layer stack (default: all);
+        ``hidden``, if a list, receives the residual stream after each layer.
         """
+        if embeds is not None:
+            embeds = np.asarray(embeds, F32)
+            ids = np.zeros(embeds.shape[:2], np.int64)
         ids = np.asarray(ids, np.int64)
         if ids.ndim == 1:
             ids = ids[:, None]
@@ -90,13 +111,17 @@ class OracleModel:
         pos = np.arange(P, P + T)
         scale = 1.0 / np.sqrt(d)
 
-        x = st(ops.embedding(ids.reshape(-1), self._weight("embed_tokens"))).reshape(B, T, H)
-        for l in range(sh.nlayer):
+        if embeds is not None:
+            x = st(embeds)
+        else:
+            x = st(ops.embedding(ids.reshape(-1), self._weight("embed_tokens"))).reshape(B, T, H)
+        lin = self._linear
+        for l in (layers if layers is not None else range(sh.nlayer)):
             W = lambda n: self._weight(n, l)          # noqa: E731
             h = st(ops.rms_norm(x, W("input_layernorm"), sh.eps))
-            q = st(ops.linear(h, W("q_proj.weight"), W("q_proj.bias"))).reshape(B, T, nh, d)
-            k = st(ops.linear(h, W("k_proj.weight"), W("k_proj.bias"))).reshape(B, T, nkv, d)
-            v = st(ops.linear(h, W("v_proj.weight"), W("v_proj.bias"))).reshape(B, T, nkv, d)
+            q = st(lin(h, W("q_proj.weight"), W("q_proj.bias"))).reshape(B, T, nh, d)
+            k = st(lin(h, W("k_proj.weight"), W("k_proj.bias"))).reshape(B, T, nkv, d)
+            v = st(lin(h, W("v_proj.weight"), W("v_proj.bias"))).reshape(B, T, nkv, d)
             o = np.empty((B, T, nh, d), F32)
             for b in range(B):
                 qb = st(ops.rope(q[b], pos, sh.theta))
@@ -106,18 +131,20 @@ class OracleModel:
                 kc = self.k_cache[l][b, :, :P + T, :].transpose(1, 0, 2)
                 vc = self.v_cache[l][b, :, :P + T, :].transpose(1, 0, 2)
                 o[b] = st(ops.attention(qb, kc, vc, scale))
-            a = st(ops.linear(o.reshape(B, T, nh * d), W("o_proj.weight")))
+            a = st(lin(o.reshape(B, T, nh * d), W("o_proj.weight")))
             x = st(ops.add(x, a))
             h2 = st(ops.rms_norm(x, W("post_attention_layernorm"), sh.eps))
-            g = st(ops.linear(h2, W("gate_proj.weight")))
-            u = st(ops.linear(h2, W("up_proj.weight")))
+            g = st(lin(h2, W("gate_proj.weight")))
+            u = st(lin(h2, W("up_proj.weight")))
             m = st(ops.swiglu(g, u))
-            dn = st(ops.linear(m, W("down_proj.weight")))
+            dn = st(lin(m, W("down_proj.weight")))
             x = st(ops.add(x, dn))
+            if hidden is not None:
+                hidden.append(x.copy())
         self.length = P + T
         xs = x if all_logits else x[:, -1, :]
         hf = st(ops.rms_norm(xs, self._weight("norm"), sh.eps))
-        logits = ops.linear(hf, self._weight("lm_head"))
+        logits = lin(hf, self._weight("lm_head"))
         nxt, _ = ops.argmax(logits if not all_logits else logits[:, -1, :])
         return logits, nxt
 

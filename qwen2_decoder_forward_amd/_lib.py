@@ -67,6 +67,8 @@ _SIGS = {
     "q2_model_device_bytes": ([ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "q2_model_load_weight": ([ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int32, _P, _S], ctypes.c_int),
     "q2_model_prefill": ([ctypes.c_void_p, _P, _P, _P, _S], ctypes.c_int),
+    "q2_model_prefill_embeds": ([ctypes.c_void_p, _P, _P, _P, _S], ctypes.c_int),
+    "q2_model_hidden_view": ([ctypes.c_void_p, _P], ctypes.c_int),
     "q2_model_decode": ([ctypes.c_void_p, _P, _P, _P, _S], ctypes.c_int),
     "q2_model_generate": ([ctypes.c_void_p, _P, ctypes.c_int32, _P, _S], ctypes.c_int),
     "q2_model_continue": ([ctypes.c_void_p, ctypes.c_int32, _P, _S], ctypes.c_int),
@@ -198,6 +200,17 @@ def q2_model_load_weight(h, name: str, layer: int, src, stream=None):
 
 def q2_model_prefill(h, ids, next_ids, logits=None, stream=None):
     _check(lib.q2_model_prefill(h, _ref(desc(ids)), _ref(desc(next_ids)), _ref(desc(logits)), _stream(stream)))
+
+
+def q2_model_prefill_embeds(h, embeds, next_ids, logits=None, stream=None):
+    _check(lib.q2_model_prefill_embeds(h, _ref(desc(embeds)), _ref(desc(next_ids)), _ref(desc(logits)),
+                                       _stream(stream)))
+
+
+def q2_model_hidden_view(h) -> Q2Tensor:
+    x = Q2Tensor()
+    _check(lib.q2_model_hidden_view(h, ctypes.byref(x)))
+    return x
 
 
 def q2_model_decode(h, ids, next_ids, logits=None, stream=None):

@@ -66,6 +66,7 @@ struct q2_model {
   // host state
   int len = 0;
   int cur_batch = 0;
+  int last_rows = 0;      // rows of x written by the last chunk / step
   bool len_dirty = true;
   hipStream_t cap = nullptr;
   std::map<std::pair<int, int>, hipGraphExec_t> graphs;
@@ -239,17 +240,33 @@ q2_status run_head(q2_model* m, int B, int Tc, float* logits, int64_t ld_logits,
   return check_launch("finalize");
 }
 
+// Copy hidden-state rows embeds[b, t0 + t, :] into x[b * tc + t, :].
+template <typename T>
+__global__ __launch_bounds__(256) void load_embeds_kernel(T* x, const T* e, int64_t e_bs, int64_t e_ts, int tc, int H) {
+  const int m = blockIdx.x;
+  const int b = m / tc, t = m - b * tc;
+  for (int i = threadIdx.x; i < H; i += 256) x[static_cast<int64_t>(m) * H + i] = e[b * e_bs + t * e_ts + i];
+}
+
 template <typename T>
 q2_status prefill_impl(q2_model* m, const int64_t* ids, int64_t ids_bs, int64_t ids_ts, int B, int Tn, float* logits,
-                       int64_t ld_logits, int64_t* next, int64_t next_stride, hipStream_t s) {
+                       int64_t ld_logits, int64_t* next, int64_t next_stride, hipStream_t s,
+                       const T* embeds = nullptr, int64_t e_bs = 0, int64_t e_ts = 0) {
   const int Tc_max = m->max_tok / B > 0 ? m->max_tok / B : 1;
   int tc = 0;
   for (int t0 = 0; t0 < Tn; t0 += tc) {
     tc = Tn - t0 < Tc_max ? Tn - t0 : Tc_max;
-    Q2_TRY(launch_embedding<T>(static_cast<T*>(m->x), m->cfg.hidden, ids + t0 * ids_ts, ids_bs, ids_ts, B, tc,
-                               static_cast<const T*>(m->embed), m->cfg.hidden, m->cfg.vocab, m->cfg.hidden, s));
+    if (embeds) {
+      hipLaunchKernelGGL(load_embeds_kernel<T>, dim3(B * tc), dim3(256), 0, s, static_cast<T*>(m->x),
+                         embeds + t0 * e_ts, e_bs, e_ts, tc, m->cfg.hidden);
+      Q2_TRY(check_launch("load_embeds"));
+    } else {
+      Q2_TRY(launch_embedding<T>(static_cast<T*>(m->x), m->cfg.hidden, ids + t0 * ids_ts, ids_bs, ids_ts, B, tc,
+                                 static_cast<const T*>(m->embed), m->cfg.hidden, m->cfg.vocab, m->cfg.hidden, s));
+    }
     Q2_TRY(run_layers<T>(m, B, tc, s));
     m->len += tc;
+    m->last_rows = B * tc;
   }
   return run_head<T>(m, B, tc, logits, ld_logits, next, next_stride, s);
 }
@@ -574,6 +591,48 @@ extern "C" q2_status q2_model_prefill(q2_model* m, const q2_tensor* ids, const q
                                  : prefill_impl<float>(m, ip, bs, ts, B, Tn, lp, lg.ld, np, ns, s);
 }
 
+extern "C" q2_status q2_model_prefill_embeds(q2_model* m, const q2_tensor* embeds, const q2_tensor* next,
+                                             const q2_tensor* logits, void* stream) {
+  clear_error();
+  Q2_CHECK(m, Q2_EINVAL, "null model");
+  Q2_TRY(check_desc(embeds, "embeds"));
+  Q2_CHECK(embeds->dtype == m->cfg.dtype, Q2_EDTYPE, "embeds must have the model dtype");
+  Q2_CHECK(embeds->ndim == 3 && embeds->shape[2] == m->cfg.hidden, Q2_ESHAPE, "embeds must be [B, T, H]");
+  Q2_CHECK(embeds->stride[2] == 1, Q2_ESTRIDE, "embeds rows must be contiguous");
+  const int B = static_cast<int>(embeds->shape[0]);
+  const int Tn = static_cast<int>(embeds->shape[1]);
+  Q2_CHECK(Tn >= 1, Q2_ESHAPE, "prefill needs at least one token");
+  Q2_TRY(check_batch(m, B, Tn));
+  int64_t ns = 0;
+  Q2_TRY(check_next(next, B, &ns));
+  Rows lg{};
+  Q2_TRY(check_logits(m, logits, B, &lg));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Q2_TRY(sync_len(m, s));
+  m->cur_batch = B;
+  int64_t* np = next ? static_cast<int64_t*>(next->data) : nullptr;
+  float* lp = logits ? reinterpret_cast<float*>(lg.data) : nullptr;
+  if (m->cfg.dtype == Q2_BF16)
+    return prefill_impl<uint16_t>(m, nullptr, 0, 0, B, Tn, lp, lg.ld, np, ns, s,
+                                  static_cast<const uint16_t*>(embeds->data), embeds->stride[0], embeds->stride[1]);
+  return prefill_impl<float>(m, nullptr, 0, 0, B, Tn, lp, lg.ld, np, ns, s, static_cast<const float*>(embeds->data),
+                             embeds->stride[0], embeds->stride[1]);
+}
+
+extern "C" q2_status q2_model_hidden_view(q2_model* m, q2_tensor* x) {
+  clear_error();
+  Q2_CHECK(m && x, Q2_EINVAL, "null argument");
+  memset(x, 0, sizeof *x);
+  x->data = m->x;
+  x->dtype = m->cfg.dtype;
+  x->ndim = 2;
+  x->shape[0] = m->last_rows;
+  x->shape[1] = m->cfg.hidden;
+  x->stride[0] = m->cfg.hidden;
+  x->stride[1] = 1;
+  return Q2_OK;
+}
+
 extern "C" q2_status q2_model_decode(q2_model* m, const q2_tensor* ids, const q2_tensor* next,
                                      const q2_tensor* logits, void* stream) {
   clear_error();
@@ -597,6 +656,7 @@ extern "C" q2_status q2_model_decode(q2_model* m, const q2_tensor* ids, const q2
   Q2_TRY(check_launch("copy_ids"));
   Q2_HIP(hipGraphLaunch(g, s));
   m->len += 1;
+  m->last_rows = B;
   if (next) {
     hipLaunchKernelGGL(copy_ids_kernel, dim3(1), dim3(64), 0, s, static_cast<int64_t*>(next->data), ns, m->ids_buf,
                        int64_t(1), B);
@@ -618,6 +678,7 @@ static q2_status run_steps(q2_model* m, int steps, const q2_tensor* out_ids, int
   const int start = m->len;  // the token produced last sits at position `start`
   for (int i = 0; i < steps; ++i) Q2_HIP(hipGraphLaunch(g, s));
   m->len += steps;
+  if (steps > 0) m->last_rows = B;
   if (out_ids) {
     const int n = static_cast<int>(out_ids->shape[1]);
     hipLaunchKernelGGL(copy_hist_kernel, dim3(cdiv(int64_t(n) * B, 256)), dim3(256), 0, s,

@@ -55,6 +55,20 @@ class Model:
         _lib.q2_model_prefill(self.handle, ids, nxt, lg)
         return (nxt, lg) if logits else nxt
 
+    def prefill_embeds(self, embeds, logits: bool = False):
+        B = embeds.shape[0]
+        nxt = torch.empty(B, dtype=torch.int64, device=embeds.device)
+        lg = torch.empty(B, self.shape.vocab, dtype=torch.float32, device=embeds.device) if logits else None
+        _lib.q2_model_prefill_embeds(self.handle, embeds, nxt, lg)
+        return (nxt, lg) if logits else nxt
+
+    def hidden(self):
+        """Copy of the residual stream rows of the last chunk, [rows, H]."""
+        view = _lib.q2_model_hidden_view(self.handle)
+        out = torch.empty(view.shape[0], view.shape[1], dtype=self.torch_dtype, device=f"cuda:{self.device}")
+        _lib.q2_rearrange(out, view)
+        return out
+
     def decode(self, ids, logits: bool = False):
         B = ids.shape[0]
         nxt = torch.empty(B, dtype=torch.int64, device=ids.device)

@@ -52,3 +52,36 @@ def test_workload_a_runs():
     toks, logits = m.generate(synth.make_prompt(wl), wl.steps)
     assert toks.shape == (1, wl.steps + 1) and len(logits) == wl.steps + 1
     assert m.length == wl.max_seq
+
+
+def test_embeds_layers_hidden_options_compose():
+    """forward(embeds=E[ids]) equals forward(ids); running layers [0, k) then
+    [k, L) from the recorded hidden state equals the full stack."""
+    sh = pins.tiny_shape(4)
+    w = synth.make_weights(sh, seed=22)
+    ids = np.array([[3, 9, 27, 1, 0]], np.int64)
+    full = oracle.OracleModel(sh, w, "bf16", 1, 8)
+    hs = []
+    ref, _ = full.forward(ids, hidden=hs)
+    assert len(hs) == sh.nlayer
+    E = w[("embed_tokens", -1)]
+    a, _ = oracle.OracleModel(sh, w, "bf16", 1, 8).forward(None, embeds=E[ids])
+    assert np.array_equal(a, ref)
+    part = oracle.OracleModel(sh, w, "bf16", 1, 8)
+    h1 = []
+    part.forward(ids, layers=range(0, 2), hidden=h1)
+    rest = oracle.OracleModel(sh, w, "bf16", 1, 8)
+    # the second half needs the first half's KV cache only for its own layers
+    b, _ = rest.forward(None, embeds=h1[-1], layers=range(2, 4))
+    assert np.array_equal(b, ref)
+
+
+def test_f64_accumulation_is_close_in_fp32_storage():
+    """In fp32 storage the two accumulation precisions agree to float32
+    rounding level (the gap only opens through bf16 storage rounding)."""
+    sh = pins.tiny_shape(3)
+    w = synth.make_weights(sh, seed=23)
+    ids = np.array([[1, 2, 3, 4]], np.int64)
+    a, _ = oracle.OracleModel(sh, w, "fp32", 1, 8, accum="f32").forward(ids)
+    b, _ = oracle.OracleModel(sh, w, "fp32", 1, 8, accum="f64").forward(ids)
+    assert np.abs(a - b).max() <= 1e-5 * np.abs(a).max()
