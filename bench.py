@@ -105,7 +105,7 @@ def dominant_kernel(wl, reps):
         out = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
         dt = time_launches(lambda: q2.q2_linear(out, X, W), reps, stream)
         traffic = N * K * 2 + M * K * 2 + M * N * 2
-        return {"kernel": "gemm_skinny_kernel (q2_linear, bf16, M=%d N=%d K=%d)" % (M, N, K),
+        return {"kernel": "gemv_kernel (q2_linear, bf16, M=%d N=%d K=%d)" % (M, N, K),
                 "bound": "hbm", "achieved": traffic / dt / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "bytes_per_launch": traffic, "avg_launch_us": dt * 1e6}
     if wl.key == "C":

@@ -7,7 +7,8 @@
 //                 query heads of the group share each K/V load.  Q K^T runs
 //                 on MFMA with K rows streamed straight from memory as the A
 //                 operand; P V runs on MFMA with V transposed through LDS.
-//                 Chunks beyond one are merged by attn_combine (split-KV).
+//                 With several chunks (split-KV) attn_combine merges the
+//                 partial results.
 //  * attn_prefill 64 queries of one head per workgroup (16 per wave), K and
 //                 V^T tiles of 64 keys staged in LDS, online softmax.
 // float32, any d <= 256: attn_f32, one wave per (query, head).
@@ -435,6 +436,11 @@ DecodePlan plan_decode(int B, int s_max, int nkv) {
 
 }  // namespace
 
+int attention_decode_splits(int B, int T, int s_max, int nh, int nkv, int d) {
+  if (d != D || T * (nh / nkv) > 16) return 0;
+  return plan_decode(B, s_max, nkv).nsplit;
+}
+
 size_t attention_scratch_bytes(int B, int T, int s_max, int nh, int nkv, int d) {
   if (d != D || T * (nh / nkv) > 16) return 0;
   DecodePlan p = plan_decode(B, s_max, nkv);
@@ -462,7 +468,7 @@ q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(attn_decode_kernel, dim3(p.nsplit, a.B * a.nkv), dim3(256), 0, s, a, p.chunk, p.nsplit,
                        part_o, part_ml);
     Q2_TRY(check_launch("attn_decode"));
-    if (p.nsplit > 1) {
+    if (p.nsplit > 1 && !a.leave_partials) {
       hipLaunchKernelGGL(attn_combine_kernel, dim3(a.B * a.nkv), dim3(256), 0, s, a, p.nsplit, part_o, part_ml);
       Q2_TRY(check_launch("attn_combine"));
     }

@@ -24,13 +24,19 @@ struct AttnArgs {
   float scale;
   const int* d_len;
   int s_max;
-  void* scratch;
+  void* scratch;               // split-KV partials
   size_t scratch_bytes;
+  bool leave_partials;         // split-KV: skip the merge, the consumer merges the partials
 };
 
 q2_status attention_bf16(const AttnArgs& a, hipStream_t s);
 q2_status attention_f32(const AttnArgs& a, hipStream_t s);
 // Scratch (bytes) the bf16 split-KV decode path needs for these sizes.
 size_t attention_scratch_bytes(int B, int T, int s_max, int nh, int nkv, int d);
+// Number of key chunks the bf16 decode kernel splits each (sequence, KV head)
+// into for these sizes; 0 when the prefill kernel handles them.  Partials
+// live at scratch: float O [B*nkv][nsplit][16][d], then float2 (max, sum)
+// [B*nkv][nsplit][16].
+int attention_decode_splits(int B, int T, int s_max, int nh, int nkv, int d);
 
 }  // namespace q2

@@ -132,7 +132,10 @@ __device__ __forceinline__ uint32_t argmax_key_index(uint64_t key) { return ~sta
 
 __host__ __device__ inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
 
-// Per-device scratch owned by the library (grown on demand, freed at exit).
+// Per-device scratch owned by the library (grown on demand, kept until the
+// process ends) for the partial results of split-K and split-KV operator
+// calls.  Calls that use it on the same device from different streams at the
+// same time race.
 q2_status device_scratch(size_t bytes, void** ptr);
 
 }  // namespace q2

@@ -41,9 +41,21 @@ struct Epi {
   const int* d_len;       // device cached length (position of t = 0) or null
   int len0;               // host cached length, used when d_len is null
   const float2* rope;     // [S_max][d/2] (cos, sin)
-  // ARGMAX
-  unsigned long long* keys;  // [M] packed keys, reset to 0 before the GEMM
+  // ARGMAX: packed (value, index) keys, KEY_SLOTS per row each on its own
+  // 128-byte line (stride KEY_STRIDE), combined with atomicMax: spreading a
+  // row's maxima over many lines keeps thousands of workgroups from queueing
+  // on one atomic unit.  Zero before the GEMM (the finalize kernel that reads
+  // them resets them).
+  unsigned long long* keys;
+  // RESID, decode path: per-row sums of squares of the new residual stream,
+  // one float per 16-feature tile (the next GEMV's fused RMSNorm reads them)
+  float* sq_out;
+  int64_t sq_ld;
 };
+
+constexpr int KEY_SLOTS = 64;
+constexpr int KEY_STRIDE = 16;  // 16 x 8 bytes = one 128-byte line per slot
+constexpr int KEY_ROW = KEY_SLOTS * KEY_STRIDE;
 
 template <typename T, int EK>
 __device__ __forceinline__ void epi_pair(const Epi& e, int m, int n, float v0, float v1, bool has1) {
@@ -124,13 +136,34 @@ struct GemmArgs {
   int64_t ldx;
   int M, N, K;
   Epi epi;
-  void* scratch;
+  void* scratch;             // float32 split-K partials (GEMV path)
   size_t scratch_bytes;
+  // fused RMSNorm of X's rows (GEMV path, M <= 16): X is the raw residual
+  // stream, the kernel multiplies it by 1/sqrt(sum(norm_sq row)/K + eps) and
+  // norm_w, rounded to the storage type, before the product
+  const void* norm_w;
+  const float* norm_sq;
+  int64_t norm_sq_ld;
+  float norm_eps;
+  // fused split-KV merge (GEMV path, M <= 16, one query token per sequence):
+  // X[m][h * 128 + d] is the attention output of sequence m, head h, merged
+  // from att_nsplit partial results (unnormalised output, running max and sum)
+  // laid out [m][kv head][split][16 rows][128] and [m][kv head][split][16]
+  const float* att_o;
+  const float2* att_ml;
+  int att_nsplit, att_group, att_nkv;
 };
 
 q2_status gemm_bf16(const GemmArgs& a, hipStream_t s);
 q2_status gemm_f32(const GemmArgs& a, hipStream_t s);
-// Split-K scratch the skinny path wants for this shape (0 if none).
+// GEMV path (M <= 64, bf16): gemv.hip.
+constexpr int GEMV_MAX_M = 64;
+constexpr int GEMV_NORM_MAX_M = 16;
+// bytes of X the GEMV path stages in LDS (fused sources need it to fit)
+constexpr size_t GEMV_STAGE_BYTES = size_t(64) << 10;
+bool gemv_can_fuse(int M, int K);
+q2_status gemv_bf16(const GemmArgs& a, hipStream_t s);
+// Split-K partial bytes the GEMV path needs for this shape (0 if unsplit).
 size_t gemm_scratch_bytes(int M, int N, int K);
 
 }  // namespace q2

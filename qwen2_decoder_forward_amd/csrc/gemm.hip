@@ -1,13 +1,10 @@
 // Linear layers: Y = X W^T with fused epilogues.
 //
-// Three kernels share one epilogue interface (epilogue.hpp):
+// Kernels sharing one epilogue interface (epilogue.hpp):
 //  * gemm_tile    bf16 MFMA, 128 features x 128 tokens per workgroup, K staged
 //                 through LDS in 64-wide double-buffered slices (prefill).
-//  * gemm_skinny  bf16 MFMA for M <= 64 tokens (decode): weights stream
-//                 straight from HBM into the A operand with 16-byte loads,
-//                 the few token rows ride in the B operand, waves split K and
-//                 reduce through LDS; optional split-K across workgroups.
 //  * gemm_f32     float32 FMA (the fp32 model), one output pair per thread.
+// Up to 64 token rows go to the weight-streaming GEMV kernel (gemv.hip).
 //
 // MFMA orientation: weights are the A operand (rows = output features) and
 // tokens the B operand, so a lane's four accumulators of a 16x16 tile are four
@@ -119,150 +116,6 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const uint16_t* __restri
   }
 }
 
-// ------------------------------------------------------------------ skinny kernel
-
-// MT token tiles of 16 (M <= 16*MT), NW waves per workgroup on the same 16
-// features, each wave taking every NW-th 32-wide K chunk of the workgroup's
-// chunk range.  gridDim.x = feature tiles, gridDim.y = K splits.
-template <typename T, int MT, int NW, int EK>
-__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const uint16_t* __restrict__ W, int64_t ldw,
-                                                              const uint16_t* __restrict__ X, int64_t ldx, int N,
-                                                              int M, int K, int chunks_per_split,
-                                                              float* __restrict__ partial, Epi epi) {
-  __shared__ floatx4_t red[NW][MT][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int f0 = blockIdx.x * 16;
-  const int row = lane & 15;
-  const int g = lane >> 4;
-  const int nchunks = (K + 31) >> 5;
-  const int c_begin = blockIdx.y * chunks_per_split;
-  const int c_end = min(c_begin + chunks_per_split, nchunks);
-
-  const bool wrow_ok = f0 + row < N;
-  const uint16_t* wp = W + static_cast<int64_t>(wrow_ok ? f0 + row : 0) * ldw + g * 8;
-  const uint16_t* xp[MT];
-  bool xok[MT];
-#pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    const int tok = j * 16 + row;
-    xok[j] = tok < M;
-    xp[j] = X + static_cast<int64_t>(xok[j] ? tok : 0) * ldx + g * 8;
-  }
-
-  floatx4_t acc[MT];
-#pragma unroll
-  for (int j = 0; j < MT; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-  constexpr int U = 4;  // chunks in flight per wave
-  const uint4 z = {0, 0, 0, 0};
-  int c = c_begin + wave;
-  for (; c + (U - 1) * NW < c_end; c += U * NW) {
-    uint4 a[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool kin = (c + u * NW) * 32 + g * 8 < K;
-      a[u] = (wrow_ok && kin) ? *reinterpret_cast<const uint4*>(wp + (c + u * NW) * 32) : z;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool kin = (c + u * NW) * 32 + g * 8 < K;
-#pragma unroll
-      for (int j = 0; j < MT; ++j) {
-        uint4 b = (xok[j] && kin) ? *reinterpret_cast<const uint4*>(xp[j] + (c + u * NW) * 32) : z;
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u]), as_bf16x8(b), acc[j], 0, 0, 0);
-      }
-    }
-  }
-  for (; c < c_end; c += NW) {
-    const bool kin = c * 32 + g * 8 < K;
-    uint4 a = (wrow_ok && kin) ? *reinterpret_cast<const uint4*>(wp + c * 32) : z;
-#pragma unroll
-    for (int j = 0; j < MT; ++j) {
-      uint4 b = (xok[j] && kin) ? *reinterpret_cast<const uint4*>(xp[j] + c * 32) : z;
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), acc[j], 0, 0, 0);
-    }
-  }
-
-  // reduce the NW waves' partial tiles
-#pragma unroll
-  for (int j = 0; j < MT; ++j) red[wave][j][lane] = acc[j];
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    floatx4_t s = red[0][j][lane];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      floatx4_t t = red[w][j][lane];
-      s[0] += t[0]; s[1] += t[1]; s[2] += t[2]; s[3] += t[3];
-    }
-    acc[j] = s;
-  }
-
-  const int f = f0 + g * 4;  // this lane's 4 features; token = j*16 + row
-  if (gridDim.y > 1) {
-#pragma unroll
-    for (int j = 0; j < MT; ++j) {
-      const int m = j * 16 + row;
-      if (m >= M) continue;
-      float* p = partial + (static_cast<int64_t>(blockIdx.y) * M + m) * N;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (f + r < N) p[f + r] = acc[j][r];
-    }
-    return;
-  }
-  if (EK == EPI_ARGMAX) {
-#pragma unroll
-    for (int j = 0; j < MT; ++j) {
-      const int m = j * 16 + row;
-      unsigned long long best = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (f + r < N && m < M) {
-          if (epi.out) static_cast<float*>(epi.out)[static_cast<int64_t>(m) * epi.ldo + f + r] = acc[j][r];
-          unsigned long long key = argmax_key(acc[j][r], f + r);
-          best = key > best ? key : best;
-        }
-      }
-      // combine the four lane groups holding the same token
-      unsigned long long o1 = __shfl_xor(best, 16, 64);
-      best = o1 > best ? o1 : best;
-      unsigned long long o2 = __shfl_xor(best, 32, 64);
-      best = o2 > best ? o2 : best;
-      if (g == 0 && m < M) atomicMax(epi.keys + m, best);
-    }
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    const int m = j * 16 + row;
-    if (m >= M) continue;
-    if (f < N) epi_pair<T, EK>(epi, m, f, acc[j][0], acc[j][1], f + 1 < N);
-    if (f + 2 < N) epi_pair<T, EK>(epi, m, f + 2, acc[j][2], acc[j][3], f + 3 < N);
-  }
-}
-
-// Sum split-K partials [splits][M][N] and apply the epilogue, one feature pair per thread.
-template <typename T, int EK>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int splits, int M,
-                                                            int N, Epi epi) {
-  const int npairs = (N + 1) >> 1;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<int64_t>(npairs) * M) return;
-  const int m = static_cast<int>(idx / npairs);
-  const int n = static_cast<int>(idx - static_cast<int64_t>(m) * npairs) * 2;
-  const bool has1 = n + 1 < N;
-  float v0 = 0.f, v1 = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float* p = partial + (static_cast<int64_t>(s) * M + m) * N + n;
-    v0 += p[0];
-    if (has1) v1 += p[1];
-  }
-  epi_pair<T, EK>(epi, m, n, v0, v1, has1);
-}
-
 // ------------------------------------------------------------------ float32 kernel
 
 template <int EK>
@@ -295,61 +148,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
       unsigned long long k1 = argmax_key(v1, n + 1);
       key = k1 > key ? k1 : key;
     }
-    atomicMax(epi.keys + m, key);
+    atomicMax(epi.keys + m * KEY_ROW + ((n >> 1) % KEY_SLOTS) * KEY_STRIDE, key);
     return;
   }
   epi_pair<float, EK>(epi, m, n, v0, v1, has1);
 }
 
-struct SkinnyPlan {
-  int mt, nw, splits, chunks_per_split;
-};
-
-SkinnyPlan plan_skinny(int M, int N, int K) {
-  SkinnyPlan p;
-  p.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
-  p.nw = 4;
-  const int tiles = cdiv(N, 16);
-  const int nchunks = cdiv(K, 32);
-  // aim for >= 512 workgroups, each wave owning at least 4 chunks
-  int splits = 1;
-  while (tiles * splits < 512 && nchunks / (splits * 2) >= 4 * p.nw) splits *= 2;
-  if (p.mt > 1 && splits > 1) splits = 1;  // partials would outweigh the weights
-  p.splits = splits;
-  p.chunks_per_split = cdiv(nchunks, splits);
-  p.splits = cdiv(nchunks, p.chunks_per_split);
-  return p;
-}
-
-template <typename T, int MT, int EK>
-q2_status launch_skinny(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
-  dim3 grid(cdiv(a.N, 16), p.splits);
-  hipLaunchKernelGGL((gemm_skinny_kernel<T, MT, 4, EK>), grid, dim3(256), 0, s, static_cast<const uint16_t*>(a.W),
-                     a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M, a.K, p.chunks_per_split,
-                     static_cast<float*>(a.scratch), a.epi);
-  Q2_TRY(check_launch("gemm_skinny"));
-  if (p.splits > 1) {
-    const int64_t work = static_cast<int64_t>((a.N + 1) / 2) * a.M;
-    hipLaunchKernelGGL((splitk_reduce_kernel<T, EK>), dim3(cdiv(work, 256)), dim3(256), 0, s,
-                       static_cast<const float*>(a.scratch), p.splits, a.M, a.N, a.epi);
-    Q2_TRY(check_launch("splitk_reduce"));
-  }
-  return Q2_OK;
-}
-
 template <int EK>
 q2_status gemm_bf16_ek(const GemmArgs& a, hipStream_t s) {
-  if (a.M <= 64) {
-    SkinnyPlan p = plan_skinny(a.M, a.N, a.K);
-    Q2_CHECK(EK != EPI_ARGMAX || p.splits == 1, Q2_ESHAPE, "argmax epilogue needs an unsplit K");
-    if (p.splits > 1) {
-      const size_t need = static_cast<size_t>(p.splits) * a.M * a.N * sizeof(float);
-      Q2_CHECK(a.scratch && a.scratch_bytes >= need, Q2_EINVAL, "linear: split-K scratch too small");
-    }
-    if (p.mt == 1) return launch_skinny<uint16_t, 1, EK>(a, p, s);
-    if (p.mt == 2) return launch_skinny<uint16_t, 2, EK>(a, p, s);
-    return launch_skinny<uint16_t, 4, EK>(a, p, s);
-  }
   if constexpr (EK == EPI_ARGMAX) {
     return fail(Q2_ESHAPE, "argmax epilogue supports at most 64 rows");
   } else {
@@ -370,15 +176,11 @@ q2_status gemm_f32_ek(const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-size_t gemm_scratch_bytes(int M, int N, int K) {
-  if (M > 64) return 0;
-  SkinnyPlan p = plan_skinny(M, N, K);
-  return p.splits > 1 ? static_cast<size_t>(p.splits) * M * N * sizeof(float) : 0;
-}
-
 q2_status gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0 || a.N == 0) return Q2_OK;
   Q2_CHECK(a.K % 8 == 0, Q2_ESHAPE, "bf16 linear: K=%d must be a multiple of 8", a.K);
+  if (a.M <= GEMV_MAX_M) return gemv_bf16(a, s);
+  Q2_CHECK(a.norm_w == nullptr, Q2_EINVAL, "fused RMSNorm needs M <= %d", GEMV_NORM_MAX_M);
   switch (a.epi.kind) {
     case EPI_STORE: return gemm_bf16_ek<EPI_STORE>(a, s);
     case EPI_RESID: return gemm_bf16_ek<EPI_RESID>(a, s);

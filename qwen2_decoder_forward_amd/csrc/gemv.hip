@@ -1,0 +1,451 @@
+// Decode-path linear layers: Y[M, N] = X[M, K] W[N, K]^T for M <= 64 rows.
+//
+// Bound by reading W once from HBM.  A workgroup owns a tile of 16 weight
+// rows; its four waves share that tile's K range, each taking 128-wide K
+// blocks in turn.  A lane (row r = lane % 16, group g = lane / 16) loads four
+// 16-byte pieces of row r per block (all issued before any math); load u of
+// the four lane groups covers 64 contiguous bytes of each of the 16 rows.
+// They feed four 16x16x32 bf16 MFMAs with the weight rows as the A operand;
+// the token rows ride in the B operand (up to 16 per MFMA, 1-4 MFMA column
+// tiles).  MFMA u of lane group g covers k = 32 u + 8 g .. + 7 on both
+// operands.
+//
+// When the tiles alone would not give every CU work (one CU streams only
+// about 20 GB/s), K is split over several workgroups that write float32
+// partials; a small second kernel sums them in a fixed order and applies the
+// epilogue, so results are deterministic.  (A last-arriving-workgroup
+// reduction needs device-scope fences, which write back the L2 and cost far
+// more than the extra launch on this chip.)
+//
+// Prologue: when it fits, the workgroup first stages the rows of X it needs
+// (its K range) in LDS, built from one of three sources: the plain rows; the
+// raw residual stream with RMSNorm applied (from per-16-feature sums of
+// squares written by the producer of X, so no normalisation kernel runs); or
+// the merge of split-KV attention partials (so no merge kernel runs).
+#include <algorithm>
+
+#include "epilogue.hpp"
+
+namespace q2 {
+
+namespace {
+
+constexpr int KB = 128;  // K per block
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
+  bf16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// rnd(x * inv * w) for 8 bf16 lanes of a 16-byte vector.
+__device__ __forceinline__ uint4 norm8(uint4 x, uint4 w, float inv) {
+  uint4 r;
+  const uint32_t* xs = &x.x;
+  const uint32_t* ws = &w.x;
+  uint32_t* rs = &r.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = (bf_lo(xs[i]) * inv) * bf_lo(ws[i]);
+    const float b = (bf_hi(xs[i]) * inv) * bf_hi(ws[i]);
+    rs[i] = pack_bf2(a, b);
+  }
+  return r;
+}
+
+enum XSrc : int { XSRC_RAW = 0, XSRC_NORM = 1, XSRC_ATTN = 2 };
+
+struct GemvSrc {
+  const uint16_t* w;   // NORM
+  const float* sq;
+  int64_t sq_ld;
+  float eps;
+  const float* att_o;  // ATTN
+  const float2* att_ml;
+  int att_nsplit, att_group, att_nkv;
+};
+
+// 8 consecutive features (h * 128 + d0 .. + 7) of the merged attention output
+// of sequence m, rounded to bf16.
+__device__ __forceinline__ uint4 attn_merge8(const GemvSrc& src, int m, int k) {
+  const int h = k >> 7;
+  const int d0 = k & 127;
+  const int g = h / src.att_group;
+  const int r = h - g * src.att_group;
+  const int64_t base = (static_cast<int64_t>(m) * src.att_nkv + g) * src.att_nsplit * 16 + r;
+  float mx = -__builtin_huge_valf();
+  for (int sp = 0; sp < src.att_nsplit; ++sp) mx = fmaxf(mx, src.att_ml[base + sp * 16].x);
+  const float bse = mx == -__builtin_huge_valf() ? 0.f : mx;
+  float l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < src.att_nsplit; ++sp) {
+    const float2 ml = src.att_ml[base + sp * 16];
+    if (ml.x == -__builtin_huge_valf()) continue;
+    const float f = __expf(ml.x - bse);
+    l += f * ml.y;
+    const float4* po = reinterpret_cast<const float4*>(src.att_o + (base + sp * 16) * 128 + d0);
+    const float4 a = po[0], b = po[1];
+    o[0] += f * a.x; o[1] += f * a.y; o[2] += f * a.z; o[3] += f * a.w;
+    o[4] += f * b.x; o[5] += f * b.y; o[6] += f * b.z; o[7] += f * b.w;
+  }
+  const float inv = 1.f / l;
+  uint4 r4;
+  r4.x = pack_bf2(o[0] * inv, o[1] * inv);
+  r4.y = pack_bf2(o[2] * inv, o[3] * inv);
+  r4.z = pack_bf2(o[4] * inv, o[5] * inv);
+  r4.w = pack_bf2(o[6] * inv, o[7] * inv);
+  return r4;
+}
+
+// Epilogue of a 16-feature tile for token row m: thread p (0..7 within an
+// aligned group of 8 lanes) owns features n0 + 2p, n0 + 2p + 1.
+template <int EK>
+__device__ __forceinline__ void gemv_epilogue(const Epi& epi, int M, int N, int n0, int tile, int m, int p, float v0,
+                                              float v1) {
+  const int n = n0 + 2 * p;
+  const bool valid = m < M && n < N;
+  const bool has1 = n + 1 < N;
+  if constexpr (EK == EPI_ARGMAX) {
+    unsigned long long key = 0;
+    if (valid) {
+      if (epi.out) {
+        float* o = static_cast<float*>(epi.out) + static_cast<int64_t>(m) * epi.ldo + n;
+        o[0] = v0;
+        if (has1) o[1] = v1;
+      }
+      key = argmax_key(v0, n);
+      if (has1) {
+        const unsigned long long k1 = argmax_key(v1, n + 1);
+        key = k1 > key ? k1 : key;
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      const unsigned long long k = __shfl_xor(key, o, 64);
+      key = k > key ? k : key;
+    }
+    if (valid && p == 0) atomicMax(epi.keys + m * KEY_ROW + (tile % KEY_SLOTS) * KEY_STRIDE, key);
+  } else if constexpr (EK == EPI_RESID) {
+    float sq = 0.f;
+    if (valid) {
+      uint16_t* o = static_cast<uint16_t*>(epi.out) + static_cast<int64_t>(m) * epi.ldo + n;
+      const float a = round_bf(bf2f(o[0]) + round_bf(v0));
+      o[0] = f2bf(a);
+      sq = a * a;
+      if (has1) {
+        const float b = round_bf(bf2f(o[1]) + round_bf(v1));
+        o[1] = f2bf(b);
+        sq += b * b;
+      }
+    }
+    sq += __shfl_xor(sq, 1, 64);
+    sq += __shfl_xor(sq, 2, 64);
+    sq += __shfl_xor(sq, 4, 64);
+    if (valid && p == 0 && epi.sq_out) epi.sq_out[m * epi.sq_ld + tile] = sq;
+  } else {
+    if (valid) epi_pair<uint16_t, EK>(epi, m, n, v0, v1, has1);
+  }
+}
+
+// gridDim.x = 16-row tiles, gridDim.y = K splits.  With SPLIT the float32
+// partial tile goes to partial[split][m][n] and gemv_reduce_kernel applies the
+// epilogue; otherwise the epilogue runs here.
+// With STAGE the X rows of this workgroup's K range are built in dynamic
+// LDS first (required for the NORM and ATTN sources).  Every wave streams
+// weights: handing the staging to a few dedicated waves lowers the loads in
+// flight more than it saves.  The occupancy bound keeps two 16-wave
+// workgroups resident per CU (at most 64 VGPRs): one more register halves the
+// workgroups in flight and costs a third of the bandwidth on the long
+// LM-head pass.
+template <int MT, int NW, int EK, int SRC, bool STAGE, bool SPLIT>
+__global__ __launch_bounds__(NW * 64, MT == 1 ? 8 : 4) void gemv_kernel(const uint16_t* __restrict__ W, int64_t ldw,
+                                                       const uint16_t* __restrict__ X, int64_t ldx, int N, int M, int K,
+                                                       int blocks_per_split, GemvSrc src, float* __restrict__ partial,
+                                                       Epi epi) {
+  constexpr int WW = NW;
+  __shared__ float s_inv[16 * MT];
+  __shared__ floatx4_t red[NW][MT][64];
+  __shared__ float tile[16 * MT][17];
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_x[];
+  constexpr bool NORM = SRC == XSRC_NORM;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int row = lane & 15;
+  const int g = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int nkb = (K + KB - 1) / KB;
+  const int kb0 = blockIdx.y * blocks_per_split;
+  const int kb1 = min(kb0 + blocks_per_split, nkb);
+  const int k_lo = kb0 * KB;
+  const int k_hi = min(kb1 * KB, K);
+  const int ld_s = k_hi - k_lo + 8;  // LDS row stride of the staged X (+16 bytes of padding)
+
+  // the weight loads do not depend on X: the first batch goes out before the
+  // prologue so that its latency overlaps the staging of X.  Loads are
+  // unconditional within the block range (out-of-range rows and the K tail
+  // read a clamped in-range address and are zeroed afterwards) so the
+  // compiler issues them back to back.
+  const bool wrow_ok = n0 + row < N;
+  const uint16_t* __restrict__ wp = W + static_cast<int64_t>(wrow_ok ? n0 + row : 0) * ldw + 8 * g;
+  const uint4 z = {0, 0, 0, 0};
+  constexpr int BATCH = 2;  // blocks whose weights are in flight at once per wave
+  uint4 wv[BATCH][4];
+  bool wok[BATCH][4];
+#define Q2_GEMV_LOAD_BATCH(KB_)                                                              \
+  _Pragma("unroll") for (int b = 0; b < BATCH; ++b) {                                       \
+    const int kk = (KB_) + NW * b;                                                          \
+    if (kk < kb1) { /* wave-uniform: no loads for blocks past the range */                  \
+      _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                       \
+        const int k = kk * KB + 32 * u + 8 * g;                                             \
+        wok[b][u] = wrow_ok && k < K;                                                       \
+        wv[b][u] = ld16(wp + (wok[b][u] ? static_cast<int64_t>(kk) * KB + 32 * u : 0));      \
+      }                                                                                     \
+    }                                                                                       \
+  }
+  Q2_GEMV_LOAD_BATCH(kb0 + wave)
+
+  if constexpr (NORM) {
+    const int ntiles = K >> 4;
+    for (int m = wave; m < M; m += NW) {
+      float ss = 0.f;
+      for (int t = lane; t < ntiles; t += 64) ss += src.sq[m * src.sq_ld + t];
+      ss = wave_sum(ss);
+      if (lane == 0) s_inv[m] = 1.0f / sqrtf(ss / static_cast<float>(K) + src.eps);
+    }
+    __syncthreads();
+  }
+  if constexpr (STAGE) {
+    // X[:, k_lo .. k_hi) into LDS
+    const int chunks = (k_hi - k_lo) >> 3;
+    for (int idx = tid; idx < M * chunks; idx += NW * 64) {
+      const int m = idx / chunks;
+      const int k = k_lo + 8 * (idx - m * chunks);
+      uint4 v;
+      if constexpr (SRC == XSRC_ATTN) {
+        v = attn_merge8(src, m, k);
+      } else {
+        v = ld16(X + static_cast<int64_t>(m) * ldx + k);
+        if constexpr (NORM) v = norm8(v, ld16(src.w + k), s_inv[m]);
+      }
+      *reinterpret_cast<uint4*>(s_x + m * ld_s + (k - k_lo)) = v;
+    }
+    __syncthreads();
+  }
+
+  const uint16_t* xp[MT];
+  bool xok[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int tok = 16 * j + row;
+    xok[j] = tok < M;
+    if constexpr (STAGE)
+      xp[j] = s_x + (xok[j] ? tok : 0) * ld_s + 8 * g - k_lo;
+    else
+      xp[j] = X + static_cast<int64_t>(xok[j] ? tok : 0) * ldx + 8 * g;
+  }
+
+  floatx4_t acc[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int kb = kb0 + wave; kb < kb1; kb += NW * BATCH) {
+    if (kb != kb0 + wave) Q2_GEMV_LOAD_BATCH(kb)
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      const int kk = kb + NW * b;
+      if (kk >= kb1) break;
+#pragma unroll
+      for (int j = 0; j < MT; ++j) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int k = kk * KB + 32 * u + 8 * g;
+          const bool ok = xok[j] && k < K;
+          uint4 xv = ld16(xp[j] + (ok ? static_cast<int64_t>(kk) * KB + 32 * u : k_lo - 8 * g));
+          if (!ok) xv = z;
+          const uint4 wvv = wok[b][u] ? wv[b][u] : z;
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wvv), as_bf16x8(xv), acc[j], 0, 0, 0);
+        }
+      }
+    }
+  }
+#undef Q2_GEMV_LOAD_BATCH
+
+  // sum the weight waves' partial tiles (fixed order)
+  if (wave < WW) {
+#pragma unroll
+    for (int j = 0; j < MT; ++j) red[wave][j][lane] = acc[j];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      floatx4_t s = red[0][j][lane];
+#pragma unroll
+      for (int w = 1; w < WW; ++w) {
+        const floatx4_t t = red[w][j][lane];
+        s[0] += t[0]; s[1] += t[1]; s[2] += t[2]; s[3] += t[3];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tile[16 * j + row][4 * g + r] = s[r];
+    }
+  }
+  __syncthreads();
+
+  if constexpr (SPLIT) {
+    for (int t = tid; t < M * 16; t += NW * 64) {
+      const int m = t >> 4, f = t & 15;
+      if (n0 + f < N) partial[(static_cast<int64_t>(blockIdx.y) * M + m) * N + n0 + f] = tile[m][f];
+    }
+    return;
+  }
+  const int Mp = 16 * MT;
+  for (int base = 0; base < Mp * 8; base += NW * 64) {
+    const int t = base + tid;
+    const int m = t >> 3;
+    const int p = t & 7;
+    const float v0 = m < Mp ? tile[m][2 * p] : 0.f;
+    const float v1 = m < Mp ? tile[m][2 * p + 1] : 0.f;
+    gemv_epilogue<EK>(epi, M, N, n0, blockIdx.x, m, p, v0, v1);
+  }
+}
+
+// Sums the split-K partials of 32 (row, tile) pairs per workgroup, in split
+// order, and applies the epilogue.
+template <int EK>
+__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ partial, int splits, int M, int N,
+                                                          Epi epi) {
+  const int ntiles = (N + 15) >> 4;
+  const int pair = blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int p = threadIdx.x & 7;
+  const int m = pair / ntiles;
+  const int tl = pair - m * ntiles;
+  const int n = tl * 16 + 2 * p;
+  float v0 = 0.f, v1 = 0.f;
+  if (m < M && n < N) {
+    const bool has1 = n + 1 < N;
+    for (int sp = 0; sp < splits; ++sp) {
+      const float* q = partial + (static_cast<int64_t>(sp) * M + m) * N + n;
+      v0 += q[0];
+      if (has1) v1 += q[1];
+    }
+  }
+  gemv_epilogue<EK>(epi, M, N, tl * 16, tl, m < M ? m : M, p, v0, v1);
+}
+
+struct GemvPlan {
+  int mt, nw, splits, bps;
+};
+
+GemvPlan plan_gemv(int M, int N, int K) {
+  GemvPlan p;
+  p.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+  p.nw = p.mt == 4 ? 8 : 16;
+  const int tiles = cdiv(N, 16);
+  const int nkb = cdiv(K, KB);
+  // every CU needs work (a CU alone streams only ~20 GB/s): split K until
+  // there are about 512 workgroups while each keeps at least NW/2 K blocks;
+  // with many token rows keep the partials well below the weight bytes
+  const int cap = p.mt == 1 ? 64 : max(1, K / (8 * M));
+  int splits = 1;
+  while (tiles * splits < 512 && nkb / (splits + 1) >= p.nw / 2 && splits + 1 <= cap) ++splits;
+  p.bps = cdiv(nkb, splits);
+  p.splits = cdiv(nkb, p.bps);
+  return p;
+}
+
+size_t stage_bytes(int M, int bps, int K) {
+  const int klen = std::min(bps * KB, K);
+  return static_cast<size_t>(M) * (klen + 8) * sizeof(uint16_t);
+}
+
+template <int MT, int NW, int EK, int SRC, bool STAGE>
+q2_status launch_gemv2(const GemmArgs& a, const GemvPlan& p, size_t lds, hipStream_t s) {
+  const GemvSrc src{static_cast<const uint16_t*>(a.norm_w), a.norm_sq, a.norm_sq_ld, a.norm_eps, a.att_o, a.att_ml,
+                    a.att_nsplit, a.att_group, a.att_nkv};
+  const dim3 grid(cdiv(a.N, 16), p.splits);
+  if (p.splits == 1) {
+    hipLaunchKernelGGL((gemv_kernel<MT, NW, EK, SRC, STAGE, false>), grid, dim3(NW * 64), lds, s,
+                       static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M,
+                       a.K, p.bps, src, nullptr, a.epi);
+    return check_launch("gemv");
+  }
+  hipLaunchKernelGGL((gemv_kernel<MT, NW, EK, SRC, STAGE, true>), grid, dim3(NW * 64), lds, s,
+                     static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M, a.K,
+                     p.bps, src, static_cast<float*>(a.scratch), a.epi);
+  return check_launch("gemv");
+}
+
+template <int MT, int NW, int EK, int SRC>
+q2_status launch_gemv(const GemmArgs& a, const GemvPlan& p, hipStream_t s) {
+  const size_t sb = stage_bytes(a.M, p.bps, a.K);
+  if constexpr (SRC != XSRC_RAW) {
+    Q2_CHECK(sb <= GEMV_STAGE_BYTES, Q2_ESHAPE, "gemv: fused source does not fit in LDS");
+    Q2_TRY((launch_gemv2<MT, NW, EK, SRC, true>(a, p, sb, s)));
+  } else {
+    if (sb <= GEMV_STAGE_BYTES)
+      Q2_TRY((launch_gemv2<MT, NW, EK, SRC, true>(a, p, sb, s)));
+    else
+      Q2_TRY((launch_gemv2<MT, NW, EK, SRC, false>(a, p, 0, s)));
+  }
+  if (p.splits == 1) return Q2_OK;
+  const int pairs = a.M * cdiv(a.N, 16);
+  hipLaunchKernelGGL((gemv_reduce_kernel<EK>), dim3(cdiv(pairs, 32)), dim3(256), 0, s,
+                     static_cast<const float*>(a.scratch), p.splits, a.M, a.N, a.epi);
+  return check_launch("gemv_reduce");
+}
+
+template <int EK>
+q2_status gemv_ek(const GemmArgs& a, const GemvPlan& p, hipStream_t s) {
+  if (a.norm_w) return launch_gemv<1, 16, EK, XSRC_NORM>(a, p, s);
+  if (a.att_o) return launch_gemv<1, 16, EK, XSRC_ATTN>(a, p, s);
+  if (p.mt == 1) return launch_gemv<1, 16, EK, XSRC_RAW>(a, p, s);
+  if (p.mt == 2) return launch_gemv<2, 16, EK, XSRC_RAW>(a, p, s);
+  return launch_gemv<4, 8, EK, XSRC_RAW>(a, p, s);
+}
+
+}  // namespace
+
+bool gemv_can_fuse(int M, int K) {
+  // the staged K range is largest without splits
+  return M <= GEMV_NORM_MAX_M && stage_bytes(M, cdiv(K, KB), K) <= GEMV_STAGE_BYTES;
+}
+
+size_t gemm_scratch_bytes(int M, int N, int K) {
+  if (M > GEMV_MAX_M) return 0;
+  GemvPlan p = plan_gemv(M, N, K);
+  return p.splits > 1 ? static_cast<size_t>(p.splits) * M * N * sizeof(float) : 0;
+}
+
+q2_status gemv_bf16(const GemmArgs& a, hipStream_t s) {
+  Q2_CHECK(a.M >= 1 && a.M <= GEMV_MAX_M, Q2_ESHAPE, "gemv: M=%d not in [1, %d]", a.M, GEMV_MAX_M);
+  Q2_CHECK(a.K % 8 == 0, Q2_ESHAPE, "gemv: K must be a multiple of 8");
+  GemvPlan p = plan_gemv(a.M, a.N, a.K);
+  if (a.norm_w) {
+    Q2_CHECK(a.M <= GEMV_NORM_MAX_M && a.norm_sq && a.K % 16 == 0, Q2_EINVAL, "gemv: bad fused-norm arguments");
+  }
+  if (a.att_o) {
+    Q2_CHECK(!a.norm_w && a.M <= GEMV_NORM_MAX_M && a.att_ml && a.att_nsplit >= 1 && a.K % 128 == 0, Q2_EINVAL,
+             "gemv: bad fused attention-merge arguments");
+  }
+  if (a.epi.kind == EPI_ARGMAX) {
+    p.splits = 1;
+    p.bps = cdiv(a.K, KB);
+  }
+  if (p.splits > 1) {
+    const size_t need = static_cast<size_t>(p.splits) * a.M * a.N * sizeof(float);
+    Q2_CHECK(a.scratch && a.scratch_bytes >= need, Q2_EINVAL, "gemv: split-K scratch too small");
+  }
+  switch (a.epi.kind) {
+    case EPI_STORE: return gemv_ek<EPI_STORE>(a, p, s);
+    case EPI_RESID: return gemv_ek<EPI_RESID>(a, p, s);
+    case EPI_SWIGLU: return gemv_ek<EPI_SWIGLU>(a, p, s);
+    case EPI_QKV: return gemv_ek<EPI_QKV>(a, p, s);
+    case EPI_ARGMAX: return gemv_ek<EPI_ARGMAX>(a, p, s);
+  }
+  return fail(Q2_EINVAL, "unknown epilogue %d", a.epi.kind);
+}
+
+}  // namespace q2

@@ -16,6 +16,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <map>
 #include <new>
 #include <string>
@@ -63,6 +64,8 @@ struct q2_model {
   size_t gscratch_bytes = 0;
   void* ascratch = nullptr;
   size_t ascratch_bytes = 0;
+  float* sq = nullptr;            // [max_tok][hidden / 16] row sums of squares (decode path)
+  int64_t sq_ld = 0;
   // host state
   int len = 0;
   int cur_batch = 0;
@@ -82,19 +85,40 @@ __global__ void copy_ids_kernel(int64_t* dst, int64_t dst_stride, const int64_t*
   if (b < B) dst[b * dst_stride] = src[b * src_stride];
 }
 
-// next token of each sequence from the packed argmax keys; stores it for the
-// next step (ids_buf), in the history at its position, optionally in `next`;
-// resets the keys for the next LM-head pass.
-__global__ void finalize_kernel(unsigned long long* keys, int64_t* ids_buf, int64_t* hist, int64_t hist_ld,
-                                const int* d_len, int64_t* next, int64_t next_stride, int B) {
-  const int b = threadIdx.x;
-  if (b >= B) return;
-  const int pos = *d_len;
-  const int64_t id = static_cast<int64_t>(argmax_key_index(keys[b]));
-  keys[b] = 0ull;
-  ids_buf[b] = id;
-  hist[b * hist_ld + pos] = id;
-  if (next) next[b * next_stride] = id;
+// Next token of each sequence from its KEY_SLOTS packed argmax keys: stores it
+// for the next step (ids_buf), in the history at its position (len + pending),
+// optionally in `next`; resets the keys; then moves the device length on by
+// `pending` (the positions of this forward not yet counted).  One workgroup.
+__global__ __launch_bounds__(256) void finalize_kernel(unsigned long long* keys, int64_t* ids_buf, int64_t* hist,
+                                                       int64_t hist_ld, int* d_len, int pending, int64_t* next,
+                                                       int64_t next_stride, int B) {
+  __shared__ unsigned long long red[4];
+  const int pos = *d_len + pending;
+  for (int b = 0; b < B; ++b) {
+    unsigned long long best = 0;
+    for (int i = threadIdx.x; i < KEY_SLOTS; i += 256) {
+      unsigned long long* slot = keys + b * KEY_ROW + i * KEY_STRIDE;
+      const unsigned long long k = *slot;
+      best = k > best ? k : best;
+      *slot = 0ull;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long k = __shfl_xor(best, o, 64);
+      best = k > best ? k : best;
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int w = 1; w < 4; ++w) best = red[w] > best ? red[w] : best;
+      const int64_t id = static_cast<int64_t>(argmax_key_index(best));
+      ids_buf[b] = id;
+      hist[b * hist_ld + pos] = id;
+      if (next) next[b * next_stride] = id;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && pending) *d_len += pending;
 }
 
 __global__ void copy_hist_kernel(int64_t* out, int64_t ld_out, const int64_t* hist, int64_t hist_ld, int start, int n,
@@ -134,21 +158,44 @@ GemmArgs gemm_args(const q2_model* m, const void* W, int64_t ldw, const void* X,
   return a;
 }
 
+// Which kernels a forward of M token rows uses: up to 64 rows of a bf16 model
+// go through the weight-streaming GEMV; up to 16 rows also fuse each RMSNorm
+// into the GEMV that consumes it (fed by per-tile sums of squares).
+struct Path {
+  bool gemv;
+  bool fused_norm;
+};
+Path path_for(const q2_model* m, int M) {
+  Path p;
+  p.gemv = m->cfg.dtype == Q2_BF16 && M <= GEMV_MAX_M;
+  p.fused_norm = p.gemv && gemv_can_fuse(M, m->cfg.hidden) && gemv_can_fuse(M, m->cfg.nh * m->cfg.dh);
+  return p;
+}
+
 // Transformer layers for B sequences x Tc new tokens whose ids are already
-// embedded in x.  Positions start at the device length.
+// embedded in x.  Positions start at the device length; with `advance` the
+// device length moves on by Tc at the end.
 template <typename T>
-q2_status run_layers(q2_model* m, int B, int Tc, hipStream_t s) {
+q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
   const q2_config& c = m->cfg;
   const int M = B * Tc;
   const int H = c.hidden, d = c.dh, qd = c.nh * c.dh;
+  const Path path = path_for(m, M);
   for (int l = 0; l < c.nlayer; ++l) {
     const q2_model::Layer& L = m->layers[l];
     void* kc = static_cast<char*>(m->kc) + l * m->kv_lstride * m->esize;
     void* vc = static_cast<char*>(m->vc) + l * m->kv_lstride * m->esize;
-    Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->h), H, static_cast<const T*>(m->x), H, static_cast<const T*>(L.w_in),
-                             M, H, c.eps, s));
+    if (!path.fused_norm)
+      Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->h), H, static_cast<const T*>(m->x), H,
+                               static_cast<const T*>(L.w_in), M, H, c.eps, s));
     {
-      GemmArgs a = gemm_args(m, L.w_qkv, H, m->h, H, M, m->qkv_out, H);
+      GemmArgs a = gemm_args(m, L.w_qkv, H, path.fused_norm ? m->x : m->h, H, M, m->qkv_out, H);
+      if (path.fused_norm) {
+        a.norm_w = L.w_in;
+        a.norm_sq = m->sq;
+        a.norm_sq_ld = m->sq_ld;
+        a.norm_eps = c.eps;
+      }
       a.epi.kind = EPI_QKV;
       a.epi.out = m->q;
       a.epi.ldo = qd;
@@ -165,8 +212,12 @@ q2_status run_layers(q2_model* m, int B, int Tc, hipStream_t s) {
       a.epi.rope = m->rope;
       Q2_TRY(gemm(m, a, s));
     }
+    // with one query per sequence and split-KV partials, o_proj merges them itself
+    const int nsplit = c.dtype == Q2_BF16 ? attention_decode_splits(B, Tc, c.max_seq, c.nh, c.nkv, d) : 0;
+    const bool merge_in_o = path.fused_norm && Tc == 1 && nsplit > 1;
     {
       AttnArgs a{};
+      a.leave_partials = merge_in_o;
       a.q = m->q;
       a.q_bs = static_cast<int64_t>(Tc) * qd;
       a.q_ts = qd;
@@ -195,15 +246,32 @@ q2_status run_layers(q2_model* m, int B, int Tc, hipStream_t s) {
     }
     {
       GemmArgs a = gemm_args(m, L.w_o, qd, m->att, qd, M, H, qd);
+      if (merge_in_o) {
+        const size_t slots = static_cast<size_t>(B) * c.nkv * nsplit * 16;
+        a.att_o = static_cast<const float*>(m->ascratch);
+        a.att_ml = reinterpret_cast<const float2*>(static_cast<const float*>(m->ascratch) + slots * d);
+        a.att_nsplit = nsplit;
+        a.att_group = c.nh / c.nkv;
+        a.att_nkv = c.nkv;
+      }
       a.epi.kind = EPI_RESID;
       a.epi.out = m->x;
       a.epi.ldo = H;
+      a.epi.sq_out = path.fused_norm ? m->sq : nullptr;
+      a.epi.sq_ld = m->sq_ld;
       Q2_TRY(gemm(m, a, s));
     }
-    Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->h), H, static_cast<const T*>(m->x), H,
-                             static_cast<const T*>(L.w_post), M, H, c.eps, s));
+    if (!path.fused_norm)
+      Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->h), H, static_cast<const T*>(m->x), H,
+                               static_cast<const T*>(L.w_post), M, H, c.eps, s));
     {
-      GemmArgs a = gemm_args(m, L.w_gu, H, m->h, H, M, 2 * c.inter, H);
+      GemmArgs a = gemm_args(m, L.w_gu, H, path.fused_norm ? m->x : m->h, H, M, 2 * c.inter, H);
+      if (path.fused_norm) {
+        a.norm_w = L.w_post;
+        a.norm_sq = m->sq;
+        a.norm_sq_ld = m->sq_ld;
+        a.norm_eps = c.eps;
+      }
       a.epi.kind = EPI_SWIGLU;
       a.epi.out = m->act;
       a.epi.ldo = c.inter;
@@ -214,38 +282,70 @@ q2_status run_layers(q2_model* m, int B, int Tc, hipStream_t s) {
       a.epi.kind = EPI_RESID;
       a.epi.out = m->x;
       a.epi.ldo = H;
+      a.epi.sq_out = path.fused_norm ? m->sq : nullptr;
+      a.epi.sq_ld = m->sq_ld;
       Q2_TRY(gemm(m, a, s));
     }
   }
+  if (!advance) return Q2_OK;
   hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(1), 0, s, m->d_len, Tc);
   return check_launch("advance_len");
 }
 
 // Final norm of each sequence's last row, LM head with argmax, finalize.
+// `pending` is the number of new positions the device length has not been
+// advanced by yet (1 for a decode step, whose finalize advances it; 0 after
+// a prefill, whose layers already did).
 template <typename T>
-q2_status run_head(q2_model* m, int B, int Tc, float* logits, int64_t ld_logits, int64_t* next, int64_t next_stride,
-                   hipStream_t s) {
+q2_status run_head(q2_model* m, int B, int Tc, int pending, float* logits, int64_t ld_logits, int64_t* next,
+                   int64_t next_stride, hipStream_t s) {
   const q2_config& c = m->cfg;
   const int H = c.hidden;
-  Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->xl), H, static_cast<const T*>(m->x) + static_cast<int64_t>(Tc - 1) * H,
-                           static_cast<int64_t>(Tc) * H, static_cast<const T*>(m->w_final), B, H, c.eps, s));
-  GemmArgs a = gemm_args(m, m->lm_head, H, m->xl, H, B, c.vocab, H);
+  const Path path = path_for(m, B * Tc);
+  const bool fused = path.fused_norm && Tc == 1;
+  if (!fused)
+    Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->xl), H,
+                             static_cast<const T*>(m->x) + static_cast<int64_t>(Tc - 1) * H,
+                             static_cast<int64_t>(Tc) * H, static_cast<const T*>(m->w_final), B, H, c.eps, s));
+  GemmArgs a = gemm_args(m, m->lm_head, H, fused ? m->x : m->xl, H, B, c.vocab, H);
+  if (fused) {
+    a.norm_w = m->w_final;
+    a.norm_sq = m->sq;
+    a.norm_sq_ld = m->sq_ld;
+    a.norm_eps = c.eps;
+  }
   a.epi.kind = EPI_ARGMAX;
   a.epi.out = logits;
   a.epi.ldo = ld_logits;
   a.epi.keys = m->keys;
   Q2_TRY(gemm(m, a, s));
-  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(64), 0, s, m->keys, m->ids_buf, m->hist,
-                     static_cast<int64_t>(c.max_seq) + 1, m->d_len, next, next_stride, B);
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(256), 0, s, m->keys, m->ids_buf, m->hist,
+                     static_cast<int64_t>(c.max_seq) + 1, m->d_len, pending, next, next_stride, B);
   return check_launch("finalize");
 }
 
 // Copy hidden-state rows embeds[b, t0 + t, :] into x[b * tc + t, :].
+// (with sq: also each row's sums of squares per 16-feature tile)
 template <typename T>
-__global__ __launch_bounds__(256) void load_embeds_kernel(T* x, const T* e, int64_t e_bs, int64_t e_ts, int tc, int H) {
+__global__ __launch_bounds__(256) void load_embeds_kernel(T* x, const T* e, int64_t e_bs, int64_t e_ts, int tc, int H,
+                                                          float* sq, int64_t sq_ld) {
   const int m = blockIdx.x;
   const int b = m / tc, t = m - b * tc;
-  for (int i = threadIdx.x; i < H; i += 256) x[static_cast<int64_t>(m) * H + i] = e[b * e_bs + t * e_ts + i];
+  for (int i0 = 0; i0 < H; i0 += 256) {
+    const int i = i0 + threadIdx.x;
+    float v = 0.f;
+    if (i < H) {
+      const T xv = e[b * e_bs + t * e_ts + i];
+      x[static_cast<int64_t>(m) * H + i] = xv;
+      v = St<T>::ld(&xv);
+    }
+    if (sq) {
+      float ss = v * v;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o, 64);
+      if (i < H && (threadIdx.x & 15) == 0) sq[m * sq_ld + i / 16] = ss;
+    }
+  }
 }
 
 template <typename T>
@@ -256,28 +356,32 @@ q2_status prefill_impl(q2_model* m, const int64_t* ids, int64_t ids_bs, int64_t 
   int tc = 0;
   for (int t0 = 0; t0 < Tn; t0 += tc) {
     tc = Tn - t0 < Tc_max ? Tn - t0 : Tc_max;
+    float* sq = path_for(m, B * tc).fused_norm ? m->sq : nullptr;
     if (embeds) {
       hipLaunchKernelGGL(load_embeds_kernel<T>, dim3(B * tc), dim3(256), 0, s, static_cast<T*>(m->x),
-                         embeds + t0 * e_ts, e_bs, e_ts, tc, m->cfg.hidden);
+                         embeds + t0 * e_ts, e_bs, e_ts, tc, m->cfg.hidden, sq, m->sq_ld);
       Q2_TRY(check_launch("load_embeds"));
     } else {
       Q2_TRY(launch_embedding<T>(static_cast<T*>(m->x), m->cfg.hidden, ids + t0 * ids_ts, ids_bs, ids_ts, B, tc,
-                                 static_cast<const T*>(m->embed), m->cfg.hidden, m->cfg.vocab, m->cfg.hidden, s));
+                                 static_cast<const T*>(m->embed), m->cfg.hidden, m->cfg.vocab, m->cfg.hidden, s, sq,
+                                 m->sq_ld));
     }
-    Q2_TRY(run_layers<T>(m, B, tc, s));
+    Q2_TRY(run_layers<T>(m, B, tc, true, s));
     m->len += tc;
     m->last_rows = B * tc;
   }
-  return run_head<T>(m, B, tc, logits, ld_logits, next, next_stride, s);
+  return run_head<T>(m, B, tc, 0, logits, ld_logits, next, next_stride, s);
 }
 
 // One decode step from ids_buf (the graph body).
 template <typename T>
 q2_status decode_body(q2_model* m, int B, bool want_logits, hipStream_t s) {
+  float* sq = path_for(m, B).fused_norm ? m->sq : nullptr;
   Q2_TRY(launch_embedding<T>(static_cast<T*>(m->x), m->cfg.hidden, m->ids_buf, 1, 0, B, 1,
-                             static_cast<const T*>(m->embed), m->cfg.hidden, m->cfg.vocab, m->cfg.hidden, s));
-  Q2_TRY(run_layers<T>(m, B, 1, s));
-  return run_head<T>(m, B, 1, want_logits ? m->logits_buf : nullptr, m->cfg.vocab, nullptr, 0, s);
+                             static_cast<const T*>(m->embed), m->cfg.hidden, m->cfg.vocab, m->cfg.hidden, s, sq,
+                             m->sq_ld));
+  Q2_TRY(run_layers<T>(m, B, 1, false, s));
+  return run_head<T>(m, B, 1, 1, want_logits ? m->logits_buf : nullptr, m->cfg.vocab, nullptr, 0, s);
 }
 
 q2_status get_graph(q2_model* m, int B, bool want_logits, hipGraphExec_t* out) {
@@ -467,14 +571,15 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
   const size_t a_x = take(mt * H * es), a_h = take(mt * H * es), a_q = take(mt * qd * es), a_att = take(mt * qd * es);
   const size_t a_act = take(mt * I * es), a_xl = take(size_t(c.max_batch) * H * es);
   const size_t a_logits = take(size_t(c.max_batch) * V * sizeof(float));
-  const size_t a_keys = take(size_t(c.max_batch) * 8), a_ids = take(size_t(c.max_batch) * 8);
+  const size_t a_keys = take(size_t(c.max_batch) * KEY_ROW * 8), a_ids = take(size_t(c.max_batch) * 8);
   const size_t a_hist = take(size_t(c.max_batch) * (c.max_seq + 1) * 8), a_len = take(sizeof(int));
+  m->sq_ld = c.hidden / 16;
+  const size_t a_sq = take(mt * size_t(m->sq_ld) * sizeof(float));
   size_t gs = 0;
   {
-    const int mm = c.max_batch < 16 ? c.max_batch : 16;
     const int shapes[4][2] = {{m->qkv_out, c.hidden}, {c.hidden, int(qd)}, {2 * c.inter, c.hidden}, {c.hidden, c.inter}};
     for (int i = 0; i < 4; ++i)
-      for (int mm2 = 1; mm2 <= mm; ++mm2) {
+      for (int mm2 = 1; mm2 <= m->max_tok && mm2 <= GEMV_MAX_M; ++mm2) {
         size_t b = gemm_scratch_bytes(mm2, shapes[i][0], shapes[i][1]);
         gs = b > gs ? b : gs;
       }
@@ -532,6 +637,7 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
   m->d_len = reinterpret_cast<int*>(m->amem + a_len);
   m->gscratch = gs ? m->amem + a_gs : nullptr;
   m->ascratch = as ? m->amem + a_as : nullptr;
+  m->sq = reinterpret_cast<float*>(m->amem + a_sq);
   if (hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking) != hipSuccess)
     return cleanup(fail(Q2_EHIP, "stream creation failed"));
   q2_status st = launch_rope_table(m->rope, c.max_seq, c.dh, c.theta, nullptr);

@@ -9,10 +9,13 @@ namespace {
 
 // ------------------------------------------------------------------ embedding
 
+// out[m] = w[ids[m]]; with sq (bf16, H % 16 == 0, vector path) also the sum of
+// squares of each 16-feature tile of the row: sq[m * sq_ld + f / 16].
 template <typename T>
 __global__ __launch_bounds__(256) void embedding_kernel(T* __restrict__ out, int64_t ldo, const int64_t* __restrict__ ids,
                                                         int64_t ids_bs, int64_t ids_ts, int Tn, const T* __restrict__ w,
-                                                        int64_t ldw, int V, int H) {
+                                                        int64_t ldw, int V, int H, float* __restrict__ sq,
+                                                        int64_t sq_ld) {
   const int m = blockIdx.x;
   const int b = m / Tn;
   const int t = m - b * Tn;
@@ -24,8 +27,24 @@ __global__ __launch_bounds__(256) void embedding_kernel(T* __restrict__ out, int
   const bool vec = (H % VEC == 0) && aligned16(o) && aligned16(src);
   if (vec) {
     const uint4 z = {0, 0, 0, 0};
-    for (int i = threadIdx.x * VEC; i < H; i += 256 * VEC)
-      *reinterpret_cast<uint4*>(o + i) = ok ? *reinterpret_cast<const uint4*>(src + i) : z;
+    for (int i0 = 0; i0 < H; i0 += 256 * VEC) {
+      const int i = i0 + threadIdx.x * VEC;
+      uint4 v = z;
+      if (i < H) {
+        v = ok ? *reinterpret_cast<const uint4*>(src + i) : z;
+        *reinterpret_cast<uint4*>(o + i) = v;
+      }
+      if constexpr (sizeof(T) == 2) {
+        if (sq) {  // two consecutive threads hold one 16-feature tile
+          float ss = 0.f;
+          const uint32_t* ws = &v.x;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) ss += bf_lo(ws[k]) * bf_lo(ws[k]) + bf_hi(ws[k]) * bf_hi(ws[k]);
+          ss += __shfl_xor(ss, 1, 64);
+          if (i < H && (threadIdx.x & 1) == 0) sq[m * sq_ld + i / 16] = ss;
+        }
+      }
+    }
   } else {
     for (int i = threadIdx.x; i < H; i += 256) o[i] = ok ? src[i] : T(0);
   }
@@ -235,10 +254,13 @@ int grid_for(int64_t n) {
 
 template <typename T>
 q2_status launch_embedding(T* out, int64_t ldo, const int64_t* ids, int64_t ids_bs, int64_t ids_ts, int B, int Tn,
-                           const T* weight, int64_t ldw, int V, int H, hipStream_t s) {
+                           const T* weight, int64_t ldw, int V, int H, hipStream_t s, float* sq, int64_t sq_ld) {
   if (B * Tn == 0) return Q2_OK;
+  if (sq)
+    Q2_CHECK(sizeof(T) == 2 && H % 16 == 0 && aligned16(out) && aligned16(weight) && ldo % 8 == 0 && ldw % 8 == 0,
+             Q2_EINVAL, "embedding: row sums of squares need aligned bf16 rows");
   hipLaunchKernelGGL(embedding_kernel<T>, dim3(B * Tn), dim3(256), 0, s, out, ldo, ids, ids_bs, ids_ts, Tn, weight, ldw,
-                     V, H);
+                     V, H, sq, sq_ld);
   return check_launch("embedding");
 }
 
@@ -267,9 +289,9 @@ q2_status launch_swiglu(T* o, int64_t ldo, const T* g, int64_t ldg, const T* u, 
 }
 
 template q2_status launch_embedding<float>(float*, int64_t, const int64_t*, int64_t, int64_t, int, int, const float*,
-                                           int64_t, int, int, hipStream_t);
+                                           int64_t, int, int, hipStream_t, float*, int64_t);
 template q2_status launch_embedding<uint16_t>(uint16_t*, int64_t, const int64_t*, int64_t, int64_t, int, int,
-                                              const uint16_t*, int64_t, int, int, hipStream_t);
+                                              const uint16_t*, int64_t, int, int, hipStream_t, float*, int64_t);
 template q2_status launch_rmsnorm<float>(float*, int64_t, const float*, int64_t, const float*, int, int, float,
                                          hipStream_t);
 template q2_status launch_rmsnorm<uint16_t>(uint16_t*, int64_t, const uint16_t*, int64_t, const uint16_t*, int, int,
@@ -388,9 +410,9 @@ extern "C" q2_status q2_linear(const q2_tensor* out, const q2_tensor* in, const 
   Q2_CHECK(a.K % 8 == 0, Q2_ESHAPE, "bf16 linear: K must be a multiple of 8");
   Q2_CHECK(aligned16(x.data) && aligned16(w.data) && (x.ld % 8 == 0 || x.rows <= 1) && (w.ld % 8 == 0 || w.rows <= 1),
            Q2_ESTRIDE, "bf16 linear: in and weight rows must be 16-byte aligned");
-  const size_t need = gemm_scratch_bytes(a.M, a.N, a.K);
-  if (need) {
-    Q2_TRY(device_scratch(need, &a.scratch));
+  if (a.M <= GEMV_MAX_M) {
+    const size_t need = gemm_scratch_bytes(a.M, a.N, a.K);
+    if (need) Q2_TRY(device_scratch(need, &a.scratch));
     a.scratch_bytes = need;
   }
   return gemm_bf16(a, s);

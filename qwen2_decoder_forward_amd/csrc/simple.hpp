@@ -7,10 +7,12 @@
 namespace q2 {
 
 // out[m, :] = weight[ids[b, t0 + t], :] for m = b * T + t (ids strides in elements).
-// Rows whose id is outside [0, V) are zero-filled.
+// Rows whose id is outside [0, V) are zero-filled.  With `sq` (bf16 only) it
+// also writes each row's sums of squares per 16-feature tile, sq[m * sq_ld + f/16].
 template <typename T>
 q2_status launch_embedding(T* out, int64_t ldo, const int64_t* ids, int64_t ids_bs, int64_t ids_ts, int B, int Tn,
-                           const T* weight, int64_t ldw, int V, int H, hipStream_t s);
+                           const T* weight, int64_t ldw, int V, int H, hipStream_t s, float* sq = nullptr,
+                           int64_t sq_ld = 0);
 
 // RMSNorm of `rows` rows; input row r is in + r*ldi.
 template <typename T>
