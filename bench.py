@@ -13,7 +13,11 @@ and prompts are resident in HBM before the timed region.
 
 Also reported:
   roofline      the dominant kernel of the step, launched through the C ABI at
-                its in-step shape and timed with HIP events on the same stream.
+                its in-step shape and timed with HIP events on the same stream
+                (bandwidth-bound kernels cycle through operands several times
+                the last-level cache); `traffic` is its HBM bytes per launch
+                from profiler counters (profiles/traffic.json) while the
+                kernel source is unchanged since they were taken.
   step_roofline algorithmic bytes (or flops) of a whole decode (prefill) step
                 against the HBM (MFMA) peak.
   cpu_baseline  the oracle (plain NumPy) timed on this host on a bounded
@@ -43,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--only-kernel", action="store_true",
+                    help="time only the dominant kernel (for profiler counter runs) and print its record")
     return ap.parse_args()
 
 
@@ -89,6 +95,13 @@ def time_launches(fn, reps, stream):
     return e0.elapsed_time(e1) / reps * 1e-3   # seconds per launch
 
 
+# Weight buffers the dominant-kernel timing cycles through: together they are
+# several times the 256 MB last-level (Infinity) cache, so every launch streams
+# its operand from HBM as it does inside a decode step.
+CYCLE_BYTES = 1 << 30
+CALIB_COPY_BYTES = 512 << 20   # plain device copy, the reference for the HBM byte counters
+
+
 def dominant_kernel(wl, reps):
     """Time the dominant kernel at its in-step shape through the C ABI."""
     import torch
@@ -97,15 +110,27 @@ def dominant_kernel(wl, reps):
     dev = "cuda:0"
     stream = torch.cuda.current_stream()
     g = torch.Generator(device=dev).manual_seed(0)
+    # a copy of known size, so that profiler byte counters can be scaled
+    src = torch.empty(CALIB_COPY_BYTES // 4, device=dev, dtype=torch.float32).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
     if wl.key in ("B", "E"):
         # decode GEMV/skinny GEMM over the packed gate/up weight [2I, H]
         M, N, K = wl.batch, 2 * sh.inter, sh.hidden
-        W = (torch.randn(N, K, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+        nbuf = max(2, -(-CYCLE_BYTES // (N * K * 2)))
+        Ws = [(torch.randn(N, K, device=dev, generator=g) * 0.02).to(torch.bfloat16) for _ in range(nbuf)]
         X = torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16)
         out = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
-        dt = time_launches(lambda: q2.q2_linear(out, X, W), reps, stream)
+        it = [0]
+
+        def launch():
+            q2.q2_linear(out, X, Ws[it[0] % nbuf])
+            it[0] += 1
+        dt = time_launches(launch, reps, stream)
         traffic = N * K * 2 + M * K * 2 + M * N * 2
-        return {"kernel": "gemv_kernel (q2_linear, bf16, M=%d N=%d K=%d)" % (M, N, K),
+        return {"kernel": "gemv_kernel (q2_linear, bf16, M=%d N=%d K=%d, %d weight buffers cycled)" % (M, N, K, nbuf),
                 "bound": "hbm", "achieved": traffic / dt / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "bytes_per_launch": traffic, "avg_launch_us": dt * 1e6}
     if wl.key == "C":
@@ -120,15 +145,45 @@ def dominant_kernel(wl, reps):
                 "flops_per_launch": flops, "avg_launch_us": dt * 1e6}
     # D: split-KV decode attention over a 4097-key cache for 64 sequences
     B, S = wl.batch, wl.prompt + 1
+    kv_bytes = 2 * B * S * sh.nkv * sh.dh * 2
+    nbuf = max(2, -(-CYCLE_BYTES // kv_bytes))
     q = torch.randn(B, 1, sh.nh, sh.dh, device=dev, generator=g).to(torch.bfloat16)
-    k = torch.randn(B, S, sh.nkv, sh.dh, device=dev, generator=g).to(torch.bfloat16)
-    v = torch.randn(B, S, sh.nkv, sh.dh, device=dev, generator=g).to(torch.bfloat16)
+    kvs = [(torch.randn(B, S, sh.nkv, sh.dh, device=dev, generator=g).to(torch.bfloat16),
+            torch.randn(B, S, sh.nkv, sh.dh, device=dev, generator=g).to(torch.bfloat16)) for _ in range(nbuf)]
     o = torch.empty_like(q)
-    dt = time_launches(lambda: q2.q2_self_attention(o, q, k, v, sh.dh ** -0.5), reps, stream)
-    traffic = 2 * B * S * sh.nkv * sh.dh * 2 + 2 * q.numel() * 2
-    return {"kernel": "attn_decode_kernel + attn_combine_kernel (q2_self_attention, B=%d S=%d)" % (B, S),
-            "bound": "hbm", "achieved": traffic / dt / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+    it = [0]
+
+    def launch():
+        k, v = kvs[it[0] % nbuf]
+        q2.q2_self_attention(o, q, k, v, sh.dh ** -0.5)
+        it[0] += 1
+    dt = time_launches(launch, reps, stream)
+    traffic = kv_bytes + 2 * q.numel() * 2
+    return {"kernel": "attn_decode_kernel + attn_combine_kernel (q2_self_attention, B=%d S=%d, %d caches cycled)"
+            % (B, S, nbuf), "bound": "hbm", "achieved": traffic / dt / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "bytes_per_launch": traffic, "avg_launch_us": dt * 1e6}
+
+
+def measured_traffic(wl):
+    """HBM bytes per launch of the dominant kernel from the committed profiler
+    counter runs, or None when they are absent or the kernel source changed
+    since they were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(wl.key)
+    except (OSError, ValueError):
+        return None
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return rec["traffic_bytes"]
 
 
 def cpu_baseline(wl, weights, budget_s):
@@ -191,6 +246,10 @@ def main():
     sh = wl.shape
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.only_kernel:
+        dk = dominant_kernel(wl, args.kernel_reps)
+        print(json.dumps({"workload": wl.key, "dominant_kernel": dk}), flush=True)
+        return
     t0 = time.perf_counter()
     weights = synth.make_weights(wl)
     t_gen = time.perf_counter() - t0
@@ -238,7 +297,7 @@ def main():
 
     dk = dominant_kernel(wl, args.kernel_reps)
     roofline = {"bound": dk["bound"], "achieved": round(dk["achieved"], 2), "peak": dk["peak"], "unit": dk["unit"],
-                "frac": round(dk["achieved"] / dk["peak"], 4), "traffic": None, "kernel": dk["kernel"],
+                "frac": round(dk["achieved"] / dk["peak"], 4), "traffic": measured_traffic(wl), "kernel": dk["kernel"],
                 "avg_launch_us": round(dk["avg_launch_us"], 2)}
     for key in ("bytes_per_launch", "flops_per_launch"):
         if key in dk:
