@@ -32,12 +32,6 @@ constexpr int K_ROW = D + 8;  // bf16 per K LDS row in attn_prefill (272 B: conf
 constexpr int VT_PRE = 72;    // bf16 per V^T LDS row in attn_prefill: 64 keys + pad
 constexpr float NEG_INF = -__builtin_huge_valf();
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
-  bf16x8_t r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
-}
-
 __device__ __forceinline__ short4_t as_short4(uint2 v) {
   short4_t r;
   __builtin_memcpy(&r, &v, 8);

@@ -69,8 +69,16 @@ __host__ __device__ inline bool aligned16(const void* p) { return (reinterpret_c
 // ---------------------------------------------------------------- device helpers
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+
+// The 16 bytes of a uint4 as an MFMA operand of eight bf16 values.
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
+  bf16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short short4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16_t;
 
 // bf16 <-> float.  Widening is exact; narrowing rounds to nearest, ties to even.
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }

@@ -1,119 +1,578 @@
 // Linear layers: Y = X W^T with fused epilogues.
 //
 // Kernels sharing one epilogue interface (epilogue.hpp):
-//  * gemm_tile    bf16 MFMA, 128 features x 128 tokens per workgroup, K staged
-//                 through LDS in 64-wide double-buffered slices (prefill).
+//  * gemm_dtl     bf16, 32x32x16 MFMA, operands loaded straight into a
+//                 four-stage LDS ring, epilogue staged through LDS for
+//                 row-contiguous stores (prefill; K % 128 == 0).
+//  * gemm_big     bf16, 16x16x32 MFMA, register-staged double-buffered LDS
+//                 (prefill shapes the first kernel does not take).
 //  * gemm_f32     float32 FMA (the fp32 model), one output pair per thread.
 // Up to 64 token rows go to the weight-streaming GEMV kernel (gemv.hip).
 //
 // MFMA orientation: weights are the A operand (rows = output features) and
-// tokens the B operand, so a lane's four accumulators of a 16x16 tile are four
+// tokens the B operand, so a lane's accumulators hold runs of four
 // consecutive features of one token -- the adjacent feature pairs the QKV
 // (rotate-half) and SwiGLU epilogues need are in the same lane.
+#include <type_traits>
+
 #include "epilogue.hpp"
 
 namespace q2 {
 
 namespace {
 
-constexpr int TB_N = 128;   // features per workgroup (tile kernel)
-constexpr int TB_M = 128;   // tokens per workgroup
-constexpr int TB_K = 64;    // K slice per LDS stage
-constexpr int LDS_STRIDE = TB_K + 8;  // bf16 elements per LDS row (+16 B padding: conflict-free b128 reads)
+// ------------------------------------------------------------------ large-tile kernel
+//
+// BN features x BM tokens per workgroup, WN x WM waves, each wave a
+// (BN/WN) x (BM/WM) block of 16x16 MFMA tiles.  K moves in 64-wide slices
+// through two LDS stages: the next slice's global loads are issued before the
+// current slice's MFMAs and written to LDS after them, one barrier per slice.
+//
+// LDS rows are 128 bytes (64 bf16) with the eight 16-byte chunks of row r
+// stored at chunk c ^ ((r ^ (r >> 1)) & 7): the fragment reads (16 rows, one
+// chunk column, per 16 lanes) and the slice writes (one row per 8 lanes)
+// both touch distinct banks, for 32 or 64 four-byte banks.
+//
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2); the tile order gives each XCD a contiguous band of tiles, token tiles
+// fastest, so the workgroups resident on one XCD share their weight tiles.
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
-  bf16x8_t r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
-}
+__device__ __forceinline__ int lds_swz(int r, int c) { return c ^ ((r ^ (r >> 1)) & 7); }
 
-// ------------------------------------------------------------------ tile kernel
+template <int BN, int BM, int WN, int WM>
+struct BigTile {
+  static constexpr int NT = WN * WM * 64;
+  static constexpr int TN = BN / WN, TM = BM / WM;
+  static constexpr int FN = TN / 16, FM = TM / 16;
+  static constexpr int BK = 64;
+  static constexpr int A_LD = BN * 8 / NT;   // 16-byte weight chunks per thread per slice
+  static constexpr int B_LD = BM * 8 / NT;   // 16-byte token chunks per thread per slice
+  static constexpr int STAGE = (BN + BM) * 8;  // uint4 per LDS stage
+  static constexpr size_t LDS_BYTES = size_t(2) * STAGE * 16;
+  static_assert(A_LD * NT == BN * 8 && B_LD * NT == BM * 8, "tile does not split over the threads");
+};
 
-template <typename T, int EK>
-__global__ __launch_bounds__(256) void gemm_tile_kernel(const uint16_t* __restrict__ W, int64_t ldw,
-                                                        const uint16_t* __restrict__ X, int64_t ldx, int N,
-                                                        int M, int K, Epi epi) {
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][TB_N * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t sX[2][TB_M * LDS_STRIDE];
+template <typename T, int EK, int BN, int BM, int WN, int WM, int PF>
+__global__ __launch_bounds__(WN * WM * 64) void gemm_big_kernel(const uint16_t* __restrict__ W, int64_t ldw,
+                                                               const uint16_t* __restrict__ X, int64_t ldx, int N,
+                                                               int M, int K, int tiles_m, int tiles, int per_xcd,
+                                                               Epi epi) {
+  using C = BigTile<BN, BM, WN, WM>;
+  extern __shared__ uint4 smem[];
+
+  // XCD-aware tile order (per_xcd == 0: plain order)
+  const int id = blockIdx.x;
+  const int t = per_xcd ? (id & 7) * per_xcd + (id >> 3) : id;
+  if (t >= tiles) return;
+  const int tn = t / tiles_m;
+  const int tm = t - tn * tiles_m;
+  const int n0 = tn * BN;
+  const int m0 = tm * BM;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int f0 = blockIdx.y * TB_N;
-  const int m0 = blockIdx.x * TB_M;
-  const int wf = (wave >> 1) * 64;  // wave's feature offset in the tile
-  const int wt = (wave & 1) * 64;   // wave's token offset in the tile
+  const int wn = wave / WM;
+  const int wm = wave - wn * WM;
 
-  // global -> register staging: each thread moves 4 rows x 16 B of W and of X per slice
-  const int lrow = tid >> 3;        // 0..31
-  const int lchunk = (tid & 7) * 8; // element offset inside the 64-wide slice
-  uint4 rw[4], rx[4];
+  // Slice loads: chunk q = tid + NT * i covers row q / 8, 16-byte chunk q % 8.
+  // Every load is issued (out-of-range rows and the K tail read a clamped
+  // in-range address and are zeroed afterwards) so that the compiler keeps
+  // the staging registers in VGPRs and leaves the loads in flight across the
+  // MFMAs of the current slice.
+  const uint16_t* __restrict__ pa[C::A_LD];
+  const uint16_t* __restrict__ pb[C::B_LD];
+  bool oka[C::A_LD], okb[C::B_LD];
+  int sa_off[C::A_LD], sb_off[C::B_LD], kq[C::A_LD > C::B_LD ? C::A_LD : C::B_LD];
+#pragma unroll
+  for (int i = 0; i < C::A_LD; ++i) {
+    const int q = tid + C::NT * i;
+    const int r = q >> 3;
+    oka[i] = n0 + r < N;
+    pa[i] = W + static_cast<int64_t>(oka[i] ? n0 + r : 0) * ldw + 8 * (q & 7);
+    sa_off[i] = r * 8 + lds_swz(r, q & 7);
+  }
+#pragma unroll
+  for (int i = 0; i < C::B_LD; ++i) {
+    const int q = tid + C::NT * i;
+    const int r = q >> 3;
+    okb[i] = m0 + r < M;
+    pb[i] = X + static_cast<int64_t>(okb[i] ? m0 + r : 0) * ldx + 8 * (q & 7);
+    sb_off[i] = BN * 8 + r * 8 + lds_swz(r, q & 7);
+  }
+  (void)kq;
+  const int kc = 8 * (tid & 7);  // k offset of this thread's chunk inside a slice (same for every i)
+  // two register sets: slices kt+1 and kt+2 are in flight while slice kt is
+  // multiplied out of LDS
+  uint4 ra0[C::A_LD], rb0[C::B_LD];
+  uint4 ra1[PF == 2 ? C::A_LD : 1], rb1[PF == 2 ? C::B_LD : 1];
+  const uint4 z = {0, 0, 0, 0};
+#define Q2_BIG_LOAD(RA_, RB_, K0_)                                                                \
+  {                                                                                               \
+    const int k0_ = (K0_);                                                                        \
+    const bool kin_ = k0_ + kc < K;                                                               \
+    const int64_t ko_ = kin_ ? k0_ : 0;                                                           \
+    _Pragma("unroll") for (int i = 0; i < C::A_LD; ++i) RA_[i] = *reinterpret_cast<const uint4*>(pa[i] + ko_); \
+    _Pragma("unroll") for (int i = 0; i < C::B_LD; ++i) RB_[i] = *reinterpret_cast<const uint4*>(pb[i] + ko_); \
+    _Pragma("unroll") for (int i = 0; i < C::A_LD; ++i) if (!(kin_ && oka[i])) RA_[i] = z;             \
+    _Pragma("unroll") for (int i = 0; i < C::B_LD; ++i) if (!(kin_ && okb[i])) RB_[i] = z;             \
+  }
+#define Q2_BIG_STORE(RA_, RB_, S_)                                                                \
+  {                                                                                               \
+    uint4* st_ = smem + (S_) * C::STAGE;                                                          \
+    _Pragma("unroll") for (int i = 0; i < C::A_LD; ++i) st_[sa_off[i]] = RA_[i];                  \
+    _Pragma("unroll") for (int i = 0; i < C::B_LD; ++i) st_[sb_off[i]] = RB_[i];                  \
+  }
 
-  auto load_slice = [&](int k0) {
+  floatx4_t acc[C::FN][C::FM];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int r = lrow + 32 * s;
-      const int k = k0 + lchunk;
-      uint4 z = {0, 0, 0, 0};
-      rw[s] = (f0 + r < N && k < K) ? *reinterpret_cast<const uint4*>(W + static_cast<int64_t>(f0 + r) * ldw + k) : z;
-      rx[s] = (m0 + r < M && k < K) ? *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(m0 + r) * ldx + k) : z;
-    }
-  };
-  auto store_slice = [&](int buf) {
+  for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int r = lrow + 32 * s;
-      *reinterpret_cast<uint4*>(&sW[buf][r * LDS_STRIDE + lchunk]) = rw[s];
-      *reinterpret_cast<uint4*>(&sX[buf][r * LDS_STRIDE + lchunk]) = rx[s];
-    }
-  };
-
-  floatx4_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = (K + TB_K - 1) / TB_K;
-  load_slice(0);
-  store_slice(0);
-  __syncthreads();
+    for (int j = 0; j < C::FM; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   const int frow = lane & 15;
-  const int fk = (lane >> 4) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_slice((kt + 1) * TB_K);
-#pragma unroll
-    for (int kk = 0; kk < TB_K; kk += 32) {
-      bf16x8_t a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = as_bf16x8(*reinterpret_cast<const uint4*>(&sW[buf][(wf + i * 16 + frow) * LDS_STRIDE + kk + fk]));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = as_bf16x8(*reinterpret_cast<const uint4*>(&sX[buf][(wt + j * 16 + frow) * LDS_STRIDE + kk + fk]));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_slice(buf ^ 1);
-    __syncthreads();
+  const int fch = lane >> 4;
+#define Q2_BIG_MMA(S_)                                                                            \
+  {                                                                                               \
+    const uint4* sa_ = smem + (S_) * C::STAGE;                                                    \
+    const uint4* sb_ = sa_ + BN * 8;                                                              \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                            \
+      const int c = 4 * kk + fch;                                                                 \
+      bf16x8_t a[C::FN], b[C::FM];                                                                \
+      _Pragma("unroll") for (int i = 0; i < C::FN; ++i) {                                         \
+        const int r = wn * C::TN + 16 * i + frow;                                                 \
+        a[i] = as_bf16x8(sa_[r * 8 + lds_swz(r, c)]);                                             \
+      }                                                                                           \
+      _Pragma("unroll") for (int j = 0; j < C::FM; ++j) {                                         \
+        const int r = wm * C::TM + 16 * j + frow;                                                 \
+        b[j] = as_bf16x8(sb_[r * 8 + lds_swz(r, c)]);                                             \
+      }                                                                                           \
+      _Pragma("unroll") for (int i = 0; i < C::FN; ++i)                                           \
+        _Pragma("unroll") for (int j = 0; j < C::FM; ++j)                                         \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);    \
+    }                                                                                             \
   }
+
+  // Slices past the end load a zeroed dummy (keeps every load unconditional)
+  // and are never stored or multiplied.
+  const int nk = (K + C::BK - 1) / C::BK;
+  Q2_BIG_LOAD(ra0, rb0, 0)
+  Q2_BIG_STORE(ra0, rb0, 0)
+  __syncthreads();
+  if constexpr (PF == 1) {
+    for (int kt = 0; kt < nk; ++kt) {
+      const int s = kt & 1;
+      Q2_BIG_LOAD(ra0, rb0, (kt + 1) * C::BK)
+      Q2_BIG_MMA(s)
+      if (kt + 1 < nk) Q2_BIG_STORE(ra0, rb0, s ^ 1)
+      __syncthreads();
+    }
+  } else {
+    Q2_BIG_LOAD(ra0, rb0, 1 * C::BK)
+    Q2_BIG_LOAD(ra1, rb1, 2 * C::BK)
+    for (int kt = 0; kt < nk; kt += 2) {
+      // even slice kt: LDS stage 0; set 0 holds slice kt+1, set 1 slice kt+2
+      Q2_BIG_MMA(0)
+      if (kt + 1 >= nk) break;
+      Q2_BIG_STORE(ra0, rb0, 1)
+      __syncthreads();
+      Q2_BIG_LOAD(ra0, rb0, (kt + 3) * C::BK)
+      // odd slice kt+1: LDS stage 1; set 1 holds slice kt+2, set 0 slice kt+3
+      Q2_BIG_MMA(1)
+      if (kt + 2 >= nk) break;
+      Q2_BIG_STORE(ra1, rb1, 0)
+      __syncthreads();
+      Q2_BIG_LOAD(ra1, rb1, (kt + 4) * C::BK)
+    }
+  }
+#undef Q2_BIG_LOAD
+#undef Q2_BIG_STORE
+#undef Q2_BIG_MMA
+
 
   // epilogue: lane holds features 4*(lane/16)+r of token lane%16 in each 16x16 tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int f = f0 + wf + i * 16 + (lane >> 4) * 4;
+  for (int i = 0; i < C::FN; ++i) {
+    const int f = n0 + wn * C::TN + i * 16 + (lane >> 4) * 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + wt + j * 16 + (lane & 15);
+    for (int j = 0; j < C::FM; ++j) {
+      const int m = m0 + wm * C::TM + j * 16 + (lane & 15);
       if (m >= M) continue;
       if (f < N) epi_pair<T, EK>(epi, m, f, acc[i][j][0], acc[i][j][1], f + 1 < N);
       if (f + 2 < N) epi_pair<T, EK>(epi, m, f + 2, acc[i][j][2], acc[i][j][3], f + 3 < N);
     }
   }
+}
+
+template <int EK, int BN, int BM, int WN, int WM, int PF = 1>
+q2_status launch_big(const GemmArgs& a, hipStream_t s, bool xcd_order = true) {
+  using C = BigTile<BN, BM, WN, WM>;
+  const int tiles_m = cdiv(a.M, BM), tiles = tiles_m * cdiv(a.N, BN);
+  const int per = xcd_order ? cdiv(tiles, 8) : 0;
+  const int grid = xcd_order ? 8 * per : tiles;
+  hipLaunchKernelGGL((gemm_big_kernel<uint16_t, EK, BN, BM, WN, WM, PF>), dim3(grid), dim3(C::NT), C::LDS_BYTES, s,
+                     static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M,
+                     a.K, tiles_m, tiles, per, a.epi);
+  return check_launch("gemm_big");
+}
+
+// ------------------------------------------------------------------ direct-to-LDS kernel
+//
+// BN features x BM tokens per workgroup, WN x WM waves of (BN/WN) x (BM/WM),
+// 32x32x16 bf16 MFMAs (on gfx950 twice the rate of 16x16x32).  K moves in
+// 32-wide slices through a ring of four LDS stages that the global loads
+// write directly (global_load_lds_dwordx4: no staging registers), so three
+// slices are in flight while one is multiplied.  The wait for a stage is
+// explicit: a wave waits until at most two stages of its own loads are
+// outstanding (loads complete in issue order), then the workgroup barrier
+// publishes every wave's part.  The two k16 steps of a slice are software-
+// pipelined: the fragments of the next step are read while the MFMAs of the
+// current one run.
+//
+// LDS rows are 64 bytes (32 bf16); chunk c of row r sits at c ^ (((r >> 1) ^
+// (r >> 2)) & 3), which keeps the 32-lane fragment reads on distinct banks
+// (for 32 or 64 banks).  A load instruction fills 64 consecutive 16-byte
+// slots, so each lane fetches the global chunk that belongs in its slot.
+// Requires K % 128 == 0 (whole trips of the four-stage ring) and 16-byte
+// aligned rows; rows beyond M or N read a clamped valid row and their results
+// are discarded.
+
+__device__ __forceinline__ int dtl_swz(int r, int c) { return c ^ (((r >> 1) ^ (r >> 2)) & 3); }
+
+// One global_load_lds_dwordx4: each lane's 16 bytes at g go to LDS at
+// lds + 16 * lane (lds is the wave's base).  Written as asm so that the
+// compiler does not track these LDS writes (it would otherwise wait for every
+// load in flight before reading any stage); the kernel waits for them
+// explicitly.  The instruction has no destination register; it reads its
+// address operands when it issues.
+__device__ __forceinline__ void dtl16(const void* g, const uint4* lds) {
+  const uint32_t la =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint4*)lds));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(la)) : "memory");
+}
+
+template <int BN, int BM, int WN, int WM>
+struct Dtl {
+  static constexpr int NT = WN * WM * 64;
+  static constexpr int TN = BN / WN, TM = BM / WM;  // wave tile
+  static constexpr int FN = TN / 32, FM = TM / 32;  // 32x32 MFMA tiles per wave
+  static constexpr int BK = 32;
+  static constexpr int SLOTS = (BN + BM) * 4;       // 16-byte slots per stage
+  static constexpr int LD = SLOTS / NT;             // load instructions per wave per stage
+  static constexpr size_t LDS_BYTES = size_t(4) * SLOTS * 16;
+  // s_waitcnt vmcnt(2 * LD) expcnt(7) lgkmcnt(0) (gfx9 encoding)
+  static constexpr int WAIT = ((2 * LD) & 15) | (((2 * LD) >> 4) << 14) | (7 << 4);
+  static_assert(LD * NT == SLOTS, "stage does not split over the threads");
+  static_assert(TN == 128, "the staged epilogue writes 128-feature rows");
+};
+
+// Staged epilogue (bf16): each wave applies the epilogue math to its
+// 128-feature block in registers (where the feature pairs are), writes the
+// results into LDS (16-byte chunk c of row r at c ^ (r & 15), 256 bytes per
+// row) and then stores whole 16-byte chunks along output rows, so a store
+// instruction covers four contiguous 256-byte row segments instead of 32
+// scattered 8-byte pieces.
+__device__ __forceinline__ int stg_idx(int r, int col) {
+  return r * 128 + ((((col >> 3) ^ (r & 15)) << 3) | (col & 7));
+}
+
+template <int EK>
+__device__ __forceinline__ void stg_put(uint16_t* sh, const Epi& e, int M, int fb0, int tb0, int r, int nl,
+                                        float x0, float x1, float x2, float x3) {
+  const uint16_t* bias = static_cast<const uint16_t*>(e.bias);
+  if constexpr (EK == EPI_STORE || EK == EPI_RESID) {
+    if (EK == EPI_STORE && bias) {
+      x0 += bf2f(bias[fb0 + nl]);
+      x1 += bf2f(bias[fb0 + nl + 1]);
+      x2 += bf2f(bias[fb0 + nl + 2]);
+      x3 += bf2f(bias[fb0 + nl + 3]);
+    }
+    const uint2 v = {pack_bf2(x0, x1), pack_bf2(x2, x3)};
+    *reinterpret_cast<uint2*>(sh + stg_idx(r, nl)) = v;
+  } else if constexpr (EK == EPI_SWIGLU) {
+    const float y0 = silu_f(round_bf(x0)) * round_bf(x1);
+    const float y1 = silu_f(round_bf(x2)) * round_bf(x3);
+    *reinterpret_cast<uint32_t*>(sh + stg_idx(r, nl >> 1)) = pack_bf2(y0, y1);
+  } else if constexpr (EK == EPI_QKV) {
+    // the block is one head (d = 128); q and k heads hold rotate-half pairs
+    // in adjacent rows (2p: original p, 2p+1: original p + 64)
+    const float a0 = round_bf(x0 + bf2f(bias[fb0 + nl])), a1 = round_bf(x1 + bf2f(bias[fb0 + nl + 1]));
+    const float a2 = round_bf(x2 + bf2f(bias[fb0 + nl + 2])), a3 = round_bf(x3 + bf2f(bias[fb0 + nl + 3]));
+    const int head = fb0 >> 7;
+    if (head < e.nh + e.nkv) {
+      const int m = tb0 + r;
+      const int p = nl >> 1;
+      float2 c0 = make_float2(1.f, 0.f), c1 = c0;
+      if (m < M) {
+        const int t = m % e.T;
+        const int64_t pos = (e.d_len ? *e.d_len : e.len0) + t;
+        c0 = e.rope[pos * 64 + p];
+        c1 = e.rope[pos * 64 + p + 1];
+      }
+      const float ra0 = a0 * c0.x - a1 * c0.y, rb0 = a1 * c0.x + a0 * c0.y;
+      const float ra1 = a2 * c1.x - a3 * c1.y, rb1 = a3 * c1.x + a2 * c1.y;
+      *reinterpret_cast<uint32_t*>(sh + stg_idx(r, p)) = pack_bf2(ra0, ra1);
+      *reinterpret_cast<uint32_t*>(sh + stg_idx(r, p + 64)) = pack_bf2(rb0, rb1);
+    } else {
+      const uint2 v = {pack_bf2(a0, a1), pack_bf2(a2, a3)};
+      *reinterpret_cast<uint2*>(sh + stg_idx(r, nl)) = v;
+    }
+  }
+}
+
+template <int EK, int ROWS>
+__device__ __forceinline__ void stg_copy_out(const uint16_t* sh, const Epi& e, int M, int N, int fb0, int tb0,
+                                             int lane) {
+  constexpr int CPR = EK == EPI_SWIGLU ? 8 : 16;  // 16-byte chunks per row of the block
+#pragma unroll 4
+  for (int it = 0; it < ROWS * CPR / 64; ++it) {
+    const int q = it * 64 + lane;
+    const int r = q / CPR, c = q % CPR;
+    const int m = tb0 + r;
+    if (m >= M) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(sh + stg_idx(r, c * 8));
+    if constexpr (EK == EPI_STORE) {
+      if (fb0 + c * 8 >= N) continue;
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(e.out) + static_cast<int64_t>(m) * e.ldo + fb0 + c * 8) = v;
+    } else if constexpr (EK == EPI_RESID) {
+      if (fb0 + c * 8 >= N) continue;
+      uint4* dst =
+          reinterpret_cast<uint4*>(static_cast<uint16_t*>(e.out) + static_cast<int64_t>(m) * e.ldo + fb0 + c * 8);
+      const uint4 o = *dst;
+      const uint32_t* os = &o.x;
+      const uint32_t* vs = &v.x;
+      uint4 w;
+      uint32_t* ws = &w.x;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ws[k] = pack_bf2(bf_lo(os[k]) + bf_lo(vs[k]), bf_hi(os[k]) + bf_hi(vs[k]));
+      *dst = w;
+    } else if constexpr (EK == EPI_SWIGLU) {
+      if ((fb0 >> 1) + c * 8 >= (N >> 1)) continue;
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(e.out) + static_cast<int64_t>(m) * e.ldo + (fb0 >> 1) +
+                                c * 8) = v;
+    } else if constexpr (EK == EPI_QKV) {
+      const int head = fb0 >> 7;
+      uint16_t* dst;
+      if (head < e.nh) {
+        dst = static_cast<uint16_t*>(e.out) + static_cast<int64_t>(m) * e.ldo + head * 128;
+      } else {
+        const int bt = m / e.T;
+        const int t = m - bt * e.T;
+        const int64_t pos = (e.d_len ? *e.d_len : e.len0) + t;
+        const bool isk = head < e.nh + e.nkv;
+        uint16_t* base = static_cast<uint16_t*>(isk ? e.kc : e.vc);
+        const int hh = isk ? head - e.nh : head - e.nh - e.nkv;
+        dst = base + bt * e.kv_bstride + hh * e.kv_hstride + pos * 128;
+      }
+      *reinterpret_cast<uint4*>(dst + c * 8) = v;
+    }
+  }
+}
+
+template <int EK, int BN, int BM, int WN, int WM, bool STAGED>
+__global__ __launch_bounds__(WN * WM * 64) void gemm_dtl_kernel(const uint16_t* __restrict__ W, int64_t ldw,
+                                                                const uint16_t* __restrict__ X, int64_t ldx, int N,
+                                                                int M, int K, int tiles_m, Epi epi) {
+  using C = Dtl<BN, BM, WN, WM>;
+  constexpr int FN = C::FN, FM = C::FM, TN = C::TN, TM = C::TM, NT = C::NT, LD = C::LD;
+  extern __shared__ uint4 dsm[];
+  const int t = blockIdx.x;
+  const int tn = t / tiles_m;
+  const int tm = t - tn * tiles_m;
+  const int n0 = tn * BN;
+  const int m0 = tm * BM;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wn = wave / WM;
+  const int wm = wave - wn * WM;
+
+  // the global chunk behind each of this lane's slots (slot = i * NT + tid;
+  // slots [0, 4 BN) hold weight rows, the rest token rows)
+  const uint16_t* src[LD];
+#pragma unroll
+  for (int i = 0; i < LD; ++i) {
+    const int slot = i * NT + tid;
+    const bool isw = slot < BN * 4;
+    const int ls = isw ? slot : slot - BN * 4;
+    const int r = ls >> 2;
+    const int c = dtl_swz(r, ls & 3);
+    if (isw) {
+      const int row = min(n0 + r, N - 1);
+      src[i] = W + static_cast<int64_t>(row) * ldw + 8 * c;
+    } else {
+      const int row = min(m0 + r, M - 1);
+      src[i] = X + static_cast<int64_t>(row) * ldx + 8 * c;
+    }
+  }
+  const int nk = K / C::BK;
+#define Q2_DTL_ISSUE(S_, KT_)                                                                        \
+  {                                                                                                  \
+    const int kt_ = (KT_);                                                                           \
+    const int64_t ko_ = kt_ < nk ? static_cast<int64_t>(kt_) * C::BK : 0; /* past the end: dummy */  \
+    const uint4* st_ = dsm + (S_) * C::SLOTS;                                                        \
+    _Pragma("unroll") for (int i = 0; i < LD; ++i) dtl16(src[i] + ko_, st_ + i * NT + wave * 64);    \
+  }
+
+  floatx16_t acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // fragment slots: row lane % 32, 8-element chunk 2 * kk + lane / 32
+  const int frow = lane & 31;
+  const int fch = lane >> 5;
+  int a_off[2][FN], b_off[2][FM];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int r = wn * TN + 32 * i + frow;
+      a_off[kk][i] = r * 4 + dtl_swz(r, 2 * kk + fch);
+    }
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int r = wm * TM + 32 * j + frow;
+      b_off[kk][j] = BN * 4 + r * 4 + dtl_swz(r, 2 * kk + fch);
+    }
+  }
+
+  // Slice kt lives in stage kt % 4.  The fragments of the next k16 step are
+  // read while the MFMAs of the current one run; slice kt+1's barrier comes
+  // before the second step of slice kt is multiplied, and by then every wave
+  // has read all of slice kt, whose stage the loads issued after that barrier
+  // (slice kt+4) overwrite.
+  bf16x8_t fa[2][FN], fb[2][FM];
+#define Q2_DTL_WAIT_BARRIER()                                                                        \
+  __builtin_amdgcn_s_waitcnt(C::WAIT);                                                               \
+  __builtin_amdgcn_s_barrier();                                                                      \
+  asm volatile("" ::: "memory");
+#define Q2_DTL_READ(SET_, S_, KK_)                                                                   \
+  {                                                                                                  \
+    const uint4* st_ = dsm + (S_) * C::SLOTS;                                                        \
+    _Pragma("unroll") for (int i = 0; i < FN; ++i) fa[SET_][i] = as_bf16x8(st_[a_off[KK_][i]]);      \
+    _Pragma("unroll") for (int j = 0; j < FM; ++j) fb[SET_][j] = as_bf16x8(st_[b_off[KK_][j]]);      \
+  }
+#define Q2_DTL_MMA(SET_)                                                                             \
+  _Pragma("unroll") for (int i = 0; i < FN; ++i)                                                     \
+    _Pragma("unroll") for (int j = 0; j < FM; ++j)                                                   \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[SET_][i], fb[SET_][j], acc[i][j], 0, 0, 0);
+#define Q2_DTL_SLICE(S_)                                                                             \
+  {                                                                                                  \
+    Q2_DTL_READ(1, S_, 1)                                                                            \
+    Q2_DTL_MMA(0)                                                                                    \
+    Q2_DTL_WAIT_BARRIER()                                                                            \
+    Q2_DTL_ISSUE(S_, kt + S_ + 4)                                                                    \
+    Q2_DTL_READ(0, (S_ + 1) & 3, 0)                                                                  \
+    Q2_DTL_MMA(1)                                                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+  }
+  Q2_DTL_ISSUE(0, 0)
+  Q2_DTL_ISSUE(1, 1)
+  Q2_DTL_ISSUE(2, 2)
+  Q2_DTL_WAIT_BARRIER()
+  Q2_DTL_ISSUE(3, 3)
+  Q2_DTL_READ(0, 0, 0)
+  for (int kt = 0; kt < nk; kt += 4) {
+    Q2_DTL_SLICE(0)
+    Q2_DTL_SLICE(1)
+    Q2_DTL_SLICE(2)
+    Q2_DTL_SLICE(3)
+  }
+  // no load into LDS may still be in flight when the stages are reused or
+  // the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef Q2_DTL_ISSUE
+#undef Q2_DTL_WAIT_BARRIER
+#undef Q2_DTL_READ
+#undef Q2_DTL_MMA
+#undef Q2_DTL_SLICE
+
+  // epilogue: element 4v+e of a 32x32 tile is feature 8v + 4*(lane/32) + e of
+  // token lane%32
+  const int fb0 = n0 + wn * TN;
+  const int tb0 = m0 + wm * TM;
+  if constexpr (STAGED) {
+    __syncthreads();  // every wave has finished reading the stages reused below
+    uint16_t* sh = reinterpret_cast<uint16_t*>(dsm) + wave * (TM * 128);
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          stg_put<EK>(sh, epi, M, fb0, tb0, 32 * j + (lane & 31), 32 * i + 8 * v + 4 * (lane >> 5),
+                      acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]);
+    stg_copy_out<EK, TM>(sh, epi, M, N, fb0, tb0, lane);
+  } else {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int m = tb0 + 32 * j + (lane & 31);
+        if (m >= M) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int f = fb0 + 32 * i + 8 * v + 4 * (lane >> 5);
+          if (f < N) epi_pair<uint16_t, EK>(epi, m, f, acc[i][j][4 * v], acc[i][j][4 * v + 1], f + 1 < N);
+          if (f + 2 < N)
+            epi_pair<uint16_t, EK>(epi, m, f + 2, acc[i][j][4 * v + 2], acc[i][j][4 * v + 3], f + 3 < N);
+        }
+      }
+    }
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// The direct-to-LDS kernel's operand requirements.
+bool dtl_ok(const GemmArgs& a) {
+  return a.K % 128 == 0 && a.ldw % 8 == 0 && a.ldx % 8 == 0 && aligned16(a.W) && aligned16(a.X);
+}
+
+// The staged epilogue's output requirements (16-byte row chunks).
+bool staged_ok(const GemmArgs& a) {
+  const Epi& e = a.epi;
+  if (a.N % 8 != 0 || e.ldo % 8 != 0 || !aligned16(e.out)) return false;
+  switch (e.kind) {
+    case EPI_STORE: return !e.out_f32;
+    case EPI_RESID: return true;
+    case EPI_SWIGLU: return (a.N / 2) % 8 == 0;
+    case EPI_QKV:
+      return e.dh == 128 && aligned16(e.kc) && aligned16(e.vc) && e.kv_bstride % 8 == 0 && e.kv_hstride % 8 == 0;
+    default: return false;
+  }
+}
+
+template <int EK, int BN, int BM, int WN, int WM>
+q2_status launch_dtl_cfg(const GemmArgs& a, hipStream_t s) {
+  using C = Dtl<BN, BM, WN, WM>;
+  const int tiles_m = cdiv(a.M, BM), tiles = tiles_m * cdiv(a.N, BN);
+  const bool staged = staged_ok(a);
+  if (staged)
+    hipLaunchKernelGGL((gemm_dtl_kernel<EK, BN, BM, WN, WM, true>), dim3(tiles), dim3(C::NT), C::LDS_BYTES, s,
+                       static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M,
+                       a.K, tiles_m, a.epi);
+  else
+    hipLaunchKernelGGL((gemm_dtl_kernel<EK, BN, BM, WN, WM, false>), dim3(tiles), dim3(C::NT), C::LDS_BYTES, s,
+                       static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M,
+                       a.K, tiles_m, a.epi);
+  return check_launch("gemm_dtl");
+}
+
+// 256 x 256 tiles (8 waves, 128 KB LDS, one workgroup per CU) when they give
+// the chip at least ~1.5 rounds of work, otherwise 128 x 128 tiles (4 waves,
+// 64 KB, two per CU).
+template <int EK>
+q2_status launch_dtl(const GemmArgs& a, hipStream_t s, int force = 0) {
+  const int big_tiles = cdiv(a.M, 256) * cdiv(a.N, 256);
+  const bool big = force ? force == 1 : big_tiles >= 384;
+  if (big) return launch_dtl_cfg<EK, 256, 256, 2, 4>(a, s);
+  return launch_dtl_cfg<EK, 128, 128, 1, 4>(a, s);
 }
 
 // ------------------------------------------------------------------ float32 kernel
@@ -159,10 +618,8 @@ q2_status gemm_bf16_ek(const GemmArgs& a, hipStream_t s) {
   if constexpr (EK == EPI_ARGMAX) {
     return fail(Q2_ESHAPE, "argmax epilogue supports at most 64 rows");
   } else {
-    dim3 grid(cdiv(a.M, TB_M), cdiv(a.N, TB_N));
-    hipLaunchKernelGGL((gemm_tile_kernel<uint16_t, EK>), grid, dim3(256), 0, s, static_cast<const uint16_t*>(a.W),
-                       a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M, a.K, a.epi);
-    return check_launch("gemm_tile");
+    if (dtl_ok(a)) return launch_dtl<EK>(a, s);
+    return launch_big<EK, 128, 128, 2, 2>(a, s);
   }
 }
 

@@ -32,12 +32,6 @@ namespace {
 
 constexpr int KB = 128;  // K per block
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
-  bf16x8_t r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
-}
-
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // rnd(x * inv * w) for 8 bf16 lanes of a 16-byte vector.
