@@ -9,8 +9,9 @@
 //                 operand; P V runs on MFMA with V transposed through LDS.
 //                 With several chunks (split-KV) attn_combine merges the
 //                 partial results.
-//  * attn_prefill 64 queries of one head per workgroup (16 per wave), K and
-//                 V^T tiles of 64 keys staged in LDS, online softmax.
+//  * attn_prefill 128 queries of one head per workgroup (32 per wave), K and
+//                 V^T tiles of 64 keys double-buffered in LDS, online softmax,
+//                 32x32x16 MFMAs.
 // float32, any d <= 256: attn_f32, one wave per (query, head).
 //
 // MFMA layout facts used below (16x16 tiles): the A operand lane l holds row
@@ -28,8 +29,6 @@ namespace {
 
 constexpr int D = 128;
 constexpr int VT_DEC = 20;    // bf16 per V^T LDS row in attn_decode: 16 keys + pad (40 B rows)
-constexpr int K_ROW = D + 8;  // bf16 per K LDS row in attn_prefill (272 B: conflict-free b128 reads)
-constexpr int VT_PRE = 72;    // bf16 per V^T LDS row in attn_prefill: 64 keys + pad
 constexpr float NEG_INF = -__builtin_huge_valf();
 
 __device__ __forceinline__ short4_t as_short4(uint2 v) {
@@ -259,12 +258,36 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
 }
 
 // ------------------------------------------------------------------ prefill (flash)
+//
+// 128 queries of one head per workgroup, 32 per wave, 32x32x16 bf16 MFMAs.
+// Keys move in tiles of 64 through two LDS buffers: the next tile's K and V
+// are loaded into registers while the current one is multiplied, then
+// written to the other buffer (one barrier per tile).
+//
+// S^T = K Q^T: K rows are the A operand, the wave's 32 queries the B operand
+// (held in registers for the whole kernel), so element 4v+e of a 32x32 result
+// is key 8v + 4*(lane/32) + e of query lane%32: each lane owns 16 scores of
+// one query and a row's softmax needs one exchange with lane ^ 32.
+// O^T = V^T P^T then takes a lane's own probabilities as its B operand: for
+// key chunk c (16 keys) lane half h holds keys 16c + 4h + {0..3} and
+// 16c + 8 + 4h + {0..3}.  V^T is written to LDS with bits 2 and 3 of the key
+// index swapped, which makes exactly those eight keys contiguous for the A
+// operand.  P is rounded to bf16 for that product.
+//
+// K rows (256 bytes) keep 16-byte chunk c of key r at c ^ (r & 15); V^T rows
+// are padded to 72 keys: both keep the fragment reads on distinct banks.
 
-__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[64 * K_ROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * VT_PRE];
+constexpr int PF_QB = 128;   // queries per workgroup
+constexpr int PF_KT = 64;    // keys per tile
+constexpr int PF_VT = 72;    // bf16 per V^T LDS row
 
-  const int nqb = (a.T + 63) / 64;
+__device__ __forceinline__ int pf_keyperm(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
+  __shared__ uint4 sK[2][PF_KT * 16];
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[2][D * PF_VT];
+
+  const int nqb = (a.T + PF_QB - 1) / PF_QB;
   const int qb = nqb - 1 - static_cast<int>(blockIdx.x);  // longest rows first
   const int h = blockIdx.y;
   const int b = blockIdx.z;
@@ -272,104 +295,158 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnArgs a) {
   const int g = h / group;
   const int S = a.d_len ? (*a.d_len + a.T) : a.S;
   const int P = S - a.T;
-  const int q0 = qb * 64;
+  const int q0 = qb * PF_QB;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int col = lane & 15;
-  const int G = lane >> 4;
+  const int hl = lane >> 5;      // lane half
+  const int qr = lane & 31;      // query row within the wave
 
-  const int tq = q0 + 16 * wave + col;
+  const int tq = q0 + 32 * wave + qr;
   const bool qvalid = tq < a.T;
   const int lim = qvalid ? P + tq : S - 1;
-  const uint4 z = {0, 0, 0, 0};
-  uint4 qf[4];
-  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_bs + static_cast<int64_t>(qvalid ? tq : 0) * a.q_ts + h * a.q_hs;
+  uint4 qf[8];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_bs +
+                         static_cast<int64_t>(qvalid ? tq : 0) * a.q_ts + h * a.q_hs;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) qf[kk] = qvalid ? ld16(qp + 32 * kk + 8 * G) : z;
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = ld16(qp + 16 * ks + 8 * hl);
+  }
 
-  const int kv_end = min(S, P + min(q0 + 64, a.T));
-  const int wave_first = q0 + 16 * wave;
-  const bool wave_active = wave_first < a.T;
-  const int wave_lim = P + min(wave_first + 15, a.T - 1);
+  const int kv_end = min(S, P + min(q0 + PF_QB, a.T));
+  const int wave_first = q0 + 32 * wave;
+  const int wave_lim = wave_first < a.T ? P + min(wave_first + 31, a.T - 1) : -1;
 
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_bs + g * a.k_hs;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.v_bs + g * a.v_hs;
 
-  float m_run = NEG_INF, l_run = 0.f;
-  floatx4_t oacc[8];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) oacc[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int j0 = 0; j0 < kv_end; j0 += 64) {
-    __syncthreads();  // the previous tile is consumed
-    {
-      const int r = tid >> 4;
-      const int c8 = (tid & 15) * 8;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int key = j0 + r + 16 * s;
-        const uint4 kv = key < kv_end ? ld16(kbase + static_cast<int64_t>(key) * a.k_ss + c8) : z;
-        *reinterpret_cast<uint4*>(&sK[(r + 16 * s) * K_ROW + c8]) = kv;
-      }
-      uint4 vf[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int key = j0 + 4 * r + s;
-        vf[s] = key < kv_end ? ld16(vbase + static_cast<int64_t>(key) * a.v_ss + c8) : z;
-      }
-      store_vt4(sVt, VT_PRE, c8, 4 * r, vf);
-    }
-    __syncthreads();
-    if (!wave_active || wave_lim < j0) continue;
-
-    floatx4_t sacc[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      sacc[kt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint4 kfr = *reinterpret_cast<const uint4*>(&sK[(kt * 16 + col) * K_ROW + 32 * kk + 8 * G]);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kfr), as_bf16x8(qf[kk]), sacc[kt], 0, 0, 0);
-      }
-    }
-    float s[16];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kj = j0 + kt * 16 + 4 * G + i;
-        s[kt * 4 + i] = (kj < kv_end && kj <= lim) ? sacc[kt][i] * a.scale : NEG_INF;
-      }
-    const float alpha = softmax_step(s, 16, m_run, l_run);
-    short4_t pf[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      uint2 pw;
-      pw.x = pack_bf2(s[kt * 4 + 0], s[kt * 4 + 1]);
-      pw.y = pack_bf2(s[kt * 4 + 2], s[kt * 4 + 3]);
-      pf[kt] = as_short4(pw);
-    }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      oacc[dt][0] *= alpha; oacc[dt][1] *= alpha; oacc[dt][2] *= alpha; oacc[dt][3] *= alpha;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const uint2 vv = *reinterpret_cast<const uint2*>(&sVt[(16 * dt + col) * VT_PRE + kt * 16 + 4 * G]);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(vv), pf[kt], oacc[dt], 0, 0, 0);
-      }
-    }
+  // tile loads: K chunk q = tid + 256 i is key q / 16, chunk q % 16; V: this
+  // thread's 8-wide d chunk vc of keys 4 vg .. 4 vg + 3.  Keys past kv_end
+  // read the last valid key: their scores are masked and their
+  // probabilities are exactly zero.
+  const int vc = tid & 15, vg = tid >> 4;
+  uint4 rk[4], rv[4];
+#define Q2_PF_LOAD(J0_)                                                                              \
+  {                                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                  \
+      const int q_ = tid + 256 * i;                                                                  \
+      const int key_ = min((J0_) + (q_ >> 4), kv_end - 1);                                           \
+      rk[i] = ld16(kbase + static_cast<int64_t>(key_) * a.k_ss + 8 * (q_ & 15));                     \
+    }                                                                                                \
+    _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) {                                               \
+      const int key_ = min((J0_) + 4 * vg + s_, kv_end - 1);                                         \
+      rv[s_] = ld16(vbase + static_cast<int64_t>(key_) * a.v_ss + 8 * vc);                           \
+    }                                                                                                \
   }
+#define Q2_PF_STORE(BUF_)                                                                            \
+  {                                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                  \
+      const int q_ = tid + 256 * i;                                                                  \
+      const int r_ = q_ >> 4;                                                                        \
+      sK[BUF_][r_ * 16 + ((q_ & 15) ^ (r_ & 15))] = rk[i];                                           \
+    }                                                                                                \
+    store_vt4(sVt[BUF_], PF_VT, 8 * vc, pf_keyperm(4 * vg), rv);                                     \
+  }
+
+  float m_run = NEG_INF, l_run = 0.f;
+  floatx16_t oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
+
+  const int ntiles = (kv_end + PF_KT - 1) / PF_KT;
+  Q2_PF_LOAD(0)
+  Q2_PF_STORE(0)
+  __syncthreads();
+  for (int jt = 0; jt < ntiles; ++jt) {
+    const int buf = jt & 1;
+    const int j0 = jt * PF_KT;
+    if (jt + 1 < ntiles) Q2_PF_LOAD(j0 + PF_KT)
+    if (j0 <= wave_lim) {
+      // S^T for two 32-key halves
+      floatx16_t sacc[2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[kh][e] = 0.f;
+        const int r = 32 * kh + qr;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const uint4 kfr = sK[buf][r * 16 + ((2 * ks + hl) ^ (r & 15))];
+          sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kfr), as_bf16x8(qf[ks]), sacc[kh], 0, 0, 0);
+        }
+      }
+      // scale, mask, online softmax of query qr (lanes qr and qr + 32)
+      float mt = NEG_INF;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kj = j0 + 32 * kh + 8 * v + 4 * hl + e;
+            const float x = kj <= lim ? sacc[kh][4 * v + e] * a.scale : NEG_INF;
+            sacc[kh][4 * v + e] = x;
+            mt = fmaxf(mt, x);
+          }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run, mt);
+      const float base = m_new == NEG_INF ? 0.f : m_new;
+      const float alpha = m_run == NEG_INF ? 0.f : __expf(m_run - base);
+      float ps = 0.f;
+      bf16x8_t pf[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint4 w;
+        uint32_t* ws = &w.x;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int v = 2 * (c & 1) + half;
+          float pr[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = sacc[c >> 1][4 * v + e];
+            pr[e] = x == NEG_INF ? 0.f : __expf(x - base);
+            ps += pr[e];
+          }
+          ws[2 * half] = pack_bf2(pr[0], pr[1]);
+          ws[2 * half + 1] = pack_bf2(pr[2], pr[3]);
+        }
+        pf[c] = as_bf16x8(w);
+      }
+      ps += __shfl_xor(ps, 32, 64);
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+      // O^T += V^T P^T
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint4 vfr = *reinterpret_cast<const uint4*>(&sVt[buf][(32 * dt + qr) * PF_VT + 16 * c + 8 * hl]);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr), pf[c], oacc[dt], 0, 0, 0);
+        }
+      }
+    }
+    if (jt + 1 < ntiles) Q2_PF_STORE(buf ^ 1)
+    __syncthreads();
+  }
+#undef Q2_PF_LOAD
+#undef Q2_PF_STORE
   if (!qvalid) return;
   const float inv = 1.f / l_run;
   uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.o_bs + static_cast<int64_t>(tq) * a.o_ts + h * a.o_hs;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    uint2 w;
-    w.x = pack_bf2(oacc[dt][0] * inv, oacc[dt][1] * inv);
-    w.y = pack_bf2(oacc[dt][2] * inv, oacc[dt][3] * inv);
-    *reinterpret_cast<uint2*>(op + 16 * dt + 4 * G) = w;
-  }
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      uint2 w;
+      w.x = pack_bf2(oacc[dt][4 * v] * inv, oacc[dt][4 * v + 1] * inv);
+      w.y = pack_bf2(oacc[dt][4 * v + 2] * inv, oacc[dt][4 * v + 3] * inv);
+      *reinterpret_cast<uint2*>(op + 32 * dt + 8 * v + 4 * hl) = w;
+    }
 }
 
 // ------------------------------------------------------------------ float32
@@ -468,7 +545,7 @@ q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
     }
     return Q2_OK;
   }
-  hipLaunchKernelGGL(attn_prefill_kernel, dim3(cdiv(a.T, 64), a.nh, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_prefill_kernel, dim3(cdiv(a.T, PF_QB), a.nh, a.B), dim3(256), 0, s, a);
   return check_launch("attn_prefill");
 }
 
