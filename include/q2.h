@@ -232,6 +232,25 @@ q2_status q2_model_length(const q2_model* m, int32_t* len);
 /* Forget the cached sequences (len = 0).  Does not touch device memory. */
 q2_status q2_model_reset(q2_model* m);
 
+/* Decode path for steps of up to 16 sequences of a bf16 model: 1 runs each
+ * step as one persistent cooperative kernel (one workgroup per CU, grid
+ * barriers between the fused stages); 0 (default) replays the graph of
+ * per-operator kernels.  Both compute the same operator chain with the same
+ * rounding points; summation order inside the products differs.  Larger
+ * batches and the float32 model always use the per-operator path.
+ * Q2_EINVAL for other values. */
+q2_status q2_model_set_decode_path(q2_model* m, int32_t persistent);
+
+/* Which path a decode step of `batch` sequences would take now (1 =
+ * persistent kernel). */
+q2_status q2_model_decode_path(const q2_model* m, int32_t batch, int32_t* persistent);
+
+/* Synchronises the device and reports failures recorded on it by earlier
+ * asynchronous calls: Q2_EHIP if a grid barrier of the persistent decode
+ * kernel timed out (the step's results are then invalid). */
+q2_status q2_model_check(q2_model* m);
+
+
 /* Free everything the model holds.  Synchronises the device first. */
 void q2_model_destroy(q2_model* m);
 

@@ -8,11 +8,13 @@ from ._lib import (Q2Error, Q2Tensor, Q2Config, header_functions, version, lib, 
                    q2_embedding, q2_linear, q2_rms_norm, q2_rope, q2_self_attention, q2_swiglu, q2_add,
                    q2_argmax, q2_rearrange, q2_model_create, q2_model_device_bytes, q2_model_load_weight,
                    q2_model_prefill, q2_model_prefill_embeds, q2_model_hidden_view, q2_model_decode, q2_model_generate, q2_model_continue, q2_model_kv_view, q2_model_length,
-                   q2_model_reset, q2_model_destroy)
+                   q2_model_reset, q2_model_set_decode_path, q2_model_decode_path, q2_model_check,
+                   q2_model_destroy)
 from .model import Model, make_config
 
 __all__ = ["Q2Error", "Q2Tensor", "Q2Config", "header_functions", "version", "lib", "LIB_PATH",
            "q2_embedding", "q2_linear", "q2_rms_norm", "q2_rope", "q2_self_attention", "q2_swiglu", "q2_add",
            "q2_argmax", "q2_rearrange", "q2_model_create", "q2_model_device_bytes", "q2_model_load_weight",
            "q2_model_prefill", "q2_model_prefill_embeds", "q2_model_hidden_view", "q2_model_decode", "q2_model_generate", "q2_model_continue", "q2_model_kv_view", "q2_model_length",
-           "q2_model_reset", "q2_model_destroy", "Model", "make_config"]
+           "q2_model_reset", "q2_model_set_decode_path", "q2_model_decode_path", "q2_model_check",
+           "q2_model_destroy", "Model", "make_config"]

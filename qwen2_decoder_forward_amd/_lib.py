@@ -75,6 +75,9 @@ _SIGS = {
     "q2_model_kv_view": ([ctypes.c_void_p, ctypes.c_int32, _P, _P], ctypes.c_int),
     "q2_model_length": ([ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
     "q2_model_reset": ([ctypes.c_void_p], ctypes.c_int),
+    "q2_model_set_decode_path": ([ctypes.c_void_p, ctypes.c_int32], ctypes.c_int),
+    "q2_model_decode_path": ([ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
+    "q2_model_check": ([ctypes.c_void_p], ctypes.c_int),
     "q2_model_destroy": ([ctypes.c_void_p], None),
 }
 for _name, (_args, _ret) in _SIGS.items():
@@ -239,6 +242,20 @@ def q2_model_length(h) -> int:
 
 def q2_model_reset(h):
     _check(lib.q2_model_reset(h))
+
+
+def q2_model_set_decode_path(h, persistent: int):
+    _check(lib.q2_model_set_decode_path(h, int(persistent)))
+
+
+def q2_model_decode_path(h, batch: int) -> int:
+    n = ctypes.c_int32()
+    _check(lib.q2_model_decode_path(h, int(batch), ctypes.byref(n)))
+    return n.value
+
+
+def q2_model_check(h):
+    _check(lib.q2_model_check(h))
 
 
 def q2_model_destroy(h):

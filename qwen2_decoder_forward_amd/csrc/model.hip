@@ -13,6 +13,12 @@
 // then rmsnorm of each sequence's last row, the LM head GEMM with a fused
 // argmax epilogue, and a finalize kernel that turns the packed argmax keys
 // into token ids, stores them for the next step and resets the keys.
+//
+// Decode steps of up to 16 sequences can also run as one persistent
+// cooperative kernel per step (decode_mk.hip) that performs the same chain
+// with grid barriers between the stages (q2_model_set_decode_path); the graph
+// of per-operator kernels is the default and serves larger batches and the
+// float32 model.
 #include <math.h>
 #include <string.h>
 
@@ -24,6 +30,7 @@
 #include <vector>
 
 #include "attention.hpp"
+#include "decode_mk.hpp"
 #include "epilogue.hpp"
 #include "simple.hpp"
 
@@ -73,6 +80,13 @@ struct q2_model {
   bool len_dirty = true;
   hipStream_t cap = nullptr;
   std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+  // persistent decode kernel (decode_mk.hip)
+  bool mk_ok = false;      // buffers exist and a cooperative grid fits
+  bool mk_on = false;      // use it when eligible (q2_model_set_decode_path)
+  int mk_grid = 0;
+  unsigned mk_epoch = 0;
+  char* mkmem = nullptr;
+  MkArgs mk{};             // everything but B, logits, epoch0
 };
 
 namespace {
@@ -498,6 +512,108 @@ q2_status find_slot(q2_model* m, const std::string& name, int layer, WeightSlot*
 
 }  // namespace
 
+// Buffers and arguments of the persistent decode kernel, when the model
+// qualifies (bf16, head_dim 128, at most MK_MAX_BATCH sequences) and a
+// cooperative grid with one workgroup per CU fits.
+static q2_status setup_persistent(q2_model* m) {
+  const q2_config& c = m->cfg;
+  if (c.dtype != Q2_BF16 || c.dh != 128 || c.max_batch > MK_MAX_BATCH || c.hidden % 16 != 0 ||
+      c.inter % 16 != 0)
+    return Q2_OK;
+  const int H = c.hidden, QD = c.nh * c.dh, B = c.max_batch, L = c.nlayer, I = c.inter;
+  int grid = 0;
+  Q2_TRY(mk_max_grid(B, H, QD, &grid));
+  if (grid <= 0) return Q2_OK;
+  MkArgs& a = m->mk;
+  a.att_nsplit_max = MK_ATT_SPLITS;
+  // split the down projection over K so that its (tile, split) work items,
+  // one workgroup each, cover most of the grid
+  const int tiles = cdiv(H, 16), nkb = cdiv(I, 128);
+  const int splits = std::max(1, std::min(nkb, grid / tiles));
+  a.down_bps = cdiv(nkb, splits);
+  a.down_splits = cdiv(nkb, a.down_bps);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t o_layers = take(sizeof(MkLayer) * L);
+  const size_t o_xres = take(size_t(L + 1) * B * H * 2), o_xmid = take(size_t(L) * B * H * 2);
+  const size_t o_q = take(size_t(L) * B * QD * 2), o_act = take(size_t(L) * B * I * 2);
+  const size_t slots = size_t(L) * B * c.nkv * a.att_nsplit_max * 16;
+  const size_t o_atto = take(slots * 128 * sizeof(float)), o_attml = take(slots * sizeof(float2));
+  const size_t o_down = take(size_t(L) * a.down_splits * B * H * sizeof(float));
+  const size_t o_bar = take((size_t(grid) + 64) * sizeof(unsigned));
+  if (hipMalloc(&m->mkmem, off) != hipSuccess) {
+    (void)hipGetLastError();
+    return Q2_OK;  // the per-operator path still works
+  }
+  Q2_HIP(hipMemset(m->mkmem, 0, off));
+  std::vector<MkLayer> hl(L);
+  for (int l = 0; l < L; ++l) {
+    const q2_model::Layer& w = m->layers[l];
+    hl[l].w_in = static_cast<const uint16_t*>(w.w_in);
+    hl[l].w_post = static_cast<const uint16_t*>(w.w_post);
+    hl[l].w_qkv = static_cast<const uint16_t*>(w.w_qkv);
+    hl[l].b_qkv = static_cast<const uint16_t*>(w.b_qkv);
+    hl[l].w_o = static_cast<const uint16_t*>(w.w_o);
+    hl[l].w_gu = static_cast<const uint16_t*>(w.w_gu);
+    hl[l].w_d = static_cast<const uint16_t*>(w.w_d);
+    hl[l].kc = static_cast<uint16_t*>(m->kc) + int64_t(l) * m->kv_lstride;
+    hl[l].vc = static_cast<uint16_t*>(m->vc) + int64_t(l) * m->kv_lstride;
+  }
+  Q2_HIP(hipMemcpy(m->mkmem + o_layers, hl.data(), sizeof(MkLayer) * L, hipMemcpyHostToDevice));
+  a.layers = reinterpret_cast<const MkLayer*>(m->mkmem + o_layers);
+  a.L = L;
+  a.H = H;
+  a.nh = c.nh;
+  a.nkv = c.nkv;
+  a.I = I;
+  a.V = c.vocab;
+  a.eps = c.eps;
+  a.scale = static_cast<float>(1.0 / sqrt(static_cast<double>(c.dh)));
+  a.embed = static_cast<const uint16_t*>(m->embed);
+  a.w_final = static_cast<const uint16_t*>(m->w_final);
+  a.lm_head = static_cast<const uint16_t*>(m->lm_head);
+  a.kv_bstride = m->kv_bstride;
+  a.kv_hstride = m->kv_hstride;
+  a.rope = m->rope;
+  a.d_len = m->d_len;
+  a.ids_buf = m->ids_buf;
+  a.hist = m->hist;
+  a.hist_ld = static_cast<int64_t>(c.max_seq) + 1;
+  a.keys = m->keys;
+  a.xres = reinterpret_cast<uint16_t*>(m->mkmem + o_xres);
+  a.xmid = reinterpret_cast<uint16_t*>(m->mkmem + o_xmid);
+  a.qbuf = reinterpret_cast<uint16_t*>(m->mkmem + o_q);
+  a.act = reinterpret_cast<uint16_t*>(m->mkmem + o_act);
+  a.att_o = reinterpret_cast<float*>(m->mkmem + o_atto);
+  a.att_ml = reinterpret_cast<float2*>(m->mkmem + o_attml);
+  a.down_part = reinterpret_cast<float*>(m->mkmem + o_down);
+  a.bar_flags = reinterpret_cast<unsigned*>(m->mkmem + o_bar);
+  a.bar_release = a.bar_flags + grid;
+  a.err = a.bar_flags + grid + 32;
+  m->mk_grid = grid;
+  m->mk_ok = true;
+  m->abytes += off;
+  return Q2_OK;
+}
+
+static bool use_persistent(const q2_model* m, int B) { return m->mk_ok && m->mk_on && B <= MK_MAX_BATCH; }
+
+// One decode step on the persistent kernel (ids_buf holds the input tokens).
+static q2_status persistent_step(q2_model* m, int B, bool want_logits, hipStream_t s) {
+  MkArgs a = m->mk;
+  a.B = B;
+  a.logits = want_logits ? m->logits_buf : nullptr;
+  a.epoch0 = m->mk_epoch;
+  a.lds_x_bytes = static_cast<int>(mk_lds_x_bytes(B, a.H, a.nh * 128));
+  Q2_TRY(mk_launch(a, m->mk_grid, s));
+  m->mk_epoch += static_cast<unsigned>(mk_barriers(a.L));
+  return Q2_OK;
+}
+
 // ==================================================================== C ABI
 
 extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_model** out) {
@@ -642,6 +758,8 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
     return cleanup(fail(Q2_EHIP, "stream creation failed"));
   q2_status st = launch_rope_table(m->rope, c.max_seq, c.dh, c.theta, nullptr);
   if (st != Q2_OK) return cleanup(st);
+  st = setup_persistent(m);
+  if (st != Q2_OK) return cleanup(st);
   if (hipDeviceSynchronize() != hipSuccess) return cleanup(fail(Q2_EHIP, "device synchronize failed"));
   *out = m;
   return Q2_OK;
@@ -754,13 +872,17 @@ extern "C" q2_status q2_model_decode(q2_model* m, const q2_tensor* ids, const q2
   Q2_TRY(check_logits(m, logits, B, &lg));
   hipStream_t s = static_cast<hipStream_t>(stream);
   Q2_TRY(sync_len(m, s));
+  const bool pers = use_persistent(m, B);
   hipGraphExec_t g = nullptr;
-  Q2_TRY(get_graph(m, B, logits != nullptr, &g));
+  if (!pers) Q2_TRY(get_graph(m, B, logits != nullptr, &g));
   m->cur_batch = B;
   hipLaunchKernelGGL(copy_ids_kernel, dim3(1), dim3(64), 0, s, m->ids_buf, int64_t(1),
                      static_cast<const int64_t*>(ids->data), ids->stride[0], B);
   Q2_TRY(check_launch("copy_ids"));
-  Q2_HIP(hipGraphLaunch(g, s));
+  if (pers)
+    Q2_TRY(persistent_step(m, B, logits != nullptr, s));
+  else
+    Q2_HIP(hipGraphLaunch(g, s));
   m->len += 1;
   m->last_rows = B;
   if (next) {
@@ -779,10 +901,16 @@ extern "C" q2_status q2_model_decode(q2_model* m, const q2_tensor* ids, const q2
 
 static q2_status run_steps(q2_model* m, int steps, const q2_tensor* out_ids, int first_col, hipStream_t s) {
   const int B = m->cur_batch;
+  const bool pers = use_persistent(m, B);
   hipGraphExec_t g = nullptr;
-  if (steps > 0) Q2_TRY(get_graph(m, B, false, &g));
+  if (steps > 0 && !pers) Q2_TRY(get_graph(m, B, false, &g));
   const int start = m->len;  // the token produced last sits at position `start`
-  for (int i = 0; i < steps; ++i) Q2_HIP(hipGraphLaunch(g, s));
+  for (int i = 0; i < steps; ++i) {
+    if (pers)
+      Q2_TRY(persistent_step(m, B, false, s));
+    else
+      Q2_HIP(hipGraphLaunch(g, s));
+  }
   m->len += steps;
   if (steps > 0) m->last_rows = B;
   if (out_ids) {
@@ -817,7 +945,7 @@ extern "C" q2_status q2_model_generate(q2_model* m, const q2_tensor* prompt, int
   Q2_TRY(check_out_ids(out_ids, B, steps + 1));
   hipStream_t s = static_cast<hipStream_t>(stream);
   Q2_TRY(sync_len(m, s));
-  if (steps > 0) {
+  if (steps > 0 && !use_persistent(m, B)) {
     hipGraphExec_t g = nullptr;
     Q2_TRY(get_graph(m, B, false, &g));  // capture before any state changes
   }
@@ -879,12 +1007,41 @@ extern "C" q2_status q2_model_reset(q2_model* m) {
   return Q2_OK;
 }
 
+extern "C" q2_status q2_model_set_decode_path(q2_model* m, int32_t persistent) {
+  clear_error();
+  Q2_CHECK(m, Q2_EINVAL, "null model");
+  Q2_CHECK(persistent == 0 || persistent == 1, Q2_EINVAL, "persistent must be 0 or 1");
+  m->mk_on = persistent == 1;
+  return Q2_OK;
+}
+
+extern "C" q2_status q2_model_decode_path(const q2_model* m, int32_t batch, int32_t* persistent) {
+  clear_error();
+  Q2_CHECK(m && persistent, Q2_EINVAL, "null argument");
+  *persistent = use_persistent(m, batch) ? 1 : 0;
+  return Q2_OK;
+}
+
+extern "C" q2_status q2_model_check(q2_model* m) {
+  clear_error();
+  Q2_CHECK(m, Q2_EINVAL, "null model");
+  Q2_HIP(hipSetDevice(m->device));
+  Q2_HIP(hipDeviceSynchronize());
+  if (m->mk_ok) {
+    unsigned err = 0;
+    Q2_HIP(hipMemcpy(&err, m->mk.err, sizeof err, hipMemcpyDeviceToHost));
+    Q2_CHECK(err == 0, Q2_EHIP, "a grid barrier of the persistent decode step timed out");
+  }
+  return Q2_OK;
+}
+
 extern "C" void q2_model_destroy(q2_model* m) {
   if (!m) return;
   (void)hipSetDevice(m->device);
   (void)hipDeviceSynchronize();
   for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
   if (m->cap) (void)hipStreamDestroy(m->cap);
+  if (m->mkmem) (void)hipFree(m->mkmem);
   if (m->wmem) (void)hipFree(m->wmem);
   if (m->kvmem) (void)hipFree(m->kvmem);
   if (m->amem) (void)hipFree(m->amem);

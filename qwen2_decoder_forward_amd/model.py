@@ -97,3 +97,12 @@ class Model:
 
     def reset(self):
         _lib.q2_model_reset(self.handle)
+
+    def set_decode_path(self, persistent: bool):
+        _lib.q2_model_set_decode_path(self.handle, 1 if persistent else 0)
+
+    def decode_path(self, batch: int) -> bool:
+        return bool(_lib.q2_model_decode_path(self.handle, batch))
+
+    def check(self):
+        _lib.q2_model_check(self.handle)
