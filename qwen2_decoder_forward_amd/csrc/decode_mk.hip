@@ -37,6 +37,9 @@
 #ifndef MK_TRACE_POINT
 #define MK_TRACE_POINT(k)
 #endif
+#ifndef MK_TRACE_SUB
+#define MK_TRACE_SUB(step, k)
+#endif
 
 namespace q2 {
 
@@ -89,7 +92,8 @@ __device__ __forceinline__ unsigned co_ld32(const unsigned* p) {
 //
 // Every workgroup publishes the barrier's epoch in its own flag (arrive);
 // workgroup 0 waits for all flags and then publishes the epoch in the release
-// word, which the others wait for (wait).  A thread's stores have completed
+// word, which the others wait for (wait).  (One release line per workgroup
+// measured slower here: the 256 stores delay the release.)  A thread's stores have completed
 // (s_waitcnt) before its workgroup's flag is written.  Between arrive and wait
 // a workgroup may issue loads that do not depend on the other workgroups (the
 // next stage's weights), so that they overlap the wait.
@@ -201,11 +205,22 @@ __device__ __forceinline__ uint4 resid_row8(const MkArgs& a, int l, int m, int k
   const uint4 xm = ld16(a.xmid + (static_cast<int64_t>(l - 1) * a.B + m) * a.H + k);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const float* pp = a.down_part + static_cast<int64_t>(l - 1) * a.down_splits * a.B * a.H;
-  for (int s = 0; s < a.down_splits; ++s) {
-    const float* q = pp + (static_cast<int64_t>(s) * a.B + m) * a.H + k;
-    const float4 p0 = ldg4f(q), p1 = ldg4f(q + 4);
-    acc[0] += p0.x; acc[1] += p0.y; acc[2] += p0.z; acc[3] += p0.w;
-    acc[4] += p1.x; acc[5] += p1.y; acc[6] += p1.z; acc[7] += p1.w;
+  // all partial loads issued before the sums (MK_DOWN_SPLITS at most), summed in split order
+  float4 p0[MK_DOWN_SPLITS], p1[MK_DOWN_SPLITS];
+#pragma unroll
+  for (int s = 0; s < MK_DOWN_SPLITS; ++s) {
+    if (s < a.down_splits) {
+      const float* q = pp + (static_cast<int64_t>(s) * a.B + m) * a.H + k;
+      p0[s] = ldg4f(q);
+      p1[s] = ldg4f(q + 4);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < MK_DOWN_SPLITS; ++s) {
+    if (s < a.down_splits) {
+      acc[0] += p0[s].x; acc[1] += p0[s].y; acc[2] += p0[s].z; acc[3] += p0[s].w;
+      acc[4] += p1[s].x; acc[5] += p1[s].y; acc[6] += p1[s].z; acc[7] += p1[s].w;
+    }
   }
   const uint32_t* xs = &xm.x;
   uint4 r;
@@ -224,48 +239,59 @@ __device__ __forceinline__ uint4 resid_row8(const MkArgs& a, int l, int m, int k
 // order.
 __device__ void stage_norm(const MkArgs& a, int l, int src, const uint16_t* w_norm, uint16_t* s_x, int ld_s,
                            float* s_ss, int wave, int lane) {
+  constexpr int MAXC = MK_NORM_CHUNKS;  // chunks per lane and row (H / 8 <= 64 * MAXC * waves per row)
   const int K = a.H, CPR = K / 8;
   const int wpr = a.B >= MK_WAVES ? 1 : MK_WAVES / a.B;
   const int rows_per_pass = MK_WAVES / wpr;
   const int part = wave % wpr;
+  uint16_t* s_w = s_x + a.B * ld_s;  // the norm weights, shared by all rows
+  // the weights go to LDS while the rows load (every load issued up front)
+  for (int c = threadIdx.x; c < CPR; c += MK_THREADS)
+    *reinterpret_cast<uint4*>(s_w + 8 * c) = ld16(w_norm + 8 * c);
   for (int m0 = 0; m0 < a.B; m0 += rows_per_pass) {
     const int m = m0 + wave / wpr;
-    if (m >= a.B || wave / wpr >= rows_per_pass) continue;
-    uint16_t* row = s_x + m * ld_s;
+    const bool active = m < a.B && wave / wpr < rows_per_pass;
     float ss = 0.f;
-    for (int c = part * 64 + lane; c < CPR; c += 64 * wpr) {
-      const int k = 8 * c;
-      uint4 x;
-      if (src == 0) {
-        x = resid_row8(a, l, m, k);
-        if (blockIdx.x == 0) {
-          uint32_t* dst = reinterpret_cast<uint32_t*>(a.xres + (static_cast<int64_t>(l) * a.B + m) * a.H + k);
-          co_st32(dst, x.x);
-          co_st32(dst + 1, x.y);
-          co_st32(dst + 2, x.z);
-          co_st32(dst + 3, x.w);
-        }
-      } else {
-        x = ld16(a.xmid + (static_cast<int64_t>(l) * a.B + m) * a.H + k);
+    if (active) {
+      uint16_t* row = s_x + m * ld_s;
+      uint4 xs[MAXC];
+#pragma unroll
+      for (int j = 0; j < MAXC; ++j) {
+        const int c = part * 64 + lane + j * 64 * wpr;
+        if (c < CPR)
+          xs[j] = src == 0 ? resid_row8(a, l, m, 8 * c)
+                           : ld16(a.xmid + (static_cast<int64_t>(l) * a.B + m) * a.H + 8 * c);
       }
-      ss += sumsq8(x);
-      *reinterpret_cast<uint4*>(row + k) = x;
+#pragma unroll
+      for (int j = 0; j < MAXC; ++j) {
+        const int c = part * 64 + lane + j * 64 * wpr;
+        if (c < CPR) {
+          const int k = 8 * c;
+          if (src == 0 && blockIdx.x == 0) {
+            uint32_t* dst = reinterpret_cast<uint32_t*>(a.xres + (static_cast<int64_t>(l) * a.B + m) * a.H + k);
+            co_st32(dst, xs[j].x);
+            co_st32(dst + 1, xs[j].y);
+            co_st32(dst + 2, xs[j].z);
+            co_st32(dst + 3, xs[j].w);
+          }
+          ss += sumsq8(xs[j]);
+          *reinterpret_cast<uint4*>(row + k) = xs[j];
+        }
+      }
     }
     ss = wave_sum(ss);
-    if (lane == 0) s_ss[m * MK_WAVES + part] = ss;
+    if (active && lane == 0) s_ss[m * MK_WAVES + part] = ss;
   }
   __syncthreads();
   for (int m0 = 0; m0 < a.B; m0 += rows_per_pass) {
     const int m = m0 + wave / wpr;
     if (m >= a.B || wave / wpr >= rows_per_pass) continue;
-    float ss = 0.f;
-    for (int p = 0; p < wpr; ++p) ss += s_ss[m * MK_WAVES + p];
-    const float inv = 1.0f / sqrtf(ss / static_cast<float>(K) + a.eps);
+    float t = 0.f;
+    for (int p = 0; p < wpr; ++p) t += s_ss[m * MK_WAVES + p];
+    const float inv = 1.0f / sqrtf(t / static_cast<float>(K) + a.eps);
     uint16_t* row = s_x + m * ld_s;
-    for (int c = part * 64 + lane; c < CPR; c += 64 * wpr) {
-      const int k = 8 * c;
-      *reinterpret_cast<uint4*>(row + k) = norm8(lds16(row + k), ld16(w_norm + k), inv);
-    }
+    for (int c = part * 64 + lane; c < CPR; c += 64 * wpr)
+      *reinterpret_cast<uint4*>(row + 8 * c) = norm8(lds16(row + 8 * c), lds16(s_w + 8 * c), inv);
   }
 }
 
@@ -607,11 +633,13 @@ __global__ __launch_bounds__(MK_THREADS) void decode_mk_kernel(MkArgs a) {
         }
       }
       if (st != ST_DOWN) __syncthreads();
+      MK_TRACE_SUB(step, 0);
       const uint16_t* xps = s_x + xrow * ld_s + 8 * g;
       const uint16_t* xpg = a.act + (static_cast<int64_t>(l) * a.B + xrow) * a.I + 8 * g;
 
       if (wg_tiles(st)) {
-        // ---- workgroup tiles: waves take the K blocks kb0 + wave + 8 j
+        // ---- workgroup tiles: round j of wave w covers K blocks
+        // kb0 + w + 8 (RB j + b); two rounds of weights in flight
         const int items = gv.ntiles * splits;
         for (int i = blockIdx.x; i < items; i += G) {
           const int t = i / splits, sp = i - t * splits;
@@ -619,44 +647,88 @@ __global__ __launch_bounds__(MK_THREADS) void decode_mk_kernel(MkArgs a) {
           const int row = t * 16 + (lane & 15);
           const bool wok = row < gv.N;
           const uint16_t* wp = gv.W + static_cast<int64_t>(wok ? row : 0) * gv.ldw + 8 * g;
+          const int nround = (kb1 - kb0 - wave + RB * MK_WAVES - 1) / (RB * MK_WAVES);
+#define MK_WG_LOAD(R_, J_)                                                                           \
+  _Pragma("unroll") for (int b_ = 0; b_ < RB; ++b_) {                                               \
+    const int kk_ = kb0 + wave + MK_WAVES * (RB * (J_) + b_);                                       \
+    if (kk_ < kb1) {                                                                                \
+      _Pragma("unroll") for (int u_ = 0; u_ < 4; ++u_) {                                            \
+        const int k_ = kk_ * KB + 32 * u_ + 8 * g;                                                  \
+        R_[b_][u_] = ld16(wp + ((wok && k_ < K) ? static_cast<int64_t>(kk_) * KB + 32 * u_ : 0));   \
+      }                                                                                             \
+    }                                                                                               \
+  }
+#define MK_WG_MMA(R_, J_, XP_, XOFF_)                                                                \
+  _Pragma("unroll") for (int b_ = 0; b_ < RB; ++b_) {                                               \
+    const int kk_ = kb0 + wave + MK_WAVES * (RB * (J_) + b_);                                       \
+    if (kk_ < kb1) {                                                                                \
+      _Pragma("unroll") for (int u_ = 0; u_ < 4; ++u_) {                                            \
+        const int k_ = kk_ * KB + 32 * u_ + 8 * g;                                                  \
+        const bool kin_ = k_ < K;                                                                   \
+        uint4 xv_ = lds16((XP_) + ((xok && kin_) ? kk_ * KB + 32 * u_ - (XOFF_) : -8 * g));         \
+        if (!(xok && kin_)) xv_ = z4;                                                               \
+        const uint4 wv_ = (wok && kin_) ? R_[b_][u_] : z4;                                          \
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv_), as_bf16x8(xv_), acc, 0, 0, 0); \
+      }                                                                                             \
+    }                                                                                               \
+  }
+          if (!pre) MK_WG_LOAD(r0, 0)
+          pre = false;
+          if (nround > 1) MK_WG_LOAD(r1, 1)
+          // down: this item's K range of the SwiGLU rows into LDS (when it fits)
+          const uint16_t* xp = xps;
+          int xoff = 0;
+          bool xlds = st != ST_DOWN;
+          if (st == ST_DOWN) {
+            const int k_lo = kb0 * KB, k_hi = min(kb1 * KB, K);
+            const int ldr = k_hi - k_lo + 8;
+            xlds = static_cast<size_t>(a.B) * ldr * 2 <= static_cast<size_t>(a.lds_x_bytes);
+            if (xlds) {
+              const int cpr = (k_hi - k_lo) / 8;
+              for (int c = tid; c < a.B * cpr; c += MK_THREADS) {
+                const int m = c / cpr, k = k_lo + 8 * (c - m * cpr);
+                *reinterpret_cast<uint4*>(s_x + m * ldr + (k - k_lo)) =
+                    ld16(a.act + (static_cast<int64_t>(l) * a.B + m) * a.I + k);
+              }
+              __syncthreads();
+              xp = s_x + xrow * ldr + 8 * g;
+              xoff = k_lo;
+            }
+          }
           floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-          for (int kb = kb0 + wave; kb < kb1; kb += RB * MK_WAVES) {
-            if (!(pre && kb == kb0 + wave)) {
+          if (xlds) {
+            for (int j = 0; j < nround; j += 2) {
+              MK_WG_MMA(r0, j, xp, xoff)
+              if (j + 1 >= nround) break;
+              if (j + 2 < nround) MK_WG_LOAD(r0, j + 2)
+              MK_WG_MMA(r1, j + 1, xp, xoff)
+              if (j + 3 < nround) MK_WG_LOAD(r1, j + 3)
+            }
+          } else {
+            // SwiGLU rows read straight from global memory (large batches)
+            for (int j = 0; j < nround; ++j) {
+              if (j > 0) MK_WG_LOAD(r0, j)
 #pragma unroll
               for (int b_ = 0; b_ < RB; ++b_) {
-                const int kk_ = kb + MK_WAVES * b_;
+                const int kk_ = kb0 + wave + MK_WAVES * (RB * j + b_);
                 if (kk_ < kb1) {
 #pragma unroll
                   for (int u_ = 0; u_ < 4; ++u_) {
                     const int k_ = kk_ * KB + 32 * u_ + 8 * g;
-                    r0[b_][u_] = ld16(wp + ((wok && k_ < K) ? static_cast<int64_t>(kk_) * KB + 32 * u_ : 0));
+                    const bool kin_ = k_ < K;
+                    uint4 xv_ = ld16(xpg + ((xok && kin_) ? static_cast<int64_t>(kk_) * KB + 32 * u_ : 0));
+                    if (!(xok && kin_)) xv_ = z4;
+                    const uint4 wv_ = (wok && kin_) ? r0[b_][u_] : z4;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv_), as_bf16x8(xv_), acc, 0, 0, 0);
                   }
-                }
-              }
-            }
-            pre = false;
-#pragma unroll
-            for (int b_ = 0; b_ < RB; ++b_) {
-              const int kk_ = kb + MK_WAVES * b_;
-              if (kk_ < kb1) {
-#pragma unroll
-                for (int u_ = 0; u_ < 4; ++u_) {
-                  const int k_ = kk_ * KB + 32 * u_ + 8 * g;
-                  const bool kin_ = k_ < K;
-                  uint4 xv_;
-                  if (st == ST_DOWN) {
-                    xv_ = ld16(xpg + ((xok && kin_) ? static_cast<int64_t>(kk_) * KB + 32 * u_ : 0));
-                  } else {
-                    xv_ = lds16(xps + ((xok && kin_) ? kk_ * KB + 32 * u_ : -8 * g));
-                  }
-                  if (!(xok && kin_)) xv_ = z4;
-                  const uint4 wv_ = (wok && kin_) ? r0[b_][u_] : z4;
-                  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv_), as_bf16x8(xv_), acc, 0, 0, 0);
                 }
               }
             }
           }
+#undef MK_WG_LOAD
+#undef MK_WG_MMA
           pre = false;
+          MK_TRACE_SUB(step, 1);
           // fixed-order sum of the waves' partial tiles; wave 0 applies the epilogue
           red[wave * 64 + lane] = acc;
           __syncthreads();
@@ -743,6 +815,7 @@ __global__ __launch_bounds__(MK_THREADS) void decode_mk_kernel(MkArgs a) {
     MK_TRACE_POINT(2 * step);
     // arrive, issue the next stage's first weight loads, then wait
     grid_arrive(a, epoch);
+    MK_TRACE_SUB(step, 2);
     pre = false;
     if (step + 1 < nstage) {
       const int l2 = (step + 1) / 5;
@@ -784,7 +857,8 @@ __global__ __launch_bounds__(MK_THREADS) void decode_mk_kernel(MkArgs a) {
 }  // namespace
 
 size_t mk_lds_x_bytes(int B, int H, int QD) {
-  const size_t x = static_cast<size_t>(B) * (std::max(H, QD) + 8) * sizeof(uint16_t);
+  // B staged rows (+ the norm weights after them)
+  const size_t x = (static_cast<size_t>(B) * (std::max(H, QD) + 8) + H + 8) * sizeof(uint16_t);
   const size_t att = static_cast<size_t>(MK_WAVES) * D * VT * sizeof(uint16_t);
   return (std::max(x, att) + 15) / 16 * 16;
 }

@@ -8,6 +8,8 @@ namespace q2 {
 constexpr int MK_THREADS = 512;   // 8 waves per workgroup, one workgroup per CU
 constexpr int MK_MAX_BATCH = 16;
 constexpr int MK_ATT_SPLITS = 8;  // key chunks per (sequence, KV head) at most
+constexpr int MK_DOWN_SPLITS = 2; // K splits of the down projection at most
+constexpr int MK_NORM_CHUNKS = 4; // 16-byte chunks of a row per lane in the norm prologue at most
 
 // Per-layer device pointers (packed weights as the model loader lays them out).
 struct MkLayer {
@@ -43,7 +45,7 @@ struct MkArgs {
   int down_splits, down_bps;
   // grid barrier
   unsigned* bar_flags;    // [grid]
-  unsigned* bar_release;
+  unsigned* bar_release;  // [grid][32] (one 128-byte line per workgroup)
   unsigned epoch0;        // barrier epoch before this launch
   unsigned* err;          // set when a barrier wait timed out
   int lds_x_bytes;        // LDS bytes of the staged-X / V^T region

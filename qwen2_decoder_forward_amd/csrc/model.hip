@@ -520,6 +520,10 @@ static q2_status setup_persistent(q2_model* m) {
   if (c.dtype != Q2_BF16 || c.dh != 128 || c.max_batch > MK_MAX_BATCH || c.hidden % 16 != 0 ||
       c.inter % 16 != 0)
     return Q2_OK;
+  // the norm prologue spreads a row over 8 / B waves (one wave per row from
+  // batch 8 on), each lane holding at most MK_NORM_CHUNKS 16-byte chunks
+  const int wpr = c.max_batch >= 8 ? 1 : 8 / c.max_batch;
+  if (c.hidden / 8 > 64 * wpr * MK_NORM_CHUNKS) return Q2_OK;
   const int H = c.hidden, QD = c.nh * c.dh, B = c.max_batch, L = c.nlayer, I = c.inter;
   int grid = 0;
   Q2_TRY(mk_max_grid(B, H, QD, &grid));
@@ -529,7 +533,7 @@ static q2_status setup_persistent(q2_model* m) {
   // split the down projection over K so that its (tile, split) work items,
   // one workgroup each, cover most of the grid
   const int tiles = cdiv(H, 16), nkb = cdiv(I, 128);
-  const int splits = std::max(1, std::min(nkb, grid / tiles));
+  const int splits = std::max(1, std::min(std::min(nkb, MK_DOWN_SPLITS), grid / tiles));
   a.down_bps = cdiv(nkb, splits);
   a.down_splits = cdiv(nkb, a.down_bps);
   size_t off = 0;
@@ -544,7 +548,7 @@ static q2_status setup_persistent(q2_model* m) {
   const size_t slots = size_t(L) * B * c.nkv * a.att_nsplit_max * 16;
   const size_t o_atto = take(slots * 128 * sizeof(float)), o_attml = take(slots * sizeof(float2));
   const size_t o_down = take(size_t(L) * a.down_splits * B * H * sizeof(float));
-  const size_t o_bar = take((size_t(grid) + 64) * sizeof(unsigned));
+  const size_t o_bar = take((size_t(grid) * 33 + 64) * sizeof(unsigned));
   if (hipMalloc(&m->mkmem, off) != hipSuccess) {
     (void)hipGetLastError();
     return Q2_OK;  // the per-operator path still works
@@ -592,8 +596,8 @@ static q2_status setup_persistent(q2_model* m) {
   a.att_ml = reinterpret_cast<float2*>(m->mkmem + o_attml);
   a.down_part = reinterpret_cast<float*>(m->mkmem + o_down);
   a.bar_flags = reinterpret_cast<unsigned*>(m->mkmem + o_bar);
-  a.bar_release = a.bar_flags + grid;
-  a.err = a.bar_flags + grid + 32;
+  a.err = a.bar_flags + grid;
+  a.bar_release = a.bar_flags + grid + 32;  // [grid][32]
   m->mk_grid = grid;
   m->mk_ok = true;
   m->abytes += off;

@@ -61,6 +61,7 @@ def test_persistent_matches_graph_path_small(batch):
     w = synth.make_weights(wl)
     prompt = synth.make_prompt(wl)
     model = build_model(SMALL_BF16, w, wl.max_seq + 8, batch)
+    model.set_decode_path(True)
     assert model.decode_path(batch)
     lg_g, fed_g, tok_g = _paths_logits(model, prompt, wl.steps, False)
     lg_p = _forced_logits(model, prompt, fed_g, True)
@@ -101,6 +102,7 @@ def test_persistent_full_width_two_layers():
     w = synth.make_weights(wl)
     prompt = synth.make_prompt(wl)
     model = build_model(shape, w, wl.max_seq + 4, 1)
+    model.set_decode_path(True)
     assert model.decode_path(1)
     orc = oracle.OracleModel(shape, w, "bf16", 1, wl.max_seq + 4)
     orc64 = oracle.OracleModel(shape, w, "bf16", 1, wl.max_seq + 4, accum="f64")
