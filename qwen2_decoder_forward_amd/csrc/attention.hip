@@ -230,20 +230,25 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
   const int d0 = (threadIdx.x & 15) * 8;
   if (r >= R) return;
   const int64_t base_slot = static_cast<int64_t>(bg) * nsplit * 16 + r;
+  // branch-free and unrolled, so the partial loads of several splits are in
+  // flight together (a split with no keys has M = -inf, L = 0, o = 0 and
+  // contributes weight 0); the sums still run in split order
   float M = NEG_INF;
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[base_slot + s * 16].x);
   const float base = (M == NEG_INF) ? 0.f : M;
   float L = 0.f, o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
+#pragma unroll 4
   for (int s = 0; s < nsplit; ++s) {
     const float2 ml = part_ml[base_slot + s * 16];
-    if (ml.x == NEG_INF) continue;
-    const float f = __expf(ml.x - base);
+    const float4* po = reinterpret_cast<const float4*>(part_o + (base_slot + s * 16) * D + d0);
+    const float4 p0 = po[0], p1 = po[1];
+    const float f = ml.x == NEG_INF ? 0.f : __expf(ml.x - base);
     L += f * ml.y;
-    const float* po = part_o + (base_slot + s * 16) * D + d0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] += f * po[i];
+    o[0] += f * p0.x; o[1] += f * p0.y; o[2] += f * p0.z; o[3] += f * p0.w;
+    o[4] += f * p1.x; o[5] += f * p1.y; o[6] += f * p1.z; o[7] += f * p1.w;
   }
   const int tt = r / group;
   const int hh = g * group + (r - tt * group);

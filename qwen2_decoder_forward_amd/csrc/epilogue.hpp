@@ -164,6 +164,11 @@ constexpr size_t GEMV_STAGE_BYTES = size_t(64) << 10;
 bool gemv_can_fuse(int M, int K);
 q2_status gemv_bf16(const GemmArgs& a, hipStream_t s);
 // Split-K partial bytes the GEMV path needs for this shape (0 if unsplit).
+size_t gemv_scratch_bytes(int M, int N, int K);
+// Split-K partial bytes any bf16 decode-size product of this shape may need.
 size_t gemm_scratch_bytes(int M, int N, int K);
+// Sums split-K float32 partials partial[split][m][n] (a.scratch) in split
+// order and applies a.epi (not the argmax epilogue).
+q2_status split_reduce(const GemmArgs& a, int splits, hipStream_t s);
 
 }  // namespace q2

@@ -369,10 +369,14 @@ __device__ __forceinline__ void stg_copy_out(const uint16_t* sh, const Epi& e, i
   }
 }
 
-template <int EK, int BN, int BM, int WN, int WM, bool STAGED>
+// With SPLIT, blockIdx.y takes slices [y * kt_split, (y + 1) * kt_split) of
+// K and the float32 tile goes to partial[y][m][n] (a second kernel sums the
+// splits in order and applies the epilogue).
+template <int EK, int BN, int BM, int WN, int WM, bool STAGED, bool SPLIT>
 __global__ __launch_bounds__(WN * WM * 64) void gemm_dtl_kernel(const uint16_t* __restrict__ W, int64_t ldw,
                                                                 const uint16_t* __restrict__ X, int64_t ldx, int N,
-                                                                int M, int K, int tiles_m, Epi epi) {
+                                                                int M, int K, int tiles_m, int kt_split,
+                                                                float* __restrict__ partial, Epi epi) {
   using C = Dtl<BN, BM, WN, WM>;
   constexpr int FN = C::FN, FM = C::FM, TN = C::TN, TM = C::TM, NT = C::NT, LD = C::LD;
   extern __shared__ uint4 dsm[];
@@ -397,7 +401,7 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_dtl_kernel(const uint16_t* 
     const bool isw = slot < BN * 4;
     const int ls = isw ? slot : slot - BN * 4;
     const int r = ls >> 2;
-    const int c = dtl_swz(r, ls & 3);
+    const int c = dtl_swz(r, ls & 3) + (SPLIT ? blockIdx.y * kt_split * (C::BK / 8) : 0);
     if (isw) {
       const int row = min(n0 + r, N - 1);
       src[i] = W + static_cast<int64_t>(row) * ldw + 8 * c;
@@ -406,7 +410,7 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_dtl_kernel(const uint16_t* 
       src[i] = X + static_cast<int64_t>(row) * ldx + 8 * c;
     }
   }
-  const int nk = K / C::BK;
+  const int nk = SPLIT ? min(kt_split, K / C::BK - static_cast<int>(blockIdx.y) * kt_split) : K / C::BK;
 #define Q2_DTL_ISSUE(S_, KT_)                                                                        \
   {                                                                                                  \
     const int kt_ = (KT_);                                                                           \
@@ -496,7 +500,47 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_dtl_kernel(const uint16_t* 
   // token lane%32
   const int fb0 = n0 + wn * TN;
   const int tb0 = m0 + wm * TM;
-  if constexpr (STAGED) {
+  if constexpr (SPLIT) {
+    // N % 4 == 0: the four features of a lane's group are stored together
+    float* pp = partial + static_cast<int64_t>(blockIdx.y) * M * N;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int m = tb0 + 32 * j + (lane & 31);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int f = fb0 + 32 * i + 8 * v + 4 * (lane >> 5);
+          if (m < M && f < N)
+            *reinterpret_cast<float4*>(pp + static_cast<int64_t>(m) * N + f) =
+                make_float4(acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]);
+        }
+      }
+  } else if constexpr (EK == EPI_ARGMAX) {
+    // logits (optional) and the row's best (value, index) key over this
+    // lane's 64 features; lanes l and l + 32 share a token row
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int m = tb0 + 32 * j + (lane & 31);
+      unsigned long long key = 0;
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int f = fb0 + 32 * i + 8 * v + 4 * (lane >> 5) + e;
+            if (m < M && f < N) {
+              if (epi.out) static_cast<float*>(epi.out)[static_cast<int64_t>(m) * epi.ldo + f] = acc[i][j][4 * v + e];
+              const unsigned long long k = argmax_key(acc[i][j][4 * v + e], f);
+              key = k > key ? k : key;
+            }
+          }
+      const unsigned long long k2 = __shfl_xor(key, 32, 64);
+      key = k2 > key ? k2 : key;
+      if (lane < 32 && m < M) atomicMax(epi.keys + m * KEY_ROW + (blockIdx.x % KEY_SLOTS) * KEY_STRIDE, key);
+    }
+  } else if constexpr (STAGED) {
     __syncthreads();  // every wave has finished reading the stages reused below
     uint16_t* sh = reinterpret_cast<uint16_t*>(dsm) + wave * (TM * 128);
 #pragma unroll
@@ -552,16 +596,87 @@ template <int EK, int BN, int BM, int WN, int WM>
 q2_status launch_dtl_cfg(const GemmArgs& a, hipStream_t s) {
   using C = Dtl<BN, BM, WN, WM>;
   const int tiles_m = cdiv(a.M, BM), tiles = tiles_m * cdiv(a.N, BN);
-  const bool staged = staged_ok(a);
+  const bool staged = EK != EPI_ARGMAX && staged_ok(a);
   if (staged)
-    hipLaunchKernelGGL((gemm_dtl_kernel<EK, BN, BM, WN, WM, true>), dim3(tiles), dim3(C::NT), C::LDS_BYTES, s,
+    hipLaunchKernelGGL((gemm_dtl_kernel<EK, BN, BM, WN, WM, true, false>), dim3(tiles), dim3(C::NT), C::LDS_BYTES, s,
                        static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M,
-                       a.K, tiles_m, a.epi);
+                       a.K, tiles_m, 0, nullptr, a.epi);
   else
-    hipLaunchKernelGGL((gemm_dtl_kernel<EK, BN, BM, WN, WM, false>), dim3(tiles), dim3(C::NT), C::LDS_BYTES, s,
-                       static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M,
-                       a.K, tiles_m, a.epi);
+    hipLaunchKernelGGL((gemm_dtl_kernel<EK, BN, BM, WN, WM, false, false>), dim3(tiles), dim3(C::NT), C::LDS_BYTES,
+                       s, static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M,
+                       a.K, tiles_m, 0, nullptr, a.epi);
   return check_launch("gemm_dtl");
+}
+
+// ------------------------------------------------------------------ skinny products (decode batches)
+//
+// 17..64 token rows: too many for the GEMV (whose workgroups own 16 weight
+// rows each, so every workgroup would re-read all of X from L2) and too few
+// for the big tiles.  The direct-to-LDS kernel with 256 weight rows and all
+// token rows (32 or 64) per tile streams W once; K is split over workgroups
+// until the chip has work, as long as the float32 partials stay below a
+// quarter of the weight bytes (or 8 MB, which the L2 and MALL absorb).  The LM head (argmax epilogue) needs no split.
+
+struct SkinnyPlan {
+  int bm, splits, kt_split;  // kt_split: 32-wide K slices per split (a multiple of 4)
+};
+
+SkinnyPlan plan_skinny(int M, int N, int K) {
+  SkinnyPlan p;
+  p.bm = M <= 32 ? 32 : 64;
+  const int tiles = cdiv(N, 256);
+  const int nblk = K / 128;
+  const double wbytes = 2.0 * N * K, per_split = 4.0 * M * N;
+  const double cap = std::max(wbytes / 4, 8.0 * (1 << 20));
+  int splits = 1;
+  while (splits + 1 <= nblk && tiles * (splits + 1) <= 512 && per_split * (splits + 1) <= cap) ++splits;
+  const int bps = cdiv(nblk, splits);
+  p.splits = cdiv(nblk, bps);
+  p.kt_split = 4 * bps;
+  return p;
+}
+
+bool skinny_shape(int M, int N, int K) { return M > 16 && M <= 64 && K % 128 == 0 && N % 8 == 0; }
+
+template <int EK, int BM>
+q2_status launch_skinny_cfg(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
+  using C = Dtl<256, BM, 2, 1>;
+  const int tiles = cdiv(a.N, 256);
+  if constexpr (EK == EPI_ARGMAX) {
+    hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, 1, false, false>), dim3(tiles), dim3(C::NT), C::LDS_BYTES, s,
+                       static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M,
+                       a.K, 1, 0, nullptr, a.epi);
+    return check_launch("gemm_skinny");
+  } else {
+    if (p.splits == 1) {
+      if (staged_ok(a))
+        hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, 1, true, false>), dim3(tiles), dim3(C::NT), C::LDS_BYTES,
+                           s, static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N,
+                           a.M, a.K, 1, 0, nullptr, a.epi);
+      else
+        hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, 1, false, false>), dim3(tiles), dim3(C::NT),
+                           C::LDS_BYTES, s, static_cast<const uint16_t*>(a.W), a.ldw,
+                           static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M, a.K, 1, 0, nullptr, a.epi);
+      return check_launch("gemm_skinny");
+    }
+    hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, 1, false, true>), dim3(tiles, p.splits), dim3(C::NT),
+                       C::LDS_BYTES, s, static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X),
+                       a.ldx, a.N, a.M, a.K, 1, p.kt_split, static_cast<float*>(a.scratch), a.epi);
+    Q2_TRY(check_launch("gemm_skinny"));
+    return split_reduce(a, p.splits, s);
+  }
+}
+
+template <int EK>
+q2_status launch_skinny(const GemmArgs& a, hipStream_t s) {
+  SkinnyPlan p = plan_skinny(a.M, a.N, a.K);
+  if (EK == EPI_ARGMAX) p.splits = 1;
+  if (p.splits > 1) {
+    const size_t need = static_cast<size_t>(p.splits) * a.M * a.N * sizeof(float);
+    Q2_CHECK(a.scratch && a.scratch_bytes >= need, Q2_EINVAL, "skinny linear: split-K scratch too small");
+  }
+  if (p.bm == 32) return launch_skinny_cfg<EK, 32>(a, p, s);
+  return launch_skinny_cfg<EK, 64>(a, p, s);
 }
 
 // 256 x 256 tiles (8 waves, 128 KB LDS, one workgroup per CU) when they give
@@ -633,9 +748,27 @@ q2_status gemm_f32_ek(const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
+size_t gemm_scratch_bytes(int M, int N, int K) {
+  size_t b = gemv_scratch_bytes(M, N, K);
+  if (skinny_shape(M, N, K)) {
+    const SkinnyPlan p = plan_skinny(M, N, K);
+    if (p.splits > 1) b = std::max(b, static_cast<size_t>(p.splits) * M * N * sizeof(float));
+  }
+  return b;
+}
+
 q2_status gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0 || a.N == 0) return Q2_OK;
   Q2_CHECK(a.K % 8 == 0, Q2_ESHAPE, "bf16 linear: K=%d must be a multiple of 8", a.K);
+  if (skinny_shape(a.M, a.N, a.K) && dtl_ok(a) && !a.norm_w && !a.att_o) {
+    switch (a.epi.kind) {
+      case EPI_STORE: return launch_skinny<EPI_STORE>(a, s);
+      case EPI_RESID: return launch_skinny<EPI_RESID>(a, s);
+      case EPI_SWIGLU: return launch_skinny<EPI_SWIGLU>(a, s);
+      case EPI_QKV: return launch_skinny<EPI_QKV>(a, s);
+      case EPI_ARGMAX: return launch_skinny<EPI_ARGMAX>(a, s);
+    }
+  }
   if (a.M <= GEMV_MAX_M) return gemv_bf16(a, s);
   Q2_CHECK(a.norm_w == nullptr, Q2_EINVAL, "fused RMSNorm needs M <= %d", GEMV_NORM_MAX_M);
   switch (a.epi.kind) {

@@ -69,17 +69,20 @@ __device__ __forceinline__ uint4 attn_merge8(const GemvSrc& src, int m, int k) {
   const int g = h / src.att_group;
   const int r = h - g * src.att_group;
   const int64_t base = (static_cast<int64_t>(m) * src.att_nkv + g) * src.att_nsplit * 16 + r;
+  // branch-free and unrolled so several splits' loads are in flight together
+  // (a split with no keys has max -inf, sum 0 and output 0: weight 0)
   float mx = -__builtin_huge_valf();
+#pragma unroll 8
   for (int sp = 0; sp < src.att_nsplit; ++sp) mx = fmaxf(mx, src.att_ml[base + sp * 16].x);
   const float bse = mx == -__builtin_huge_valf() ? 0.f : mx;
   float l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int sp = 0; sp < src.att_nsplit; ++sp) {
     const float2 ml = src.att_ml[base + sp * 16];
-    if (ml.x == -__builtin_huge_valf()) continue;
-    const float f = __expf(ml.x - bse);
-    l += f * ml.y;
     const float4* po = reinterpret_cast<const float4*>(src.att_o + (base + sp * 16) * 128 + d0);
     const float4 a = po[0], b = po[1];
+    const float f = ml.x == -__builtin_huge_valf() ? 0.f : __expf(ml.x - bse);
+    l += f * ml.y;
     o[0] += f * a.x; o[1] += f * a.y; o[2] += f * a.z; o[3] += f * a.w;
     o[4] += f * b.x; o[5] += f * b.y; o[6] += f * b.z; o[7] += f * b.w;
   }
@@ -320,10 +323,21 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
   float v0 = 0.f, v1 = 0.f;
   if (m < M && n < N) {
     const bool has1 = n + 1 < N;
-    for (int sp = 0; sp < splits; ++sp) {
-      const float* q = partial + (static_cast<int64_t>(sp) * M + m) * N + n;
-      v0 += q[0];
-      if (has1) v1 += q[1];
+    if (has1 && (N & 1) == 0) {
+      // n is even: one 8-byte load per split, unrolled so that several
+      // splits' loads are in flight together; sums in split order
+#pragma unroll 8
+      for (int sp = 0; sp < splits; ++sp) {
+        const float2 q = *reinterpret_cast<const float2*>(partial + (static_cast<int64_t>(sp) * M + m) * N + n);
+        v0 += q.x;
+        v1 += q.y;
+      }
+    } else {
+      for (int sp = 0; sp < splits; ++sp) {
+        const float* q = partial + (static_cast<int64_t>(sp) * M + m) * N + n;
+        v0 += q[0];
+        if (has1) v1 += q[1];
+      }
     }
   }
   gemv_epilogue<EK>(epi, M, N, tl * 16, tl, m < M ? m : M, p, v0, v1);
@@ -346,6 +360,10 @@ GemvPlan plan_gemv(int M, int N, int K) {
   int splits = 1;
   while (tiles * splits < 512 && nkb / (splits + 1) >= p.nw / 2 && splits + 1 <= cap) ++splits;
   p.bps = cdiv(nkb, splits);
+  // the X rows of a split's K range must fit the LDS stage: reading them from
+  // L2 inside the block loop puts a dependent load behind every weight batch
+  const int bps_fit = std::max(1, static_cast<int>((GEMV_STAGE_BYTES / (2 * M) - 8) / KB));
+  p.bps = std::min(p.bps, bps_fit);
   p.splits = cdiv(nkb, p.bps);
   return p;
 }
@@ -403,11 +421,32 @@ q2_status gemv_ek(const GemmArgs& a, const GemvPlan& p, hipStream_t s) {
 }  // namespace
 
 bool gemv_can_fuse(int M, int K) {
-  // the staged K range is largest without splits
-  return M <= GEMV_NORM_MAX_M && stage_bytes(M, cdiv(K, KB), K) <= GEMV_STAGE_BYTES;
+  // The fused prologues rebuild X in every workgroup; that pays only while one
+  // pass of the workgroup's threads (16 B each) covers it.  Beyond that the
+  // dependent L2 round trips of the prologue cost more than a separate
+  // normalisation kernel.  (The staged K range is largest without splits.)
+  return M <= GEMV_NORM_MAX_M && static_cast<int64_t>(M) * (K / 8) <= 16 * 64 &&
+         stage_bytes(M, cdiv(K, KB), K) <= GEMV_STAGE_BYTES;
 }
 
-size_t gemm_scratch_bytes(int M, int N, int K) {
+q2_status split_reduce(const GemmArgs& a, int splits, hipStream_t s) {
+  const int pairs = a.M * cdiv(a.N, 16);
+  switch (a.epi.kind) {
+#define Q2_REDUCE_CASE(EK_)                                                                                     \
+  case EK_:                                                                                                     \
+    hipLaunchKernelGGL((gemv_reduce_kernel<EK_>), dim3(cdiv(pairs, 32)), dim3(256), 0, s,                        \
+                       static_cast<const float*>(a.scratch), splits, a.M, a.N, a.epi);                          \
+    return check_launch("split_reduce");
+    Q2_REDUCE_CASE(EPI_STORE)
+    Q2_REDUCE_CASE(EPI_RESID)
+    Q2_REDUCE_CASE(EPI_SWIGLU)
+    Q2_REDUCE_CASE(EPI_QKV)
+#undef Q2_REDUCE_CASE
+  }
+  return fail(Q2_EINVAL, "split reduce: unsupported epilogue %d", a.epi.kind);
+}
+
+size_t gemv_scratch_bytes(int M, int N, int K) {
   if (M > GEMV_MAX_M) return 0;
   GemvPlan p = plan_gemv(M, N, K);
   return p.splits > 1 ? static_cast<size_t>(p.splits) * M * N * sizeof(float) : 0;

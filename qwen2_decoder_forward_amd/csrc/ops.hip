@@ -72,6 +72,55 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(T* __restrict__ out, int64
   for (int i = lane; i < H; i += 64) S::st(y + i, (S::ld(x + i) * inv) * S::ld(w + i));
 }
 
+// bf16 rows with H % 8 == 0 and 16-byte aligned rows: one wave per row, the
+// row held in registers (CH 16-byte chunks per lane), every load issued before
+// the first use, so a row costs one memory round trip instead of H / 64.
+template <int CH>
+__global__ __launch_bounds__(256) void rmsnorm_vec_kernel(uint16_t* __restrict__ out, int64_t ldo,
+                                                          const uint16_t* __restrict__ in, int64_t ldi,
+                                                          const uint16_t* __restrict__ w, int rows, int H, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int nch = H >> 3;
+  const uint16_t* x = in + static_cast<int64_t>(row) * ldi;
+  uint4 v[CH];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = lane + 64 * c;
+    v[c] = i < nch ? *reinterpret_cast<const uint4*>(x + 8 * i) : uint4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const uint32_t* e = &v[c].x;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float a = bf_lo(e[k]), b = bf_hi(e[k]);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+    }
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / static_cast<float>(H) + eps);
+  uint16_t* y = out + static_cast<int64_t>(row) * ldo;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = lane + 64 * c;
+    if (i < nch) {
+      const uint4 wv = *reinterpret_cast<const uint4*>(w + 8 * i);
+      const uint32_t* e = &v[c].x;
+      const uint32_t* we = &wv.x;
+      uint4 r;
+      uint32_t* re = &r.x;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        re[k] = pack_bf2((bf_lo(e[k]) * inv) * bf_lo(we[k]), (bf_hi(e[k]) * inv) * bf_hi(we[k]));
+      *reinterpret_cast<uint4*>(y + 8 * i) = r;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ add / swiglu
 
 template <typename T>
@@ -268,6 +317,20 @@ template <typename T>
 q2_status launch_rmsnorm(T* out, int64_t ldo, const T* in, int64_t ldi, const T* w, int rows, int H, float eps,
                          hipStream_t s) {
   if (rows == 0) return Q2_OK;
+  if constexpr (sizeof(T) == 2) {
+    const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    const int ch = cdiv(H / 8, 64);
+    if (H % 8 == 0 && ldo % 8 == 0 && ldi % 8 == 0 && a16(out) && a16(in) && a16(w) && ch <= 8) {
+      const dim3 g(cdiv(rows, 4)), b(256);
+      if (ch <= 2)
+        hipLaunchKernelGGL(rmsnorm_vec_kernel<2>, g, b, 0, s, out, ldo, in, ldi, w, rows, H, eps);
+      else if (ch <= 4)
+        hipLaunchKernelGGL(rmsnorm_vec_kernel<4>, g, b, 0, s, out, ldo, in, ldi, w, rows, H, eps);
+      else
+        hipLaunchKernelGGL(rmsnorm_vec_kernel<8>, g, b, 0, s, out, ldo, in, ldi, w, rows, H, eps);
+      return check_launch("rms_norm");
+    }
+  }
   hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(cdiv(rows, 4)), dim3(256), 0, s, out, ldo, in, ldi, w, rows, H, eps);
   return check_launch("rms_norm");
 }

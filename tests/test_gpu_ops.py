@@ -52,7 +52,7 @@ def test_embedding_bit_exact(dtype):
 
 # ------------------------------------------------------------------ rms_norm
 
-@pytest.mark.parametrize("rows,H", [(1, 1536), (7, 3584), (130, 128), (5, 100)])
+@pytest.mark.parametrize("rows,H", [(1, 1536), (7, 3584), (130, 128), (5, 100), (64, 1536), (3, 4096), (2, 8192)])
 def test_rms_norm_bf16(rows, H):
     r = rng(2)
     x = bf16_vals(r, (rows, H))
@@ -107,7 +107,10 @@ def test_rope_batched_in_place_large_theta():
 # ------------------------------------------------------------------ linear
 
 @pytest.mark.parametrize("M,N,K", [(1, 300, 1536), (5, 2048, 1536), (16, 96, 8960), (33, 300, 200), (64, 130, 64),
-                                   (65, 300, 200), (200, 2048, 1536), (300, 260, 136)])
+                                   (65, 300, 200), (200, 2048, 1536), (300, 260, 136),
+                                   # 17..64 rows with K % 128 == 0: the skinny tiles, split over K or not
+                                   (17, 520, 384), (24, 264, 1024), (48, 1536, 8960), (64, 2048, 1536),
+                                   (64, 17920, 1536)])
 @pytest.mark.parametrize("bias,out_f32", [(True, False), (False, True)])
 def test_linear_bf16(M, N, K, bias, out_f32):
     r = rng(M * 1000 + N + K)
