@@ -21,6 +21,8 @@
 // four consecutive keys of one query: exactly the B-operand layout of the
 // 16x16x16 MFMA that computes O^T = V^T P^T.  No shuffles are needed between
 // the two products.
+#include <algorithm>
+
 #include "attention.hpp"
 
 namespace q2 {
@@ -90,9 +92,13 @@ __device__ __forceinline__ float softmax_step(float* s, int n, float& m_run, flo
 
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk, int nsplit,
                                                           float* __restrict__ part_o, float2* __restrict__ part_ml) {
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[4][D * VT_DEC];
-  __shared__ float sO[4][D][17];
+  // the V^T tiles of the key loop and the merge buffers of the four waves
+  // are never live together (a barrier separates them): one LDS region
+  constexpr int VT_BYTES = 4 * D * VT_DEC * 2, O_BYTES = 4 * D * 17 * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[VT_BYTES > O_BYTES ? VT_BYTES : O_BYTES];
   __shared__ float sM[4][16], sL[4][16];
+  uint16_t (*sVt)[D * VT_DEC] = reinterpret_cast<uint16_t (*)[D * VT_DEC]>(smem);
+  float (*sO)[D][17] = reinterpret_cast<float (*)[D][17]>(smem);
 
   const int split = blockIdx.x;
   const int bg = blockIdx.y;
@@ -129,17 +135,25 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int j0 = j_begin + 16 * wave; j0 < j_end; j0 += 64) {
-    // K rows j0 + col: 4 x 16 B (d = 32kk + 8G .. +8); V rows j0 + 4G + s, d-chunk 8*col
-    const int key = j0 + col;
-    uint4 kf[4], vf[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) kf[kk] = key < j_end ? ld16(kbase + static_cast<int64_t>(key) * a.k_ss + 32 * kk + 8 * G) : z;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int vk = j0 + 4 * G + s;
-      vf[s] = vk < j_end ? ld16(vbase + static_cast<int64_t>(vk) * a.v_ss + 8 * col) : z;
-    }
+  // K rows j0 + col: 4 x 16 B (d = 32kk + 8G .. +8); V rows j0 + 4G + s,
+  // d-chunk 8*col.  The next block's loads are issued before this block's
+  // math (double-buffered registers), so a wave always has a block in flight.
+#define Q2_DEC_LOAD(KF_, VF_, J0_)                                                                   \
+  {                                                                                                  \
+    const int key_ = (J0_) + col;                                                                    \
+    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) KF_[kk] =                                       \
+        key_ < j_end ? ld16(kbase + static_cast<int64_t>(key_) * a.k_ss + 32 * kk + 8 * G) : z;      \
+    _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) {                                               \
+      const int vk_ = (J0_) + 4 * G + s_;                                                            \
+      VF_[s_] = vk_ < j_end ? ld16(vbase + static_cast<int64_t>(vk_) * a.v_ss + 8 * col) : z;        \
+    }                                                                                                \
+  }
+  uint4 kf[4], vf[4];
+  int j0 = j_begin + 16 * wave;
+  if (j0 < j_end) Q2_DEC_LOAD(kf, vf, j0)
+  for (; j0 < j_end; j0 += 64) {
+    uint4 kn[4], vn[4];
+    if (j0 + 64 < j_end) Q2_DEC_LOAD(kn, vn, j0 + 64)
     floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -165,7 +179,14 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(vv), pf, oacc[dt], 0, 0, 0);
     }
     wave_lds_sync();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      kf[kk] = kn[kk];
+      vf[kk] = vn[kk];
+    }
   }
+#undef Q2_DEC_LOAD
+  __syncthreads();  // every wave is done with its V^T tile before sO reuses the region
 
   // merge the four waves
 #pragma unroll
@@ -499,14 +520,18 @@ struct DecodePlan {
   int chunk, nsplit;
 };
 
+// Keys per split: 64 to start with, doubled while there would be more than
+// two workgroups per CU (each workgroup's partials cost a write and a read,
+// and longer key loops keep the double-buffered loads busy); then the splits
+// are evened out (multiples of 64 keys).
 DecodePlan plan_decode(int B, int s_max, int nkv) {
   DecodePlan p;
   const int64_t heads = static_cast<int64_t>(B) * nkv;
   int chunk = 64;
-  while (chunk < 1024 && heads * cdiv(s_max, chunk) > 1024) chunk *= 2;
-  p.chunk = chunk;
-  p.nsplit = cdiv(s_max, chunk);
-  if (p.nsplit < 1) p.nsplit = 1;
+  while (chunk < 8192 && heads * cdiv(s_max, chunk) > 512) chunk *= 2;
+  const int nsplit = std::max(1, cdiv(s_max, chunk));
+  p.chunk = cdiv(cdiv(s_max, nsplit), 64) * 64;
+  p.nsplit = std::max(1, cdiv(s_max, p.chunk));
   return p;
 }
 
