@@ -41,6 +41,13 @@ __device__ __forceinline__ short4_t as_short4(uint2 v) {
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Marks a loaded value as arrived.  The query fragments are loaded once and
+// used in every iteration of a key loop that also issues loads; without this
+// the compiler cannot tell across the loop's back edge whether they are still
+// pending and waits for every outstanding load (the next block's prefetch
+// included) before the first product of each iteration.
+__device__ __forceinline__ void settle(uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
+
 // Order the wave's own LDS writes before its later LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
@@ -90,6 +97,38 @@ __device__ __forceinline__ float softmax_step(float* s, int n, float& m_run, flo
 
 // ------------------------------------------------------------------ decode (split-KV)
 
+// One 16-key block of the decode loop for the calling wave: S^T = K Q^T,
+// online softmax, O^T += V^T P^T (V^T through the wave's LDS tile).
+__device__ __forceinline__ void dec_block(const uint4 (&kf)[4], const uint4 (&vf)[4], const uint4 (&qf)[4],
+                                          uint16_t* vt, int j0, int j_end, int lim, float scale, int col, int G,
+                                          floatx4_t (&oacc)[8], float& m_run, float& l_run) {
+  floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kk]), as_bf16x8(qf[kk]), sacc, 0, 0, 0);
+  store_vt4(vt, VT_DEC, 8 * col, 4 * G, vf);
+
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kj = j0 + 4 * G + i;
+    s[i] = (kj < j_end && kj <= lim) ? sacc[i] * scale : NEG_INF;
+  }
+  const float alpha = softmax_step(s, 4, m_run, l_run);
+  uint2 pw;
+  pw.x = pack_bf2(s[0], s[1]);
+  pw.y = pack_bf2(s[2], s[3]);
+  const short4_t pf = as_short4(pw);
+  wave_lds_sync();
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    oacc[dt][0] *= alpha; oacc[dt][1] *= alpha; oacc[dt][2] *= alpha; oacc[dt][3] *= alpha;
+    const uint2 vv = *reinterpret_cast<const uint2*>(vt + (16 * dt + col) * VT_DEC + 4 * G);
+    oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(vv), pf, oacc[dt], 0, 0, 0);
+  }
+  wave_lds_sync();
+}
+
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk, int nsplit,
                                                           float* __restrict__ part_o, float2* __restrict__ part_ml) {
   // the V^T tiles of the key loop and the merge buffers of the four waves
@@ -125,6 +164,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
   const uint4 z = {0, 0, 0, 0};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qf[kk] = rvalid ? ld16(qp + 32 * kk + 8 * G) : z;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) settle(qf[kk]);
 
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_bs + g * a.k_hs;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.v_bs + g * a.v_hs;
@@ -136,54 +177,33 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   // K rows j0 + col: 4 x 16 B (d = 32kk + 8G .. +8); V rows j0 + 4G + s,
-  // d-chunk 8*col.  The next block's loads are issued before this block's
-  // math (double-buffered registers), so a wave always has a block in flight.
+  // d-chunk 8*col.  Loads are unconditional (keys past the split read its
+  // last key: their scores are masked and their probabilities exactly 0), so
+  // the compiler can count them and wait for one block only.
 #define Q2_DEC_LOAD(KF_, VF_, J0_)                                                                   \
   {                                                                                                  \
-    const int key_ = (J0_) + col;                                                                    \
+    const int key_ = max(min((J0_) + col, j_end - 1), 0);                                           \
     _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) KF_[kk] =                                       \
-        key_ < j_end ? ld16(kbase + static_cast<int64_t>(key_) * a.k_ss + 32 * kk + 8 * G) : z;      \
+        ld16(kbase + static_cast<int64_t>(key_) * a.k_ss + 32 * kk + 8 * G);                         \
     _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) {                                               \
-      const int vk_ = (J0_) + 4 * G + s_;                                                            \
-      VF_[s_] = vk_ < j_end ? ld16(vbase + static_cast<int64_t>(vk_) * a.v_ss + 8 * col) : z;        \
+      const int vk_ = max(min((J0_) + 4 * G + s_, j_end - 1), 0);                                    \
+      VF_[s_] = ld16(vbase + static_cast<int64_t>(vk_) * a.v_ss + 8 * col);                          \
     }                                                                                                \
   }
-  uint4 kf[4], vf[4];
+  // two register sets, loop unrolled by two: the next block's loads are in
+  // flight while this block is multiplied
+  // Every load is issued unconditionally (past the end it rereads a valid
+  // key): with a load count that does not depend on the path, the compiler
+  // waits for the older set only.
+  uint4 kf0[4], vf0[4], kf1[4], vf1[4];
   int j0 = j_begin + 16 * wave;
-  if (j0 < j_end) Q2_DEC_LOAD(kf, vf, j0)
-  for (; j0 < j_end; j0 += 64) {
-    uint4 kn[4], vn[4];
-    if (j0 + 64 < j_end) Q2_DEC_LOAD(kn, vn, j0 + 64)
-    floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kk]), as_bf16x8(qf[kk]), sacc, 0, 0, 0);
-    store_vt4(vt, VT_DEC, 8 * col, 4 * G, vf);
-
-    float s[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kj = j0 + 4 * G + i;
-      s[i] = (kj < j_end && kj <= lim) ? sacc[i] * a.scale : NEG_INF;
-    }
-    const float alpha = softmax_step(s, 4, m_run, l_run);
-    uint2 pw;
-    pw.x = pack_bf2(s[0], s[1]);
-    pw.y = pack_bf2(s[2], s[3]);
-    const short4_t pf = as_short4(pw);
-    wave_lds_sync();
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      oacc[dt][0] *= alpha; oacc[dt][1] *= alpha; oacc[dt][2] *= alpha; oacc[dt][3] *= alpha;
-      const uint2 vv = *reinterpret_cast<const uint2*>(vt + (16 * dt + col) * VT_DEC + 4 * G);
-      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(vv), pf, oacc[dt], 0, 0, 0);
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      kf[kk] = kn[kk];
-      vf[kk] = vn[kk];
-    }
+  Q2_DEC_LOAD(kf0, vf0, j0)
+  for (; j0 < j_end; j0 += 128) {
+    Q2_DEC_LOAD(kf1, vf1, j0 + 64)
+    dec_block(kf0, vf0, qf, vt, j0, j_end, lim, a.scale, col, G, oacc, m_run, l_run);
+    if (j0 + 64 >= j_end) break;
+    Q2_DEC_LOAD(kf0, vf0, j0 + 128)
+    dec_block(kf1, vf1, qf, vt, j0 + 64, j_end, lim, a.scale, col, G, oacc, m_run, l_run);
   }
 #undef Q2_DEC_LOAD
   __syncthreads();  // every wave is done with its V^T tile before sO reuses the region
@@ -288,7 +308,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
 // 128 queries of one head per workgroup, 32 per wave, 32x32x16 bf16 MFMAs.
 // Keys move in tiles of 64 through two LDS buffers: the next tile's K and V
 // are loaded into registers while the current one is multiplied, then
-// written to the other buffer (one barrier per tile).
+// written to the other buffer (one barrier per tile).  Two workgroups per
+// CU, so one's softmax arithmetic overlaps the other's products.
 //
 // S^T = K Q^T: K rows are the A operand, the wave's 32 queries the B operand
 // (held in registers for the whole kernel), so element 4v+e of a 32x32 result
@@ -308,6 +329,96 @@ constexpr int PF_KT = 64;    // keys per tile
 constexpr int PF_VT = 72;    // bf16 per V^T LDS row
 
 __device__ __forceinline__ int pf_keyperm(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+// One 64-key tile of the prefill loop for the calling wave: S^T from the
+// K tile, online softmax of the wave's 32 queries, O^T += V^T P^T.
+// Scores are kept in base-2 units (scale * log2 e folded in), so each
+// probability is one exp2; a tile entirely inside every query's causal
+// window skips the mask; the accumulator is rescaled only when some lane's
+// running maximum moved (alpha == 1 exactly otherwise).  exp2(-inf) = 0
+// covers masked keys.
+__device__ __forceinline__ void pf_tile(const uint4* __restrict__ sKb, const uint16_t* __restrict__ sVtb, int j0,
+                                        bool full, int lim, float sl2, int qr, int hl, const uint4 (&qf)[8],
+                                        floatx16_t (&oacc)[4], float& m_run, float& l_run) {
+  // S^T for two 32-key halves
+  floatx16_t sacc[2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[kh][e] = 0.f;
+    const int r = 32 * kh + qr;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 kfr = sKb[r * 16 + ((2 * ks + hl) ^ (r & 15))];
+      sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kfr), as_bf16x8(qf[ks]), sacc[kh], 0, 0, 0);
+    }
+  }
+  // scale (and mask), running max of query qr (lanes qr and qr + 32)
+  float mt = NEG_INF;
+  if (full) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sacc[kh][i] *= sl2;
+        mt = fmaxf(mt, sacc[kh][i]);
+      }
+  } else {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kj = j0 + 32 * kh + 8 * v + 4 * hl + e;
+          const float x = kj <= lim ? sacc[kh][4 * v + e] * sl2 : NEG_INF;
+          sacc[kh][4 * v + e] = x;
+          mt = fmaxf(mt, x);
+        }
+  }
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float m_new = fmaxf(m_run, mt);
+  const float base = m_new == NEG_INF ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(m_run - base);
+  float ps = 0.f;
+  bf16x8_t pf[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint4 w;
+    uint32_t* ws = &w.x;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int v = 2 * (c & 1) + half;
+      float pr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pr[e] = __builtin_amdgcn_exp2f(sacc[c >> 1][4 * v + e] - base);
+        ps += pr[e];
+      }
+      ws[2 * half] = pack_bf2(pr[0], pr[1]);
+      ws[2 * half + 1] = pack_bf2(pr[2], pr[3]);
+    }
+    pf[c] = as_bf16x8(w);
+  }
+  ps += __shfl_xor(ps, 32, 64);
+  l_run = l_run * alpha + ps;
+  m_run = m_new;
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
+  }
+  // O^T += V^T P^T
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 vfr = *reinterpret_cast<const uint4*>(&sVtb[(32 * dt + qr) * PF_VT + 16 * c + 8 * hl]);
+      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr), pf[c], oacc[dt], 0, 0, 0);
+    }
+  }
+}
 
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
   __shared__ uint4 sK[2][PF_KT * 16];
@@ -337,6 +448,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
                          static_cast<int64_t>(qvalid ? tq : 0) * a.q_ts + h * a.q_hs;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = ld16(qp + 16 * ks + 8 * hl);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) settle(qf[ks]);
   }
 
   const int kv_end = min(S, P + min(q0 + PF_QB, a.T));
@@ -352,26 +465,26 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
   // probabilities are exactly zero.
   const int vc = tid & 15, vg = tid >> 4;
   uint4 rk[4], rv[4];
-#define Q2_PF_LOAD(J0_)                                                                              \
+#define Q2_PF_LOAD(RK_, RV_, J0_)                                                                              \
   {                                                                                                  \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                  \
       const int q_ = tid + 256 * i;                                                                  \
       const int key_ = min((J0_) + (q_ >> 4), kv_end - 1);                                           \
-      rk[i] = ld16(kbase + static_cast<int64_t>(key_) * a.k_ss + 8 * (q_ & 15));                     \
+      RK_[i] = ld16(kbase + static_cast<int64_t>(key_) * a.k_ss + 8 * (q_ & 15));                    \
     }                                                                                                \
     _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) {                                               \
       const int key_ = min((J0_) + 4 * vg + s_, kv_end - 1);                                         \
-      rv[s_] = ld16(vbase + static_cast<int64_t>(key_) * a.v_ss + 8 * vc);                           \
+      RV_[s_] = ld16(vbase + static_cast<int64_t>(key_) * a.v_ss + 8 * vc);                          \
     }                                                                                                \
   }
-#define Q2_PF_STORE(BUF_)                                                                            \
+#define Q2_PF_STORE(BUF_, RK_, RV_)                                                                  \
   {                                                                                                  \
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                  \
       const int q_ = tid + 256 * i;                                                                  \
       const int r_ = q_ >> 4;                                                                        \
-      sK[BUF_][r_ * 16 + ((q_ & 15) ^ (r_ & 15))] = rk[i];                                           \
+      sK[BUF_][r_ * 16 + ((q_ & 15) ^ (r_ & 15))] = RK_[i];                                          \
     }                                                                                                \
-    store_vt4(sVt[BUF_], PF_VT, 8 * vc, pf_keyperm(4 * vg), rv);                                     \
+    store_vt4(sVt[BUF_], PF_VT, 8 * vc, pf_keyperm(4 * vg), RV_);                                    \
   }
 
   float m_run = NEG_INF, l_run = 0.f;
@@ -382,81 +495,21 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
 
   const int ntiles = (kv_end + PF_KT - 1) / PF_KT;
-  Q2_PF_LOAD(0)
-  Q2_PF_STORE(0)
+  // The loads are issued unconditionally (past kv_end they reread the last
+  // key), so the compiler's count of loads in flight does not depend on the
+  // path.  The wave's first query decides whether a tile needs the mask.
+  const float sl2 = a.scale * 1.4426950408889634f;
+  const int wave_full = wave_first < a.T ? P + wave_first : -1;
+  Q2_PF_LOAD(rk, rv, 0)
+  Q2_PF_STORE(0, rk, rv)
   __syncthreads();
   for (int jt = 0; jt < ntiles; ++jt) {
     const int buf = jt & 1;
     const int j0 = jt * PF_KT;
-    if (jt + 1 < ntiles) Q2_PF_LOAD(j0 + PF_KT)
-    if (j0 <= wave_lim) {
-      // S^T for two 32-key halves
-      floatx16_t sacc[2];
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[kh][e] = 0.f;
-        const int r = 32 * kh + qr;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const uint4 kfr = sK[buf][r * 16 + ((2 * ks + hl) ^ (r & 15))];
-          sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kfr), as_bf16x8(qf[ks]), sacc[kh], 0, 0, 0);
-        }
-      }
-      // scale, mask, online softmax of query qr (lanes qr and qr + 32)
-      float mt = NEG_INF;
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int kj = j0 + 32 * kh + 8 * v + 4 * hl + e;
-            const float x = kj <= lim ? sacc[kh][4 * v + e] * a.scale : NEG_INF;
-            sacc[kh][4 * v + e] = x;
-            mt = fmaxf(mt, x);
-          }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run, mt);
-      const float base = m_new == NEG_INF ? 0.f : m_new;
-      const float alpha = m_run == NEG_INF ? 0.f : __expf(m_run - base);
-      float ps = 0.f;
-      bf16x8_t pf[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint4 w;
-        uint32_t* ws = &w.x;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int v = 2 * (c & 1) + half;
-          float pr[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = sacc[c >> 1][4 * v + e];
-            pr[e] = x == NEG_INF ? 0.f : __expf(x - base);
-            ps += pr[e];
-          }
-          ws[2 * half] = pack_bf2(pr[0], pr[1]);
-          ws[2 * half + 1] = pack_bf2(pr[2], pr[3]);
-        }
-        pf[c] = as_bf16x8(w);
-      }
-      ps += __shfl_xor(ps, 32, 64);
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-      // O^T += V^T P^T
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint4 vfr = *reinterpret_cast<const uint4*>(&sVt[buf][(32 * dt + qr) * PF_VT + 16 * c + 8 * hl]);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr), pf[c], oacc[dt], 0, 0, 0);
-        }
-      }
-    }
-    if (jt + 1 < ntiles) Q2_PF_STORE(buf ^ 1)
+    Q2_PF_LOAD(rk, rv, j0 + PF_KT)
+    if (j0 <= wave_lim)
+      pf_tile(sK[buf], sVt[buf], j0, j0 + PF_KT - 1 <= wave_full, lim, sl2, qr, hl, qf, oacc, m_run, l_run);
+    if (jt + 1 < ntiles) Q2_PF_STORE(buf ^ 1, rk, rv)
     __syncthreads();
   }
 #undef Q2_PF_LOAD

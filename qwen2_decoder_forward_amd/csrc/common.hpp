@@ -84,16 +84,16 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16_t;
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;  // NaN stays NaN
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
-__device__ __forceinline__ float round_bf(float f) { return bf2f(f2bf(f)); }
+// (gfx950 converts in hardware: v_cvt_pk_bf16_f32, round to nearest even,
+// NaN stays NaN.)
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float float2_hw __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
+  const float2_hw f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_hw));
 }
+__device__ __forceinline__ uint16_t f2bf(float f) { return static_cast<uint16_t>(pack_bf2(f, 0.f)); }
+__device__ __forceinline__ float round_bf(float f) { return bf2f(f2bf(f)); }
 
 // Storage traits: float (no rounding) and bf16 (uint16_t bit patterns).
 template <typename T> struct St;

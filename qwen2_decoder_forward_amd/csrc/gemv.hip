@@ -69,20 +69,17 @@ __device__ __forceinline__ uint4 attn_merge8(const GemvSrc& src, int m, int k) {
   const int g = h / src.att_group;
   const int r = h - g * src.att_group;
   const int64_t base = (static_cast<int64_t>(m) * src.att_nkv + g) * src.att_nsplit * 16 + r;
-  // branch-free and unrolled so several splits' loads are in flight together
-  // (a split with no keys has max -inf, sum 0 and output 0: weight 0)
   float mx = -__builtin_huge_valf();
-#pragma unroll 8
   for (int sp = 0; sp < src.att_nsplit; ++sp) mx = fmaxf(mx, src.att_ml[base + sp * 16].x);
   const float bse = mx == -__builtin_huge_valf() ? 0.f : mx;
   float l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
   for (int sp = 0; sp < src.att_nsplit; ++sp) {
     const float2 ml = src.att_ml[base + sp * 16];
+    if (ml.x == -__builtin_huge_valf()) continue;
+    const float f = __expf(ml.x - bse);
+    l += f * ml.y;
     const float4* po = reinterpret_cast<const float4*>(src.att_o + (base + sp * 16) * 128 + d0);
     const float4 a = po[0], b = po[1];
-    const float f = ml.x == -__builtin_huge_valf() ? 0.f : __expf(ml.x - bse);
-    l += f * ml.y;
     o[0] += f * a.x; o[1] += f * a.y; o[2] += f * a.z; o[3] += f * a.w;
     o[4] += f * b.x; o[5] += f * b.y; o[6] += f * b.z; o[7] += f * b.w;
   }
