@@ -321,8 +321,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
 // index swapped, which makes exactly those eight keys contiguous for the A
 // operand.  P is rounded to bf16 for that product.
 //
-// K rows (256 bytes) keep 16-byte chunk c of key r at c ^ (r & 15); V^T rows
-// are padded to 72 keys: both keep the fragment reads on distinct banks.
+// K rows (256 bytes) keep 16-byte chunk c of key r at c ^ (r & 15).  V^T
+// rows are padded to 72 keys and the 8-key chunk k of row d sits at
+// k ^ ((d / 8) % 8): the transposing writes (16 rows 8 apart per wave
+// instruction) then spread over the banks as evenly as the fragment reads.
 
 constexpr int PF_QB = 128;   // queries per workgroup
 constexpr int PF_KT = 64;    // keys per tile
@@ -414,7 +416,9 @@ __device__ __forceinline__ void pf_tile(const uint4* __restrict__ sKb, const uin
   for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint4 vfr = *reinterpret_cast<const uint4*>(&sVtb[(32 * dt + qr) * PF_VT + 16 * c + 8 * hl]);
+      const int vr = 32 * dt + qr;
+      const uint4 vfr =
+          *reinterpret_cast<const uint4*>(&sVtb[vr * PF_VT + ((16 * c + 8 * hl) ^ (((vr >> 3) & 7) << 3))]);
       oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr), pf[c], oacc[dt], 0, 0, 0);
     }
   }
@@ -425,8 +429,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sVt[2][D * PF_VT];
 
   const int nqb = (a.T + PF_QB - 1) / PF_QB;
-  const int qb = nqb - 1 - static_cast<int>(blockIdx.x);  // longest rows first
-  const int h = blockIdx.y;
+  // heads vary fastest, query blocks from the last (longest causal rows)
+  // down: workgroups are dispatched roughly longest first, so the short
+  // blocks dispatched last share a CU with a long one only briefly
+  const int qb = nqb - 1 - static_cast<int>(blockIdx.y);
+  const int h = blockIdx.x;
   const int b = blockIdx.z;
   const int group = a.nh / a.nkv;
   const int g = h / group;
@@ -484,7 +491,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
       const int r_ = q_ >> 4;                                                                        \
       sK[BUF_][r_ * 16 + ((q_ & 15) ^ (r_ & 15))] = RK_[i];                                          \
     }                                                                                                \
-    store_vt4(sVt[BUF_], PF_VT, 8 * vc, pf_keyperm(4 * vg), RV_);                                    \
+    store_vt4(sVt[BUF_], PF_VT, 8 * vc, pf_keyperm(4 * vg) ^ ((vc & 7) << 3), RV_);                  \
   }
 
   float m_run = NEG_INF, l_run = 0.f;
@@ -628,7 +635,7 @@ q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
     }
     return Q2_OK;
   }
-  hipLaunchKernelGGL(attn_prefill_kernel, dim3(cdiv(a.T, PF_QB), a.nh, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_prefill_kernel, dim3(a.nh, cdiv(a.T, PF_QB), a.B), dim3(256), 0, s, a);
   return check_launch("attn_prefill");
 }
 

@@ -31,6 +31,7 @@ namespace q2 {
 namespace {
 
 constexpr int KB = 128;  // K per block
+constexpr int GEMV_WGS = 256;  // workgroups the tile loops aim at (one 16-wave workgroup per CU)
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
@@ -153,7 +154,7 @@ __device__ __forceinline__ void gemv_epilogue(const Epi& epi, int M, int N, int 
 // workgroups in flight and costs a third of the bandwidth on the long
 // LM-head pass.
 template <int MT, int NW, int EK, int SRC, bool STAGE, bool SPLIT>
-__global__ __launch_bounds__(NW * 64, MT == 1 ? 8 : 4) void gemv_kernel(const uint16_t* __restrict__ W, int64_t ldw,
+__global__ __launch_bounds__(NW * 64, 1) void gemv_kernel(const uint16_t* __restrict__ W, int64_t ldw,
                                                        const uint16_t* __restrict__ X, int64_t ldx, int N, int M, int K,
                                                        int blocks_per_split, GemvSrc src, float* __restrict__ partial,
                                                        Epi epi) {
@@ -169,7 +170,9 @@ __global__ __launch_bounds__(NW * 64, MT == 1 ? 8 : 4) void gemv_kernel(const ui
   const int wave = tid >> 6;
   const int row = lane & 15;
   const int g = lane >> 4;
-  const int n0 = blockIdx.x * 16;
+  const int ntile = (N + 15) >> 4;
+  int tl = blockIdx.x;  // this workgroup's tiles: blockIdx.x, + gridDim.x, ...
+  int n0 = tl * 16;
   const int nkb = (K + KB - 1) / KB;
   const int kb0 = blockIdx.y * blocks_per_split;
   const int kb1 = min(kb0 + blocks_per_split, nkb);
@@ -180,22 +183,21 @@ __global__ __launch_bounds__(NW * 64, MT == 1 ? 8 : 4) void gemv_kernel(const ui
   // the weight loads do not depend on X: the first batch goes out before the
   // prologue so that its latency overlaps the staging of X.  Loads are
   // unconditional within the block range (out-of-range rows and the K tail
-  // read a clamped in-range address and are zeroed afterwards) so the
-  // compiler issues them back to back.
-  const bool wrow_ok = n0 + row < N;
+  // read a clamped in-range address of real weights) so the compiler issues
+  // them back to back.  The X operand is zero past K, so a clamped weight
+  // adds nothing; results of out-of-range rows are never stored.
+  bool wrow_ok = n0 + row < N;
   const uint16_t* __restrict__ wp = W + static_cast<int64_t>(wrow_ok ? n0 + row : 0) * ldw + 8 * g;
   const uint4 z = {0, 0, 0, 0};
   constexpr int BATCH = 2;  // blocks whose weights are in flight at once per wave
   uint4 wv[BATCH][4];
-  bool wok[BATCH][4];
 #define Q2_GEMV_LOAD_BATCH(KB_)                                                              \
   _Pragma("unroll") for (int b = 0; b < BATCH; ++b) {                                       \
     const int kk = (KB_) + NW * b;                                                          \
     if (kk < kb1) { /* wave-uniform: no loads for blocks past the range */                  \
       _Pragma("unroll") for (int u = 0; u < 4; ++u) {                                       \
         const int k = kk * KB + 32 * u + 8 * g;                                             \
-        wok[b][u] = wrow_ok && k < K;                                                       \
-        wv[b][u] = ld16(wp + (wok[b][u] ? static_cast<int64_t>(kk) * KB + 32 * u : 0));      \
+        wv[b][u] = ld16(wp + (k < K ? static_cast<int64_t>(kk) * KB + 32 * u : 0));          \
       }                                                                                     \
     }                                                                                       \
   }
@@ -241,6 +243,7 @@ __global__ __launch_bounds__(NW * 64, MT == 1 ? 8 : 4) void gemv_kernel(const ui
       xp[j] = X + static_cast<int64_t>(xok[j] ? tok : 0) * ldx + 8 * g;
   }
 
+  for (;;) {
   floatx4_t acc[MT];
 #pragma unroll
   for (int j = 0; j < MT; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -259,13 +262,22 @@ __global__ __launch_bounds__(NW * 64, MT == 1 ? 8 : 4) void gemv_kernel(const ui
           const bool ok = xok[j] && k < K;
           uint4 xv = ld16(xp[j] + (ok ? static_cast<int64_t>(kk) * KB + 32 * u : k_lo - 8 * g));
           if (!ok) xv = z;
-          const uint4 wvv = wok[b][u] ? wv[b][u] : z;
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wvv), as_bf16x8(xv), acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[b][u]), as_bf16x8(xv), acc[j], 0, 0, 0);
         }
       }
     }
   }
-#undef Q2_GEMV_LOAD_BATCH
+
+  // the next tile's first weight batch goes out before this tile's
+  // reduction and epilogue (the X rows in LDS serve every tile)
+  const int cur = tl, c0 = n0;
+  tl += gridDim.x;
+  if (tl < ntile) {
+    n0 = tl * 16;
+    wrow_ok = n0 + row < N;
+    wp = W + static_cast<int64_t>(wrow_ok ? n0 + row : 0) * ldw + 8 * g;
+    Q2_GEMV_LOAD_BATCH(kb0 + wave)
+  }
 
   // sum the weight waves' partial tiles (fixed order)
   if (wave < WW) {
@@ -291,19 +303,24 @@ __global__ __launch_bounds__(NW * 64, MT == 1 ? 8 : 4) void gemv_kernel(const ui
   if constexpr (SPLIT) {
     for (int t = tid; t < M * 16; t += NW * 64) {
       const int m = t >> 4, f = t & 15;
-      if (n0 + f < N) partial[(static_cast<int64_t>(blockIdx.y) * M + m) * N + n0 + f] = tile[m][f];
+      if (c0 + f < N) partial[(static_cast<int64_t>(blockIdx.y) * M + m) * N + c0 + f] = tile[m][f];
     }
-    return;
+  } else {
+    const int Mp = 16 * MT;
+    for (int base = 0; base < Mp * 8; base += NW * 64) {
+      const int t = base + tid;
+      const int m = t >> 3;
+      const int p = t & 7;
+      const float v0 = m < Mp ? tile[m][2 * p] : 0.f;
+      const float v1 = m < Mp ? tile[m][2 * p + 1] : 0.f;
+      gemv_epilogue<EK>(epi, M, N, c0, cur, m, p, v0, v1);
+    }
   }
-  const int Mp = 16 * MT;
-  for (int base = 0; base < Mp * 8; base += NW * 64) {
-    const int t = base + tid;
-    const int m = t >> 3;
-    const int p = t & 7;
-    const float v0 = m < Mp ? tile[m][2 * p] : 0.f;
-    const float v1 = m < Mp ? tile[m][2 * p + 1] : 0.f;
-    gemv_epilogue<EK>(epi, M, N, n0, blockIdx.x, m, p, v0, v1);
+  // the next tile's reduction writes red only after every wave has passed
+  // the barriers above, and tile only after the barrier that follows it
+  if (tl >= ntile) break;
   }
+#undef Q2_GEMV_LOAD_BATCH
 }
 
 // Sums the split-K partials of 32 (row, tile) pairs per workgroup, in split
@@ -374,7 +391,9 @@ template <int MT, int NW, int EK, int SRC, bool STAGE>
 q2_status launch_gemv2(const GemmArgs& a, const GemvPlan& p, size_t lds, hipStream_t s) {
   const GemvSrc src{static_cast<const uint16_t*>(a.norm_w), a.norm_sq, a.norm_sq_ld, a.norm_eps, a.att_o, a.att_ml,
                     a.att_nsplit, a.att_group, a.att_nkv};
-  const dim3 grid(cdiv(a.N, 16), p.splits);
+  // at most two rounds of 16-wave workgroups on the chip; each loops over
+  // its tiles with the next tile's weights in flight
+  const dim3 grid(std::min(cdiv(a.N, 16), std::max(1, GEMV_WGS / p.splits)), p.splits);
   if (p.splits == 1) {
     hipLaunchKernelGGL((gemv_kernel<MT, NW, EK, SRC, STAGE, false>), grid, dim3(NW * 64), lds, s,
                        static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M,
