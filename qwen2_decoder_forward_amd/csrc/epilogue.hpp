@@ -152,6 +152,18 @@ struct GemmArgs {
   const float* att_o;
   const float2* att_ml;
   int att_nsplit, att_group, att_nkv;
+  // deferred residual add (GEMV path with norm_w, M <= 16): X is the residual
+  // stream before the previous layer's down projection, whose split-K
+  // partials (resid_splits of them, [split][M][K] float32) are still pending.
+  // The kernel forms rnd(X + rnd(sum of partials)) (what the split reduction
+  // would have stored), normalises that row itself (norm_sq unused) and one
+  // workgroup writes the new residual row to resid_out (not X).
+  const float* resid_part;
+  int resid_splits;
+  void* resid_out;
+  // split-K GEMV: leave the float32 partials in scratch and skip the
+  // reduction kernel (a later product's prologue consumes them)
+  bool defer_reduce;
 };
 
 q2_status gemm_bf16(const GemmArgs& a, hipStream_t s);
@@ -165,6 +177,8 @@ bool gemv_can_fuse(int M, int K);
 q2_status gemv_bf16(const GemmArgs& a, hipStream_t s);
 // Split-K partial bytes the GEMV path needs for this shape (0 if unsplit).
 size_t gemv_scratch_bytes(int M, int N, int K);
+// Number of K splits the GEMV path uses for this shape.
+int gemv_splits(int M, int N, int K);
 // Split-K partial bytes any bf16 decode-size product of this shape may need.
 size_t gemm_scratch_bytes(int M, int N, int K);
 // Sums split-K float32 partials partial[split][m][n] (a.scratch) in split

@@ -50,7 +50,7 @@ __device__ __forceinline__ uint4 norm8(uint4 x, uint4 w, float inv) {
   return r;
 }
 
-enum XSrc : int { XSRC_RAW = 0, XSRC_NORM = 1, XSRC_ATTN = 2 };
+enum XSrc : int { XSRC_RAW = 0, XSRC_NORM = 1, XSRC_ATTN = 2, XSRC_NORMR = 3 };
 
 struct GemvSrc {
   const uint16_t* w;   // NORM
@@ -60,6 +60,9 @@ struct GemvSrc {
   const float* att_o;  // ATTN
   const float2* att_ml;
   int att_nsplit, att_group, att_nkv;
+  const float* rp;     // NORMR: pending split-K partials [split][M][K]
+  int rsplits;
+  uint16_t* x_out;     // NORMR: the new residual rows (written by workgroup 0)
 };
 
 // 8 consecutive features (h * 128 + d0 .. + 7) of the merged attention output
@@ -160,6 +163,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemv_kernel(const uint16_t* __rest
                                                        Epi epi) {
   constexpr int WW = NW;
   __shared__ float s_inv[16 * MT];
+  __shared__ float s_ssw[NW];
   __shared__ floatx4_t red[NW][MT][64];
   __shared__ float tile[16 * MT][17];
   extern __shared__ __attribute__((aligned(16))) uint16_t s_x[];
@@ -203,6 +207,49 @@ __global__ __launch_bounds__(NW * 64, 1) void gemv_kernel(const uint16_t* __rest
   }
   Q2_GEMV_LOAD_BATCH(kb0 + wave)
 
+  if constexpr (SRC == XSRC_NORMR) {
+    // The pending residual add, then RMSNorm, row by row (one pass of the
+    // threads covers a row: K / 8 <= 64 NW).  Rounding as the split
+    // reduction's epilogue: rnd(x + rnd(sum of partials in split order)).
+    const int chunks = K >> 3;
+    const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
+    for (int m = 0; m < M; ++m) {
+      const int k = 8 * tid;
+      uint4 xn = {0, 0, 0, 0};
+      float ss = 0.f;
+      if (tid < chunks) {
+        const uint4 xv = ld16(X + static_cast<int64_t>(m) * ldx + k);
+        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < src.rsplits; ++sp) {
+          const float4* q = reinterpret_cast<const float4*>(src.rp + (static_cast<int64_t>(sp) * M + m) * K + k);
+          const float4 p0 = q[0], p1 = q[1];
+          a[0] += p0.x; a[1] += p0.y; a[2] += p0.z; a[3] += p0.w;
+          a[4] += p1.x; a[5] += p1.y; a[6] += p1.z; a[7] += p1.w;
+        }
+        const uint32_t* xs = &xv.x;
+        uint32_t* ns = &xn.x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = round_bf(bf_lo(xs[i]) + round_bf(a[2 * i]));
+          const float hi = round_bf(bf_hi(xs[i]) + round_bf(a[2 * i + 1]));
+          ns[i] = pack_bf2(lo, hi);
+          ss += lo * lo + hi * hi;
+        }
+        if (writer) *reinterpret_cast<uint4*>(src.x_out + static_cast<int64_t>(m) * ldx + k) = xn;
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) s_ssw[wave] = ss;
+      __syncthreads();
+      if (tid == 0) {
+        float t = 0.f;
+        for (int w = 0; w < NW; ++w) t += s_ssw[w];
+        s_inv[m] = 1.0f / sqrtf(t / static_cast<float>(K) + src.eps);
+      }
+      __syncthreads();
+      if (tid < chunks) *reinterpret_cast<uint4*>(s_x + m * ld_s + k) = norm8(xn, ld16(src.w + k), s_inv[m]);
+    }
+    __syncthreads();
+  }
   if constexpr (NORM) {
     const int ntiles = K >> 4;
     for (int m = wave; m < M; m += NW) {
@@ -213,7 +260,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemv_kernel(const uint16_t* __rest
     }
     __syncthreads();
   }
-  if constexpr (STAGE) {
+  if constexpr (STAGE && SRC != XSRC_NORMR) {
     // X[:, k_lo .. k_hi) into LDS
     const int chunks = (k_hi - k_lo) >> 3;
     for (int idx = tid; idx < M * chunks; idx += NW * 64) {
@@ -390,7 +437,8 @@ size_t stage_bytes(int M, int bps, int K) {
 template <int MT, int NW, int EK, int SRC, bool STAGE>
 q2_status launch_gemv2(const GemmArgs& a, const GemvPlan& p, size_t lds, hipStream_t s) {
   const GemvSrc src{static_cast<const uint16_t*>(a.norm_w), a.norm_sq, a.norm_sq_ld, a.norm_eps, a.att_o, a.att_ml,
-                    a.att_nsplit, a.att_group, a.att_nkv};
+                    a.att_nsplit, a.att_group, a.att_nkv, a.resid_part, a.resid_splits,
+                    static_cast<uint16_t*>(a.resid_out)};
   // at most two rounds of 16-wave workgroups on the chip; each loops over
   // its tiles with the next tile's weights in flight
   const dim3 grid(std::min(cdiv(a.N, 16), std::max(1, GEMV_WGS / p.splits)), p.splits);
@@ -418,7 +466,7 @@ q2_status launch_gemv(const GemmArgs& a, const GemvPlan& p, hipStream_t s) {
     else
       Q2_TRY((launch_gemv2<MT, NW, EK, SRC, false>(a, p, 0, s)));
   }
-  if (p.splits == 1) return Q2_OK;
+  if (p.splits == 1 || a.defer_reduce) return Q2_OK;
   const int pairs = a.M * cdiv(a.N, 16);
   hipLaunchKernelGGL((gemv_reduce_kernel<EK>), dim3(cdiv(pairs, 32)), dim3(256), 0, s,
                      static_cast<const float*>(a.scratch), p.splits, a.M, a.N, a.epi);
@@ -427,6 +475,7 @@ q2_status launch_gemv(const GemmArgs& a, const GemvPlan& p, hipStream_t s) {
 
 template <int EK>
 q2_status gemv_ek(const GemmArgs& a, const GemvPlan& p, hipStream_t s) {
+  if (a.norm_w && a.resid_part) return launch_gemv<1, 16, EK, XSRC_NORMR>(a, p, s);
   if (a.norm_w) return launch_gemv<1, 16, EK, XSRC_NORM>(a, p, s);
   if (a.att_o) return launch_gemv<1, 16, EK, XSRC_ATTN>(a, p, s);
   if (p.mt == 1) return launch_gemv<1, 16, EK, XSRC_RAW>(a, p, s);
@@ -462,6 +511,8 @@ q2_status split_reduce(const GemmArgs& a, int splits, hipStream_t s) {
   return fail(Q2_EINVAL, "split reduce: unsupported epilogue %d", a.epi.kind);
 }
 
+int gemv_splits(int M, int N, int K) { return plan_gemv(M, N, K).splits; }
+
 size_t gemv_scratch_bytes(int M, int N, int K) {
   if (M > GEMV_MAX_M) return 0;
   GemvPlan p = plan_gemv(M, N, K);
@@ -479,10 +530,17 @@ q2_status gemv_bf16(const GemmArgs& a, hipStream_t s) {
     Q2_CHECK(!a.norm_w && a.M <= GEMV_NORM_MAX_M && a.att_ml && a.att_nsplit >= 1 && a.K % 128 == 0, Q2_EINVAL,
              "gemv: bad fused attention-merge arguments");
   }
-  if (a.epi.kind == EPI_ARGMAX) {
+  if (a.resid_part) {
+    Q2_CHECK(a.norm_w && a.resid_out && a.resid_out != a.X && a.resid_splits >= 1 && a.K % 8 == 0 &&
+                 a.K / 8 <= 16 * 64 && !a.defer_reduce,
+             Q2_EINVAL, "gemv: bad deferred-residual arguments");
+  }
+  if (a.epi.kind == EPI_ARGMAX || a.resid_part) {
+    // the argmax needs whole sums; the deferred residual add needs whole rows
     p.splits = 1;
     p.bps = cdiv(a.K, KB);
   }
+  Q2_CHECK(!a.defer_reduce || a.epi.kind != EPI_ARGMAX, Q2_EINVAL, "gemv: argmax cannot defer its reduction");
   if (p.splits > 1) {
     const size_t need = static_cast<size_t>(p.splits) * a.M * a.N * sizeof(float);
     Q2_CHECK(a.scratch && a.scratch_bytes >= need, Q2_EINVAL, "gemv: split-K scratch too small");

@@ -62,6 +62,9 @@ struct q2_model {
   float2* rope = nullptr;
   // arena
   void *x = nullptr, *h = nullptr, *q = nullptr, *att = nullptr, *act = nullptr, *xl = nullptr;
+  // the buffer that holds the residual stream after the last forward: x, or
+  // h when the fused decode path ping-pongs between the two
+  void* xcur = nullptr;
   float* logits_buf = nullptr;
   unsigned long long* keys = nullptr;
   int64_t* ids_buf = nullptr;
@@ -195,6 +198,13 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
   const int M = B * Tc;
   const int H = c.hidden, d = c.dh, qd = c.nh * c.dh;
   const Path path = path_for(m, M);
+  // With the fused norms the down projection's split-K reduction is folded
+  // into the next layer's QKV prologue, which writes the completed residual
+  // rows to the other of x / h (the reduction's in-place add would race with
+  // the other workgroups reading the old rows).  The last layer reduces as
+  // usual, for the head.
+  void* cur = m->x;
+  int pend_splits = 0;  // > 0: down-projection partials of the previous layer pending in gscratch
   for (int l = 0; l < c.nlayer; ++l) {
     const q2_model::Layer& L = m->layers[l];
     void* kc = static_cast<char*>(m->kc) + l * m->kv_lstride * m->esize;
@@ -203,12 +213,19 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
       Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->h), H, static_cast<const T*>(m->x), H,
                                static_cast<const T*>(L.w_in), M, H, c.eps, s));
     {
-      GemmArgs a = gemm_args(m, L.w_qkv, H, path.fused_norm ? m->x : m->h, H, M, m->qkv_out, H);
+      GemmArgs a = gemm_args(m, L.w_qkv, H, path.fused_norm ? cur : m->h, H, M, m->qkv_out, H);
+      void* nxt = cur;
       if (path.fused_norm) {
         a.norm_w = L.w_in;
         a.norm_sq = m->sq;
         a.norm_sq_ld = m->sq_ld;
         a.norm_eps = c.eps;
+        if (pend_splits > 0) {
+          nxt = cur == m->x ? m->h : m->x;
+          a.resid_part = static_cast<const float*>(m->gscratch);
+          a.resid_splits = pend_splits;
+          a.resid_out = nxt;
+        }
       }
       a.epi.kind = EPI_QKV;
       a.epi.out = m->q;
@@ -225,6 +242,8 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
       a.epi.d_len = m->d_len;
       a.epi.rope = m->rope;
       Q2_TRY(gemm(m, a, s));
+      cur = nxt;
+      pend_splits = 0;
     }
     // with one query per sequence and split-KV partials, o_proj merges them itself
     const int nsplit = c.dtype == Q2_BF16 ? attention_decode_splits(B, Tc, c.max_seq, c.nh, c.nkv, d) : 0;
@@ -269,7 +288,7 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
         a.att_nkv = c.nkv;
       }
       a.epi.kind = EPI_RESID;
-      a.epi.out = m->x;
+      a.epi.out = cur;
       a.epi.ldo = H;
       a.epi.sq_out = path.fused_norm ? m->sq : nullptr;
       a.epi.sq_ld = m->sq_ld;
@@ -279,7 +298,7 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
       Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->h), H, static_cast<const T*>(m->x), H,
                                static_cast<const T*>(L.w_post), M, H, c.eps, s));
     {
-      GemmArgs a = gemm_args(m, L.w_gu, H, path.fused_norm ? m->x : m->h, H, M, 2 * c.inter, H);
+      GemmArgs a = gemm_args(m, L.w_gu, H, path.fused_norm ? cur : m->h, H, M, 2 * c.inter, H);
       if (path.fused_norm) {
         a.norm_w = L.w_post;
         a.norm_sq = m->sq;
@@ -294,13 +313,21 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
     {
       GemmArgs a = gemm_args(m, L.w_d, c.inter, m->act, c.inter, M, H, c.inter);
       a.epi.kind = EPI_RESID;
-      a.epi.out = m->x;
+      a.epi.out = cur;
       a.epi.ldo = H;
       a.epi.sq_out = path.fused_norm ? m->sq : nullptr;
       a.epi.sq_ld = m->sq_ld;
+      if (path.fused_norm && l + 1 < c.nlayer && c.dtype == Q2_BF16) {
+        const int sp = gemv_splits(M, H, c.inter);
+        if (sp > 1) {
+          a.defer_reduce = true;
+          pend_splits = sp;
+        }
+      }
       Q2_TRY(gemm(m, a, s));
     }
   }
+  m->xcur = cur;
   if (!advance) return Q2_OK;
   hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(1), 0, s, m->d_len, Tc);
   return check_launch("advance_len");
@@ -319,9 +346,9 @@ q2_status run_head(q2_model* m, int B, int Tc, int pending, float* logits, int64
   const bool fused = path.fused_norm && Tc == 1;
   if (!fused)
     Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->xl), H,
-                             static_cast<const T*>(m->x) + static_cast<int64_t>(Tc - 1) * H,
+                             static_cast<const T*>(m->xcur) + static_cast<int64_t>(Tc - 1) * H,
                              static_cast<int64_t>(Tc) * H, static_cast<const T*>(m->w_final), B, H, c.eps, s));
-  GemmArgs a = gemm_args(m, m->lm_head, H, fused ? m->x : m->xl, H, B, c.vocab, H);
+  GemmArgs a = gemm_args(m, m->lm_head, H, fused ? m->xcur : m->xl, H, B, c.vocab, H);
   if (fused) {
     a.norm_w = m->w_final;
     a.norm_sq = m->sq;
@@ -746,6 +773,7 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
   m->rope = reinterpret_cast<float2*>(m->amem + a_rope);
   m->x = m->amem + a_x;
   m->h = m->amem + a_h;
+  m->xcur = m->x;
   m->q = m->amem + a_q;
   m->att = m->amem + a_att;
   m->act = m->amem + a_act;
@@ -851,7 +879,7 @@ extern "C" q2_status q2_model_hidden_view(q2_model* m, q2_tensor* x) {
   clear_error();
   Q2_CHECK(m && x, Q2_EINVAL, "null argument");
   memset(x, 0, sizeof *x);
-  x->data = m->x;
+  x->data = m->xcur;
   x->dtype = m->cfg.dtype;
   x->ndim = 2;
   x->shape[0] = m->last_rows;
