@@ -164,8 +164,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
   const uint4 z = {0, 0, 0, 0};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qf[kk] = rvalid ? ld16(qp + 32 * kk + 8 * G) : z;
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) settle(qf[kk]);
 
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_bs + g * a.k_hs;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.v_bs + g * a.v_hs;
@@ -198,6 +196,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
   uint4 kf0[4], vf0[4], kf1[4], vf1[4];
   int j0 = j_begin + 16 * wave;
   Q2_DEC_LOAD(kf0, vf0, j0)
+  // the query fragments were loaded before the first block: mark them
+  // arrived here, so that their wait does not hold back the block's loads
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) settle(qf[kk]);
   for (; j0 < j_end; j0 += 128) {
     Q2_DEC_LOAD(kf1, vf1, j0 + 64)
     dec_block(kf0, vf0, qf, vt, j0, j_end, lim, a.scale, col, G, oacc, m_run, l_run);

@@ -73,19 +73,47 @@ __device__ __forceinline__ uint4 attn_merge8(const GemvSrc& src, int m, int k) {
   const int g = h / src.att_group;
   const int r = h - g * src.att_group;
   const int64_t base = (static_cast<int64_t>(m) * src.att_nkv + g) * src.att_nsplit * 16 + r;
+  // with up to 4 splits every load (max/sum and output of each split) is
+  // issued before any is used: one memory round trip
   float mx = -__builtin_huge_valf();
-  for (int sp = 0; sp < src.att_nsplit; ++sp) mx = fmaxf(mx, src.att_ml[base + sp * 16].x);
-  const float bse = mx == -__builtin_huge_valf() ? 0.f : mx;
   float l = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < src.att_nsplit; ++sp) {
-    const float2 ml = src.att_ml[base + sp * 16];
-    if (ml.x == -__builtin_huge_valf()) continue;
-    const float f = __expf(ml.x - bse);
-    l += f * ml.y;
-    const float4* po = reinterpret_cast<const float4*>(src.att_o + (base + sp * 16) * 128 + d0);
-    const float4 a = po[0], b = po[1];
-    o[0] += f * a.x; o[1] += f * a.y; o[2] += f * a.z; o[3] += f * a.w;
-    o[4] += f * b.x; o[5] += f * b.y; o[6] += f * b.z; o[7] += f * b.w;
+  if (src.att_nsplit <= 4) {
+    float2 ml[4];
+    float4 pa[4], pb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sp = min(i, src.att_nsplit - 1);
+      ml[i] = src.att_ml[base + sp * 16];
+      const float4* po = reinterpret_cast<const float4*>(src.att_o + (base + sp * 16) * 128 + d0);
+      pa[i] = po[0];
+      pb[i] = po[1];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i < src.att_nsplit) mx = fmaxf(mx, ml[i].x);
+    const float bse = mx == -__builtin_huge_valf() ? 0.f : mx;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < src.att_nsplit && ml[i].x != -__builtin_huge_valf()) {
+        const float f = __expf(ml[i].x - bse);
+        l += f * ml[i].y;
+        o[0] += f * pa[i].x; o[1] += f * pa[i].y; o[2] += f * pa[i].z; o[3] += f * pa[i].w;
+        o[4] += f * pb[i].x; o[5] += f * pb[i].y; o[6] += f * pb[i].z; o[7] += f * pb[i].w;
+      }
+    }
+  } else {
+    for (int sp = 0; sp < src.att_nsplit; ++sp) mx = fmaxf(mx, src.att_ml[base + sp * 16].x);
+    const float bse = mx == -__builtin_huge_valf() ? 0.f : mx;
+    for (int sp = 0; sp < src.att_nsplit; ++sp) {
+      const float2 ml = src.att_ml[base + sp * 16];
+      if (ml.x == -__builtin_huge_valf()) continue;
+      const float f = __expf(ml.x - bse);
+      l += f * ml.y;
+      const float4* po = reinterpret_cast<const float4*>(src.att_o + (base + sp * 16) * 128 + d0);
+      const float4 a = po[0], b = po[1];
+      o[0] += f * a.x; o[1] += f * a.y; o[2] += f * a.z; o[3] += f * a.w;
+      o[4] += f * b.x; o[5] += f * b.y; o[6] += f * b.z; o[7] += f * b.w;
+    }
   }
   const float inv = 1.f / l;
   uint4 r4;
@@ -220,11 +248,24 @@ __global__ __launch_bounds__(NW * 64, 1) void gemv_kernel(const uint16_t* __rest
       if (tid < chunks) {
         const uint4 xv = ld16(X + static_cast<int64_t>(m) * ldx + k);
         float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < src.rsplits; ++sp) {
-          const float4* q = reinterpret_cast<const float4*>(src.rp + (static_cast<int64_t>(sp) * M + m) * K + k);
-          const float4 p0 = q[0], p1 = q[1];
-          a[0] += p0.x; a[1] += p0.y; a[2] += p0.z; a[3] += p0.w;
-          a[4] += p1.x; a[5] += p1.y; a[6] += p1.z; a[7] += p1.w;
+        // four splits' partials are loaded before any is summed (one memory
+        // round trip per four splits); the sums still run in split order
+        for (int s0 = 0; s0 < src.rsplits; s0 += 4) {
+          float4 p0[4], p1[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int sp = min(s0 + i, src.rsplits - 1);
+            const float4* q = reinterpret_cast<const float4*>(src.rp + (static_cast<int64_t>(sp) * M + m) * K + k);
+            p0[i] = q[0];
+            p1[i] = q[1];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (s0 + i < src.rsplits) {
+              a[0] += p0[i].x; a[1] += p0[i].y; a[2] += p0[i].z; a[3] += p0[i].w;
+              a[4] += p1[i].x; a[5] += p1[i].y; a[6] += p1[i].z; a[7] += p1[i].w;
+            }
+          }
         }
         const uint32_t* xs = &xv.x;
         uint32_t* ns = &xn.x;
