@@ -380,9 +380,25 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_dtl_kernel(const uint16_t* 
   using C = Dtl<BN, BM, WN, WM>;
   constexpr int FN = C::FN, FM = C::FM, TN = C::TN, TM = C::TM, NT = C::NT, LD = C::LD;
   extern __shared__ uint4 dsm[];
-  const int t = blockIdx.x;
-  const int tn = t / tiles_m;
-  const int tm = t - tn * tiles_m;
+  // Tile order.  Workgroups are dealt to the 8 XCDs in turn, each with its
+  // own L2: logical tile L = (t % 8) * (T / 8) + t / 8 makes a run of
+  // consecutive tiles live on one XCD, and walking them in groups of 4 token
+  // tiles x all weight tiles keeps the ~32 tiles resident on an XCD within 4
+  // token panels and 8 weight panels, which its L2 then serves.
+  int tn, tm;
+  {
+    const int T = gridDim.x;
+    const int t = blockIdx.x;
+    const int L = T % 8 == 0 ? (t % 8) * (T / 8) + t / 8 : t;
+    const int tiles_n = T / tiles_m;
+    constexpr int GM = 4;
+    const int per_group = GM * tiles_n;
+    const int fm = L / per_group * GM;
+    const int gs = min(tiles_m - fm, GM);
+    const int r = L - fm * tiles_n;
+    tm = fm + r % gs;
+    tn = r / gs;
+  }
   const int n0 = tn * BN;
   const int m0 = tm * BM;
 
