@@ -461,12 +461,34 @@ GemvPlan plan_gemv(int M, int N, int K) {
   const int cap = p.mt == 1 ? 64 : max(1, K / (8 * M));
   int splits = 1;
   while (tiles * splits < 512 && nkb / (splits + 1) >= p.nw / 2 && splits + 1 <= cap) ++splits;
-  p.bps = cdiv(nkb, splits);
   // the X rows of a split's K range must fit the LDS stage: reading them from
   // L2 inside the block loop puts a dependent load behind every weight batch
   const int bps_fit = std::max(1, static_cast<int>((GEMV_STAGE_BYTES / (2 * M) - 8) / KB));
-  p.bps = std::min(p.bps, bps_fit);
-  p.splits = cdiv(nkb, p.bps);
+  auto fit = [&](int sp, int* bps, int* spl) {
+    *bps = std::min(cdiv(nkb, sp), bps_fit);
+    *spl = cdiv(nkb, *bps);
+  };
+  fit(splits, &p.bps, &p.splits);
+  if (p.splits > 1) {
+    // Each workgroup loops over ceil(tiles / grid) tiles of bps blocks: among
+    // up to twice as many splits, take the one whose busiest workgroup has
+    // the fewest blocks (whole tile rounds per workgroup, no idle tail).
+    auto work = [&](int spl, int bps) {
+      const int grid = std::min(tiles, std::max(1, GEMV_WGS / spl));
+      return static_cast<int64_t>(cdiv(tiles, grid)) * bps;
+    };
+    int64_t best = work(p.splits, p.bps);
+    for (int sp = p.splits + 1; sp <= 2 * p.splits && sp <= cap && sp <= nkb; ++sp) {
+      int b, spl;
+      fit(sp, &b, &spl);
+      const int64_t w = work(spl, b);
+      if (w < best) {
+        best = w;
+        p.bps = b;
+        p.splits = spl;
+      }
+    }
+  }
   return p;
 }
 
