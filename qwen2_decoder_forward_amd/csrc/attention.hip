@@ -426,7 +426,13 @@ __device__ __forceinline__ void pf_tile(const uint4* __restrict__ sKb, const uin
   }
 }
 
-__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
+// Grid (nh, items, B).  The nsq last query blocks (the longest causal rows)
+// are split in two halves of their key tiles, items 2 i and 2 i + 1 for
+// block nqb - 1 - i; each half leaves its unnormalised output and running
+// (max, sum) in base-2 units at part_o / part_ml, merged by
+// attn_prefill_combine.  The other blocks follow, last first, whole.
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int nsq, float* __restrict__ part_o,
+                                                              float2* __restrict__ part_ml) {
   __shared__ uint4 sK[2][PF_KT * 16];
   __shared__ __attribute__((aligned(16))) uint16_t sVt[2][D * PF_VT];
 
@@ -434,7 +440,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
   // heads vary fastest, query blocks from the last (longest causal rows)
   // down: workgroups are dispatched roughly longest first, so the short
   // blocks dispatched last share a CU with a long one only briefly
-  const int qb = nqb - 1 - static_cast<int>(blockIdx.y);
+  const int y = blockIdx.y;
+  const int part = y < 2 * nsq ? (y & 1) : -1;
+  const int qb = y < 2 * nsq ? nqb - 1 - (y >> 1) : nqb - 1 - nsq - (y - 2 * nsq);
   const int h = blockIdx.x;
   const int b = blockIdx.z;
   const int group = a.nh / a.nkv;
@@ -504,26 +512,42 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
     for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
 
   const int ntiles = (kv_end + PF_KT - 1) / PF_KT;
+  const int jt0 = part == 1 ? ntiles / 2 : 0;
+  const int jt1 = part == 0 ? ntiles / 2 : ntiles;
   // The loads are issued unconditionally (past kv_end they reread the last
   // key), so the compiler's count of loads in flight does not depend on the
   // path.  The wave's first query decides whether a tile needs the mask.
   const float sl2 = a.scale * 1.4426950408889634f;
   const int wave_full = wave_first < a.T ? P + wave_first : -1;
-  Q2_PF_LOAD(rk, rv, 0)
+  Q2_PF_LOAD(rk, rv, jt0 * PF_KT)
   Q2_PF_STORE(0, rk, rv)
   __syncthreads();
-  for (int jt = 0; jt < ntiles; ++jt) {
-    const int buf = jt & 1;
+  for (int jt = jt0; jt < jt1; ++jt) {
+    const int buf = (jt - jt0) & 1;
     const int j0 = jt * PF_KT;
     Q2_PF_LOAD(rk, rv, j0 + PF_KT)
     if (j0 <= wave_lim)
       pf_tile(sK[buf], sVt[buf], j0, j0 + PF_KT - 1 <= wave_full, lim, sl2, qr, hl, qf, oacc, m_run, l_run);
-    if (jt + 1 < ntiles) Q2_PF_STORE(buf ^ 1, rk, rv)
+    if (jt + 1 < jt1) Q2_PF_STORE(buf ^ 1, rk, rv)
     __syncthreads();
   }
 #undef Q2_PF_LOAD
 #undef Q2_PF_STORE
   if (!qvalid) return;
+  if (part >= 0) {
+    // lane half hl holds d = 32 dt + 8 v + 4 hl .. + 3 of query row 32 wave + qr
+    const int64_t pi = ((static_cast<int64_t>(b) * a.nh + h) * nsq + (nqb - 1 - qb)) * 2 + part;
+    const int r = 32 * wave + qr;
+    float* po = part_o + (pi * PF_QB + r) * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        *reinterpret_cast<float4*>(po + 32 * dt + 8 * v + 4 * hl) =
+            make_float4(oacc[dt][4 * v], oacc[dt][4 * v + 1], oacc[dt][4 * v + 2], oacc[dt][4 * v + 3]);
+    if (hl == 0) part_ml[pi * PF_QB + r] = make_float2(m_run, l_run);
+    return;
+  }
   const float inv = 1.f / l_run;
   uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.o_bs + static_cast<int64_t>(tq) * a.o_ts + h * a.o_hs;
 #pragma unroll
@@ -535,6 +559,63 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a) {
       w.y = pack_bf2(oacc[dt][4 * v + 2] * inv, oacc[dt][4 * v + 3] * inv);
       *reinterpret_cast<uint2*>(op + 32 * dt + 8 * v + 4 * hl) = w;
     }
+}
+
+// Merges the two halves of each split query block: thread (row r, half of d)
+// of block nqb - 1 - blockIdx.x.
+__global__ __launch_bounds__(256) void attn_prefill_combine(AttnArgs a, int nsq, const float* __restrict__ part_o,
+                                                            const float2* __restrict__ part_ml) {
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int nqb = (a.T + PF_QB - 1) / PF_QB;
+  const int qb = nqb - 1 - i;
+  const int r = threadIdx.x >> 1;
+  const int d0 = (threadIdx.x & 1) * 64;
+  const int tq = qb * PF_QB + r;
+  if (tq >= a.T) return;
+  const int64_t pi = ((static_cast<int64_t>(b) * a.nh + h) * nsq + i) * 2;
+  const float2 ml0 = part_ml[pi * PF_QB + r], ml1 = part_ml[(pi + 1) * PF_QB + r];
+  // the first half always holds key 0; the second may hold no visible key
+  const float mx = fmaxf(ml0.x, ml1.x);
+  const float w0 = __builtin_amdgcn_exp2f(ml0.x - mx);
+  const float w1 = ml1.x == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(ml1.x - mx);
+  const float inv = 1.f / (w0 * ml0.y + w1 * ml1.y);
+  const float4* p0 = reinterpret_cast<const float4*>(part_o + (pi * PF_QB + r) * D + d0);
+  const float4* p1 = reinterpret_cast<const float4*>(part_o + ((pi + 1) * PF_QB + r) * D + d0);
+  uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.o_bs + static_cast<int64_t>(tq) * a.o_ts + h * a.o_hs + d0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float4 x0 = p0[2 * c], x1 = p0[2 * c + 1], y0 = p1[2 * c], y1 = p1[2 * c + 1];
+    uint4 w;
+    w.x = pack_bf2((w0 * x0.x + w1 * y0.x) * inv, (w0 * x0.y + w1 * y0.y) * inv);
+    w.y = pack_bf2((w0 * x0.z + w1 * y0.z) * inv, (w0 * x0.w + w1 * y0.w) * inv);
+    w.z = pack_bf2((w0 * x1.x + w1 * y1.x) * inv, (w0 * x1.y + w1 * y1.y) * inv);
+    w.w = pack_bf2((w0 * x1.z + w1 * y1.z) * inv, (w0 * x1.w + w1 * y1.w) * inv);
+    *reinterpret_cast<uint4*>(op + 8 * c) = w;
+  }
+}
+
+// Query blocks of a prefill call whose key ranges are split (host view of
+// the lengths): those with more than half the key tiles of the last block.
+// Only when the longest block (at least 8 tiles) would outlast the whole
+// grid's work spread over two workgroups per CU by half again: otherwise
+// the chip is full anyway and the split's partials only cost traffic.
+int prefill_split_blocks(int B, int nh, int T, int S) {
+  const int nqb = cdiv(T, PF_QB);
+  const int P = S - T;
+  auto nt = [&](int qb) { return cdiv(std::min(S, P + std::min((qb + 1) * PF_QB, T)), PF_KT); };
+  const int top = nt(nqb - 1);
+  if (top < 8) return 0;
+  int64_t work = 0;
+  for (int qb = 0; qb < nqb; ++qb) work += nt(qb);
+  work *= static_cast<int64_t>(B) * nh;
+  if (2 * static_cast<int64_t>(top) * 512 <= 3 * work) return 0;
+  int n = 0;
+  for (int qb = nqb - 1; qb >= 0 && nt(qb) > cdiv(top, 2); --qb) ++n;
+  return n;
+}
+
+size_t prefill_split_bytes(int B, int nh, int nsq) {
+  return static_cast<size_t>(B) * nh * nsq * 2 * PF_QB * (D * sizeof(float) + sizeof(float2));
 }
 
 // ------------------------------------------------------------------ float32
@@ -605,7 +686,8 @@ int attention_decode_splits(int B, int T, int s_max, int nh, int nkv, int d) {
 }
 
 size_t attention_scratch_bytes(int B, int T, int s_max, int nh, int nkv, int d) {
-  if (d != D || T * (nh / nkv) > 16) return 0;
+  if (d != D) return 0;
+  if (T * (nh / nkv) > 16) return prefill_split_bytes(B, nh, cdiv(T, PF_QB));  // at most every block split
   DecodePlan p = plan_decode(B, s_max, nkv);
   if (p.nsplit == 1) return 0;
   const size_t slots = static_cast<size_t>(B) * nkv * p.nsplit * 16;
@@ -637,8 +719,17 @@ q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
     }
     return Q2_OK;
   }
-  hipLaunchKernelGGL(attn_prefill_kernel, dim3(a.nh, cdiv(a.T, PF_QB), a.B), dim3(256), 0, s, a);
-  return check_launch("attn_prefill");
+  const int nqb = cdiv(a.T, PF_QB);
+  int nsq = prefill_split_blocks(a.B, a.nh, a.T, a.S);
+  if (nsq && (!a.scratch || a.scratch_bytes < prefill_split_bytes(a.B, a.nh, nsq))) nsq = 0;
+  float* part_o = static_cast<float*>(a.scratch);
+  float2* part_ml =
+      nsq ? reinterpret_cast<float2*>(part_o + static_cast<size_t>(a.B) * a.nh * nsq * 2 * PF_QB * D) : nullptr;
+  hipLaunchKernelGGL(attn_prefill_kernel, dim3(a.nh, nqb + nsq, a.B), dim3(256), 0, s, a, nsq, part_o, part_ml);
+  Q2_TRY(check_launch("attn_prefill"));
+  if (nsq == 0) return Q2_OK;
+  hipLaunchKernelGGL(attn_prefill_combine, dim3(nsq, a.nh, a.B), dim3(256), 0, s, a, nsq, part_o, part_ml);
+  return check_launch("attn_prefill_combine");
 }
 
 q2_status attention_f32(const AttnArgs& a, hipStream_t s) {

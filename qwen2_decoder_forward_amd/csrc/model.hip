@@ -741,6 +741,12 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
         size_t x = attention_scratch_bytes(b, t, c.max_seq, c.nh, c.nkv, c.dh);
         as = x > as ? x : as;
       }
+      // prefill chunks of up to max_tok / b tokens (split query blocks)
+      const int tc = std::max(1, std::min(m->max_tok / b, c.max_seq));
+      if (tc * group > 16) {
+        const size_t x = attention_scratch_bytes(b, tc, c.max_seq, c.nh, c.nkv, c.dh);
+        as = x > as ? x : as;
+      }
     }
   m->ascratch_bytes = as;
   const size_t a_as = take(as);

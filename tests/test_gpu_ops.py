@@ -188,6 +188,8 @@ def _attn_case(seed, B, T, S, nh, nkv, d, dtype, cache_layout=False, smax=None):
     (1, 64, 64, 12, 2),      # one full prefill block
     (1, 100, 300, 12, 2),    # prefill with a cached past, ragged
     (2, 130, 130, 28, 4),    # several query blocks, batch 2
+    (1, 1024, 1024, 12, 2),  # causal prefill whose last query blocks are split over two workgroups
+    (2, 200, 3000, 12, 2),   # long cached past: every query block split, ragged last block
 ])
 def test_attention_bf16(B, T, S, nh, nkv):
     _attn_case(B * 7 + T * 13 + S, B, T, S, nh, nkv, 128, BF)
