@@ -174,6 +174,8 @@ constexpr int GEMV_NORM_MAX_M = 16;
 // bytes of X the GEMV path stages in LDS (fused sources need it to fit)
 constexpr size_t GEMV_STAGE_BYTES = size_t(64) << 10;
 bool gemv_can_fuse(int M, int K);
+// Whether a split-K residual add may be left to the next normalising GEMV.
+bool gemv_can_defer(int M, int K);
 q2_status gemv_bf16(const GemmArgs& a, hipStream_t s);
 // Split-K partial bytes the GEMV path needs for this shape (0 if unsplit).
 size_t gemv_scratch_bytes(int M, int N, int K);

@@ -549,12 +549,16 @@ q2_status gemv_ek(const GemmArgs& a, const GemvPlan& p, hipStream_t s) {
 }  // namespace
 
 bool gemv_can_fuse(int M, int K) {
-  // The fused prologues rebuild X in every workgroup; that pays only while one
-  // pass of the workgroup's threads (16 B each) covers it.  Beyond that the
-  // dependent L2 round trips of the prologue cost more than a separate
-  // normalisation kernel.  (The staged K range is largest without splits.)
-  return M <= GEMV_NORM_MAX_M && static_cast<int64_t>(M) * (K / 8) <= 16 * 64 &&
-         stage_bytes(M, cdiv(K, KB), K) <= GEMV_STAGE_BYTES;
+  // The fused prologues rebuild X once per workgroup (each loops over its
+  // tiles), so they pay while X fits the LDS stage.  (The staged K range is
+  // largest without splits.)
+  return M <= GEMV_NORM_MAX_M && stage_bytes(M, cdiv(K, KB), K) <= GEMV_STAGE_BYTES;
+}
+
+bool gemv_can_defer(int M, int K) {
+  // the deferred residual add normalises row by row, one pass of the
+  // workgroup's threads per row: only for a few short rows
+  return gemv_can_fuse(M, K) && M <= 2 && K / 8 <= 16 * 64;
 }
 
 q2_status split_reduce(const GemmArgs& a, int splits, hipStream_t s) {

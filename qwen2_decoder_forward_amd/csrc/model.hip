@@ -181,11 +181,13 @@ GemmArgs gemm_args(const q2_model* m, const void* W, int64_t ldw, const void* X,
 struct Path {
   bool gemv;
   bool fused_norm;
+  bool defer;  // split-K residual adds left to the next normalising GEMV
 };
 Path path_for(const q2_model* m, int M) {
   Path p;
   p.gemv = m->cfg.dtype == Q2_BF16 && M <= GEMV_MAX_M;
   p.fused_norm = p.gemv && gemv_can_fuse(M, m->cfg.hidden) && gemv_can_fuse(M, m->cfg.nh * m->cfg.dh);
+  p.defer = p.fused_norm && gemv_can_defer(M, m->cfg.hidden);
   return p;
 }
 
@@ -317,7 +319,7 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
       a.epi.ldo = H;
       a.epi.sq_out = path.fused_norm ? m->sq : nullptr;
       a.epi.sq_ld = m->sq_ld;
-      if (path.fused_norm && l + 1 < c.nlayer && c.dtype == Q2_BF16) {
+      if (path.defer && l + 1 < c.nlayer) {
         const int sp = gemv_splits(M, H, c.inter);
         if (sp > 1) {
           a.defer_reduce = true;
