@@ -124,11 +124,40 @@ __device__ __forceinline__ uint4 attn_merge8(const GemvSrc& src, int m, int k) {
   return r4;
 }
 
+// Operands an epilogue thread reads besides the product, loaded before the
+// tile's weights arrive so that the epilogue issues no load of its own (a
+// load there would also wait for the next tile's weights, issued earlier):
+// the residual pair (RESID), the bias pair and RoPE cos/sin (QKV).
+struct EpiPre {
+  uint32_t x01;
+  float b0, b1;
+  float2 cs;
+  int pos;
+};
+
+template <int EK>
+__device__ __forceinline__ void epi_preload(const Epi& e, int M, int N, int n0, int m, int p, EpiPre& pre) {
+  const int n = n0 + 2 * p;
+  if (m >= M || n >= N) return;
+  if constexpr (EK == EPI_RESID) {
+    const uint16_t* o = static_cast<const uint16_t*>(e.out) + static_cast<int64_t>(m) * e.ldo + n;
+    pre.x01 = static_cast<uint32_t>(o[0]) | (n + 1 < N ? static_cast<uint32_t>(o[1]) << 16 : 0u);
+  } else if constexpr (EK == EPI_QKV) {
+    const uint16_t* b = static_cast<const uint16_t*>(e.bias);
+    pre.b0 = bf2f(b[n]);
+    pre.b1 = bf2f(b[n + 1]);
+    const int head = n / e.dh;
+    const int t = m % e.T;
+    pre.pos = (e.d_len ? *e.d_len : e.len0) + t;
+    if (head < e.nh + e.nkv) pre.cs = e.rope[static_cast<int64_t>(pre.pos) * (e.dh >> 1) + ((n - head * e.dh) >> 1)];
+  }
+}
+
 // Epilogue of a 16-feature tile for token row m: thread p (0..7 within an
 // aligned group of 8 lanes) owns features n0 + 2p, n0 + 2p + 1.
 template <int EK>
 __device__ __forceinline__ void gemv_epilogue(const Epi& epi, int M, int N, int n0, int tile, int m, int p, float v0,
-                                              float v1) {
+                                              float v1, const EpiPre* pre = nullptr) {
   const int n = n0 + 2 * p;
   const bool valid = m < M && n < N;
   const bool has1 = n + 1 < N;
@@ -156,11 +185,13 @@ __device__ __forceinline__ void gemv_epilogue(const Epi& epi, int M, int N, int 
     float sq = 0.f;
     if (valid) {
       uint16_t* o = static_cast<uint16_t*>(epi.out) + static_cast<int64_t>(m) * epi.ldo + n;
-      const float a = round_bf(bf2f(o[0]) + round_bf(v0));
+      const float x0 = pre ? bf_lo(pre->x01) : bf2f(o[0]);
+      const float a = round_bf(x0 + round_bf(v0));
       o[0] = f2bf(a);
       sq = a * a;
       if (has1) {
-        const float b = round_bf(bf2f(o[1]) + round_bf(v1));
+        const float x1 = pre ? bf_hi(pre->x01) : bf2f(o[1]);
+        const float b = round_bf(x1 + round_bf(v1));
         o[1] = f2bf(b);
         sq += b * b;
       }
@@ -169,6 +200,37 @@ __device__ __forceinline__ void gemv_epilogue(const Epi& epi, int M, int N, int 
     sq += __shfl_xor(sq, 2, 64);
     sq += __shfl_xor(sq, 4, 64);
     if (valid && p == 0 && epi.sq_out) epi.sq_out[m * epi.sq_ld + tile] = sq;
+  } else if constexpr (EK == EPI_QKV) {
+    if (!valid) return;
+    if (!pre) {
+      epi_pair<uint16_t, EK>(epi, m, n, v0, v1, has1);
+      return;
+    }
+    // as epi_pair's QKV case, with the preloaded bias, position and cos/sin
+    const float a = round_bf(v0 + pre->b0);
+    const float c = round_bf(v1 + pre->b1);
+    const int d = epi.dh;
+    const int head = n / d;
+    const int r = n - head * d;
+    const int bt = m / epi.T;
+    if (head < epi.nh + epi.nkv) {
+      const int q = r >> 1;
+      const float ra = round_bf(a * pre->cs.x - c * pre->cs.y);
+      const float rb = round_bf(c * pre->cs.x + a * pre->cs.y);
+      uint16_t* dst;
+      if (head < epi.nh)
+        dst = static_cast<uint16_t*>(epi.out) + static_cast<int64_t>(m) * epi.ldo + head * d;
+      else
+        dst = static_cast<uint16_t*>(epi.kc) + bt * epi.kv_bstride + (head - epi.nh) * epi.kv_hstride +
+              static_cast<int64_t>(pre->pos) * d;
+      dst[q] = f2bf(ra);
+      dst[q + (d >> 1)] = f2bf(rb);
+    } else {
+      uint16_t* dst = static_cast<uint16_t*>(epi.vc) + bt * epi.kv_bstride + (head - epi.nh - epi.nkv) * epi.kv_hstride +
+                      static_cast<int64_t>(pre->pos) * d + r;
+      dst[0] = f2bf(a);
+      dst[1] = f2bf(c);
+    }
   } else {
     if (valid) epi_pair<uint16_t, EK>(epi, m, n, v0, v1, has1);
   }
@@ -234,6 +296,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemv_kernel(const uint16_t* __rest
     }                                                                                       \
   }
   Q2_GEMV_LOAD_BATCH(kb0 + wave)
+  // the epilogue thread of (row tid / 8, pair tid % 8) loads its operands now
+  constexpr bool PRE = !SPLIT && (EK == EPI_RESID || EK == EPI_QKV);
+  EpiPre pre{};
+  if (PRE && tid < 16 * MT * 8) epi_preload<EK>(epi, M, N, n0, tid >> 3, tid & 7, pre);
 
   if constexpr (SRC == XSRC_NORMR) {
     // The pending residual add, then RMSNorm, row by row (one pass of the
@@ -359,12 +425,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemv_kernel(const uint16_t* __rest
   // the next tile's first weight batch goes out before this tile's
   // reduction and epilogue (the X rows in LDS serve every tile)
   const int cur = tl, c0 = n0;
+  const EpiPre pc = pre;
   tl += gridDim.x;
   if (tl < ntile) {
     n0 = tl * 16;
     wrow_ok = n0 + row < N;
     wp = W + static_cast<int64_t>(wrow_ok ? n0 + row : 0) * ldw + 8 * g;
     Q2_GEMV_LOAD_BATCH(kb0 + wave)
+    if (PRE && tid < 16 * MT * 8) epi_preload<EK>(epi, M, N, n0, tid >> 3, tid & 7, pre);
   }
 
   // sum the weight waves' partial tiles (fixed order)
@@ -401,7 +469,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemv_kernel(const uint16_t* __rest
       const int p = t & 7;
       const float v0 = m < Mp ? tile[m][2 * p] : 0.f;
       const float v1 = m < Mp ? tile[m][2 * p + 1] : 0.f;
-      gemv_epilogue<EK>(epi, M, N, c0, cur, m, p, v0, v1);
+      gemv_epilogue<EK>(epi, M, N, c0, cur, m, p, v0, v1, PRE ? &pc : nullptr);
     }
   }
   // the next tile's reduction writes red only after every wave has passed
