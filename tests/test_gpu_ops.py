@@ -110,7 +110,9 @@ def test_rope_batched_in_place_large_theta():
                                    (65, 300, 200), (200, 2048, 1536), (300, 260, 136),
                                    # 17..64 rows with K % 128 == 0: the skinny tiles, split over K or not
                                    (17, 520, 384), (24, 264, 1024), (48, 1536, 8960), (64, 2048, 1536),
-                                   (64, 17920, 1536)])
+                                   (64, 17920, 1536),
+                                   # long K with few output tiles
+                                   (300, 1536, 8960), (520, 264, 4096)])
 @pytest.mark.parametrize("bias,out_f32", [(True, False), (False, True)])
 def test_linear_bf16(M, N, K, bias, out_f32):
     r = rng(M * 1000 + N + K)
