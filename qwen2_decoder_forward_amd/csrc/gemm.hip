@@ -695,14 +695,19 @@ q2_status launch_skinny(const GemmArgs& a, hipStream_t s) {
   return launch_skinny_cfg<EK, 64>(a, p, s);
 }
 
-// 256 x 256 tiles (8 waves, 128 KB LDS, one workgroup per CU) when they give
-// the chip at least ~1.5 rounds of work, otherwise 128 x 128 tiles (4 waves,
-// 64 KB, two per CU).
+// Tile shape by how many tiles the product has for 256 CUs:
+//  * 256 x 256 (8 waves of 128 x 64, 128 KB LDS, one workgroup per CU) when
+//    that gives at least ~1.5 rounds of work;
+//  * otherwise, with at least 512 token rows, 128 features x 256 tokens
+//    (8 waves of 128 x 32, 96 KB): twice the tiles of the square shape, so
+//    products with few output features (o_proj and down at hidden 1536: 96
+//    square tiles) spread over most CUs instead of a third of them;
+//  * otherwise 128 x 128 tiles (4 waves, 64 KB, two per CU).
 template <int EK>
-q2_status launch_dtl(const GemmArgs& a, hipStream_t s, int force = 0) {
+q2_status launch_dtl(const GemmArgs& a, hipStream_t s) {
   const int big_tiles = cdiv(a.M, 256) * cdiv(a.N, 256);
-  const bool big = force ? force == 1 : big_tiles >= 384;
-  if (big) return launch_dtl_cfg<EK, 256, 256, 2, 4>(a, s);
+  if (big_tiles >= 384) return launch_dtl_cfg<EK, 256, 256, 2, 4>(a, s);
+  if (a.M >= 512) return launch_dtl_cfg<EK, 128, 256, 1, 8>(a, s);
   return launch_dtl_cfg<EK, 128, 128, 1, 4>(a, s);
 }
 
