@@ -369,38 +369,35 @@ __device__ __forceinline__ void stg_copy_out(const uint16_t* sh, const Epi& e, i
   }
 }
 
+// Tile order.  Workgroups are dealt to the 8 XCDs in turn, each with its own
+// L2: logical tile L = (t % 8) * (T / 8) + t / 8 makes a run of consecutive
+// tiles live on one XCD, and walking them in groups of 4 token tiles x all
+// weight tiles keeps the ~32 tiles resident on an XCD within 4 token panels
+// and 8 weight panels, which its L2 then serves.  t: this workgroup's index
+// among the T tiles (tiles_m token tiles per weight panel).
+__device__ __forceinline__ void xcd_tile(int t, int T, int tiles_m, int& tn, int& tm) {
+  const int L = T % 8 == 0 ? (t % 8) * (T / 8) + t / 8 : t;
+  const int tiles_n = T / tiles_m;
+  constexpr int GM = 4;
+  const int per_group = GM * tiles_n;
+  const int fm = L / per_group * GM;
+  const int gs = min(tiles_m - fm, GM);
+  const int r = L - fm * tiles_n;
+  tm = fm + r % gs;
+  tn = r / gs;
+}
+
+// One BN x BM output tile at features n0.., tokens m0...
 // With SPLIT, blockIdx.y takes slices [y * kt_split, (y + 1) * kt_split) of
 // K and the float32 tile goes to partial[y][m][n] (a second kernel sums the
 // splits in order and applies the epilogue).
 template <int EK, int BN, int BM, int WN, int WM, bool STAGED, bool SPLIT>
-__global__ __launch_bounds__(WN * WM * 64) void gemm_dtl_kernel(const uint16_t* __restrict__ W, int64_t ldw,
-                                                                const uint16_t* __restrict__ X, int64_t ldx, int N,
-                                                                int M, int K, int tiles_m, int kt_split,
-                                                                float* __restrict__ partial, Epi epi) {
+__device__ __forceinline__ void dtl_tile(const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ X,
+                                         int64_t ldx, int N, int M, int K, int n0, int m0, int kt_split,
+                                         float* __restrict__ partial, const Epi& epi) {
   using C = Dtl<BN, BM, WN, WM>;
   constexpr int FN = C::FN, FM = C::FM, TN = C::TN, TM = C::TM, NT = C::NT, LD = C::LD;
   extern __shared__ uint4 dsm[];
-  // Tile order.  Workgroups are dealt to the 8 XCDs in turn, each with its
-  // own L2: logical tile L = (t % 8) * (T / 8) + t / 8 makes a run of
-  // consecutive tiles live on one XCD, and walking them in groups of 4 token
-  // tiles x all weight tiles keeps the ~32 tiles resident on an XCD within 4
-  // token panels and 8 weight panels, which its L2 then serves.
-  int tn, tm;
-  {
-    const int T = gridDim.x;
-    const int t = blockIdx.x;
-    const int L = T % 8 == 0 ? (t % 8) * (T / 8) + t / 8 : t;
-    const int tiles_n = T / tiles_m;
-    constexpr int GM = 4;
-    const int per_group = GM * tiles_n;
-    const int fm = L / per_group * GM;
-    const int gs = min(tiles_m - fm, GM);
-    const int r = L - fm * tiles_n;
-    tm = fm + r % gs;
-    tn = r / gs;
-  }
-  const int n0 = tn * BN;
-  const int m0 = tm * BM;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -587,6 +584,40 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_dtl_kernel(const uint16_t* 
   }
 }
 
+
+template <int EK, int BN, int BM, int WN, int WM, bool STAGED, bool SPLIT>
+__global__ __launch_bounds__(WN * WM * 64) void gemm_dtl_kernel(const uint16_t* __restrict__ W, int64_t ldw,
+                                                                const uint16_t* __restrict__ X, int64_t ldx, int N,
+                                                                int M, int K, int tiles_m, int kt_split,
+                                                                float* __restrict__ partial, Epi epi) {
+  int tn, tm;
+  xcd_tile(blockIdx.x, gridDim.x, tiles_m, tn, tm);
+  dtl_tile<EK, BN, BM, WN, WM, STAGED, SPLIT>(W, ldw, X, ldx, N, M, K, tn * BN, tm * BM, kt_split, partial, epi);
+}
+
+// Products whose 256 x 256 tiles leave the last round mostly idle: the
+// first main_tiles workgroups take 256 x 256 tiles over features [0, n_main)
+// (whole rounds of the chip), the rest 128-feature x 256-token tiles over the
+// remaining features, which take a little over half the time of a square
+// tile.  Both are 8-wave shapes; the launch gives the larger LDS ring.
+template <int EK, bool STAGED>
+__global__ __launch_bounds__(512) void gemm_dtl_mix_kernel(const uint16_t* __restrict__ W, int64_t ldw,
+                                                           const uint16_t* __restrict__ X, int64_t ldx, int N, int M,
+                                                           int K, int tiles_m, int main_tiles, Epi epi) {
+  const int t = blockIdx.x;
+  if (t < main_tiles) {
+    int tn, tm;
+    xcd_tile(t, main_tiles, tiles_m, tn, tm);
+    dtl_tile<EK, 256, 256, 2, 4, STAGED, false>(W, ldw, X, ldx, N, M, K, tn * 256, tm * 256, 0, nullptr, epi);
+  } else {
+    const int n_main = main_tiles / tiles_m * 256;
+    int tn, tm;
+    xcd_tile(t - main_tiles, gridDim.x - main_tiles, tiles_m, tn, tm);
+    dtl_tile<EK, 128, 256, 1, 8, STAGED, false>(W, ldw, X, ldx, N, M, K, n_main + tn * 128, tm * 256, 0, nullptr,
+                                               epi);
+  }
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // The direct-to-LDS kernel's operand requirements.
@@ -697,16 +728,60 @@ q2_status launch_skinny(const GemmArgs& a, hipStream_t s) {
 
 // Tile shape by how many tiles the product has for 256 CUs:
 //  * 256 x 256 (8 waves of 128 x 64, 128 KB LDS, one workgroup per CU) when
-//    that gives at least ~1.5 rounds of work;
+//    that gives at least ~1.5 rounds of work, with a 128 x 256 tail when the
+//    last round would be mostly idle (gemm_dtl_mix_kernel);
 //  * otherwise, with at least 512 token rows, 128 features x 256 tokens
 //    (8 waves of 128 x 32, 96 KB): twice the tiles of the square shape, so
 //    products with few output features (o_proj and down at hidden 1536: 96
 //    square tiles) spread over most CUs instead of a third of them;
 //  * otherwise 128 x 128 tiles (4 waves, 64 KB, two per CU).
+// Main/tail split for gemm_dtl_mix_kernel: the number of 256 x 256 tiles,
+// over leading weight panels and in whole rounds of 256 CUs, whose remainder
+// as 128 x 256 tiles (about 0.6 of a square tile's time each) ends well
+// before the plain grid's partly idle last round would.  0: no split.
+int mix_main_tiles(int M, int N) {
+  const int tiles_m = cdiv(M, 256), tiles_n = cdiv(N, 256);
+  constexpr double kTail = 0.6;
+  double best_cost = cdiv(tiles_m * tiles_n, 256);
+  int best = 0;
+  for (int tn = tiles_n - 1; tn >= 1; --tn) {
+    const int main_tiles = tiles_m * tn;
+    if (main_tiles % 256 != 0) continue;
+    const int tail = tiles_m * cdiv(N - tn * 256, 128);
+    const double cost = main_tiles / 256 + kTail * cdiv(tail, 256);
+    if (cost < best_cost - 0.25) {
+      best = main_tiles;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+template <int EK>
+q2_status launch_dtl_mix(const GemmArgs& a, int main_tiles, hipStream_t s) {
+  const int tiles_m = cdiv(a.M, 256);
+  const int n_main = main_tiles / tiles_m * 256;
+  const int tiles = main_tiles + tiles_m * cdiv(a.N - n_main, 128);
+  const size_t lds = Dtl<256, 256, 2, 4>::LDS_BYTES;
+  if (staged_ok(a))
+    hipLaunchKernelGGL((gemm_dtl_mix_kernel<EK, true>), dim3(tiles), dim3(512), lds, s,
+                       static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M,
+                       a.K, tiles_m, main_tiles, a.epi);
+  else
+    hipLaunchKernelGGL((gemm_dtl_mix_kernel<EK, false>), dim3(tiles), dim3(512), lds, s,
+                       static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M,
+                       a.K, tiles_m, main_tiles, a.epi);
+  return check_launch("gemm_dtl_mix");
+}
+
 template <int EK>
 q2_status launch_dtl(const GemmArgs& a, hipStream_t s) {
   const int big_tiles = cdiv(a.M, 256) * cdiv(a.N, 256);
-  if (big_tiles >= 384) return launch_dtl_cfg<EK, 256, 256, 2, 4>(a, s);
+  if (big_tiles >= 384) {
+    const int main_tiles = mix_main_tiles(a.M, a.N);
+    if (main_tiles > 0) return launch_dtl_mix<EK>(a, main_tiles, s);
+    return launch_dtl_cfg<EK, 256, 256, 2, 4>(a, s);
+  }
   if (a.M >= 512) return launch_dtl_cfg<EK, 128, 256, 1, 8>(a, s);
   return launch_dtl_cfg<EK, 128, 128, 1, 4>(a, s);
 }

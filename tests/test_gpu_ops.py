@@ -112,7 +112,10 @@ def test_rope_batched_in_place_large_theta():
                                    (17, 520, 384), (24, 264, 1024), (48, 1536, 8960), (64, 2048, 1536),
                                    (64, 17920, 1536),
                                    # long K with few output tiles
-                                   (300, 1536, 8960), (520, 264, 4096)])
+                                   (300, 1536, 8960), (520, 264, 4096),
+                                   # 256 x 256 tiles over whole rounds of the chip plus a
+                                   # 128 x 256 tail (ragged rows and features)
+                                   (4000, 8600, 256)])
 @pytest.mark.parametrize("bias,out_f32", [(True, False), (False, True)])
 def test_linear_bf16(M, N, K, bias, out_f32):
     r = rng(M * 1000 + N + K)
