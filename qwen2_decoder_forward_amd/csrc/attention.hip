@@ -324,9 +324,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
 // operand.  P is rounded to bf16 for that product.
 //
 // K rows (256 bytes) keep 16-byte chunk c of key r at c ^ (r & 15).  V^T
-// rows are padded to 72 keys and the 8-key chunk k of row d sits at
-// k ^ ((d / 8) % 8): the transposing writes (16 rows 8 apart per wave
-// instruction) then spread over the banks as evenly as the fragment reads.
+// rows are padded to 72 keys (144 bytes, 9 sixteen-byte slots) and the
+// 8-key chunk k of row d sits at k ^ ((d / 16) % 8).  A fragment read (16
+// consecutive rows, one chunk) then lands on 16 distinct slots of a 256-byte
+// bank line, and a transposing write (rows 8 apart, 8 bytes per lane) has
+// the 32 lanes of a half-wave fill both halves of 16 distinct slots: the
+// two 16-lane groups of a half-wave load key groups that share a chunk.
 
 constexpr int PF_QB = 128;   // queries per workgroup
 constexpr int PF_KT = 64;    // keys per tile
@@ -336,8 +339,9 @@ __device__ __forceinline__ int pf_keyperm(int k) { return (k & ~12) | ((k & 4) <
 
 // One 64-key tile of the prefill loop for the calling wave: S^T from the
 // K tile, online softmax of the wave's 32 queries, O^T += V^T P^T.
-// Scores are kept in base-2 units (scale * log2 e folded in), so each
-// probability is one exp2; a tile entirely inside every query's causal
+// The running max and sum are kept in base-2 units (scale * log2 e folded
+// in), so each probability is one fma and one exp2, and the sum is taken
+// over the bf16-rounded probabilities that the V product uses; a tile entirely inside every query's causal
 // window skips the mask; the accumulator is rescaled only when some lane's
 // running maximum moved (alpha == 1 exactly otherwise).  exp2(-inf) = 0
 // covers masked keys.
@@ -357,16 +361,15 @@ __device__ __forceinline__ void pf_tile(const uint4* __restrict__ sKb, const uin
       sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kfr), as_bf16x8(qf[ks]), sacc[kh], 0, 0, 0);
     }
   }
-  // scale (and mask), running max of query qr (lanes qr and qr + 32)
+  // running max of query qr's raw scores (lanes qr and qr + 32), masked
+  // keys at -inf; the scale goes into one fma per probability:
+  // p = exp2(s * scale * log2 e - m)
   float mt = NEG_INF;
   if (full) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sacc[kh][i] *= sl2;
-        mt = fmaxf(mt, sacc[kh][i]);
-      }
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kh][i]);
   } else {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -375,16 +378,18 @@ __device__ __forceinline__ void pf_tile(const uint4* __restrict__ sKb, const uin
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int kj = j0 + 32 * kh + 8 * v + 4 * hl + e;
-          const float x = kj <= lim ? sacc[kh][4 * v + e] * sl2 : NEG_INF;
+          const float x = kj <= lim ? sacc[kh][4 * v + e] : NEG_INF;
           sacc[kh][4 * v + e] = x;
           mt = fmaxf(mt, x);
         }
   }
   mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-  const float m_new = fmaxf(m_run, mt);
+  const float m_new = fmaxf(m_run, mt * sl2);
   const float base = m_new == NEG_INF ? 0.f : m_new;
   const float alpha = __builtin_amdgcn_exp2f(m_run - base);
+  // the row sum adds the bf16 probabilities that multiply V, two per dot2
   float ps = 0.f;
+  const bf16x2_hw ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
   bf16x8_t pf[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -395,12 +400,11 @@ __device__ __forceinline__ void pf_tile(const uint4* __restrict__ sKb, const uin
       const int v = 2 * (c & 1) + half;
       float pr[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pr[e] = __builtin_amdgcn_exp2f(sacc[c >> 1][4 * v + e] - base);
-        ps += pr[e];
-      }
+      for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(sacc[c >> 1][4 * v + e], sl2, -base));
       ws[2 * half] = pack_bf2(pr[0], pr[1]);
       ws[2 * half + 1] = pack_bf2(pr[2], pr[3]);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_hw, ws[2 * half]), ones, ps, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_hw, ws[2 * half + 1]), ones, ps, false);
     }
     pf[c] = as_bf16x8(w);
   }
@@ -420,7 +424,7 @@ __device__ __forceinline__ void pf_tile(const uint4* __restrict__ sKb, const uin
     for (int c = 0; c < 4; ++c) {
       const int vr = 32 * dt + qr;
       const uint4 vfr =
-          *reinterpret_cast<const uint4*>(&sVtb[vr * PF_VT + ((16 * c + 8 * hl) ^ (((vr >> 3) & 7) << 3))]);
+          *reinterpret_cast<const uint4*>(&sVtb[vr * PF_VT + ((16 * c + 8 * hl) ^ (((vr >> 4) & 7) << 3))]);
       oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr), pf[c], oacc[dt], 0, 0, 0);
     }
   }
@@ -477,10 +481,13 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int ns
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.v_bs + g * a.v_hs;
 
   // tile loads: K chunk q = tid + 256 i is key q / 16, chunk q % 16; V: this
-  // thread's 8-wide d chunk vc of keys 4 vg .. 4 vg + 3.  Keys past kv_end
+  // thread's 8-wide d chunk vc of keys 4 vg .. 4 vg + 3, where the 16-lane
+  // groups 0..3 of wave w take key groups 4 w + {0, 2, 1, 3} (groups 0 and
+  // 2 share an 8-key chunk after the key permutation).  Keys past kv_end
   // read the last valid key: their scores are masked and their
   // probabilities are exactly zero.
-  const int vc = tid & 15, vg = tid >> 4;
+  const int vc = tid & 15, vq = (tid >> 4) & 3;
+  const int vg = 4 * (tid >> 6) + (((vq & 1) << 1) | (vq >> 1));
   uint4 rk[4], rv[4];
 #define Q2_PF_LOAD(RK_, RV_, J0_)                                                                              \
   {                                                                                                  \
@@ -501,7 +508,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int ns
       const int r_ = q_ >> 4;                                                                        \
       sK[BUF_][r_ * 16 + ((q_ & 15) ^ (r_ & 15))] = RK_[i];                                          \
     }                                                                                                \
-    store_vt4(sVt[BUF_], PF_VT, 8 * vc, pf_keyperm(4 * vg) ^ ((vc & 7) << 3), RV_);                  \
+    store_vt4(sVt[BUF_], PF_VT, 8 * vc, pf_keyperm(4 * vg) ^ (((vc >> 1) & 7) << 3), RV_);           \
   }
 
   float m_run = NEG_INF, l_run = 0.f;
