@@ -62,12 +62,15 @@ __device__ __forceinline__ uint32_t elem16(const uint4& v, int i) {
 
 // Write four keys' 8-element d-chunks transposed: row (d0 + i) gets the 4 keys
 // at column `col` (4 consecutive bf16 = 8 bytes).
+// (v_perm_b32 picks the two 16-bit elements: selector bytes 0-3 address its
+// second operand, 4-7 its first.)
 __device__ __forceinline__ void store_vt4(uint16_t* base, int row_stride, int d0, int col, const uint4 (&v)[4]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
+    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
     uint2 w;
-    w.x = elem16(v[0], i) | (elem16(v[1], i) << 16);
-    w.y = elem16(v[2], i) | (elem16(v[3], i) << 16);
+    w.x = __builtin_amdgcn_perm((&v[1].x)[i >> 1], (&v[0].x)[i >> 1], sel);
+    w.y = __builtin_amdgcn_perm((&v[3].x)[i >> 1], (&v[2].x)[i >> 1], sel);
     *reinterpret_cast<uint2*>(base + (d0 + i) * row_stride + col) = w;
   }
 }
@@ -483,23 +486,34 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int ns
   // tile loads: K chunk q = tid + 256 i is key q / 16, chunk q % 16; V: this
   // thread's 8-wide d chunk vc of keys 4 vg .. 4 vg + 3, where the 16-lane
   // groups 0..3 of wave w take key groups 4 w + {0, 2, 1, 3} (groups 0 and
-  // 2 share an 8-key chunk after the key permutation).  Keys past kv_end
-  // read the last valid key: their scores are masked and their
-  // probabilities are exactly zero.
+  // 2 share an 8-key chunk after the key permutation).
   const int vc = tid & 15, vq = (tid >> 4) & 3;
   const int vg = 4 * (tid >> 6) + (((vq & 1) << 1) | (vq >> 1));
+  // The loads go through buffer descriptors whose base is the tile's first
+  // key and whose range ends at kv_end: each lane's byte offset is fixed for
+  // the kernel, and keys past kv_end read as zeros (hardware range check), so
+  // their scores are masked and their probabilities exactly zero.  The host
+  // keeps kv_end * row stride below 2^31 bytes.
+  const int kbytes = static_cast<int>(a.k_ss) * 2, vbytes = static_cast<int>(a.v_ss) * 2;
+  int koff[4], voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    koff[i] = ((tid >> 4) + 16 * i) * kbytes + (tid & 15) * 16;
+    voff[i] = (4 * vg + i) * vbytes + vc * 16;
+  }
   uint4 rk[4], rv[4];
-#define Q2_PF_LOAD(RK_, RV_, J0_)                                                                              \
+#define Q2_PF_LOAD(RK_, RV_, J0_)                                                                    \
   {                                                                                                  \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                  \
-      const int q_ = tid + 256 * i;                                                                  \
-      const int key_ = min((J0_) + (q_ >> 4), kv_end - 1);                                           \
-      RK_[i] = ld16(kbase + static_cast<int64_t>(key_) * a.k_ss + 8 * (q_ & 15));                    \
-    }                                                                                                \
-    _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) {                                               \
-      const int key_ = min((J0_) + 4 * vg + s_, kv_end - 1);                                         \
-      RV_[s_] = ld16(vbase + static_cast<int64_t>(key_) * a.v_ss + 8 * vc);                          \
-    }                                                                                                \
+    const int j_ = (J0_);                                                                            \
+    const int n_ = max(kv_end - j_, 0);                                                              \
+    const __amdgpu_buffer_rsrc_t kr_ = __builtin_amdgcn_make_buffer_rsrc(                            \
+        const_cast<uint16_t*>(kbase) + static_cast<int64_t>(j_) * a.k_ss, 0, n_ * kbytes, 0x00020000); \
+    const __amdgpu_buffer_rsrc_t vr_ = __builtin_amdgcn_make_buffer_rsrc(                            \
+        const_cast<uint16_t*>(vbase) + static_cast<int64_t>(j_) * a.v_ss, 0, n_ * vbytes, 0x00020000); \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
+      RK_[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr_, koff[i], 0, 0));  \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
+      RV_[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr_, voff[i], 0, 0));  \
   }
 #define Q2_PF_STORE(BUF_, RK_, RV_)                                                                  \
   {                                                                                                  \
@@ -521,9 +535,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int ns
   const int ntiles = (kv_end + PF_KT - 1) / PF_KT;
   const int jt0 = part == 1 ? ntiles / 2 : 0;
   const int jt1 = part == 0 ? ntiles / 2 : ntiles;
-  // The loads are issued unconditionally (past kv_end they reread the last
-  // key), so the compiler's count of loads in flight does not depend on the
-  // path.  The wave's first query decides whether a tile needs the mask.
+  // The loads are issued unconditionally (past kv_end they read zeros), so
+  // the compiler's count of loads in flight does not depend on the path.
+  // The wave's first query decides whether a tile needs the mask.
   const float sl2 = a.scale * 1.4426950408889634f;
   const int wave_full = wave_first < a.T ? P + wave_first : -1;
   Q2_PF_LOAD(rk, rv, jt0 * PF_KT)
@@ -726,6 +740,12 @@ q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
     }
     return Q2_OK;
   }
+  // the prefill kernel's buffer loads address a head's keys with 32-bit
+  // byte offsets
+  const int64_t max_keys = a.d_len ? a.s_max : a.S;
+  Q2_CHECK(max_keys * std::max(a.k_ss, a.v_ss) * 2 < (int64_t(1) << 31), Q2_ESHAPE,
+           "bf16 prefill attention: %lld keys at row strides %lld / %lld exceed 2 GiB per head",
+           static_cast<long long>(max_keys), static_cast<long long>(a.k_ss), static_cast<long long>(a.v_ss));
   const int nqb = cdiv(a.T, PF_QB);
   int nsq = prefill_split_blocks(a.B, a.nh, a.T, a.S);
   if (nsq && (!a.scratch || a.scratch_bytes < prefill_split_bytes(a.B, a.nh, nsq))) nsq = 0;

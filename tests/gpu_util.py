@@ -38,7 +38,9 @@ def assert_close(got, ref, atol, rtol, what=""):
     assert got.shape == ref.shape, (got.shape, ref.shape)
     err = np.abs(got - ref)
     bound = np.asarray(atol, np.float64) + rtol * np.abs(ref)
-    bad = err > bound
+    # NaN anywhere in got fails (it compares false against any bound); exact
+    # matches, infinities included, pass
+    bad = ~((err <= bound) | (got == ref))
     if bad.any():
         i = np.unravel_index(np.argmax(err - bound), err.shape)
         a = np.broadcast_to(np.asarray(atol, np.float64), err.shape)[i]

@@ -155,7 +155,7 @@ def test_linear_f32():
 
 # ------------------------------------------------------------------ attention
 
-def _attn_case(seed, B, T, S, nh, nkv, d, dtype, cache_layout=False, smax=None):
+def _attn_case(seed, B, T, S, nh, nkv, d, dtype, cache_layout=False, smax=None, fill=0.0):
     r = rng(seed)
     q = bf16_vals(r, (B, T, nh, d))
     k = bf16_vals(r, (B, S, nkv, d))
@@ -163,8 +163,8 @@ def _attn_case(seed, B, T, S, nh, nkv, d, dtype, cache_layout=False, smax=None):
     scale = 1 / math.sqrt(d)
     if cache_layout:
         smax = smax or S + 7
-        kc = torch.zeros(B, nkv, smax, d, dtype=dtype, device=DEV)
-        vc = torch.zeros(B, nkv, smax, d, dtype=dtype, device=DEV)
+        kc = torch.full((B, nkv, smax, d), fill, dtype=dtype, device=DEV)
+        vc = torch.full((B, nkv, smax, d), fill, dtype=dtype, device=DEV)
         kc[:, :, :S] = up(k, dtype).permute(0, 2, 1, 3)
         vc[:, :, :S] = up(v, dtype).permute(0, 2, 1, 3)
         kt = kc.permute(0, 2, 1, 3)[:, :S]
@@ -203,6 +203,13 @@ def test_attention_bf16(B, T, S, nh, nkv):
 @pytest.mark.parametrize("T,S", [(1, 33), (70, 200)])
 def test_attention_bf16_kv_cache_layout(T, S):
     _attn_case(T + S, 2, T, S, 12, 2, 128, BF, cache_layout=True)
+
+
+@pytest.mark.parametrize("T,S", [(1, 33), (70, 200), (130, 130)])
+def test_attention_bf16_never_reads_unused_cache_rows(T, S):
+    # cache rows past the sequence hold NaN: no masked or out-of-range key may
+    # reach the output (0 * NaN would)
+    _attn_case(T + S + 1, 2, T, S, 12, 2, 128, BF, cache_layout=True, fill=float("nan"))
 
 
 @pytest.mark.parametrize("B,T,S,nh,nkv,d", [(1, 16, 16, 4, 2, 32), (2, 1, 40, 4, 2, 32), (1, 5, 9, 3, 1, 48)])
