@@ -684,16 +684,16 @@ struct DecodePlan {
   int chunk, nsplit;
 };
 
-// Keys per split: 64 to start with, doubled while there would be more than
-// two workgroups per CU (each workgroup's partials cost a write and a read,
-// and longer key loops keep the double-buffered loads busy); then the splits
-// are evened out (multiples of 64 keys).
+// Splits per (sequence, KV head): as many as keep the grid within two
+// workgroups per CU (512 in all; each split's partials cost a write and a
+// read), each of at least 64 keys; then the split lengths are evened out
+// (multiples of 64 keys).  Filling the two slots of every CU matters for
+// long caches: at 1.5 workgroups per CU half the CUs stream twice the keys.
 DecodePlan plan_decode(int B, int s_max, int nkv) {
   DecodePlan p;
   const int64_t heads = static_cast<int64_t>(B) * nkv;
-  int chunk = 64;
-  while (chunk < 8192 && heads * cdiv(s_max, chunk) > 512) chunk *= 2;
-  const int nsplit = std::max(1, cdiv(s_max, chunk));
+  const int64_t fit = std::max<int64_t>(1, 512 / heads);
+  const int nsplit = static_cast<int>(std::min<int64_t>(std::max(1, cdiv(s_max, 64)), fit));
   p.chunk = cdiv(cdiv(s_max, nsplit), 64) * 64;
   p.nsplit = std::max(1, cdiv(s_max, p.chunk));
   return p;

@@ -106,35 +106,45 @@ __global__ void copy_ids_kernel(int64_t* dst, int64_t dst_stride, const int64_t*
 // for the next step (ids_buf), in the history at its position (len + pending),
 // optionally in `next`; resets the keys; then moves the device length on by
 // `pending` (the positions of this forward not yet counted).  One workgroup.
-__global__ __launch_bounds__(256) void finalize_kernel(unsigned long long* keys, int64_t* ids_buf, int64_t* hist,
-                                                       int64_t hist_ld, int* d_len, int pending, int64_t* next,
-                                                       int64_t next_stride, int B) {
-  __shared__ unsigned long long red[4];
+__global__ __launch_bounds__(1024) void finalize_kernel(unsigned long long* keys, int64_t* ids_buf, int64_t* hist,
+                                                        int64_t hist_ld, int* d_len, int pending, int64_t* next,
+                                                        int64_t next_stride, int B) {
+  // one wave per row, FIN_ROWS rows per wave at a time with their slot loads
+  // in flight together; lane i takes key slot i
+  static_assert(KEY_SLOTS == 64, "one key slot per lane");
+  constexpr int FIN_ROWS = 4;
   const int pos = *d_len + pending;
-  for (int b = 0; b < B; ++b) {
-    unsigned long long best = 0;
-    for (int i = threadIdx.x; i < KEY_SLOTS; i += 256) {
-      unsigned long long* slot = keys + b * KEY_ROW + i * KEY_STRIDE;
-      const unsigned long long k = *slot;
-      best = k > best ? k : best;
-      *slot = 0ull;
-    }
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  for (int b0 = wave * FIN_ROWS; b0 < B; b0 += nw * FIN_ROWS) {
+    unsigned long long best[FIN_ROWS];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const unsigned long long k = __shfl_xor(best, o, 64);
-      best = k > best ? k : best;
+    for (int r = 0; r < FIN_ROWS; ++r)
+      best[r] = b0 + r < B ? keys[static_cast<int64_t>(b0 + r) * KEY_ROW + lane * KEY_STRIDE] : 0ull;
+#pragma unroll
+    for (int r = 0; r < FIN_ROWS; ++r)
+      if (b0 + r < B) keys[static_cast<int64_t>(b0 + r) * KEY_ROW + lane * KEY_STRIDE] = 0ull;
+#pragma unroll
+    for (int r = 0; r < FIN_ROWS; ++r)
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long k = __shfl_xor(best[r], o, 64);
+        best[r] = k > best[r] ? k : best[r];
+      }
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < FIN_ROWS; ++r) {
+        const int b = b0 + r;
+        if (b >= B) break;
+        const int64_t id = static_cast<int64_t>(argmax_key_index(best[r]));
+        ids_buf[b] = id;
+        hist[b * hist_ld + pos] = id;
+        if (next) next[b * next_stride] = id;
+      }
     }
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int w = 1; w < 4; ++w) best = red[w] > best ? red[w] : best;
-      const int64_t id = static_cast<int64_t>(argmax_key_index(best));
-      ids_buf[b] = id;
-      hist[b * hist_ld + pos] = id;
-      if (next) next[b * next_stride] = id;
-    }
-    __syncthreads();
   }
+  __syncthreads();  // every wave has read *d_len
   if (threadIdx.x == 0 && pending) *d_len += pending;
 }
 
@@ -362,7 +372,7 @@ q2_status run_head(q2_model* m, int B, int Tc, int pending, float* logits, int64
   a.epi.ldo = ld_logits;
   a.epi.keys = m->keys;
   Q2_TRY(gemm(m, a, s));
-  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(256), 0, s, m->keys, m->ids_buf, m->hist,
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1024), 0, s, m->keys, m->ids_buf, m->hist,
                      static_cast<int64_t>(c.max_seq) + 1, m->d_len, pending, next, next_stride, B);
   return check_launch("finalize");
 }
