@@ -140,7 +140,7 @@ def dominant_kernel(wl, reps):
         out = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
         dt = time_launches(lambda: q2.q2_linear(out, X, W), reps, stream)
         flops = 2 * M * N * K
-        return {"kernel": "gemm_dtl_kernel (q2_linear, bf16, M=%d N=%d K=%d)" % (M, N, K),
+        return {"kernel": "gemm_dtl_mix_kernel (q2_linear, bf16, M=%d N=%d K=%d)" % (M, N, K),
                 "bound": "mfma", "achieved": flops / dt / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "flops_per_launch": flops, "avg_launch_us": dt * 1e6}
     # D: split-KV decode attention over a 4097-key cache for 64 sequences

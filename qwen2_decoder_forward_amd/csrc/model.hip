@@ -257,9 +257,12 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
       cur = nxt;
       pend_splits = 0;
     }
-    // with one query per sequence and split-KV partials, o_proj merges them itself
+    // with one query per sequence and split-KV partials, o_proj merges them
+    // itself -- when there are few: every o_proj workgroup merges all rows of
+    // its heads, so the merge reads grow with rows x splits (8 rows x 10
+    // splits cost more than the combine kernel and a plain product)
     const int nsplit = c.dtype == Q2_BF16 ? attention_decode_splits(B, Tc, c.max_seq, c.nh, c.nkv, d) : 0;
-    const bool merge_in_o = path.fused_norm && Tc == 1 && nsplit > 1;
+    const bool merge_in_o = path.fused_norm && Tc == 1 && nsplit > 1 && B * nsplit <= 16;
     {
       AttnArgs a{};
       a.leave_partials = merge_in_o;
