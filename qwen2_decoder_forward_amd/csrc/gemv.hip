@@ -556,6 +556,15 @@ GemvPlan plan_gemv(int M, int N, int K) {
         p.splits = spl;
       }
     }
+    // A split costs a reduction kernel, about as long as streaming 16 more
+    // blocks per workgroup: keep one split when that is no slower (7B
+    // products at batch 8: 224-288 tiles already occupy the chip).
+    int b1, s1;
+    fit(1, &b1, &s1);
+    if (s1 == 1 && work(1, b1) <= best + 16) {
+      p.bps = b1;
+      p.splits = 1;
+    }
   }
   return p;
 }
