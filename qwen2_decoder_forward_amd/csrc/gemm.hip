@@ -276,16 +276,20 @@ __device__ __forceinline__ int stg_idx(int r, int col) {
   return r * 128 + ((((col >> 3) ^ (r & 15)) << 3) | (col & 7));
 }
 
+// len0: position of token 0 of each sequence (QKV), read once per tile.
+// The four features fb0 + nl .. + 3 (nl % 4 == 0) take their bias as one
+// 8-byte load and the two RoPE (cos, sin) pairs as one 16-byte load.
 template <int EK>
 __device__ __forceinline__ void stg_put(uint16_t* sh, const Epi& e, int M, int fb0, int tb0, int r, int nl,
-                                        float x0, float x1, float x2, float x3) {
+                                        int len0, float x0, float x1, float x2, float x3) {
   const uint16_t* bias = static_cast<const uint16_t*>(e.bias);
   if constexpr (EK == EPI_STORE || EK == EPI_RESID) {
     if (EK == EPI_STORE && bias) {
-      x0 += bf2f(bias[fb0 + nl]);
-      x1 += bf2f(bias[fb0 + nl + 1]);
-      x2 += bf2f(bias[fb0 + nl + 2]);
-      x3 += bf2f(bias[fb0 + nl + 3]);
+      const uint2 bb = *reinterpret_cast<const uint2*>(bias + fb0 + nl);
+      x0 += bf_lo(bb.x);
+      x1 += bf_hi(bb.x);
+      x2 += bf_lo(bb.y);
+      x3 += bf_hi(bb.y);
     }
     const uint2 v = {pack_bf2(x0, x1), pack_bf2(x2, x3)};
     *reinterpret_cast<uint2*>(sh + stg_idx(r, nl)) = v;
@@ -296,18 +300,19 @@ __device__ __forceinline__ void stg_put(uint16_t* sh, const Epi& e, int M, int f
   } else if constexpr (EK == EPI_QKV) {
     // the block is one head (d = 128); q and k heads hold rotate-half pairs
     // in adjacent rows (2p: original p, 2p+1: original p + 64)
-    const float a0 = round_bf(x0 + bf2f(bias[fb0 + nl])), a1 = round_bf(x1 + bf2f(bias[fb0 + nl + 1]));
-    const float a2 = round_bf(x2 + bf2f(bias[fb0 + nl + 2])), a3 = round_bf(x3 + bf2f(bias[fb0 + nl + 3]));
+    const uint2 bb = *reinterpret_cast<const uint2*>(bias + fb0 + nl);
+    const float a0 = round_bf(x0 + bf_lo(bb.x)), a1 = round_bf(x1 + bf_hi(bb.x));
+    const float a2 = round_bf(x2 + bf_lo(bb.y)), a3 = round_bf(x3 + bf_hi(bb.y));
     const int head = fb0 >> 7;
     if (head < e.nh + e.nkv) {
       const int m = tb0 + r;
       const int p = nl >> 1;
       float2 c0 = make_float2(1.f, 0.f), c1 = c0;
       if (m < M) {
-        const int t = m % e.T;
-        const int64_t pos = (e.d_len ? *e.d_len : e.len0) + t;
-        c0 = e.rope[pos * 64 + p];
-        c1 = e.rope[pos * 64 + p + 1];
+        const int64_t pos = len0 + m % e.T;
+        const float4 cs = *reinterpret_cast<const float4*>(e.rope + pos * 64 + p);
+        c0 = make_float2(cs.x, cs.y);
+        c1 = make_float2(cs.z, cs.w);
       }
       const float ra0 = a0 * c0.x - a1 * c0.y, rb0 = a1 * c0.x + a0 * c0.y;
       const float ra1 = a2 * c1.x - a3 * c1.y, rb1 = a3 * c1.x + a2 * c1.y;
@@ -322,7 +327,7 @@ __device__ __forceinline__ void stg_put(uint16_t* sh, const Epi& e, int M, int f
 
 template <int EK, int ROWS>
 __device__ __forceinline__ void stg_copy_out(const uint16_t* sh, const Epi& e, int M, int N, int fb0, int tb0,
-                                             int lane) {
+                                             int lane, int len0) {
   constexpr int CPR = EK == EPI_SWIGLU ? 8 : 16;  // 16-byte chunks per row of the block
 #pragma unroll 4
   for (int it = 0; it < ROWS * CPR / 64; ++it) {
@@ -358,7 +363,7 @@ __device__ __forceinline__ void stg_copy_out(const uint16_t* sh, const Epi& e, i
       } else {
         const int bt = m / e.T;
         const int t = m - bt * e.T;
-        const int64_t pos = (e.d_len ? *e.d_len : e.len0) + t;
+        const int64_t pos = len0 + t;
         const bool isk = head < e.nh + e.nkv;
         uint16_t* base = static_cast<uint16_t*>(isk ? e.kc : e.vc);
         const int hh = isk ? head - e.nh : head - e.nh - e.nkv;
@@ -556,15 +561,16 @@ __device__ __forceinline__ void dtl_tile(const uint16_t* __restrict__ W, int64_t
   } else if constexpr (STAGED) {
     __syncthreads();  // every wave has finished reading the stages reused below
     uint16_t* sh = reinterpret_cast<uint16_t*>(dsm) + wave * (TM * 128);
+    const int len0 = EK == EPI_QKV ? (epi.d_len ? *epi.d_len : epi.len0) : 0;
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int j = 0; j < FM; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          stg_put<EK>(sh, epi, M, fb0, tb0, 32 * j + (lane & 31), 32 * i + 8 * v + 4 * (lane >> 5),
+          stg_put<EK>(sh, epi, M, fb0, tb0, 32 * j + (lane & 31), 32 * i + 8 * v + 4 * (lane >> 5), len0,
                       acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]);
-    stg_copy_out<EK, TM>(sh, epi, M, N, fb0, tb0, lane);
+    stg_copy_out<EK, TM>(sh, epi, M, N, fb0, tb0, lane, len0);
   } else {
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
@@ -629,6 +635,7 @@ bool dtl_ok(const GemmArgs& a) {
 bool staged_ok(const GemmArgs& a) {
   const Epi& e = a.epi;
   if (a.N % 8 != 0 || e.ldo % 8 != 0 || !aligned16(e.out)) return false;
+  if (e.bias && (reinterpret_cast<uintptr_t>(e.bias) & 7) != 0) return false;  // 8-byte bias loads
   switch (e.kind) {
     case EPI_STORE: return !e.out_f32;
     case EPI_RESID: return true;
