@@ -556,12 +556,12 @@ GemvPlan plan_gemv(int M, int N, int K) {
         p.splits = spl;
       }
     }
-    // A split costs a reduction kernel, about as long as streaming 16 more
+    // A split costs a reduction kernel, about as long as streaming 24 more
     // blocks per workgroup: keep one split when that is no slower (7B
     // products at batch 8: 224-288 tiles already occupy the chip).
     int b1, s1;
     fit(1, &b1, &s1);
-    if (s1 == 1 && work(1, b1) <= best + 16) {
+    if (s1 == 1 && work(1, b1) <= best + 24) {
       p.bps = b1;
       p.splits = 1;
     }
