@@ -164,6 +164,13 @@ struct GemmArgs {
   // split-K GEMV: leave the float32 partials in scratch and skip the
   // reduction kernel (a later product's prologue consumes them)
   bool defer_reduce;
+  // RESID product followed by an RMSNorm of the new residual rows: where the
+  // product's split-K reduction runs as a kernel of its own
+  // (gemm_post_norm), that kernel also writes RMSNorm(rows) * post_w to
+  // post_out (ld = N), exactly as the RMSNorm operator would
+  void* post_out;
+  const void* post_w;
+  float post_eps;
 };
 
 q2_status gemm_bf16(const GemmArgs& a, hipStream_t s);
@@ -184,7 +191,10 @@ int gemv_splits(int M, int N, int K);
 // Split-K partial bytes any bf16 decode-size product of this shape may need.
 size_t gemm_scratch_bytes(int M, int N, int K);
 // Sums split-K float32 partials partial[split][m][n] (a.scratch) in split
-// order and applies a.epi (not the argmax epilogue).
+// order and applies a.epi (not the argmax epilogue); with a.post_out and the
+// residual epilogue, also the RMSNorm of the new rows.
 q2_status split_reduce(const GemmArgs& a, int splits, hipStream_t s);
+// Whether gemm_bf16(a) writes a.post_out itself (else the caller norms).
+bool gemm_post_norm(const GemmArgs& a);
 
 }  // namespace q2

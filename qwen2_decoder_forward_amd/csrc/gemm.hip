@@ -860,7 +860,18 @@ size_t gemm_scratch_bytes(int M, int N, int K) {
   return b;
 }
 
-q2_status gemm_bf16(const GemmArgs& a, hipStream_t s) {
+bool gemm_post_norm(const GemmArgs& a) {
+  // the skinny path's split-K reduction of a residual product (rows of 16-byte
+  // chunks, row-contiguous output)
+  return a.post_out && a.post_w && a.epi.kind == EPI_RESID && a.M > 0 && skinny_shape(a.M, a.N, a.K) &&
+         dtl_ok(a) && !a.norm_w && !a.att_o && a.epi.ldo % 8 == 0 && aligned16(a.epi.out) &&
+         aligned16(a.post_out) && aligned16(a.post_w) && plan_skinny(a.M, a.N, a.K).splits > 1;
+}
+
+q2_status gemm_bf16(const GemmArgs& a_in, hipStream_t s) {
+  // the fused norm applies only where gemm_post_norm says so
+  GemmArgs a = a_in;
+  if (!gemm_post_norm(a)) a.post_out = nullptr;
   if (a.M == 0 || a.N == 0) return Q2_OK;
   Q2_CHECK(a.K % 8 == 0, Q2_ESHAPE, "bf16 linear: K=%d must be a multiple of 8", a.K);
   if (skinny_shape(a.M, a.N, a.K) && dtl_ok(a) && !a.norm_w && !a.att_o) {

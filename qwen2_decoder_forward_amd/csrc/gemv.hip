@@ -513,6 +513,86 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
   gemv_epilogue<EK>(epi, M, N, tl * 16, tl, m < M ? m : M, p, v0, v1);
 }
 
+// Split-K reduction of a residual product fused with the RMSNorm of the new
+// residual rows.  One workgroup per row m: each thread sums the partials of
+// its 8-feature chunks in split order and forms x = rnd(x + rnd(sum)) (the
+// residual epilogue's rounding), written back and kept in LDS; wave 0 then
+// takes the sum of squares in rmsnorm_vec_kernel's order (lane l: chunks l,
+// l + 64, ..., then the wave sum), and every thread writes
+// rnd((x * inv) * w) for its chunks -- the RMSNorm operator's result, bit for
+// bit.  N % 8 == 0.
+__global__ __launch_bounds__(256) void reduce_resid_norm_kernel(const float* __restrict__ partial, int splits, int M,
+                                                                int N, uint16_t* __restrict__ x, int64_t ldx,
+                                                                uint16_t* __restrict__ out,
+                                                                const uint16_t* __restrict__ w, float eps) {
+  extern __shared__ uint4 s_row[];  // the new row, N / 8 chunks
+  __shared__ float s_inv;
+  const int m = blockIdx.x;
+  const int nch = N >> 3;
+  uint16_t* xr = x + static_cast<int64_t>(m) * ldx;
+  for (int i = threadIdx.x; i < nch; i += 256) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // four splits' loads in flight at a time
+    for (int s0 = 0; s0 < splits; s0 += 4) {
+      float4 p0[4], p1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int sp = min(s0 + j, splits - 1);
+        const float4* q = reinterpret_cast<const float4*>(partial + (static_cast<int64_t>(sp) * M + m) * N + 8 * i);
+        p0[j] = q[0];
+        p1[j] = q[1];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (s0 + j < splits) {
+          a[0] += p0[j].x; a[1] += p0[j].y; a[2] += p0[j].z; a[3] += p0[j].w;
+          a[4] += p1[j].x; a[5] += p1[j].y; a[6] += p1[j].z; a[7] += p1[j].w;
+        }
+      }
+    }
+    const uint4 xv = *reinterpret_cast<const uint4*>(xr + 8 * i);
+    const uint32_t* xs = &xv.x;
+    uint4 xn;
+    uint32_t* ns = &xn.x;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      ns[k] = pack_bf2(round_bf(bf_lo(xs[k]) + round_bf(a[2 * k])), round_bf(bf_hi(xs[k]) + round_bf(a[2 * k + 1])));
+    *reinterpret_cast<uint4*>(xr + 8 * i) = xn;
+    s_row[i] = xn;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    float ss = 0.f;
+    for (int i = lane; i < nch; i += 64) {
+      const uint32_t* e = &s_row[i].x;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lo = bf_lo(e[k]), hi = bf_hi(e[k]);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) s_inv = 1.0f / sqrtf(ss / static_cast<float>(N) + eps);
+  }
+  __syncthreads();
+  const float inv = s_inv;
+  uint16_t* y = out + static_cast<int64_t>(m) * N;
+  for (int i = threadIdx.x; i < nch; i += 256) {
+    const uint4 xv = s_row[i];
+    const uint4 wv = *reinterpret_cast<const uint4*>(w + 8 * i);
+    const uint32_t* e = &xv.x;
+    const uint32_t* we = &wv.x;
+    uint4 r;
+    uint32_t* re = &r.x;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      re[k] = pack_bf2((bf_lo(e[k]) * inv) * bf_lo(we[k]), (bf_hi(e[k]) * inv) * bf_hi(we[k]));
+    *reinterpret_cast<uint4*>(y + 8 * i) = r;
+  }
+}
+
 struct GemvPlan {
   int mt, nw, splits, bps;
 };
@@ -639,6 +719,14 @@ bool gemv_can_defer(int M, int K) {
 }
 
 q2_status split_reduce(const GemmArgs& a, int splits, hipStream_t s) {
+  if (a.epi.kind == EPI_RESID && a.post_out) {
+    Q2_CHECK(a.N % 8 == 0 && a.epi.ldo % 8 == 0, Q2_EINVAL, "split reduce: fused norm needs N %% 8 == 0");
+    hipLaunchKernelGGL(reduce_resid_norm_kernel, dim3(a.M), dim3(256), static_cast<size_t>(a.N) * 2, s,
+                       static_cast<const float*>(a.scratch), splits, a.M, a.N, static_cast<uint16_t*>(a.epi.out),
+                       a.epi.ldo, static_cast<uint16_t*>(a.post_out), static_cast<const uint16_t*>(a.post_w),
+                       a.post_eps);
+    return check_launch("split_reduce_norm");
+  }
   const int pairs = a.M * cdiv(a.N, 16);
   switch (a.epi.kind) {
 #define Q2_REDUCE_CASE(EK_)                                                                                     \

@@ -217,13 +217,17 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
   // usual, for the head.
   void* cur = m->x;
   int pend_splits = 0;  // > 0: down-projection partials of the previous layer pending in gscratch
+  // without the fused norms: h already holds the RMSNorm of the residual rows
+  // (written by the previous residual product's split-K reduction)
+  bool h_ready = false;
   for (int l = 0; l < c.nlayer; ++l) {
     const q2_model::Layer& L = m->layers[l];
     void* kc = static_cast<char*>(m->kc) + l * m->kv_lstride * m->esize;
     void* vc = static_cast<char*>(m->vc) + l * m->kv_lstride * m->esize;
-    if (!path.fused_norm)
+    if (!path.fused_norm && !h_ready)
       Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->h), H, static_cast<const T*>(m->x), H,
                                static_cast<const T*>(L.w_in), M, H, c.eps, s));
+    h_ready = false;
     {
       GemmArgs a = gemm_args(m, L.w_qkv, H, path.fused_norm ? cur : m->h, H, M, m->qkv_out, H);
       void* nxt = cur;
@@ -307,11 +311,18 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
       a.epi.ldo = H;
       a.epi.sq_out = path.fused_norm ? m->sq : nullptr;
       a.epi.sq_ld = m->sq_ld;
+      if (!path.fused_norm && c.dtype == Q2_BF16) {
+        a.post_out = m->h;
+        a.post_w = L.w_post;
+        a.post_eps = c.eps;
+        h_ready = gemm_post_norm(a);
+      }
       Q2_TRY(gemm(m, a, s));
     }
-    if (!path.fused_norm)
+    if (!path.fused_norm && !h_ready)
       Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->h), H, static_cast<const T*>(m->x), H,
                                static_cast<const T*>(L.w_post), M, H, c.eps, s));
+    h_ready = false;
     {
       GemmArgs a = gemm_args(m, L.w_gu, H, path.fused_norm ? cur : m->h, H, M, 2 * c.inter, H);
       if (path.fused_norm) {
@@ -338,6 +349,12 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
           a.defer_reduce = true;
           pend_splits = sp;
         }
+      }
+      if (!path.fused_norm && c.dtype == Q2_BF16 && l + 1 < c.nlayer) {
+        a.post_out = m->h;
+        a.post_w = m->layers[l + 1].w_in;
+        a.post_eps = c.eps;
+        h_ready = gemm_post_norm(a);
       }
       Q2_TRY(gemm(m, a, s));
     }

@@ -206,15 +206,22 @@ def test_chunked_prefill_equals_one_shot_small_bf16():
     assert np.abs(one - two).max() <= 2e-2
 
 
-def test_fused_model_equals_unfused_operator_chain():
+@pytest.mark.parametrize("T", [7, 40])
+def test_fused_model_equals_unfused_operator_chain(T):
     """The model's fused kernels store what the chain of standalone operators
     (embedding, rms_norm, linear, rope, rearrange into the KV cache,
-    self_attention, linear, add, swiglu, argmax) stores."""
+    self_attention, linear, add, swiglu, argmax) stores.  7 tokens take the
+    GEMV path with its fused norms; 40 take the skinny split-K products, whose
+    residual reductions also write the following RMSNorm."""
     sh = SMALL_BF16
     w = synth.make_weights(sh, seed=6)
-    ids = np.array([[1, 2, 3, 500, 999, 0, 42]], np.int64)
-    T, H, nh, nkv, d, I = ids.shape[1], sh.hidden, sh.nh, sh.nkv, sh.dh, sh.inter
-    m = build_model(sh, w, 16, 1)
+    if T == 7:
+        ids = np.array([[1, 2, 3, 500, 999, 0, 42]], np.int64)
+    else:
+        ids = ((np.arange(T, dtype=np.int64) * 37 + 1) % sh.vocab)[None, :]
+    H, nh, nkv, d, I = sh.hidden, sh.nh, sh.nkv, sh.dh, sh.inter
+    smax = max(16, T)
+    m = build_model(sh, w, smax, 1)
     nxt_model, lg_model = m.prefill(torch.from_numpy(ids).to(DEV), logits=True)
     from tests.model_util import to_device
     W = {k: to_device(v) for k, v in w.items()}
@@ -223,8 +230,8 @@ def test_fused_model_equals_unfused_operator_chain():
     pos = torch.arange(T, dtype=torch.int64, device=DEV)
     x = torch.empty(T, H, dtype=bf, device=DEV)
     q2.q2_embedding(x, tid, W[("embed_tokens", -1)])
-    kc = torch.zeros(nkv, 16, d, dtype=bf, device=DEV)
-    vc = torch.zeros(nkv, 16, d, dtype=bf, device=DEV)
+    kc = torch.zeros(nkv, smax, d, dtype=bf, device=DEV)
+    vc = torch.zeros(nkv, smax, d, dtype=bf, device=DEV)
     for l in range(sh.nlayer):
         h = torch.empty_like(x)
         q2.q2_rms_norm(h, x, W[("input_layernorm", l)], sh.eps)
