@@ -236,7 +236,7 @@ __device__ __forceinline__ void gemv_epilogue(const Epi& epi, int M, int N, int 
   }
 }
 
-// gridDim.x = 16-row tiles, gridDim.y = K splits.  With SPLIT the float32
+// gridDim.x = workgroups along N, gridDim.y = K splits.  With SPLIT the float32
 // partial tile goes to partial[split][m][n] and gemv_reduce_kernel applies the
 // epilogue; otherwise the epilogue runs here.
 // With STAGE the X rows of this workgroup's K range are built in dynamic
@@ -264,9 +264,25 @@ __global__ __launch_bounds__(NW * 64, 1) void gemv_kernel(const uint16_t* __rest
   const int wave = tid >> 6;
   const int row = lane & 15;
   const int g = lane >> 4;
+  // This workgroup's tiles: blockIdx.x, + gridDim.x, ... over the whole
+  // rounds of the grid (adjacent workgroups stream adjacent tiles); the rows
+  // left over after them, which would give a last round to only some
+  // workgroups, are shared out evenly instead (an even number of rows each,
+  // the rest of the tile masked: its clamped loads hit L2).  The residual
+  // epilogue keeps whole tiles (it stores per-tile sums of squares).
   const int ntile = (N + 15) >> 4;
-  int tl = blockIdx.x;  // this workgroup's tiles: blockIdx.x, + gridDim.x, ...
-  int n0 = tl * 16;
+  const int G = gridDim.x;
+  const int nround = EK == EPI_RESID ? (ntile - blockIdx.x + G - 1) / G : ntile / G;
+  const int r_rest = nround * G * 16;  // first row of the shared-out rest (non-residual epilogues)
+  const int rest = N - r_rest;
+  const int rest_rows = EK == EPI_RESID || rest <= 0 ? 0 : ((rest + G - 1) / G + 1) & ~1;
+  int k_tile = 0;  // index of the current tile among this workgroup's
+  int n0 = blockIdx.x * 16;
+  int nlim = N;    // rows of the current tile at or past nlim are not stored
+  if (nround == 0) {
+    n0 = r_rest + blockIdx.x * rest_rows;
+    nlim = min(n0 + rest_rows, N);
+  }
   const int nkb = (K + KB - 1) / KB;
   const int kb0 = blockIdx.y * blocks_per_split;
   const int kb1 = min(kb0 + blocks_per_split, nkb);
@@ -280,7 +296,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemv_kernel(const uint16_t* __rest
   // read a clamped in-range address of real weights) so the compiler issues
   // them back to back.  The X operand is zero past K, so a clamped weight
   // adds nothing; results of out-of-range rows are never stored.
-  bool wrow_ok = n0 + row < N;
+  bool wrow_ok = n0 + row < nlim;
   const uint16_t* __restrict__ wp = W + static_cast<int64_t>(wrow_ok ? n0 + row : 0) * ldw + 8 * g;
   const uint4 z = {0, 0, 0, 0};
   constexpr int BATCH = 2;  // blocks whose weights are in flight at once per wave
@@ -299,7 +315,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemv_kernel(const uint16_t* __rest
   // the epilogue thread of (row tid / 8, pair tid % 8) loads its operands now
   constexpr bool PRE = !SPLIT && (EK == EPI_RESID || EK == EPI_QKV);
   EpiPre pre{};
-  if (PRE && tid < 16 * MT * 8) epi_preload<EK>(epi, M, N, n0, tid >> 3, tid & 7, pre);
+  if (PRE && tid < 16 * MT * 8) epi_preload<EK>(epi, M, nlim, n0, tid >> 3, tid & 7, pre);
 
   if constexpr (SRC == XSRC_NORMR) {
     // The pending residual add, then RMSNorm, row by row (one pass of the
@@ -424,15 +440,24 @@ __global__ __launch_bounds__(NW * 64, 1) void gemv_kernel(const uint16_t* __rest
 
   // the next tile's first weight batch goes out before this tile's
   // reduction and epilogue (the X rows in LDS serve every tile)
-  const int cur = tl, c0 = n0;
+  const int c0 = n0, cur = n0 >> 4, clim = nlim;
   const EpiPre pc = pre;
-  tl += gridDim.x;
-  if (tl < ntile) {
-    n0 = tl * 16;
-    wrow_ok = n0 + row < N;
+  ++k_tile;
+  bool more;
+  if (k_tile < nround) {
+    n0 = (blockIdx.x + k_tile * G) * 16;
+    nlim = N;
+    more = true;
+  } else {
+    n0 = r_rest + blockIdx.x * rest_rows;
+    nlim = min(n0 + rest_rows, N);
+    more = k_tile == nround && n0 < nlim;
+  }
+  if (more) {
+    wrow_ok = n0 + row < nlim;
     wp = W + static_cast<int64_t>(wrow_ok ? n0 + row : 0) * ldw + 8 * g;
     Q2_GEMV_LOAD_BATCH(kb0 + wave)
-    if (PRE && tid < 16 * MT * 8) epi_preload<EK>(epi, M, N, n0, tid >> 3, tid & 7, pre);
+    if (PRE && tid < 16 * MT * 8) epi_preload<EK>(epi, M, nlim, n0, tid >> 3, tid & 7, pre);
   }
 
   // sum the weight waves' partial tiles (fixed order)
@@ -459,7 +484,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemv_kernel(const uint16_t* __rest
   if constexpr (SPLIT) {
     for (int t = tid; t < M * 16; t += NW * 64) {
       const int m = t >> 4, f = t & 15;
-      if (c0 + f < N) partial[(static_cast<int64_t>(blockIdx.y) * M + m) * N + c0 + f] = tile[m][f];
+      if (c0 + f < clim) partial[(static_cast<int64_t>(blockIdx.y) * M + m) * N + c0 + f] = tile[m][f];
     }
   } else {
     const int Mp = 16 * MT;
@@ -469,12 +494,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemv_kernel(const uint16_t* __rest
       const int p = t & 7;
       const float v0 = m < Mp ? tile[m][2 * p] : 0.f;
       const float v1 = m < Mp ? tile[m][2 * p + 1] : 0.f;
-      gemv_epilogue<EK>(epi, M, N, c0, cur, m, p, v0, v1, PRE ? &pc : nullptr);
+      gemv_epilogue<EK>(epi, M, clim, c0, cur, m, p, v0, v1, PRE ? &pc : nullptr);
     }
   }
   // the next tile's reduction writes red only after every wave has passed
   // the barriers above, and tile only after the barrier that follows it
-  if (tl >= ntile) break;
+  if (!more) break;
   }
 #undef Q2_GEMV_LOAD_BATCH
 }
