@@ -692,28 +692,32 @@ SkinnyPlan plan_skinny(int M, int N, int K) {
 
 bool skinny_shape(int M, int N, int K) { return M > 16 && M <= 64 && K % 128 == 0 && N % 8 == 0; }
 
+// 64-token tiles run 4 waves (2 x 2 of 128 x 32): about a quarter faster
+// than 2 waves of 128 x 64 (more loads in flight per workgroup); 32-token
+// tiles have one 32-row MFMA block per wave column, so 2 waves.
 template <int EK, int BM>
 q2_status launch_skinny_cfg(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
-  using C = Dtl<256, BM, 2, 1>;
+  constexpr int WM = BM == 64 ? 2 : 1;
+  using C = Dtl<256, BM, 2, WM>;
   const int tiles = cdiv(a.N, 256);
   if constexpr (EK == EPI_ARGMAX) {
-    hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, 1, false, false>), dim3(tiles), dim3(C::NT), C::LDS_BYTES, s,
+    hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, WM, false, false>), dim3(tiles), dim3(C::NT), C::LDS_BYTES, s,
                        static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M,
                        a.K, 1, 0, nullptr, a.epi);
     return check_launch("gemm_skinny");
   } else {
     if (p.splits == 1) {
       if (staged_ok(a))
-        hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, 1, true, false>), dim3(tiles), dim3(C::NT), C::LDS_BYTES,
+        hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, WM, true, false>), dim3(tiles), dim3(C::NT), C::LDS_BYTES,
                            s, static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N,
                            a.M, a.K, 1, 0, nullptr, a.epi);
       else
-        hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, 1, false, false>), dim3(tiles), dim3(C::NT),
+        hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, WM, false, false>), dim3(tiles), dim3(C::NT),
                            C::LDS_BYTES, s, static_cast<const uint16_t*>(a.W), a.ldw,
                            static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M, a.K, 1, 0, nullptr, a.epi);
       return check_launch("gemm_skinny");
     }
-    hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, 1, false, true>), dim3(tiles, p.splits), dim3(C::NT),
+    hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, WM, false, true>), dim3(tiles, p.splits), dim3(C::NT),
                        C::LDS_BYTES, s, static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X),
                        a.ldx, a.N, a.M, a.K, 1, p.kt_split, static_cast<float*>(a.scratch), a.epi);
     Q2_TRY(check_launch("gemm_skinny"));
