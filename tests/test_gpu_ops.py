@@ -189,6 +189,7 @@ def _attn_case(seed, B, T, S, nh, nkv, d, dtype, cache_layout=False, smax=None, 
     (1, 2, 50, 12, 2),       # two queries per head group (12 rows) in the decode kernel
     (8, 1, 300, 28, 4),      # 7B-shaped group of 7
     (64, 1, 1000, 12, 2),    # decode batch: several 16-key blocks per wave (double-buffered loads)
+    (64, 1, 4097, 12, 2),    # the 64-sequence decode at its full cache length: 4 splits of 1088 keys
     (4, 1, 5000, 28, 4),     # long splits with a ragged last one
     (1, 64, 64, 12, 2),      # one full prefill block
     (1, 100, 300, 12, 2),    # prefill with a cached past, ragged
