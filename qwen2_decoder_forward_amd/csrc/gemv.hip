@@ -686,7 +686,11 @@ q2_status launch_gemv2(const GemmArgs& a, const GemvPlan& p, size_t lds, hipStre
                     static_cast<uint16_t*>(a.resid_out)};
   // at most two rounds of 16-wave workgroups on the chip; each loops over
   // its tiles with the next tile's weights in flight
-  const dim3 grid(std::min(cdiv(a.N, 16), std::max(1, GEMV_WGS / p.splits)), p.splits);
+  // (the residual epilogue needs whole 16-row tiles; the others may give a
+  // workgroup fewer rows, down to 8, when there are fewer tiles than slots)
+  const int wgs = std::max(1, GEMV_WGS / p.splits);
+  const int gx = EK == EPI_RESID ? std::min(cdiv(a.N, 16), wgs) : std::max(std::min(cdiv(a.N, 16), wgs), std::min(wgs, a.N / 8));
+  const dim3 grid(gx, p.splits);
   if (p.splits == 1) {
     hipLaunchKernelGGL((gemv_kernel<MT, NW, EK, SRC, STAGE, false>), grid, dim3(NW * 64), lds, s,
                        static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M,
