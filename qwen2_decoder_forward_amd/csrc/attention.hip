@@ -582,37 +582,36 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int ns
     }
 }
 
-// Merges the two halves of each split query block: thread (row r, half of d)
-// of block nqb - 1 - blockIdx.x.
+// Merges the two halves of each split query block.  Workgroup x of a head
+// takes rows 16 (x % 8) .. + 15 of block nqb - 1 - x / 8; 16 adjacent lanes
+// cover a row's 128 features in 32-byte pieces, so every load instruction
+// reads whole rows.
 __global__ __launch_bounds__(256) void attn_prefill_combine(AttnArgs a, int nsq, const float* __restrict__ part_o,
                                                             const float2* __restrict__ part_ml) {
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int i = blockIdx.x >> 3, h = blockIdx.y, b = blockIdx.z;
   const int nqb = (a.T + PF_QB - 1) / PF_QB;
   const int qb = nqb - 1 - i;
-  const int r = threadIdx.x >> 1;
-  const int d0 = (threadIdx.x & 1) * 64;
+  const int r = (blockIdx.x & 7) * 16 + (threadIdx.x >> 4);
+  const int d0 = (threadIdx.x & 15) * 8;
   const int tq = qb * PF_QB + r;
   if (tq >= a.T) return;
   const int64_t pi = ((static_cast<int64_t>(b) * a.nh + h) * nsq + i) * 2;
   const float2 ml0 = part_ml[pi * PF_QB + r], ml1 = part_ml[(pi + 1) * PF_QB + r];
+  const float4* p0 = reinterpret_cast<const float4*>(part_o + (pi * PF_QB + r) * D + d0);
+  const float4* p1 = reinterpret_cast<const float4*>(part_o + ((pi + 1) * PF_QB + r) * D + d0);
+  const float4 x0 = p0[0], x1 = p0[1], y0 = p1[0], y1 = p1[1];
   // the first half always holds key 0; the second may hold no visible key
   const float mx = fmaxf(ml0.x, ml1.x);
   const float w0 = __builtin_amdgcn_exp2f(ml0.x - mx);
   const float w1 = ml1.x == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(ml1.x - mx);
   const float inv = 1.f / (w0 * ml0.y + w1 * ml1.y);
-  const float4* p0 = reinterpret_cast<const float4*>(part_o + (pi * PF_QB + r) * D + d0);
-  const float4* p1 = reinterpret_cast<const float4*>(part_o + ((pi + 1) * PF_QB + r) * D + d0);
+  uint4 w;
+  w.x = pack_bf2((w0 * x0.x + w1 * y0.x) * inv, (w0 * x0.y + w1 * y0.y) * inv);
+  w.y = pack_bf2((w0 * x0.z + w1 * y0.z) * inv, (w0 * x0.w + w1 * y0.w) * inv);
+  w.z = pack_bf2((w0 * x1.x + w1 * y1.x) * inv, (w0 * x1.y + w1 * y1.y) * inv);
+  w.w = pack_bf2((w0 * x1.z + w1 * y1.z) * inv, (w0 * x1.w + w1 * y1.w) * inv);
   uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.o_bs + static_cast<int64_t>(tq) * a.o_ts + h * a.o_hs + d0;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const float4 x0 = p0[2 * c], x1 = p0[2 * c + 1], y0 = p1[2 * c], y1 = p1[2 * c + 1];
-    uint4 w;
-    w.x = pack_bf2((w0 * x0.x + w1 * y0.x) * inv, (w0 * x0.y + w1 * y0.y) * inv);
-    w.y = pack_bf2((w0 * x0.z + w1 * y0.z) * inv, (w0 * x0.w + w1 * y0.w) * inv);
-    w.z = pack_bf2((w0 * x1.x + w1 * y1.x) * inv, (w0 * x1.y + w1 * y1.y) * inv);
-    w.w = pack_bf2((w0 * x1.z + w1 * y1.z) * inv, (w0 * x1.w + w1 * y1.w) * inv);
-    *reinterpret_cast<uint4*>(op + 8 * c) = w;
-  }
+  *reinterpret_cast<uint4*>(op) = w;
 }
 
 // Query blocks of a prefill call whose key ranges are split (host view of
@@ -755,7 +754,7 @@ q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(attn_prefill_kernel, dim3(a.nh, nqb + nsq, a.B), dim3(256), 0, s, a, nsq, part_o, part_ml);
   Q2_TRY(check_launch("attn_prefill"));
   if (nsq == 0) return Q2_OK;
-  hipLaunchKernelGGL(attn_prefill_combine, dim3(nsq, a.nh, a.B), dim3(256), 0, s, a, nsq, part_o, part_ml);
+  hipLaunchKernelGGL(attn_prefill_combine, dim3(nsq * 8, a.nh, a.B), dim3(256), 0, s, a, nsq, part_o, part_ml);
   return check_launch("attn_prefill_combine");
 }
 
