@@ -265,6 +265,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
   if ((threadIdx.x & 15) == 0) part_ml[slot] = make_float2(M, L);
 }
 
+template <int SMAX>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nsplit, const float* __restrict__ part_o,
                                                            const float2* __restrict__ part_ml) {
   const int bg = blockIdx.x;
@@ -276,25 +277,52 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
   const int d0 = (threadIdx.x & 15) * 8;
   if (r >= R) return;
   const int64_t base_slot = static_cast<int64_t>(bg) * nsplit * 16 + r;
-  // branch-free and unrolled, so the partial loads of several splits are in
-  // flight together (a split with no keys has M = -inf, L = 0, o = 0 and
-  // contributes weight 0); the sums still run in split order
+  // Up to SMAX splits' partials are loaded before any is used (clamped
+  // indices: a fixed load count, one memory round trip); a split with no
+  // keys has M = -inf, L = 0, o = 0 and weight 0.  The maximum is taken over
+  // all splits first and the sums run in split order.
   float M = NEG_INF;
-#pragma unroll 8
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[base_slot + s * 16].x);
-  const float base = (M == NEG_INF) ? 0.f : M;
   float L = 0.f, o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  if (nsplit <= SMAX) {
+    float2 ml[SMAX];
+    float4 p0[SMAX], p1[SMAX];
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      const int64_t slot = base_slot + min(s, nsplit - 1) * 16;
+      ml[s] = part_ml[slot];
+      const float4* po = reinterpret_cast<const float4*>(part_o + slot * D + d0);
+      p0[s] = po[0];
+      p1[s] = po[1];
+    }
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s)
+      if (s < nsplit) M = fmaxf(M, ml[s].x);
+    const float base = (M == NEG_INF) ? 0.f : M;
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      if (s < nsplit) {
+        const float f = ml[s].x == NEG_INF ? 0.f : __expf(ml[s].x - base);
+        L += f * ml[s].y;
+        o[0] += f * p0[s].x; o[1] += f * p0[s].y; o[2] += f * p0[s].z; o[3] += f * p0[s].w;
+        o[4] += f * p1[s].x; o[5] += f * p1[s].y; o[6] += f * p1[s].z; o[7] += f * p1[s].w;
+      }
+    }
+  } else {
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[base_slot + s * 16].x);
+    const float base = (M == NEG_INF) ? 0.f : M;
 #pragma unroll 4
-  for (int s = 0; s < nsplit; ++s) {
-    const float2 ml = part_ml[base_slot + s * 16];
-    const float4* po = reinterpret_cast<const float4*>(part_o + (base_slot + s * 16) * D + d0);
-    const float4 p0 = po[0], p1 = po[1];
-    const float f = ml.x == NEG_INF ? 0.f : __expf(ml.x - base);
-    L += f * ml.y;
-    o[0] += f * p0.x; o[1] += f * p0.y; o[2] += f * p0.z; o[3] += f * p0.w;
-    o[4] += f * p1.x; o[5] += f * p1.y; o[6] += f * p1.z; o[7] += f * p1.w;
+    for (int s = 0; s < nsplit; ++s) {
+      const float2 ml = part_ml[base_slot + s * 16];
+      const float4* po = reinterpret_cast<const float4*>(part_o + (base_slot + s * 16) * D + d0);
+      const float4 p0 = po[0], p1 = po[1];
+      const float f = ml.x == NEG_INF ? 0.f : __expf(ml.x - base);
+      L += f * ml.y;
+      o[0] += f * p0.x; o[1] += f * p0.y; o[2] += f * p0.z; o[3] += f * p0.w;
+      o[4] += f * p1.x; o[5] += f * p1.y; o[6] += f * p1.z; o[7] += f * p1.w;
+    }
   }
   const int tt = r / group;
   const int hh = g * group + (r - tt * group);
@@ -734,7 +762,10 @@ q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
                        part_o, part_ml);
     Q2_TRY(check_launch("attn_decode"));
     if (p.nsplit > 1 && !a.leave_partials) {
-      hipLaunchKernelGGL(attn_combine_kernel, dim3(a.B * a.nkv), dim3(256), 0, s, a, p.nsplit, part_o, part_ml);
+      if (p.nsplit <= 8)
+        hipLaunchKernelGGL(attn_combine_kernel<8>, dim3(a.B * a.nkv), dim3(256), 0, s, a, p.nsplit, part_o, part_ml);
+      else
+        hipLaunchKernelGGL(attn_combine_kernel<16>, dim3(a.B * a.nkv), dim3(256), 0, s, a, p.nsplit, part_o, part_ml);
       Q2_TRY(check_launch("attn_combine"));
     }
     return Q2_OK;
