@@ -115,7 +115,10 @@ def test_rope_batched_in_place_large_theta():
                                    (300, 1536, 8960), (520, 264, 4096),
                                    # 256 x 256 tiles over whole rounds of the chip plus a
                                    # 128 x 256 tail (ragged rows and features)
-                                   (4000, 8600, 256)])
+                                   (4000, 8600, 256),
+                                   # odd feature counts: the GEMV's shared-out last rows end
+                                   # in an unpaired feature
+                                   (1, 257, 1536), (7, 1001, 640)])
 @pytest.mark.parametrize("bias,out_f32", [(True, False), (False, True)])
 def test_linear_bf16(M, N, K, bias, out_f32):
     r = rng(M * 1000 + N + K)
