@@ -140,3 +140,22 @@ def test_persistent_generate_continue_history():
     assert np.array_equal(outs[0][0], outs[1][0])
     assert np.array_equal(outs[0][1], outs[1][1])
     model.close()
+
+
+def test_persistent_workload_b_full_depth_teacher_forced():
+    """The 28-layer 1.5B model (prompt 64, 32 decode steps) on the persistent
+    path, teacher-forced against the oracle with the same bar as the graph
+    path's full-workload test."""
+    wl = synth.Workload("b-depth", synth.WORKLOADS["B"].shape, 1, 64, 32)
+    w = synth.make_weights(wl)
+    prompt = synth.make_prompt(wl)
+    model = build_model(wl.shape, w, wl.max_seq, 1)
+    model.set_decode_path(True)
+    assert model.decode_path(1)
+    orc = oracle.OracleModel(wl.shape, w, "bf16", 1, wl.max_seq)
+    orc64 = oracle.OracleModel(wl.shape, w, "bf16", 1, wl.max_seq, accum="f64")
+    r = teacher_forced(model, orc, prompt, wl.steps, orc64)
+    model.check()
+    model.close()
+    print(f"\n[persistent, full workload B] {r.summary()}", flush=True)
+    assert r.ok(), r.summary()
