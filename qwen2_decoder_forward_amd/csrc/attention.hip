@@ -354,7 +354,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
 // index swapped, which makes exactly those eight keys contiguous for the A
 // operand.  P is rounded to bf16 for that product.
 //
-// K rows (256 bytes) keep 16-byte chunk c of key r at c ^ (r & 15).  V^T
+// K rows are padded from 256 to 272 bytes (17 sixteen-byte slots), so the
+// 16 rows of a fragment read fall on 16 distinct slots of a 256-byte bank
+// line and every read address is one per-lane base plus a constant.  V^T
 // rows are padded to 72 keys (144 bytes, 9 sixteen-byte slots) and the
 // 8-key chunk k of row d sits at k ^ ((d / 16) % 8).  A fragment read (16
 // consecutive rows, one chunk) then lands on 16 distinct slots of a 256-byte
@@ -365,6 +367,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
 constexpr int PF_QB = 128;   // queries per workgroup
 constexpr int PF_KT = 64;    // keys per tile
 constexpr int PF_VT = 72;    // bf16 per V^T LDS row
+constexpr int PF_KR = 17;    // 16-byte slots per K LDS row
 
 __device__ __forceinline__ int pf_keyperm(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
@@ -385,13 +388,25 @@ __device__ __forceinline__ void pf_tile(const uint4* __restrict__ sKb, const uin
   for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) sacc[kh][e] = 0.f;
-    const int r = 32 * kh + qr;
+    // all eight fragments are read before the first product, so the reads
+    // overlap one another instead of each product waiting on its own
+    const uint4* kr = sKb + (32 * kh + qr) * PF_KR + hl;
+    uint4 kf[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint4 kfr = sKb[r * 16 + ((2 * ks + hl) ^ (r & 15))];
-      sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kfr), as_bf16x8(qf[ks]), sacc[kh], 0, 0, 0);
-    }
+    for (int ks = 0; ks < 8; ++ks) kf[ks] = kr[2 * ks];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[ks]), as_bf16x8(qf[ks]), sacc[kh], 0, 0, 0);
   }
+  // schedule: the first half's eight reads, then its products each followed
+  // by one read of the second half, then the second half's products
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   // running max of query qr's raw scores (lanes qr and qr + 32), masked
   // keys at -inf; the scale goes into one fma per probability:
   // p = exp2(s * scale * log2 e - m)
@@ -448,17 +463,27 @@ __device__ __forceinline__ void pf_tile(const uint4* __restrict__ sKb, const uin
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[dt][e] *= alpha;
   }
-  // O^T += V^T P^T
+  // O^T += V^T P^T.  Row 32 dt + qr has swizzle key 2 dt + qr / 16, so the
+  // lane's chunk 2 c + hl sits at 2 (c ^ dt) + (hl ^ qr / 16): a per-lane
+  // base plus a constant for each (dt, c).
+  const uint16_t* vl = sVtb + qr * PF_VT + 8 * (hl ^ (qr >> 4));
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
+    uint4 vf[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int vr = 32 * dt + qr;
-      const uint4 vfr =
-          *reinterpret_cast<const uint4*>(&sVtb[vr * PF_VT + ((16 * c + 8 * hl) ^ (((vr >> 4) & 7) << 3))]);
-      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vfr), pf[c], oacc[dt], 0, 0, 0);
-    }
+    for (int c = 0; c < 4; ++c) vf[c] = *reinterpret_cast<const uint4*>(vl + 32 * dt * PF_VT + 16 * (c ^ dt));
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[c]), pf[c], oacc[dt], 0, 0, 0);
   }
+  // schedule: four reads ahead of the products
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < 12; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
 // Grid (nh, items, B).  The nsq last query blocks (the longest causal rows)
@@ -468,7 +493,7 @@ __device__ __forceinline__ void pf_tile(const uint4* __restrict__ sKb, const uin
 // attn_prefill_combine.  The other blocks follow, last first, whole.
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int nsq, float* __restrict__ part_o,
                                                               float2* __restrict__ part_ml) {
-  __shared__ uint4 sK[2][PF_KT * 16];
+  __shared__ uint4 sK[2][PF_KT * PF_KR];
   __shared__ __attribute__((aligned(16))) uint16_t sVt[2][D * PF_VT];
 
   const int nqb = (a.T + PF_QB - 1) / PF_QB;
@@ -548,7 +573,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int ns
     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                  \
       const int q_ = tid + 256 * i;                                                                  \
       const int r_ = q_ >> 4;                                                                        \
-      sK[BUF_][r_ * 16 + ((q_ & 15) ^ (r_ & 15))] = RK_[i];                                          \
+      sK[BUF_][r_ * PF_KR + (q_ & 15)] = RK_[i];                                                     \
     }                                                                                                \
     store_vt4(sVt[BUF_], PF_VT, 8 * vc, pf_keyperm(4 * vg) ^ (((vc >> 1) & 7) << 3), RV_);           \
   }
