@@ -354,15 +354,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
 // index swapped, which makes exactly those eight keys contiguous for the A
 // operand.  P is rounded to bf16 for that product.
 //
-// K rows are padded from 256 to 272 bytes (17 sixteen-byte slots), so the
-// 16 rows of a fragment read fall on 16 distinct slots of a 256-byte bank
-// line and every read address is one per-lane base plus a constant.  V^T
-// rows are padded to 72 keys (144 bytes, 9 sixteen-byte slots) and the
-// 8-key chunk k of row d sits at k ^ ((d / 16) % 8).  A fragment read (16
-// consecutive rows, one chunk) then lands on 16 distinct slots of a 256-byte
-// bank line, and a transposing write (rows 8 apart, 8 bytes per lane) has
-// the 32 lanes of a half-wave fill both halves of 16 distinct slots: the
-// two 16-lane groups of a half-wave load key groups that share a chunk.
+// K rows are padded from 256 to 272 bytes (17 sixteen-byte slots), so every
+// fragment read address is one per-lane base plus a constant.  V^T rows are
+// padded to 72 keys (144 bytes) and the 8-key chunk k of row d sits at
+// k ^ ((d / 16) % 8).  Measured on gfx950 (SQ_LDS_BANK_CONFLICT of
+// single-wave probes of these exact access patterns): the K reads and writes
+// take no conflict cycles; the V^T fragment reads and the 8-byte transposing
+// writes conflict two ways.  160-byte V^T rows remove the read conflicts but
+// cost 4 KB more LDS and measured no faster, so the smaller tile stays.
 
 constexpr int PF_QB = 128;   // queries per workgroup
 constexpr int PF_KT = 64;    // keys per tile
