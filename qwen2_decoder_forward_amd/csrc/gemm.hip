@@ -666,19 +666,24 @@ q2_status launch_dtl_cfg(const GemmArgs& a, hipStream_t s) {
 //
 // 17..64 token rows: too many for the GEMV (whose workgroups own 16 weight
 // rows each, so every workgroup would re-read all of X from L2) and too few
-// for the big tiles.  The direct-to-LDS kernel with 256 weight rows and all
-// token rows (32 or 64) per tile streams W once; K is split over workgroups
-// until the chip has work, as long as the float32 partials stay below a
-// quarter of the weight bytes (or 8 MB, which the L2 and MALL absorb).  The LM head (argmax epilogue) needs no split.
+// for the big tiles.  The direct-to-LDS kernel with 256 weight rows (128 when
+// that gives fewer than 32 tiles: twice the workgroups for the products with
+// few output features, QKV, o_proj and down at hidden 1536) and all token
+// rows (32 or 64) per tile streams W once; K is split over workgroups until
+// the chip has work, as long as the float32 partials stay below a quarter of
+// the weight bytes (or 8 MB, which the L2 and MALL absorb).  The LM head
+// (argmax epilogue) needs no split.
 
 struct SkinnyPlan {
   int bm, splits, kt_split;  // kt_split: 32-wide K slices per split (a multiple of 4)
+  int bn = 256;               // weight rows per tile: 256 or 128
 };
 
 SkinnyPlan plan_skinny(int M, int N, int K) {
   SkinnyPlan p;
   p.bm = M <= 32 ? 32 : 64;
-  const int tiles = cdiv(N, 256);
+  p.bn = cdiv(N, 256) < 32 ? 128 : 256;
+  const int tiles = cdiv(N, p.bn);
   const int nblk = K / 128;
   const double wbytes = 2.0 * N * K, per_split = 4.0 * M * N;
   const double cap = std::max(wbytes / 4, 8.0 * (1 << 20));
@@ -692,32 +697,34 @@ SkinnyPlan plan_skinny(int M, int N, int K) {
 
 bool skinny_shape(int M, int N, int K) { return M > 16 && M <= 64 && K % 128 == 0 && N % 8 == 0; }
 
-// 64-token tiles run 4 waves (2 x 2 of 128 x 32): about a quarter faster
-// than 2 waves of 128 x 64 (more loads in flight per workgroup); 32-token
-// tiles have one 32-row MFMA block per wave column, so 2 waves.
-template <int EK, int BM>
+// 64-token tiles run 2 x 2 waves of 128 x 32 (256 weight rows; 1 x 2 for
+// 128): about a quarter faster than 2 waves of 128 x 64 (more loads in
+// flight per workgroup); 32-token tiles have one 32-row MFMA block per wave
+// column.
+template <int EK, int BM, int BN>
 q2_status launch_skinny_cfg(const GemmArgs& a, const SkinnyPlan& p, hipStream_t s) {
   constexpr int WM = BM == 64 ? 2 : 1;
-  using C = Dtl<256, BM, 2, WM>;
-  const int tiles = cdiv(a.N, 256);
+  constexpr int WN = BN / 128;
+  using C = Dtl<BN, BM, WN, WM>;
+  const int tiles = cdiv(a.N, BN);
   if constexpr (EK == EPI_ARGMAX) {
-    hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, WM, false, false>), dim3(tiles), dim3(C::NT), C::LDS_BYTES, s,
+    hipLaunchKernelGGL((gemm_dtl_kernel<EK, BN, BM, WN, WM, false, false>), dim3(tiles), dim3(C::NT), C::LDS_BYTES, s,
                        static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M,
                        a.K, 1, 0, nullptr, a.epi);
     return check_launch("gemm_skinny");
   } else {
     if (p.splits == 1) {
       if (staged_ok(a))
-        hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, WM, true, false>), dim3(tiles), dim3(C::NT), C::LDS_BYTES,
+        hipLaunchKernelGGL((gemm_dtl_kernel<EK, BN, BM, WN, WM, true, false>), dim3(tiles), dim3(C::NT), C::LDS_BYTES,
                            s, static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N,
                            a.M, a.K, 1, 0, nullptr, a.epi);
       else
-        hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, WM, false, false>), dim3(tiles), dim3(C::NT),
+        hipLaunchKernelGGL((gemm_dtl_kernel<EK, BN, BM, WN, WM, false, false>), dim3(tiles), dim3(C::NT),
                            C::LDS_BYTES, s, static_cast<const uint16_t*>(a.W), a.ldw,
                            static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M, a.K, 1, 0, nullptr, a.epi);
       return check_launch("gemm_skinny");
     }
-    hipLaunchKernelGGL((gemm_dtl_kernel<EK, 256, BM, 2, WM, false, true>), dim3(tiles, p.splits), dim3(C::NT),
+    hipLaunchKernelGGL((gemm_dtl_kernel<EK, BN, BM, WN, WM, false, true>), dim3(tiles, p.splits), dim3(C::NT),
                        C::LDS_BYTES, s, static_cast<const uint16_t*>(a.W), a.ldw, static_cast<const uint16_t*>(a.X),
                        a.ldx, a.N, a.M, a.K, 1, p.kt_split, static_cast<float*>(a.scratch), a.epi);
     Q2_TRY(check_launch("gemm_skinny"));
@@ -733,8 +740,12 @@ q2_status launch_skinny(const GemmArgs& a, hipStream_t s) {
     const size_t need = static_cast<size_t>(p.splits) * a.M * a.N * sizeof(float);
     Q2_CHECK(a.scratch && a.scratch_bytes >= need, Q2_EINVAL, "skinny linear: split-K scratch too small");
   }
-  if (p.bm == 32) return launch_skinny_cfg<EK, 32>(a, p, s);
-  return launch_skinny_cfg<EK, 64>(a, p, s);
+  if (p.bn == 128) {
+    if (p.bm == 32) return launch_skinny_cfg<EK, 32, 128>(a, p, s);
+    return launch_skinny_cfg<EK, 64, 128>(a, p, s);
+  }
+  if (p.bm == 32) return launch_skinny_cfg<EK, 32, 256>(a, p, s);
+  return launch_skinny_cfg<EK, 64, 256>(a, p, s);
 }
 
 // Tile shape by how many tiles the product has for 256 CUs:

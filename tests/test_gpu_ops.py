@@ -111,6 +111,9 @@ def test_rope_batched_in_place_large_theta():
                                    # 17..64 rows with K % 128 == 0: the skinny tiles, split over K or not
                                    (17, 520, 384), (24, 264, 1024), (48, 1536, 8960), (64, 2048, 1536),
                                    (64, 17920, 1536),
+                                   # 128-row skinny tiles (fewer than 32 of 256 rows): ragged
+                                   # last tile with 32 token rows, and the largest such N
+                                   (30, 3000, 1536), (40, 7936, 256),
                                    # long K with few output tiles
                                    (300, 1536, 8960), (520, 264, 4096),
                                    # 256 x 256 tiles over whole rounds of the chip plus a
