@@ -19,15 +19,23 @@ sections 3.2 fourth layer and 3.5):
 
 Storage model ("bf16" mode): every operator output is rounded to bf16 before
 the next operator reads it, following section 3.3 item 3 of the report (low
-precision storage, float compute, low precision write-back).  The rounding
-points are: q/k/v after the bias add and again after RoPE, the attention
-output, o_proj output, each residual sum, each RMSNorm output, gate and up
-outputs, the SwiGLU output and the down output.  The logits stay float32 and
-argmax runs on them.  "fp32" mode performs no rounding (the tiny fp32 model).
+precision storage, float compute, low precision write-back).  Every rounding
+goes through ``_st`` with the name of its storage point: the embedding row
+("embed"), each RMSNorm output ("attn_norm", "mlp_norm", "final_norm"), q/k/v
+after the bias add ("q", "k", "v") and q/k again after RoPE ("q_rope",
+"k_rope"), the attention output ("attn"), the o_proj and down outputs
+("o_proj", "down"), each residual sum ("resid_attn", "resid_mlp"), gate and
+up ("gate", "up") and the SwiGLU output ("swiglu").  The logits stay float32
+and argmax runs on them.  "fp32" mode performs no rounding (the tiny fp32
+model).
 
-Pinned by: the operator pins, an fp64 brute-force forward on tiny shapes, the
-KV-cache decode equalling a full recompute of the prefix, batch independence,
-and the closed form when every o_proj and down weight is zero.
+Pinned by: the operator pins, an fp64 brute-force forward on tiny shapes (fp32
+mode), a loop-written bf16 forward that rounds at the same named points with
+float64 sums (bf16 mode: identical stored values, logits to float32 rounding;
+each storage point dropped in turn, or a rounding added inside RMSNorm or
+SwiGLU, fails it), the KV-cache decode equalling a full recompute of the
+prefix, batch independence, and the closed form when every o_proj and down
+weight is zero.
 """
 from __future__ import annotations
 
@@ -65,12 +73,22 @@ class OracleModel:
         self.k_cache = [np.zeros((batch, nkv, max_seq, d), F32) for _ in range(L)]
         self.v_cache = [np.zeros((batch, nkv, max_seq, d), F32) for _ in range(L)]
         self.length = 0
+        self.record = None
 
     def reset(self):
         self.length = 0
 
-    def _st(self, x):
-        return ops.bf16_round(x) if self.storage == "bf16" else np.asarray(x, F32)
+    def _st(self, x, point=None):
+        """The write-back of one operator output (``point`` names it).
+
+        bf16 storage rounds to bf16 here and nowhere else; fp32 storage keeps
+        the float32 value.  When ``self.record`` is a dict, the stored value
+        is appended under its point name (for the tests that check where the
+        forward rounds)."""
+        y = ops.bf16_round(x) if self.storage == "bf16" else np.asarray(x, F32)
+        if self.record is not None and point is not None:
+            self.record.setdefault(point, []).append(y.copy())
+        return y
 
     def _weight(self, name, layer=-1):
         return self.w[(name, layer)]
@@ -112,38 +130,38 @@ class OracleModel:
         scale = 1.0 / np.sqrt(d)
 
         if embeds is not None:
-            x = st(embeds)
+            x = st(embeds, "embed")
         else:
-            x = st(ops.embedding(ids.reshape(-1), self._weight("embed_tokens"))).reshape(B, T, H)
+            x = st(ops.embedding(ids.reshape(-1), self._weight("embed_tokens")), "embed").reshape(B, T, H)
         lin = self._linear
         for l in (layers if layers is not None else range(sh.nlayer)):
             W = lambda n: self._weight(n, l)          # noqa: E731
-            h = st(ops.rms_norm(x, W("input_layernorm"), sh.eps))
-            q = st(lin(h, W("q_proj.weight"), W("q_proj.bias"))).reshape(B, T, nh, d)
-            k = st(lin(h, W("k_proj.weight"), W("k_proj.bias"))).reshape(B, T, nkv, d)
-            v = st(lin(h, W("v_proj.weight"), W("v_proj.bias"))).reshape(B, T, nkv, d)
+            h = st(ops.rms_norm(x, W("input_layernorm"), sh.eps), "attn_norm")
+            q = st(lin(h, W("q_proj.weight"), W("q_proj.bias")), "q").reshape(B, T, nh, d)
+            k = st(lin(h, W("k_proj.weight"), W("k_proj.bias")), "k").reshape(B, T, nkv, d)
+            v = st(lin(h, W("v_proj.weight"), W("v_proj.bias")), "v").reshape(B, T, nkv, d)
             o = np.empty((B, T, nh, d), F32)
             for b in range(B):
-                qb = st(ops.rope(q[b], pos, sh.theta))
-                kb = st(ops.rope(k[b], pos, sh.theta))
+                qb = st(ops.rope(q[b], pos, sh.theta), "q_rope")
+                kb = st(ops.rope(k[b], pos, sh.theta), "k_rope")
                 self.k_cache[l][b, :, P:P + T, :] = kb.transpose(1, 0, 2)
                 self.v_cache[l][b, :, P:P + T, :] = v[b].transpose(1, 0, 2)
                 kc = self.k_cache[l][b, :, :P + T, :].transpose(1, 0, 2)
                 vc = self.v_cache[l][b, :, :P + T, :].transpose(1, 0, 2)
-                o[b] = st(ops.attention(qb, kc, vc, scale))
-            a = st(lin(o.reshape(B, T, nh * d), W("o_proj.weight")))
-            x = st(ops.add(x, a))
-            h2 = st(ops.rms_norm(x, W("post_attention_layernorm"), sh.eps))
-            g = st(lin(h2, W("gate_proj.weight")))
-            u = st(lin(h2, W("up_proj.weight")))
-            m = st(ops.swiglu(g, u))
-            dn = st(lin(m, W("down_proj.weight")))
-            x = st(ops.add(x, dn))
+                o[b] = st(ops.attention(qb, kc, vc, scale), "attn")
+            a = st(lin(o.reshape(B, T, nh * d), W("o_proj.weight")), "o_proj")
+            x = st(ops.add(x, a), "resid_attn")
+            h2 = st(ops.rms_norm(x, W("post_attention_layernorm"), sh.eps), "mlp_norm")
+            g = st(lin(h2, W("gate_proj.weight")), "gate")
+            u = st(lin(h2, W("up_proj.weight")), "up")
+            m = st(ops.swiglu(g, u), "swiglu")
+            dn = st(lin(m, W("down_proj.weight")), "down")
+            x = st(ops.add(x, dn), "resid_mlp")
             if hidden is not None:
                 hidden.append(x.copy())
         self.length = P + T
         xs = x if all_logits else x[:, -1, :]
-        hf = st(ops.rms_norm(xs, self._weight("norm"), sh.eps))
+        hf = st(ops.rms_norm(xs, self._weight("norm"), sh.eps), "final_norm")
         logits = lin(hf, self._weight("lm_head"))
         nxt, _ = ops.argmax(logits if not all_logits else logits[:, -1, :])
         return logits, nxt

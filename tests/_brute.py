@@ -2,18 +2,50 @@
 
 An independent second reading of the same definition, written element by
 element with explicit indices so that a transposed operand, a wrong head
-mapping or a dropped term in the NumPy oracle shows up as a mismatch.  It
-performs no bf16 rounding: it pins the oracle's "fp32" mode.
+mapping or a dropped term in the NumPy oracle shows up as a mismatch.
+
+With ``bf16_storage=True`` it also applies the low-precision write-back of
+"LLAISYS 训练营结项报告" section 3.3 item 3 (store bf16, compute float, write
+back bf16) at the storage points the forward takes: the embedding row, each
+RMSNorm output, q/k/v after the bias, q and k again after RoPE, the attention
+output, the o_proj and down products, each residual sum, gate and up, the
+SwiGLU output.  Logits stay unrounded.  The rounding is a pure-Python
+round-to-nearest-even of the float64 value to 8 significant bits
+(``bf16``), written from the format's definition, not from the oracle's
+bit-pattern routine.  This pins where the oracle's bf16 mode rounds.
 """
 import math
+import struct
+
+
+def bf16_bits_to_float(b):
+    """The number a bf16 bit pattern encodes: the upper half of a float32."""
+    return struct.unpack("<f", struct.pack("<I", (int(b) & 0xFFFF) << 16))[0]
+
+
+def bf16(x):
+    """Round a Python float to the nearest bfloat16 value (8 significant
+    bits, exponent range of float32), ties to even."""
+    if x == 0.0 or math.isinf(x) or math.isnan(x):
+        return x
+    m, e = math.frexp(x)            # x = m * 2**e, 0.5 <= |m| < 1
+    e = max(e, -125)                # below 2**-126 the format is subnormal: fixed step 2**-133
+    step = math.ldexp(1.0, e - 8)
+    return round(x / step) * step   # round() on a float ties to even
+
+
+def _num(v, bits):
+    return bf16_bits_to_float(v) if bits else float(v)
 
 
 def _vec(a):
-    return [float(v) for v in a]
+    bits = str(a.dtype) == "uint16"
+    return [_num(v, bits) for v in a]
 
 
 def _mat(a):
-    return [[float(v) for v in row] for row in a]
+    bits = str(a.dtype) == "uint16"
+    return [[_num(v, bits) for v in row] for row in a]
 
 
 def rmsnorm(x, w, eps):
@@ -52,8 +84,10 @@ def silu(g):
 
 
 class BruteModel:
-    def __init__(self, shape, weights):
+    def __init__(self, shape, weights, bf16_storage=False):
         self.sh = shape
+        self.bf16 = bf16_storage
+        self.record = {}            # storage point -> list of stored vectors, in order
         self.W = {}
         for key, arr in weights.items():
             self.W[key] = _mat(arr) if arr.ndim == 2 else _vec(arr)
@@ -61,25 +95,39 @@ class BruteModel:
         self.V = [[[] for _ in range(shape.nkv)] for _ in range(shape.nlayer)]
         self.pos = 0
 
+    def _store(self, point, vec):
+        out = [bf16(v) for v in vec] if self.bf16 else vec
+        self.record.setdefault(point, []).append(out)
+        return out
+
     def step(self, token):
         """Process one token of a single sequence; returns its logits (list)."""
         sh = self.sh
         d, nh, nkv = sh.dh, sh.nh, sh.nkv
         grp = nh // nkv
-        x = list(self.W[("embed_tokens", -1)][token])
+        st = self._store
+        x = st("embed", list(self.W[("embed_tokens", -1)][token]))
         for l in range(sh.nlayer):
             W = lambda n: self.W[(n, l)]  # noqa: E731
-            h = rmsnorm(x, W("input_layernorm"), sh.eps)
-            q = matvec(W("q_proj.weight"), h, W("q_proj.bias"))
-            k = matvec(W("k_proj.weight"), h, W("k_proj.bias"))
-            v = matvec(W("v_proj.weight"), h, W("v_proj.bias"))
+            h = st("attn_norm", rmsnorm(x, W("input_layernorm"), sh.eps))
+            q = st("q", matvec(W("q_proj.weight"), h, W("q_proj.bias")))
+            k = st("k", matvec(W("k_proj.weight"), h, W("k_proj.bias")))
+            v = st("v", matvec(W("v_proj.weight"), h, W("v_proj.bias")))
+            krot = []
             for g in range(nkv):
-                self.K[l][g].append(rope_head(k[g * d:(g + 1) * d], self.pos, sh.theta))
+                krot += rope_head(k[g * d:(g + 1) * d], self.pos, sh.theta)
+            krot = st("k_rope", krot)
+            for g in range(nkv):
+                self.K[l][g].append(krot[g * d:(g + 1) * d])
                 self.V[l][g].append(v[g * d:(g + 1) * d])
+            qrot = []
+            for hh in range(nh):
+                qrot += rope_head(q[hh * d:(hh + 1) * d], self.pos, sh.theta)
+            qrot = st("q_rope", qrot)
             att = []
             for hh in range(nh):
                 g = hh // grp
-                qh = rope_head(q[hh * d:(hh + 1) * d], self.pos, sh.theta)
+                qh = qrot[hh * d:(hh + 1) * d]
                 keys = self.K[l][g]
                 scores = [sum(qh[i] * kk[i] for i in range(d)) / math.sqrt(d) for kk in keys]
                 m = max(scores)
@@ -90,14 +138,15 @@ class BruteModel:
                     for i in range(d):
                         o[i] += e[j] / z * vv[i]
                 att += o
-            a = matvec(W("o_proj.weight"), att)
-            x = [x[i] + a[i] for i in range(len(x))]
-            h2 = rmsnorm(x, W("post_attention_layernorm"), sh.eps)
-            gt = matvec(W("gate_proj.weight"), h2)
-            up = matvec(W("up_proj.weight"), h2)
-            mm = [silu(gt[i]) * up[i] for i in range(len(gt))]
-            dn = matvec(W("down_proj.weight"), mm)
-            x = [x[i] + dn[i] for i in range(len(x))]
+            att = st("attn", att)
+            a = st("o_proj", matvec(W("o_proj.weight"), att))
+            x = st("resid_attn", [x[i] + a[i] for i in range(len(x))])
+            h2 = st("mlp_norm", rmsnorm(x, W("post_attention_layernorm"), sh.eps))
+            gt = st("gate", matvec(W("gate_proj.weight"), h2))
+            up = st("up", matvec(W("up_proj.weight"), h2))
+            mm = st("swiglu", [silu(gt[i]) * up[i] for i in range(len(gt))])
+            dn = st("down", matvec(W("down_proj.weight"), mm))
+            x = st("resid_mlp", [x[i] + dn[i] for i in range(len(x))])
         self.pos += 1
-        hf = rmsnorm(x, self.W[("norm", -1)], sh.eps)
+        hf = st("final_norm", rmsnorm(x, self.W[("norm", -1)], sh.eps))
         return matvec(self.W[("lm_head", -1)], hf)

@@ -314,3 +314,114 @@ def check_zero_mixers_closed_form(model_cls):
         e = E[ids[0, t]]
         hf = e / np.sqrt(np.mean(e * e) + sh.eps) * wf
         assert np.allclose(logits[0, t], Wl @ hf, rtol=1e-5, atol=1e-6)
+
+
+# ----------------------------------------------------------------------------- bf16 write-back points
+
+# The storage points of the bf16 forward, in the order one layer stores them
+# (plus the embedding row before the layers and the final norm after them).
+BF16_POINTS = ("embed", "attn_norm", "q", "k", "v", "k_rope", "q_rope", "attn", "o_proj", "resid_attn",
+               "mlp_norm", "gate", "up", "swiglu", "down", "resid_mlp", "final_norm")
+LAYER_POINTS = BF16_POINTS[1:-1]
+
+
+def tiny_bf16_shape(nlayer=2):
+    from synth import ModelShape
+    return ModelShape("pin-tiny-bf16", "bf16", nlayer, 32, 4, 2, 8, 48, 64, 10000.0, 1e-6)
+
+
+def _oracle_points(rec, shape, calls):
+    """Oracle record -> {point: float64 array [tokens, layers, n]} (one sequence)."""
+    L = shape.nlayer
+    out = {}
+    for p, entries in rec.items():
+        if p in ("embed", "final_norm"):
+            rows = [np.asarray(e, np.float64).reshape(-1, np.asarray(e).shape[-1]) for e in entries]
+            out[p] = np.concatenate(rows)[:, None, :]
+            continue
+        per_call = []
+        i = 0
+        for T in calls:
+            layers = []
+            for _ in range(L):
+                layers.append(np.asarray(entries[i], np.float64).reshape(T, -1))
+                i += 1
+            per_call.append(np.stack(layers, axis=1))
+        out[p] = np.concatenate(per_call)
+    return out
+
+
+def _brute_points(rec, shape):
+    L = shape.nlayer
+    out = {}
+    for p, entries in rec.items():
+        a = np.asarray(entries, np.float64)
+        out[p] = a[:, None, :] if p in ("embed", "final_norm") else a.reshape(-1, L, a.shape[-1])
+    return out
+
+
+def run_bf16_writeback(model_cls):
+    """Run the bf16-storage model and the loop-written bf16 forward on the
+    same tiny input (a 5-token prefill, then 3 decode steps); return both
+    point records and both logit sequences."""
+    import synth
+    sh = tiny_bf16_shape()
+    w = synth.make_weights(sh, seed=31)
+    # q and k weights and biases scaled by 16 (exact on bf16 bit patterns: the
+    # exponent field grows by 4) so that the scores spread over several units
+    # and the softmax is sensitive to the rounding of q and k
+    for l in range(sh.nlayer):
+        for n in ("q_proj.weight", "q_proj.bias", "k_proj.weight", "k_proj.bias"):
+            b = w[(n, l)]
+            nz = (b & np.uint16(0x7FFF)) != 0
+            w[(n, l)] = np.where(nz, b + np.uint16(4 << 7), b).astype(np.uint16)
+    prompt = np.array([[3, 17, 39, 0, 22]], np.int64)
+    m = model_cls(sh, w, "bf16", 1, 16)
+    m.record = {}
+    logits, nxt = m.forward(prompt, all_logits=True)
+    got_logits = [logits[0, t] for t in range(prompt.shape[1])]
+    brute = _brute.BruteModel(sh, w, bf16_storage=True)
+    ref_logits = [brute.step(int(t)) for t in prompt[0]]
+    calls = [prompt.shape[1]]
+    tok = int(nxt[0])
+    for _ in range(3):
+        lg, nx = m.forward(np.array([[tok]]))
+        got_logits.append(lg[0])
+        ref_logits.append(brute.step(tok))
+        calls.append(1)
+        tok = int(nx[0])
+    return (_oracle_points(m.record, sh, calls), _brute_points(brute.record, sh),
+            np.array(got_logits, np.float64), np.array(ref_logits, np.float64))
+
+
+def check_bf16_writeback_points(model_cls):
+    """Every stored intermediate of the bf16 forward is a bf16 number, at
+    exactly the storage points of the low-precision write-back rule."""
+    got, _, logits, _ = run_bf16_writeback(model_cls)
+    assert set(got) == set(BF16_POINTS), sorted(set(got) ^ set(BF16_POINTS))
+    for p, a in got.items():
+        a32 = a.astype(np.float32)
+        assert np.array_equal(a32.astype(np.float64), a), p
+        assert not (a32.view(np.uint32) & np.uint32(0xFFFF)).any(), f"{p}: not a bf16 value"
+    # the logits are float32 results, not bf16
+    assert (logits.astype(np.float32).view(np.uint32) & np.uint32(0xFFFF)).any()
+
+
+def check_bf16_writeback_vs_brute(model_cls, min_equal=0.99, logit_rel=1e-5):
+    """The bf16-storage model against the loop-written bf16 forward: the two
+    round at the same points, so they store the same bf16 numbers except
+    where a float32 and a float64 sum straddle a rounding boundary (none do
+    at this size and seed; ``min_equal`` leaves room for one), and their
+    logits then differ only by float32 summation rounding.  A rounding point
+    dropped or added anywhere flips a large share of the later stored values
+    and moves the logits by about a bf16 step (~1e-3 relative)."""
+    got, ref, lg, lr = run_bf16_writeback(model_cls)
+    assert set(got) == set(ref), sorted(set(got) ^ set(ref))
+    for p in BF16_POINTS:
+        assert got[p].shape == ref[p].shape, (p, got[p].shape, ref[p].shape)
+        eq = float(np.mean(got[p] == ref[p]))
+        # a flip is one bf16 step of that value
+        rel = np.abs(got[p] - ref[p]) / np.maximum(np.abs(ref[p]), 1e-30)
+        assert eq >= min_equal, f"{p}: only {eq:.4f} of stored values equal"
+        assert float(rel.max()) <= 2 ** -7 + 1e-12, f"{p}: differs by {rel.max():.3e} relative"
+    assert np.abs(lg - lr).max() <= logit_rel * np.abs(lr).max(), np.abs(lg - lr).max() / np.abs(lr).max()

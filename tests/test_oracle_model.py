@@ -85,3 +85,15 @@ def test_f64_accumulation_is_close_in_fp32_storage():
     a, _ = oracle.OracleModel(sh, w, "fp32", 1, 8, accum="f32").forward(ids)
     b, _ = oracle.OracleModel(sh, w, "fp32", 1, 8, accum="f64").forward(ids)
     assert np.abs(a - b).max() <= 1e-5 * np.abs(a).max()
+
+
+def test_bf16_writeback_points_are_bf16():
+    """Every stored intermediate of the bf16 forward is a bf16 number, at the
+    named storage points of the low-precision write-back rule."""
+    pins.check_bf16_writeback_points(oracle.OracleModel)
+
+
+def test_bf16_writeback_matches_loop_forward():
+    """The bf16 forward against the loop-written bf16 forward that rounds at
+    the same points (float64 sums): same stored values, same logits."""
+    pins.check_bf16_writeback_vs_brute(oracle.OracleModel)

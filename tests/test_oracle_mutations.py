@@ -181,3 +181,79 @@ def test_model_mutation_cache_not_used(monkeypatch):
 
     monkeypatch.setattr(ops, "attention", only_new)
     assert _fails(pins.check_decode_equals_recompute, oracle.OracleModel, "fp32")
+
+
+# ----------------------------------------------------------------------------- bf16 write-back points
+
+def _skip_rounding_at(point):
+    """An oracle that forgets the bf16 write-back at one storage point (the
+    value is kept in float32 there)."""
+    real = oracle.OracleModel._st
+
+    def st(self, x, p=None):
+        if p == point:
+            y = np.asarray(x, F32)
+            if self.record is not None:
+                self.record.setdefault(p, []).append(y.copy())
+            return y
+        return real(self, x, p)
+    return st
+
+
+def _skip_rounding_unrecorded(point):
+    """As above, but the point still records a rounded copy, so only the
+    downstream values can reveal the mistake."""
+    real = oracle.OracleModel._st
+
+    def st(self, x, p=None):
+        if p == point:
+            if self.record is not None:
+                self.record.setdefault(p, []).append(oracle.bf16_round(x))
+            return np.asarray(x, F32)
+        return real(self, x, p)
+    return st
+
+
+# Storage points whose rounding changes later values (the embedding row and
+# the value projection are bf16 numbers already: weights are bf16 and v is
+# stored as it leaves the bias add).
+DROPPABLE = [p for p in pins.BF16_POINTS if p not in ("embed",)]
+
+
+@pytest.mark.parametrize("point", DROPPABLE)
+def test_bf16_dropped_rounding_fails_representability(monkeypatch, point):
+    monkeypatch.setattr(oracle.OracleModel, "_st", _skip_rounding_at(point))
+    assert _fails(pins.check_bf16_writeback_points, oracle.OracleModel), point
+
+
+@pytest.mark.parametrize("point", DROPPABLE)
+def test_bf16_dropped_rounding_fails_brute(monkeypatch, point):
+    """A dropped write-back caught by the loop-written bf16 forward alone,
+    through the values stored after it (the final norm: through the logits)."""
+    monkeypatch.setattr(oracle.OracleModel, "_st", _skip_rounding_unrecorded(point))
+    assert _fails(pins.check_bf16_writeback_vs_brute, oracle.OracleModel), point
+
+
+def test_bf16_extra_rounding_inside_rmsnorm_fails_brute(monkeypatch):
+    """Rounding x / rms to bf16 before the weight multiply (two roundings
+    where the rule has one)."""
+    def rms_two_roundings(x, w, eps):
+        x = np.asarray(x, F32)
+        ms = np.mean(x * x, axis=-1, keepdims=True, dtype=F32)
+        y = oracle.bf16_round(x * (F32(1.0) / np.sqrt(ms + F32(eps))))
+        return y * np.asarray(w, F32)
+    monkeypatch.setattr(ops, "rms_norm", rms_two_roundings)
+    assert _fails(pins.check_bf16_writeback_vs_brute, oracle.OracleModel)
+
+
+def test_bf16_extra_rounding_inside_swiglu_fails_brute(monkeypatch):
+    """Rounding silu(g) before the multiply by u."""
+    monkeypatch.setattr(ops, "swiglu", lambda g, u: oracle.bf16_round(ops.silu(g)) * np.asarray(u, F32))
+    assert _fails(pins.check_bf16_writeback_vs_brute, oracle.OracleModel)
+
+
+def test_bf16_residual_rounded_once_fails_brute(monkeypatch):
+    """x + round(o_proj) rounded once, written as round(x + o_proj): the
+    product is not rounded before the add."""
+    monkeypatch.setattr(oracle.OracleModel, "_st", _skip_rounding_unrecorded("o_proj"))
+    assert _fails(pins.check_bf16_writeback_vs_brute, oracle.OracleModel)
