@@ -21,7 +21,12 @@ Also reported:
   step_roofline algorithmic bytes (or flops) of a whole decode (prefill) step
                 against the HBM (MFMA) peak.
   cpu_baseline  the oracle (plain NumPy) timed on this host on a bounded
-                sample of the same workload.
+                sample of the same workload (for B: the whole workload),
+                with the BLAS thread count and the CPU model.
+  parity        (B) after the timed region: the GPU fed the oracle's greedy
+                tokens, its logits against the oracle's at every position
+                (raw max abs error, raw and decisive top-1 agreement, the
+                oracle's own float32/float64 spread and the derived bound).
 """
 from __future__ import annotations
 
@@ -123,10 +128,11 @@ def dominant_kernel(wl, reps):
         Ws = [(torch.randn(N, K, device=dev, generator=g) * 0.02).to(torch.bfloat16) for _ in range(nbuf)]
         X = torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16)
         out = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+        ws = q2.workspace(q2.q2_linear_workspace_bytes(M, N, K))
         it = [0]
 
         def launch():
-            q2.q2_linear(out, X, Ws[it[0] % nbuf])
+            q2.q2_linear(out, X, Ws[it[0] % nbuf], None, ws)
             it[0] += 1
         dt = time_launches(launch, reps, stream)
         traffic = N * K * 2 + M * K * 2 + M * N * 2
@@ -151,11 +157,12 @@ def dominant_kernel(wl, reps):
     kvs = [(torch.randn(B, S, sh.nkv, sh.dh, device=dev, generator=g).to(torch.bfloat16),
             torch.randn(B, S, sh.nkv, sh.dh, device=dev, generator=g).to(torch.bfloat16)) for _ in range(nbuf)]
     o = torch.empty_like(q)
+    ws = q2.workspace(q2.q2_self_attention_workspace_bytes(B, 1, S, sh.nh, sh.nkv, sh.dh))
     it = [0]
 
     def launch():
         k, v = kvs[it[0] % nbuf]
-        q2.q2_self_attention(o, q, k, v, sh.dh ** -0.5)
+        q2.q2_self_attention(o, q, k, v, sh.dh ** -0.5, ws)
         it[0] += 1
     dt = time_launches(launch, reps, stream)
     traffic = kv_bytes + 2 * q.numel() * 2
@@ -186,26 +193,60 @@ def measured_traffic(wl):
     return rec["traffic_bytes"]
 
 
-def cpu_baseline(wl, weights, budget_s):
-    """Time the oracle, as it stands, on a bounded sample of the workload."""
-    import numpy as np
-    import oracle
-    import synth
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        return max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:
-        cores = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(wl, weights, budget_s):
+    """Time the oracle, as it stands, on a bounded sample of the workload.
+    Returns (record, reference) where reference holds the oracle's greedy
+    tokens and logits when the sample is the whole workload (B), for the
+    parity check, else None."""
+    import oracle
+    import synth
     sh = wl.shape
-    if wl.key == "B" or wl.key == "D":
-        batch = 1 if wl.key == "B" else 2
-        plen = wl.prompt if wl.key == "B" else 512
+    base = {"unit": "tok/s", "cores": int(blas_threads()), "cpu_model": cpu_model(), "kind": "oracle"}
+    if wl.key == "B":
+        # the whole workload: prefill of the prompt, then every greedy decode step
+        prompt = synth.make_prompt(wl)
+        orc = oracle.OracleModel(sh, weights, "bf16", 1, wl.prompt + wl.steps)
+        t0 = time.perf_counter()
+        logits, nxt = orc.forward(prompt)
+        t_pre = time.perf_counter() - t0
+        toks, all_logits = [nxt], [logits]
+        t0 = time.perf_counter()
+        for _ in range(wl.steps):
+            logits, nxt = orc.forward(nxt[:, None])
+            toks.append(nxt)
+            all_logits.append(logits)
+        t_dec = time.perf_counter() - t0
+        sample = (f"the whole workload on the oracle (bf16 storage, float32 sums): batch 1, prefill "
+                  f"{wl.prompt} tokens, then {wl.steps} greedy decode steps (decode timed)")
+        rec = dict(base, value=wl.steps / t_dec, sample=sample, prefill_tok_s=wl.prompt / t_pre)
+        import numpy as np
+        return rec, (orc, prompt, np.stack(toks, axis=1), all_logits)
+    if wl.key == "D":
+        batch, plen, n = 2, 512, 0
         prompt = synth.make_prompt(wl, batch=batch, length=plen)
         orc = oracle.OracleModel(sh, weights, "bf16", batch, plen + 256)
         t0 = time.perf_counter()
         _, nxt = orc.forward(prompt)
         t_pre = time.perf_counter() - t0
-        n = 0
         t0 = time.perf_counter()
         while n < 256 and (n < 2 or time.perf_counter() - t0 < budget_s):
             _, nxt = orc.forward(nxt[:, None])
@@ -213,8 +254,7 @@ def cpu_baseline(wl, weights, budget_s):
         t_dec = time.perf_counter() - t0
         sample = (f"oracle bf16-storage forward, batch {batch}, prefill {plen} tokens then {n} greedy decode "
                   f"steps (decode timed)")
-        return {"value": batch * n / t_dec, "unit": "tok/s", "cores": int(cores), "kind": "oracle",
-                "sample": sample, "prefill_tok_s": batch * plen / t_pre}
+        return dict(base, value=batch * n / t_dec, sample=sample, prefill_tok_s=batch * plen / t_pre), None
     if wl.key == "C":
         plen = 512
         prompt = synth.make_prompt(wl, length=plen)
@@ -222,9 +262,38 @@ def cpu_baseline(wl, weights, budget_s):
         t0 = time.perf_counter()
         orc.forward(prompt)
         dt = time.perf_counter() - t0
-        return {"value": plen / dt, "unit": "tok/s", "cores": int(cores), "kind": "oracle",
-                "sample": f"oracle bf16-storage prefill of the first {plen} prompt tokens (of 4096)"}
-    return None
+        return dict(base, value=plen / dt,
+                    sample=f"oracle bf16-storage prefill of the first {plen} prompt tokens (of 4096)"), None
+    return None, None
+
+
+def parity_record(model, wl, weights, ref):
+    """The GPU fed the oracle's greedy tokens over the whole workload, against
+    the oracle's logits (oracle.parity: raw max abs error and top-1 agreement,
+    the float32/float64 spread of the oracle itself, and the derived bound)."""
+    import numpy as np
+    import torch
+    import oracle
+    from oracle import parity
+    orc, prompt, toks, ref_logits = ref
+    orc64 = oracle.OracleModel(wl.shape, weights, "bf16", 1, wl.prompt + wl.steps, accum="f64", share_from=orc)
+    _, l64 = orc64.generate(prompt, wl.steps, teacher=toks)
+    spread = max(float(np.abs(oracle.bf16_round(a) - oracle.bf16_round(b)).max()) for a, b in zip(ref_logits, l64))
+    del orc64
+    model.reset()
+    dev = "cuda:0"
+    nxt, lg = model.prefill(torch.from_numpy(prompt).to(dev), logits=True)
+    got_logits, got_toks = [lg.cpu().numpy()], [nxt.cpu().numpy()]
+    for s in range(1, wl.steps + 1):
+        nxt, lg = model.decode(torch.from_numpy(np.ascontiguousarray(toks[:, s - 1])).to(dev), logits=True)
+        got_logits.append(lg.cpu().numpy())
+        got_toks.append(nxt.cpu().numpy())
+    r = parity.compare(got_logits, np.stack(got_toks, axis=1), ref_logits, toks, spread, True)
+    rec = r.record()
+    rec["ok"] = bool(r.ok())
+    rec["what"] = ("teacher-forced logits of the prefill and every decode step against the oracle "
+                   "(bf16-rounded on both sides); bound max(2e-2, 1.5 x spread)")
+    return rec
 
 
 # ----------------------------------------------------------------------------- main
@@ -240,7 +309,6 @@ def main():
 
     import synth
     import qwen2_decoder_forward_amd as q2
-    from tests.model_util import build_model
 
     wl = synth.WORKLOADS[args.workload]
     sh = wl.shape
@@ -255,7 +323,7 @@ def main():
     t_gen = time.perf_counter() - t0
     max_seq = wl.prompt + wl.steps
     t0 = time.perf_counter()
-    model = build_model(sh, weights, max_seq, wl.batch)
+    model = q2.load_model(sh, weights, max_seq, wl.batch)
     torch.cuda.synchronize()
     t_load = time.perf_counter() - t0
     prompt = torch.from_numpy(synth.make_prompt(wl)).to(dev)
@@ -315,9 +383,11 @@ def main():
         step_roof = {"what": "prefill", "bound": "mfma", "flops": fl, "achieved": round(tf, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
 
-    cpu = None
+    cpu = par = None
     if not args.no_cpu:
-        cpu = cpu_baseline(wl, weights, args.cpu_seconds)
+        cpu, ref = cpu_baseline(wl, weights, args.cpu_seconds)
+        if ref is not None:
+            par = parity_record(model, wl, weights, ref)
 
     if wl.steps:
         metric, value = "decode tok/s", decode_tok_s
@@ -333,7 +403,7 @@ def main():
         "prefill_tok_s": round(prefill_tok_s, 1),
         "decode_tok_s": round(decode_tok_s, 2) if decode_tok_s else None,
         "prefill_ms": round(pre_s * 1e3, 3), "decode_ms": round(dec_s * 1e3, 3),
-        "roofline": roofline, "step_roofline": step_roof, "cpu_baseline": cpu,
+        "roofline": roofline, "step_roofline": step_roof, "cpu_baseline": cpu, "parity": par,
         "wall_s_timed": round(wall, 3), "weight_gen_s": round(t_gen, 1), "load_s": round(t_load, 2),
         "library": q2.version(),
     }

@@ -13,7 +13,11 @@
  * --------------------------------
  *  - Tensors are passed as q2_tensor descriptors: a device pointer, a dtype,
  *    the rank and per-dimension sizes and strides (in elements, not bytes).
- *    The caller owns every tensor; no call allocates or frees caller memory.
+ *    The caller owns every tensor.  Operator calls never allocate, free or
+ *    synchronise: memory beyond their inputs and outputs (split partial
+ *    results) comes from a caller-owned `workspace` argument, so an operator
+ *    call can be captured into a HIP graph.  Only q2_model_create and
+ *    q2_model_destroy allocate and free (the model's own memory).
  *  - Unless a call says otherwise the last dimension must have stride 1 and
  *    the outer dimensions may have any non-negative strides.
  *  - Arithmetic is float32 whatever the storage type ("low precision storage,
@@ -82,9 +86,20 @@ q2_status q2_embedding(const q2_tensor* out, const q2_tensor* ids, const q2_tens
  * ([out features, in features]); bias: [N] or NULL; out: [M, N] / [B, T, N].
  * dtype: all f32, or in/weight/bias bf16 with out bf16 or f32.  bf16 path:
  * MFMA with float32 accumulation; K must be a multiple of 8 and rows and
- * pointers 16-byte aligned.  Rows of `in` and `out` may be strided. */
+ * pointers 16-byte aligned.  Rows of `in` and `out` may be strided.
+ * workspace: NULL or a contiguous, 16-byte aligned tensor of any dtype whose
+ * bytes the call may overwrite (it must not overlap the operands).  Products
+ * of at most 64 rows split K over workgroups when the workspace holds the
+ * float32 partial sums (q2_linear_workspace_bytes); with a smaller or no
+ * workspace they run unsplit (slower on small N; the sums are then added in
+ * another order, so results can differ by float32 rounding).  Calls that
+ * share a workspace must be ordered (same stream). */
 q2_status q2_linear(const q2_tensor* out, const q2_tensor* in, const q2_tensor* weight,
-                    const q2_tensor* bias, void* stream);
+                    const q2_tensor* bias, const q2_tensor* workspace, void* stream);
+
+/* Workspace bytes q2_linear needs to run its split plan for M rows, N out
+ * features, K in features of dtype Q2_F32 / Q2_BF16 (0: it never splits). */
+q2_status q2_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t dtype, size_t* bytes);
 
 /* out = in / sqrt(mean(in^2) + eps) * weight over the last dimension
  * (section 3.2, rms_norm; epsilon inside the root).  in/out: [..., H];
@@ -110,10 +125,17 @@ q2_status q2_rope(const q2_tensor* out, const q2_tensor* in, const q2_tensor* po
  * scores = (q . k) * scale, softmax in float32.  k and v may be strided views
  * (e.g. of a KV cache laid out [B, nkv, S_max, d]); their last dim must be
  * contiguous.  dtype f32 (any d <= 256) or bf16 (d = 128 only).
- * The library keeps a per-device scratch buffer (allocated on first use) for
- * split-KV partial results. */
+ * workspace: NULL or a caller-owned tensor as for q2_linear.  The bf16 path
+ * splits long key ranges over workgroups (decode) and the longest query
+ * blocks in two (prefill) when the workspace holds their partial results
+ * (q2_self_attention_workspace_bytes); otherwise it runs unsplit. */
 q2_status q2_self_attention(const q2_tensor* out, const q2_tensor* q, const q2_tensor* k,
-                            const q2_tensor* v, float scale, void* stream);
+                            const q2_tensor* v, float scale, const q2_tensor* workspace, void* stream);
+
+/* Workspace bytes q2_self_attention needs to run its split plan for B
+ * sequences of T queries over S keys, nh query / nkv KV heads of size d. */
+q2_status q2_self_attention_workspace_bytes(int32_t B, int32_t T, int32_t S, int32_t nh, int32_t nkv, int32_t d,
+                                            int32_t dtype, size_t* bytes);
 
 /* out = silu(gate) * up, silu(g) = g / (1 + exp(-g))  (section 3.2, swiglu).
  * Same shape [..., I] and dtype for all three. */
@@ -186,7 +208,9 @@ q2_status q2_model_load_weight(q2_model* m, const char* name, int32_t layer, con
  * next: [B] int64 greedy tokens of the last position.  logits: NULL or
  * [B, V] f32 (last position).  B must not exceed max_batch and must equal
  * the batch of earlier calls since the last reset; len + T must not exceed
- * max_seq (else Q2_ESTATE and nothing changes). */
+ * max_seq (else Q2_ESTATE and nothing changes).  Ids are not range-checked
+ * on the host (they are device data): an id outside [0, vocab) embeds as a
+ * zero row, as in q2_embedding. */
 q2_status q2_model_prefill(q2_model* m, const q2_tensor* ids, const q2_tensor* next,
                            const q2_tensor* logits, void* stream);
 

@@ -58,7 +58,14 @@ class OracleModel:
     differ only in summation rounding drift apart after bf16 storage rounding.
     """
 
-    def __init__(self, shape, weights, storage: str, batch: int, max_seq: int, accum: str = "f32"):
+    # float64 copies of the matrices are kept (rather than widened at every
+    # product) while they take at most this many bytes
+    F64_CACHE_BYTES = 16 << 30
+
+    def __init__(self, shape, weights, storage: str, batch: int, max_seq: int, accum: str = "f32",
+                 share_from: "OracleModel | None" = None):
+        """``share_from``: another oracle of the same shape whose float32
+        weight copies this one reuses (read-only) instead of widening its own."""
         if storage not in ("bf16", "fp32") or accum not in ("f32", "f64"):
             raise ValueError((storage, accum))
         self.shape = shape
@@ -66,9 +73,18 @@ class OracleModel:
         self.accum = accum
         self.batch = batch
         self.max_seq = max_seq
-        self.w = {}
-        for key, arr in weights.items():
-            self.w[key] = ops.widen_bf16(arr) if arr.dtype == np.uint16 else np.asarray(arr, F32)
+        if share_from is not None:
+            if share_from.shape != shape:
+                raise ValueError("share_from has another shape")
+            self.w = share_from.w
+        else:
+            self.w = {}
+            for key, arr in weights.items():
+                self.w[key] = ops.widen_bf16(arr) if arr.dtype == np.uint16 else np.asarray(arr, F32)
+        self.w64 = {}
+        if accum == "f64" and sum(a.size for a in self.w.values()) * 8 <= self.F64_CACHE_BYTES:
+            self.w64 = {id(a): a.astype(np.float64) for a in self.w.values() if a.ndim == 2}
+        self.on_layer = None        # optional callback(layer) after each layer (progress reports)
         L, nkv, d = shape.nlayer, shape.nkv, shape.dh
         self.k_cache = [np.zeros((batch, nkv, max_seq, d), F32) for _ in range(L)]
         self.v_cache = [np.zeros((batch, nkv, max_seq, d), F32) for _ in range(L)]
@@ -96,7 +112,8 @@ class OracleModel:
     def _linear(self, x, w, b=None):
         if self.accum == "f32":
             return ops.linear(x, w, b)
-        y = np.matmul(np.asarray(x, np.float64), np.asarray(w, np.float64).T)
+        w64 = self.w64.get(id(w))
+        y = np.matmul(np.asarray(x, np.float64), (w64 if w64 is not None else np.asarray(w, np.float64)).T)
         if b is not None:
             y = y + np.asarray(b, np.float64)
         return y.astype(F32)
@@ -159,6 +176,8 @@ class OracleModel:
             x = st(ops.add(x, dn), "resid_mlp")
             if hidden is not None:
                 hidden.append(x.copy())
+            if self.on_layer is not None:
+                self.on_layer(l)
         self.length = P + T
         xs = x if all_logits else x[:, -1, :]
         hf = st(ops.rms_norm(xs, self._weight("norm"), sh.eps), "final_norm")

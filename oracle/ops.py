@@ -40,13 +40,17 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     at most half a bf16 ulp on a random sample (compared in float64).
     """
     x = np.ascontiguousarray(x, dtype=F32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    out = (r & 0xFFFFFFFF).astype(np.uint32).view(F32)
+    u = x.view(np.uint32)
+    # r = u + 0x7FFF + (bit 16 of u), then clear the low 16 bits.  For every
+    # non-NaN pattern the sum stays below 2^32 (the largest, -inf or -max,
+    # is 0xFF80xxxx), so uint32 arithmetic is exact; NaNs are replaced below.
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += u
+    r += np.uint32(0x7FFF)
+    r &= np.uint32(0xFFFF0000)
+    out = r.view(F32)
     nan = np.isnan(x)
     if nan.any():
-        out = out.copy()
         out[nan] = np.float32("nan")
     return out
 

@@ -55,10 +55,13 @@ _SIGS = {
     "q2_last_error": ([], ctypes.c_char_p),
     "q2_version": ([], ctypes.c_char_p),
     "q2_embedding": ([_P, _P, _P, _S], ctypes.c_int),
-    "q2_linear": ([_P, _P, _P, _P, _S], ctypes.c_int),
+    "q2_linear": ([_P, _P, _P, _P, _P, _S], ctypes.c_int),
+    "q2_linear_workspace_bytes": ([ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                   ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "q2_rms_norm": ([_P, _P, _P, ctypes.c_float, _S], ctypes.c_int),
     "q2_rope": ([_P, _P, _P, ctypes.c_float, _S], ctypes.c_int),
-    "q2_self_attention": ([_P, _P, _P, _P, ctypes.c_float, _S], ctypes.c_int),
+    "q2_self_attention": ([_P, _P, _P, _P, ctypes.c_float, _P, _S], ctypes.c_int),
+    "q2_self_attention_workspace_bytes": ([ctypes.c_int32] * 7 + [ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "q2_swiglu": ([_P, _P, _P, _S], ctypes.c_int),
     "q2_add": ([_P, _P, _P, _S], ctypes.c_int),
     "q2_argmax": ([_P, _P, _P, _S], ctypes.c_int),
@@ -142,9 +145,16 @@ def q2_embedding(out, ids, weight, stream=None):
     return out
 
 
-def q2_linear(out, inp, weight, bias=None, stream=None):
-    _check(lib.q2_linear(_ref(desc(out)), _ref(desc(inp)), _ref(desc(weight)), _ref(desc(bias)), _stream(stream)))
+def q2_linear(out, inp, weight, bias=None, workspace=None, stream=None):
+    _check(lib.q2_linear(_ref(desc(out)), _ref(desc(inp)), _ref(desc(weight)), _ref(desc(bias)),
+                         _ref(desc(workspace)), _stream(stream)))
     return out
+
+
+def q2_linear_workspace_bytes(M, N, K, dtype=Q2_BF16) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.q2_linear_workspace_bytes(int(M), int(N), int(K), int(dtype), ctypes.byref(n)))
+    return n.value
 
 
 def q2_rms_norm(out, inp, weight, eps, stream=None):
@@ -157,10 +167,24 @@ def q2_rope(out, inp, pos, theta, stream=None):
     return out
 
 
-def q2_self_attention(out, q, k, v, scale, stream=None):
+def q2_self_attention(out, q, k, v, scale, workspace=None, stream=None):
     _check(lib.q2_self_attention(_ref(desc(out)), _ref(desc(q)), _ref(desc(k)), _ref(desc(v)), float(scale),
-                                 _stream(stream)))
+                                 _ref(desc(workspace)), _stream(stream)))
     return out
+
+
+def q2_self_attention_workspace_bytes(B, T, S, nh, nkv, d, dtype=Q2_BF16) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.q2_self_attention_workspace_bytes(int(B), int(T), int(S), int(nh), int(nkv), int(d), int(dtype),
+                                                 ctypes.byref(n)))
+    return n.value
+
+
+def workspace(nbytes: int, device=None) -> torch.Tensor:
+    """A device tensor of at least ``nbytes`` bytes to pass as an operator's
+    workspace (float32 elements; 16-byte aligned like every torch allocation)."""
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    return torch.empty(max(4, -(-int(nbytes) // 16) * 4), dtype=torch.float32, device=dev)
 
 
 def q2_swiglu(out, gate, up, stream=None):

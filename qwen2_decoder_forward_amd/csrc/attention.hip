@@ -775,6 +775,13 @@ q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
     DecodePlan p = plan_decode(a.B, s_max, a.nkv);
     float* part_o = nullptr;
     float2* part_ml = nullptr;
+    if (p.nsplit > 1 && a.unsplit_if_short) {
+      const size_t slots = static_cast<size_t>(a.B) * a.nkv * p.nsplit * 16;
+      if (!a.scratch || a.scratch_bytes < slots * (D * sizeof(float) + sizeof(float2))) {
+        p.nsplit = 1;
+        p.chunk = cdiv(s_max, 64) * 64;
+      }
+    }
     if (p.nsplit > 1) {
       const size_t slots = static_cast<size_t>(a.B) * a.nkv * p.nsplit * 16;
       const size_t need = slots * (D * sizeof(float) + sizeof(float2));

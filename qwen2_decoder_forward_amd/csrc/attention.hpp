@@ -27,6 +27,7 @@ struct AttnArgs {
   void* scratch;               // split-KV partials
   size_t scratch_bytes;
   bool leave_partials;         // split-KV: skip the merge, the consumer merges the partials
+  bool unsplit_if_short;       // run unsplit when the partials exceed scratch_bytes (else fail)
 };
 
 q2_status attention_bf16(const AttnArgs& a, hipStream_t s);

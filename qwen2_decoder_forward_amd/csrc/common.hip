@@ -1,10 +1,6 @@
-// Host side of the shared helpers: error messages, descriptor checks, the
-// per-device scratch buffer used by operators that keep partial results.
+// Host side of the shared helpers: error messages and descriptor checks.
 #include <stdarg.h>
 #include <stdio.h>
-
-#include <mutex>
-#include <vector>
 
 #include "common.hpp"
 
@@ -84,34 +80,6 @@ q2_status as_rows(const q2_tensor* t, const char* name, Rows* out) {
   }
   Q2_CHECK(rows <= 1 || ld >= out->cols, Q2_ESTRIDE, "%s: overlapping rows", name);
   out->ld = ld;
-  return Q2_OK;
-}
-
-struct Scratch {
-  void* ptr = nullptr;
-  size_t bytes = 0;
-};
-static std::mutex g_scratch_mu;
-static std::vector<Scratch> g_scratch;
-
-q2_status device_scratch(size_t bytes, void** ptr) {
-  int dev = 0;
-  Q2_HIP(hipGetDevice(&dev));
-  std::lock_guard<std::mutex> lk(g_scratch_mu);
-  if (static_cast<int>(g_scratch.size()) <= dev) g_scratch.resize(dev + 1);
-  Scratch& s = g_scratch[dev];
-  if (s.bytes < bytes) {
-    if (s.ptr) {
-      Q2_HIP(hipDeviceSynchronize());  // earlier launches may still read it
-      Q2_HIP(hipFree(s.ptr));
-      s.ptr = nullptr;
-      s.bytes = 0;
-    }
-    size_t want = bytes < (size_t(16) << 20) ? (size_t(16) << 20) : bytes;
-    Q2_HIP(hipMalloc(&s.ptr, want));
-    s.bytes = want;
-  }
-  *ptr = s.ptr;
   return Q2_OK;
 }
 

@@ -138,6 +138,9 @@ struct GemmArgs {
   Epi epi;
   void* scratch;             // float32 split-K partials (GEMV path)
   size_t scratch_bytes;
+  // a split plan whose partials exceed scratch_bytes runs unsplit instead of
+  // failing (operator calls with a caller-sized workspace)
+  bool unsplit_if_short;
   // fused RMSNorm of X's rows (GEMV path, M <= 16): X is the raw residual
   // stream, the kernel multiplies it by 1/sqrt(sum(norm_sq row)/K + eps) and
   // norm_w, rounded to the storage type, before the product

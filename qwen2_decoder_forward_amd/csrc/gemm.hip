@@ -738,7 +738,9 @@ q2_status launch_skinny(const GemmArgs& a, hipStream_t s) {
   if (EK == EPI_ARGMAX) p.splits = 1;
   if (p.splits > 1) {
     const size_t need = static_cast<size_t>(p.splits) * a.M * a.N * sizeof(float);
-    Q2_CHECK(a.scratch && a.scratch_bytes >= need, Q2_EINVAL, "skinny linear: split-K scratch too small");
+    if (a.unsplit_if_short && (!a.scratch || a.scratch_bytes < need)) p.splits = 1;
+    Q2_CHECK(p.splits == 1 || (a.scratch && a.scratch_bytes >= need), Q2_EINVAL,
+             "skinny linear: split-K scratch too small");
   }
   if (p.bn == 128) {
     if (p.bm == 32) return launch_skinny_cfg<EK, 32, 128>(a, p, s);

@@ -804,7 +804,11 @@ q2_status gemv_bf16(const GemmArgs& a, hipStream_t s) {
   Q2_CHECK(!a.defer_reduce || a.epi.kind != EPI_ARGMAX, Q2_EINVAL, "gemv: argmax cannot defer its reduction");
   if (p.splits > 1) {
     const size_t need = static_cast<size_t>(p.splits) * a.M * a.N * sizeof(float);
-    Q2_CHECK(a.scratch && a.scratch_bytes >= need, Q2_EINVAL, "gemv: split-K scratch too small");
+    if (a.unsplit_if_short && (!a.scratch || a.scratch_bytes < need)) {
+      p.splits = 1;
+      p.bps = cdiv(a.K, KB);
+    }
+    Q2_CHECK(p.splits == 1 || (a.scratch && a.scratch_bytes >= need), Q2_EINVAL, "gemv: split-K scratch too small");
   }
   switch (a.epi.kind) {
     case EPI_STORE: return gemv_ek<EPI_STORE>(a, p, s);

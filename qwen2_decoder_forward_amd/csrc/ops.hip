@@ -433,9 +433,23 @@ extern "C" q2_status q2_embedding(const q2_tensor* out, const q2_tensor* ids, co
                                     static_cast<int>(w.rows), static_cast<int>(w.cols), s);
 }
 
-extern "C" q2_status q2_linear(const q2_tensor* out, const q2_tensor* in, const q2_tensor* weight,
-                               const q2_tensor* bias, void* stream) {
-  clear_error();
+// Caller-owned workspace of an operator call: a contiguous, 16-byte aligned
+// tensor of any dtype whose bytes the call may overwrite (NULL: none).
+static q2_status workspace_of(const q2_tensor* ws, void** ptr, size_t* bytes) {
+  *ptr = nullptr;
+  *bytes = 0;
+  if (!ws) return Q2_OK;
+  Q2_TRY(check_desc(ws, "workspace"));
+  Q2_CHECK(is_contiguous(*ws), Q2_ESTRIDE, "workspace must be contiguous");
+  Q2_CHECK(aligned16(ws->data), Q2_ESTRIDE, "workspace must be 16-byte aligned");
+  *ptr = ws->data;
+  *bytes = static_cast<size_t>(numel(*ws) * dtype_size(ws->dtype));
+  return Q2_OK;
+}
+
+// Checks the operands of q2_linear and fills the product's descriptor.
+static q2_status linear_args(const q2_tensor* out, const q2_tensor* in, const q2_tensor* weight,
+                             const q2_tensor* bias, GemmArgs* args, int32_t* dtype) {
   Rows o, x, w;
   Q2_TRY(as_rows(out, "out", &o));
   Q2_TRY(as_rows(in, "in", &x));
@@ -468,17 +482,43 @@ extern "C" q2_status q2_linear(const q2_tensor* out, const q2_tensor* in, const 
   a.epi.ldo = o.ld;
   a.epi.out_f32 = o.dtype == Q2_F32;
   a.epi.bias = bias ? bias->data : nullptr;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (x.dtype == Q2_F32) return gemm_f32(a, s);
-  Q2_CHECK(a.K % 8 == 0, Q2_ESHAPE, "bf16 linear: K must be a multiple of 8");
-  Q2_CHECK(aligned16(x.data) && aligned16(w.data) && (x.ld % 8 == 0 || x.rows <= 1) && (w.ld % 8 == 0 || w.rows <= 1),
-           Q2_ESTRIDE, "bf16 linear: in and weight rows must be 16-byte aligned");
-  if (a.M <= GEMV_MAX_M) {
-    const size_t need = gemm_scratch_bytes(a.M, a.N, a.K);
-    if (need) Q2_TRY(device_scratch(need, &a.scratch));
-    a.scratch_bytes = need;
+  if (x.dtype == Q2_BF16) {
+    Q2_CHECK(a.K % 8 == 0, Q2_ESHAPE, "bf16 linear: K must be a multiple of 8");
+    Q2_CHECK(aligned16(x.data) && aligned16(w.data) && (x.ld % 8 == 0 || x.rows <= 1) &&
+                 (w.ld % 8 == 0 || w.rows <= 1),
+             Q2_ESTRIDE, "bf16 linear: in and weight rows must be 16-byte aligned");
   }
+  *args = a;
+  *dtype = x.dtype;
+  return Q2_OK;
+}
+
+static size_t linear_partial_bytes(int32_t dtype, int64_t M, int64_t N, int64_t K) {
+  if (dtype != Q2_BF16 || M > GEMV_MAX_M || M == 0 || N == 0) return 0;
+  return gemm_scratch_bytes(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+}
+
+extern "C" q2_status q2_linear(const q2_tensor* out, const q2_tensor* in, const q2_tensor* weight,
+                               const q2_tensor* bias, const q2_tensor* workspace, void* stream) {
+  clear_error();
+  GemmArgs a{};
+  int32_t dt = 0;
+  Q2_TRY(linear_args(out, in, weight, bias, &a, &dt));
+  Q2_TRY(workspace_of(workspace, &a.scratch, &a.scratch_bytes));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dt == Q2_F32) return gemm_f32(a, s);
+  a.unsplit_if_short = true;
   return gemm_bf16(a, s);
+}
+
+extern "C" q2_status q2_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t dtype, size_t* bytes) {
+  clear_error();
+  Q2_CHECK(bytes != nullptr, Q2_EINVAL, "bytes is null");
+  Q2_CHECK(M >= 0 && N >= 0 && K >= 0 && M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX, Q2_ESHAPE,
+           "sizes must be in [0, 2^31)");
+  Q2_CHECK(dtype == Q2_F32 || dtype == Q2_BF16, Q2_EDTYPE, "dtype must be f32 or bf16");
+  *bytes = linear_partial_bytes(dtype, M, N, K);
+  return Q2_OK;
 }
 
 extern "C" q2_status q2_rms_norm(const q2_tensor* out, const q2_tensor* in, const q2_tensor* weight, float eps,
@@ -550,7 +590,7 @@ extern "C" q2_status q2_rope(const q2_tensor* out, const q2_tensor* in, const q2
 }
 
 extern "C" q2_status q2_self_attention(const q2_tensor* out, const q2_tensor* q, const q2_tensor* k,
-                                       const q2_tensor* v, float scale, void* stream) {
+                                       const q2_tensor* v, float scale, const q2_tensor* workspace, void* stream) {
   clear_error();
   Q2_TRY(check_desc(out, "out"));
   Q2_TRY(check_desc(q, "q"));
@@ -603,12 +643,19 @@ extern "C" q2_status q2_self_attention(const q2_tensor* out, const q2_tensor* q,
     for (int i = 0; i < nd - 1; ++i)
       Q2_CHECK(t->stride[i] % 8 == 0 || t->shape[i] <= 1, Q2_ESTRIDE, "bf16 attention: strides must be multiples of 8");
   }
-  const size_t need = attention_scratch_bytes(a.B, a.T, a.S, a.nh, a.nkv, a.d);
-  if (need) {
-    Q2_TRY(device_scratch(need, &a.scratch));
-    a.scratch_bytes = need;
-  }
+  Q2_TRY(workspace_of(workspace, &a.scratch, &a.scratch_bytes));
+  a.unsplit_if_short = true;
   return attention_bf16(a, s);
+}
+
+extern "C" q2_status q2_self_attention_workspace_bytes(int32_t B, int32_t T, int32_t S, int32_t nh, int32_t nkv,
+                                                       int32_t d, int32_t dtype, size_t* bytes) {
+  clear_error();
+  Q2_CHECK(bytes != nullptr, Q2_EINVAL, "bytes is null");
+  Q2_CHECK(B >= 0 && T >= 0 && S >= T && nkv > 0 && nh % nkv == 0 && d > 0, Q2_ESHAPE, "bad attention sizes");
+  Q2_CHECK(dtype == Q2_F32 || dtype == Q2_BF16, Q2_EDTYPE, "dtype must be f32 or bf16");
+  *bytes = (dtype == Q2_BF16 && B > 0 && T > 0) ? attention_scratch_bytes(B, T, S, nh, nkv, d) : 0;
+  return Q2_OK;
 }
 
 static q2_status elementwise3(const q2_tensor* o, const q2_tensor* x, const q2_tensor* y, Rows* ro, Rows* rx,

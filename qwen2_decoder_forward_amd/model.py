@@ -1,6 +1,7 @@
 """Python handle around the q2 model driver (argument marshalling only)."""
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -106,3 +107,26 @@ class Model:
 
     def check(self):
         _lib.q2_model_check(self.handle)
+
+
+def weight_tensor(arr, device: int = 0) -> torch.Tensor:
+    """A host weight as a device tensor, bit for bit: uint16 arrays hold bf16
+    bit patterns, float32 arrays float32 values."""
+    dev = f"cuda:{device}"
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(dev)
+
+
+def load_model(shape, weights, max_seq: int, max_batch: int, device: int = 0) -> Model:
+    """Create a model and copy every weight of ``weights`` ({(name, layer):
+    host array}, Hugging Face Qwen2 names, layer -1 for the global tensors)
+    into it, one tensor at a time (each upload is freed once the library has
+    packed it)."""
+    m = Model(shape, max_seq, max_batch, device)
+    for (name, layer), arr in weights.items():
+        t = weight_tensor(arr, device)
+        m.load_weight(name, layer, t)
+        torch.cuda.synchronize(device)
+        del t
+    return m

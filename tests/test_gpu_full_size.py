@@ -1,0 +1,92 @@
+"""Full-size parity of the large workloads against the oracle.
+
+  * 1.5B shape, 28 layers, a 4096-token prefill: the last position's logits,
+    then 4 decode steps at context 4097-4100.
+  * 1.5B shape, 64 sequences x 4096-token prefill, then 4 batched decode
+    steps: sequences 0 and 63 against the oracle run on those two sequences
+    alone (a sequence's results do not depend on the other sequences of the
+    batch, so the comparison is the same as for the whole batch).
+  * 7B shape (hidden 3584, 28/4 heads, theta 1e6), 28 layers, 8 sequences x
+    1024-token prefill, then 16 batched decode steps: sequences 0 and 7.
+
+The GPU runs each workload at its real size in the launch configuration the
+benchmark times; the oracle is fed the same tokens (teacher forcing) and the
+comparison is oracle.parity's (bound max(2e-2, 1.5 x spread), decisive top-1
+agreement >= 99 %, valid picks).  The oracle's share takes minutes of host
+CPU per workload, so these run only with Q2_FULL_SIZE=1.
+"""
+import os
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import parity
+import synth
+from tests.model_util import build_model, gpu_teacher_forced
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.slow,
+    pytest.mark.skipif(os.environ.get("Q2_FULL_SIZE") != "1",
+                       reason="full-size oracle runs take minutes of host CPU: set Q2_FULL_SIZE=1"),
+]
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _progress(tag):
+    t0 = time.time()
+    last = [t0]
+
+    def cb(layer):
+        now = time.time()
+        if now - last[0] >= 20:
+            _say(f"  [{tag}] oracle layer {layer} at {now - t0:.0f} s")
+            last[0] = now
+    return cb
+
+
+def _full_case(name, wl, steps, rows):
+    t0 = time.time()
+    sh = wl.shape
+    w = synth.make_weights(wl)
+    prompt = synth.make_prompt(wl)
+    max_seq = wl.prompt + steps
+    _say(f"[{name}] weights drawn ({time.time() - t0:.0f} s)")
+    orc = oracle.OracleModel(sh, w, "bf16", len(rows), max_seq)
+    orc64 = oracle.OracleModel(sh, w, "bf16", len(rows), max_seq, accum="f64", share_from=orc)
+    orc.on_layer = _progress(name + " f32")
+    orc64.on_layer = _progress(name + " f64")
+    ref_toks, ref_logits, spread = parity.reference(orc, prompt[rows], steps, orc64)
+    _say(f"[{name}] oracle done ({time.time() - t0:.0f} s), spread {spread:.4f}")
+    del orc, orc64
+    model = build_model(sh, w, max_seq, wl.batch)
+    del w
+    # sequences the oracle did not run are fed token 0 (their results do not
+    # reach the compared rows)
+    teacher = np.zeros((wl.batch, steps), np.int64)
+    teacher[rows] = ref_toks[:, :steps]
+    got_logits, got_toks = gpu_teacher_forced(model, prompt, teacher, steps, rows=rows)
+    model.close()
+    r = parity.compare(got_logits, got_toks, ref_logits, ref_toks, spread, True)
+    _say(f"\n[{name}] {r.summary()} ({time.time() - t0:.0f} s)")
+    return r
+
+
+def test_full_c_prefill_4096():
+    r = _full_case("C full", synth.WORKLOADS["C"], 4, [0])
+    assert r.ok(), r.summary()
+
+
+def test_full_d_batch64_ctx4096():
+    r = _full_case("D full", synth.WORKLOADS["D"], 4, [0, 63])
+    assert r.ok(), r.summary()
+
+
+def test_full_e_7b_batch8():
+    r = _full_case("E full", synth.WORKLOADS["E"], 16, [0, 7])
+    assert r.ok(), r.summary()

@@ -1,27 +1,27 @@
 """Model-level parity on the GPU: the q2 model driver against the oracle under
 teacher forcing, layer by layer, and through invariants that hold at any size.
 
-Bars (from the arithmetic and the workload definitions):
+Bars (from the arithmetic and the workload definitions; oracle.parity holds
+the comparison):
   * fp32 model (workload A): logits within 1e-4 of the oracle relative to the
     largest logit, every greedy token equal.
   * bf16 models, whole model: the stated bound is 2e-2 max abs error on bf16
     logits with >= 99 % top-1 agreement.  With bf16 storage rounding after
     every operator, two exact implementations that differ only in float32
     summation order drift apart by more than that at depth (measured here on
-    every run: the oracle against itself with float64 accumulation, the
-    `spread`).  So the bound applied is max(2e-2, 2 * spread); the GPU must
-    pick the oracle's token wherever the oracle's top-1 margin exceeds it
-    (>= 99 % of those positions) and elsewhere a token whose oracle logit is
-    within it of the maximum.
+    every run: the oracle against itself with float64 sums, the `spread`).
+    So the bound applied is max(2e-2, 1.5 * spread); the GPU must pick the
+    oracle's token at >= 99 % of the positions whose oracle top-1 margin
+    exceeds the spread (at least a fifth of all positions must be such), and
+    elsewhere a token whose oracle logit is within the bound of the maximum.
+    Raw max abs error and raw top-1 agreement are printed for every case.
   * bf16 models, layer by layer: each GPU layer, fed the oracle's input hidden
     state, must reproduce the oracle's output hidden state within
     max(2 * spread_l, 2^-7 * max|x|), spread_l being the same float64
     cross-check for that layer alone; the error must not grow with depth.
-Where the oracle cannot run a workload at full size in seconds (the 4096-token
-prefill, the 64 x 4096 batched decode, the 7B shape) the same kernels are
-checked on the full shape with fewer layers or a shorter context against the
-oracle, and at full size through invariants (decode equals recompute,
-chunked prefill equals one-shot prefill, batch independence).
+The full-size prefill (4096 tokens), batched decode (64 x 4096) and 7B
+workloads are in test_gpu_full_size.py; here they run with fewer layers or a
+shorter context.
 """
 import math
 
@@ -46,7 +46,7 @@ def _run(shape, batch, prompt_len, steps, seed=1234, prompt_seed=5678):
     model = build_model(shape, w, wl.max_seq, batch)
     bf = shape.dtype == "bf16"
     orc = oracle.OracleModel(shape, w, "bf16" if bf else "fp32", batch, wl.max_seq)
-    orc64 = oracle.OracleModel(shape, w, "bf16", batch, wl.max_seq, accum="f64") if bf else None
+    orc64 = oracle.OracleModel(shape, w, "bf16", batch, wl.max_seq, accum="f64", share_from=orc) if bf else None
     res = teacher_forced(model, orc, prompt, steps, orc64)
     model.close()
     return res
@@ -60,8 +60,7 @@ def test_workload_a_fp32_full():
     wl = synth.WORKLOADS["A"]
     r = _run(wl.shape, wl.batch, wl.prompt, wl.steps)
     _print("A", r)
-    assert r.max_rel_err <= 1e-4
-    assert np.array_equal(r.gpu_tokens, r.ref_tokens)
+    assert r.max_rel_err <= 1e-4 and r.top1_raw == 1.0, r.summary()
 
 
 def test_workload_a_generate_matches_oracle_greedy():
@@ -122,7 +121,9 @@ def _layerwise(shape, prompt_len, seed=1234):
     w = synth.make_weights(wl)
     prompt = synth.make_prompt(wl)
     hs = []
-    oracle.OracleModel(shape, w, "bf16", 1, prompt_len).forward(prompt, hidden=hs)
+    orc = oracle.OracleModel(shape, w, "bf16", 1, prompt_len)
+    orc.forward(prompt, hidden=hs)
+    orc64 = oracle.OracleModel(shape, w, "bf16", 1, prompt_len, accum="f64", share_from=orc)
     E = oracle.widen_bf16(w[("embed_tokens", -1)])
     inputs = [oracle.bf16_round(E[prompt])] + hs[:-1]
     one = reduced_shape(shape, nlayer=1)
@@ -136,8 +137,8 @@ def _layerwise(shape, prompt_len, seed=1234):
         m.close()
         ref = hs[l][0]
         h64 = []
-        oracle.OracleModel(shape, w, "bf16", 1, prompt_len, accum="f64").forward(
-            None, embeds=inputs[l], layers=range(l, l + 1), hidden=h64)
+        orc64.reset()
+        orc64.forward(None, embeds=inputs[l], layers=range(l, l + 1), hidden=h64)
         rows.append((float(np.abs(got - ref).max()), float(np.abs(h64[0][0] - ref).max()),
                      float(np.abs(ref).max())))
     return rows
@@ -208,11 +209,17 @@ def test_chunked_prefill_equals_one_shot_small_bf16():
 
 @pytest.mark.parametrize("T", [7, 40])
 def test_fused_model_equals_unfused_operator_chain(T):
-    """The model's fused kernels store what the chain of standalone operators
+    """The model's fused kernels against the chain of standalone operators
     (embedding, rms_norm, linear, rope, rearrange into the KV cache,
-    self_attention, linear, add, swiglu, argmax) stores.  7 tokens take the
-    GEMV path with its fused norms; 40 take the skinny split-K products, whose
-    residual reductions also write the following RMSNorm."""
+    self_attention, linear, add, swiglu, argmax) on the same input.  7 tokens
+    take the GEMV path with its fused norms; 40 take the skinny split-K
+    products, whose residual reductions also write the following RMSNorm.
+    Checked: the K and V caches of every layer are bit-equal (the fused QKV
+    epilogue rounds bias-added q/k/v, then RoPE'd q/k, exactly as the
+    operators do); the final hidden state and the logits agree to float32
+    summation order (the fused products split K differently from the
+    standalone ones): hidden state within one bf16 ulp of its largest value,
+    logits within 1e-2, same argmax."""
     sh = SMALL_BF16
     w = synth.make_weights(sh, seed=6)
     if T == 7:
@@ -255,6 +262,11 @@ def test_fused_model_equals_unfused_operator_chain(T):
         fake.shape[1] = T
         q2.q2_rearrange(got_k, fake)
         assert torch.equal(got_k[0], kc.permute(1, 0, 2)[:T]), l
+        got_v = torch.empty(1, T, nkv, d, dtype=bf, device=DEV)
+        fake_v = q2.Q2Tensor.from_buffer_copy(kv_v)
+        fake_v.shape[1] = T
+        q2.q2_rearrange(got_v, fake_v)
+        assert torch.equal(got_v[0], vc.permute(1, 0, 2)[:T]), l
         a = torch.empty(T, H, dtype=bf, device=DEV)
         q2.q2_linear(a, att.view(T, nh * d), W[("o_proj.weight", l)])
         q2.q2_add(x, x, a)
@@ -275,8 +287,16 @@ def test_fused_model_equals_unfused_operator_chain(T):
     idx = torch.empty(1, dtype=torch.int64, device=DEV)
     val = torch.empty(1, dtype=torch.float32, device=DEV)
     q2.q2_argmax(idx, val, logits)
+    hid = m.hidden().float()
     m.close()
-    assert torch.allclose(logits, lg_model, atol=1e-2, rtol=0)
+    xf = x.float()
+    dh = float((hid - xf).abs().max())
+    dl = float((logits - lg_model).abs().max())
+    ulp = 2.0 ** (math.floor(math.log2(float(xf.abs().max()))) - 7)
+    print(f"\n[fused vs operators, T={T}] hidden max|d| = {dh:.3e} (bf16 ulp of max {ulp:.3e}, "
+          f"{int((hid != xf).sum())} of {hid.numel()} differ), logits max|d| = {dl:.3e}", flush=True)
+    assert dh <= ulp
+    assert dl <= 1e-2
     assert int(idx[0]) == int(nxt_model[0])
 
 

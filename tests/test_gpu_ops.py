@@ -122,14 +122,17 @@ def test_rope_batched_in_place_large_theta():
                                    # odd feature counts: the GEMV's shared-out last rows end
                                    # in an unpaired feature
                                    (1, 257, 1536), (7, 1001, 640)])
-@pytest.mark.parametrize("bias,out_f32", [(True, False), (False, True)])
-def test_linear_bf16(M, N, K, bias, out_f32):
+@pytest.mark.parametrize("bias,out_f32,ws", [(True, False, True), (False, True, True), (True, False, False)])
+def test_linear_bf16(M, N, K, bias, out_f32, ws):
+    """With a workspace of the size q2_linear_workspace_bytes asks for (the
+    split-K plan), and without one (every product unsplit)."""
     r = rng(M * 1000 + N + K)
     x = bf16_vals(r, (M, K))
     w = bf16_vals(r, (N, K), 0.05)
     b = bf16_vals(r, (N,), 0.1) if bias else None
     out = torch.empty(M, N, dtype=torch.float32 if out_f32 else BF, device=DEV)
-    q2.q2_linear(out, up(x, BF), up(w, BF), up(b, BF) if bias else None)
+    work = q2.workspace(q2.q2_linear_workspace_bytes(M, N, K)) if ws else None
+    q2.q2_linear(out, up(x, BF), up(w, BF), up(b, BF) if bias else None, work)
     ref = oracle.linear(x, w, b)
     absprod = np.abs(x) @ np.abs(w).T
     if out_f32:
@@ -161,7 +164,7 @@ def test_linear_f32():
 
 # ------------------------------------------------------------------ attention
 
-def _attn_case(seed, B, T, S, nh, nkv, d, dtype, cache_layout=False, smax=None, fill=0.0):
+def _attn_case(seed, B, T, S, nh, nkv, d, dtype, cache_layout=False, smax=None, fill=0.0, use_ws=True):
     r = rng(seed)
     q = bf16_vals(r, (B, T, nh, d))
     k = bf16_vals(r, (B, S, nkv, d))
@@ -178,7 +181,8 @@ def _attn_case(seed, B, T, S, nh, nkv, d, dtype, cache_layout=False, smax=None, 
     else:
         kt, vt = up(k, dtype), up(v, dtype)
     out = torch.empty(B, T, nh, d, dtype=dtype, device=DEV)
-    q2.q2_self_attention(out, up(q, dtype), kt, vt, scale)
+    nbytes = q2.q2_self_attention_workspace_bytes(B, T, S, nh, nkv, d, 1 if dtype == BF else 0)
+    q2.q2_self_attention(out, up(q, dtype), kt, vt, scale, q2.workspace(nbytes) if use_ws else None)
     got = down(out)
     for b in range(B):
         ref = oracle.attention(q[b], k[b], v[b], scale)
@@ -294,3 +298,77 @@ def test_rearrange_bit_exact(dtype):
     q2.q2_rearrange(cache.permute(0, 2, 1, 3)[:, 10:13], new)
     assert torch.equal(cache.permute(0, 2, 1, 3)[:, 10:13].cpu(), new.cpu())
     assert int((cache != 0).sum()) == int((new != 0).sum())
+
+
+@pytest.mark.parametrize("B,T,S", [(2, 1, 4097), (64, 1, 1000), (1, 1024, 1024)])
+def test_attention_bf16_without_workspace(B, T, S):
+    """No workspace: the split-KV decode and the split prefill blocks run
+    unsplit, with the same results up to float32 rounding."""
+    assert q2.q2_self_attention_workspace_bytes(B, T, S, 12, 2, 128) > 0
+    _attn_case(B + T + S + 5, B, T, S, 12, 2, 128, BF, use_ws=False)
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_ops_with_workspace_captured_in_a_graph():
+    """q2_linear and q2_self_attention at sizes whose plans split (so their
+    partials live in the caller's workspace) captured into one HIP graph,
+    replayed three times on fresh inputs with eager work and host
+    synchronisation between the replays; every replay matches the oracle."""
+    r = rng(77)
+    shapes = [(1, 17920, 1536), (48, 1536, 8960)]
+    lin = []
+    for M, N, K in shapes:
+        nb = q2.q2_linear_workspace_bytes(M, N, K)
+        assert nb > 0, (M, N, K)
+        w = bf16_vals(r, (N, K), 0.05)
+        lin.append(dict(M=M, N=N, K=K, w=w, W=up(w, BF), X=torch.empty(M, K, dtype=BF, device=DEV),
+                        out=torch.empty(M, N, dtype=BF, device=DEV), ws=q2.workspace(nb)))
+    att = []
+    for B, T, S in [(2, 1, 4097), (1, 1024, 1024)]:
+        nb = q2.q2_self_attention_workspace_bytes(B, T, S, 12, 2, 128)
+        assert nb > 0, (B, T, S)
+        att.append(dict(B=B, T=T, S=S, q=torch.empty(B, T, 12, 128, dtype=BF, device=DEV),
+                        k=torch.empty(B, S, 2, 128, dtype=BF, device=DEV),
+                        v=torch.empty(B, S, 2, 128, dtype=BF, device=DEV),
+                        out=torch.empty(B, T, 12, 128, dtype=BF, device=DEV), ws=q2.workspace(nb)))
+    scale = 1 / math.sqrt(128)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in lin:
+            q2.q2_linear(c["out"], c["X"], c["W"], None, c["ws"])
+        for c in att:
+            q2.q2_self_attention(c["out"], c["q"], c["k"], c["v"], scale, c["ws"])
+    for rep in range(3):
+        xs = []
+        for c in lin:
+            x = bf16_vals(r, (c["M"], c["K"]))
+            c["X"].copy_(up(x, BF))
+            xs.append(x)
+        qkv = []
+        for c in att:
+            q = bf16_vals(r, (c["B"], c["T"], 12, 128))
+            k = bf16_vals(r, (c["B"], c["S"], 2, 128))
+            v = bf16_vals(r, (c["B"], c["S"], 2, 128))
+            c["q"].copy_(up(q, BF))
+            c["k"].copy_(up(k, BF))
+            c["v"].copy_(up(v, BF))
+            qkv.append((q, k, v))
+        # eager work on the same stream between replays (overwrites the workspaces)
+        for c in lin:
+            junk = torch.empty_like(c["out"])
+            q2.q2_linear(junk, c["X"], c["W"], None, c["ws"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for c, x in zip(lin, xs):
+            ref = oracle.bf16_round(oracle.linear(x, c["w"]))
+            assert_close(down(c["out"]), ref, 1e-6 * (np.abs(x) @ np.abs(c["w"]).T), 2 ** -7,
+                         f"captured linear {c['M']}x{c['N']}x{c['K']} replay {rep}")
+        for c, (q, k, v) in zip(att, qkv):
+            got = down(c["out"])
+            for b in range(c["B"]):
+                ref = oracle.bf16_round(oracle.attention(q[b], k[b], v[b], scale))
+                assert_close(got[b], ref, 4e-3 * np.abs(v).max(), 2 ** -7,
+                             f"captured attention B={c['B']} T={c['T']} S={c['S']} replay {rep} b={b}")

@@ -84,7 +84,7 @@ def test_persistent_against_oracle_small():
     model = build_model(SMALL_BF16, w, wl.max_seq, 2)
     model.set_decode_path(True)
     orc = oracle.OracleModel(SMALL_BF16, w, "bf16", 2, wl.max_seq)
-    orc64 = oracle.OracleModel(SMALL_BF16, w, "bf16", 2, wl.max_seq, accum="f64")
+    orc64 = oracle.OracleModel(SMALL_BF16, w, "bf16", 2, wl.max_seq, accum="f64", share_from=orc)
     r = teacher_forced(model, orc, prompt, wl.steps, orc64)
     model.check()
     print(f"\n[persistent small vs oracle] {r.summary()}", flush=True)
@@ -105,7 +105,7 @@ def test_persistent_full_width_two_layers():
     model.set_decode_path(True)
     assert model.decode_path(1)
     orc = oracle.OracleModel(shape, w, "bf16", 1, wl.max_seq + 4)
-    orc64 = oracle.OracleModel(shape, w, "bf16", 1, wl.max_seq + 4, accum="f64")
+    orc64 = oracle.OracleModel(shape, w, "bf16", 1, wl.max_seq + 4, accum="f64", share_from=orc)
     model.set_decode_path(True)
     r = teacher_forced(model, orc, prompt, wl.steps, orc64)
     model.check()
@@ -153,7 +153,7 @@ def test_persistent_workload_b_full_depth_teacher_forced():
     model.set_decode_path(True)
     assert model.decode_path(1)
     orc = oracle.OracleModel(wl.shape, w, "bf16", 1, wl.max_seq)
-    orc64 = oracle.OracleModel(wl.shape, w, "bf16", 1, wl.max_seq, accum="f64")
+    orc64 = oracle.OracleModel(wl.shape, w, "bf16", 1, wl.max_seq, accum="f64", share_from=orc)
     r = teacher_forced(model, orc, prompt, wl.steps, orc64)
     model.check()
     model.close()
