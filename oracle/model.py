@@ -63,9 +63,12 @@ class OracleModel:
     F64_CACHE_BYTES = 16 << 30
 
     def __init__(self, shape, weights, storage: str, batch: int, max_seq: int, accum: str = "f32",
-                 share_from: "OracleModel | None" = None):
+                 share_from: "OracleModel | None" = None, cache_f64: bool | None = None):
         """``share_from``: another oracle of the same shape whose float32
-        weight copies this one reuses (read-only) instead of widening its own."""
+        weight copies this one reuses (read-only) instead of widening its own.
+        ``cache_f64`` (accum "f64"): keep float64 copies of the matrices
+        instead of widening them at every product; None keeps them while they
+        take at most F64_CACHE_BYTES."""
         if storage not in ("bf16", "fp32") or accum not in ("f32", "f64"):
             raise ValueError((storage, accum))
         self.shape = shape
@@ -82,7 +85,9 @@ class OracleModel:
             for key, arr in weights.items():
                 self.w[key] = ops.widen_bf16(arr) if arr.dtype == np.uint16 else np.asarray(arr, F32)
         self.w64 = {}
-        if accum == "f64" and sum(a.size for a in self.w.values()) * 8 <= self.F64_CACHE_BYTES:
+        if cache_f64 is None:
+            cache_f64 = sum(a.size for a in self.w.values()) * 8 <= self.F64_CACHE_BYTES
+        if accum == "f64" and cache_f64:
             self.w64 = {id(a): a.astype(np.float64) for a in self.w.values() if a.ndim == 2}
         self.on_layer = None        # optional callback(layer) after each layer (progress reports)
         L, nkv, d = shape.nlayer, shape.nkv, shape.dh

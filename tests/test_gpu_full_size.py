@@ -58,7 +58,7 @@ def _full_case(name, wl, steps, rows):
     max_seq = wl.prompt + steps
     _say(f"[{name}] weights drawn ({time.time() - t0:.0f} s)")
     orc = oracle.OracleModel(sh, w, "bf16", len(rows), max_seq)
-    orc64 = oracle.OracleModel(sh, w, "bf16", len(rows), max_seq, accum="f64", share_from=orc)
+    orc64 = oracle.OracleModel(sh, w, "bf16", len(rows), max_seq, accum="f64", share_from=orc, cache_f64=True)
     orc.on_layer = _progress(name + " f32")
     orc64.on_layer = _progress(name + " f64")
     ref_toks, ref_logits, spread = parity.reference(orc, prompt[rows], steps, orc64)

@@ -214,12 +214,14 @@ def test_fused_model_equals_unfused_operator_chain(T):
     self_attention, linear, add, swiglu, argmax) on the same input.  7 tokens
     take the GEMV path with its fused norms; 40 take the skinny split-K
     products, whose residual reductions also write the following RMSNorm.
-    Checked: the K and V caches of every layer are bit-equal (the fused QKV
-    epilogue rounds bias-added q/k/v, then RoPE'd q/k, exactly as the
-    operators do); the final hidden state and the logits agree to float32
-    summation order (the fused products split K differently from the
-    standalone ones): hidden state within one bf16 ulp of its largest value,
-    logits within 1e-2, same argmax."""
+    At 7 tokens every product sums K in the same order on both sides, so the
+    K and V caches of every layer, the final hidden state and the logits are
+    bit-equal (the fused epilogues and prologues round exactly where the
+    operators do).  At 40 tokens the fused products split K differently from
+    the standalone ones (float32 sums in another order, and from layer 1 on
+    an input that differs by those flips), so the caches are held to two
+    bf16 steps of their largest value, the hidden state to one bf16 step of
+    its largest value and the logits to 1e-2, with the same argmax."""
     sh = SMALL_BF16
     w = synth.make_weights(sh, seed=6)
     if T == 7:
@@ -227,6 +229,7 @@ def test_fused_model_equals_unfused_operator_chain(T):
     else:
         ids = ((np.arange(T, dtype=np.int64) * 37 + 1) % sh.vocab)[None, :]
     H, nh, nkv, d, I = sh.hidden, sh.nh, sh.nkv, sh.dh, sh.inter
+    exact = T == 7
     smax = max(16, T)
     m = build_model(sh, w, smax, 1)
     nxt_model, lg_model = m.prefill(torch.from_numpy(ids).to(DEV), logits=True)
@@ -261,12 +264,16 @@ def test_fused_model_equals_unfused_operator_chain(T):
         fake = q2.Q2Tensor.from_buffer_copy(kv_k)
         fake.shape[1] = T
         q2.q2_rearrange(got_k, fake)
-        assert torch.equal(got_k[0], kc.permute(1, 0, 2)[:T]), l
         got_v = torch.empty(1, T, nkv, d, dtype=bf, device=DEV)
         fake_v = q2.Q2Tensor.from_buffer_copy(kv_v)
         fake_v.shape[1] = T
         q2.q2_rearrange(got_v, fake_v)
-        assert torch.equal(got_v[0], vc.permute(1, 0, 2)[:T]), l
+        for got_c, ref_c in ((got_k[0], kc.permute(1, 0, 2)[:T]), (got_v[0], vc.permute(1, 0, 2)[:T])):
+            if exact:
+                assert torch.equal(got_c, ref_c), l
+            else:
+                dc = float((got_c.float() - ref_c.float()).abs().max())
+                assert dc <= 2 ** -6 * float(ref_c.float().abs().max()), (l, dc)
         a = torch.empty(T, H, dtype=bf, device=DEV)
         q2.q2_linear(a, att.view(T, nh * d), W[("o_proj.weight", l)])
         q2.q2_add(x, x, a)
@@ -295,6 +302,8 @@ def test_fused_model_equals_unfused_operator_chain(T):
     ulp = 2.0 ** (math.floor(math.log2(float(xf.abs().max()))) - 7)
     print(f"\n[fused vs operators, T={T}] hidden max|d| = {dh:.3e} (bf16 ulp of max {ulp:.3e}, "
           f"{int((hid != xf).sum())} of {hid.numel()} differ), logits max|d| = {dl:.3e}", flush=True)
+    if exact:
+        assert dh == 0 and dl == 0
     assert dh <= ulp
     assert dl <= 1e-2
     assert int(idx[0]) == int(nxt_model[0])
