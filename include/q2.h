@@ -101,6 +101,23 @@ q2_status q2_linear(const q2_tensor* out, const q2_tensor* in, const q2_tensor* 
  * features, K in features of dtype Q2_F32 / Q2_BF16 (0: it never splits). */
 q2_status q2_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t dtype, size_t* bytes);
 
+/* Bytes of the fixed device scratch of q2_linear_noalloc (per GPU). */
+#define Q2_LINEAR_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* q2_linear for callers that cannot allocate or pass a workspace (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid device
+ * allocation): the same operation, operands, layout and plan as q2_linear
+ * with a large enough workspace, but the split-K partials live in a fixed
+ * Q2_LINEAR_NOALLOC_SCRATCH_BYTES array inside the library, one per GPU,
+ * held until the process ends.  Calls no allocating routine.  Products whose
+ * partials would exceed that size fail with Q2_ESHAPE (nothing launched).
+ * Every call on one GPU shares that GPU's array: calls that can overlap on
+ * one GPU (different streams, or different host threads) race and must be
+ * ordered by the caller.  The array is looked up on the first call on each
+ * GPU. */
+q2_status q2_linear_noalloc(const q2_tensor* out, const q2_tensor* in, const q2_tensor* weight,
+                            const q2_tensor* bias, void* stream);
+
 /* out = in / sqrt(mean(in^2) + eps) * weight over the last dimension
  * (section 3.2, rms_norm; epsilon inside the root).  in/out: [..., H];
  * weight: [H]; all the same dtype (f32 or bf16).  The output is rounded once. */

@@ -56,6 +56,7 @@ _SIGS = {
     "q2_version": ([], ctypes.c_char_p),
     "q2_embedding": ([_P, _P, _P, _S], ctypes.c_int),
     "q2_linear": ([_P, _P, _P, _P, _P, _S], ctypes.c_int),
+    "q2_linear_noalloc": ([_P, _P, _P, _P, _S], ctypes.c_int),
     "q2_linear_workspace_bytes": ([ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                    ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "q2_rms_norm": ([_P, _P, _P, ctypes.c_float, _S], ctypes.c_int),
@@ -149,6 +150,15 @@ def q2_linear(out, inp, weight, bias=None, workspace=None, stream=None):
     _check(lib.q2_linear(_ref(desc(out)), _ref(desc(inp)), _ref(desc(weight)), _ref(desc(bias)),
                          _ref(desc(workspace)), _stream(stream)))
     return out
+
+
+def q2_linear_noalloc(out, inp, weight, bias=None, stream=None):
+    _check(lib.q2_linear_noalloc(_ref(desc(out)), _ref(desc(inp)), _ref(desc(weight)), _ref(desc(bias)),
+                                 _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def q2_linear_workspace_bytes(M, N, K, dtype=Q2_BF16) -> int:

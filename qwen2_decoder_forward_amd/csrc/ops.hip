@@ -1,4 +1,6 @@
 // Memory-bound operator kernels and the operator entry points of the C ABI.
+#include <mutex>
+
 #include "attention.hpp"
 #include "epilogue.hpp"
 #include "simple.hpp"
@@ -508,6 +510,56 @@ extern "C" q2_status q2_linear(const q2_tensor* out, const q2_tensor* in, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dt == Q2_F32) return gemm_f32(a, s);
   a.unsplit_if_short = true;
+  return gemm_bf16(a, s);
+}
+
+// ------------------------------------------------------------ allocation-free linear
+
+// Split-K partials of q2_linear_noalloc: a fixed array in the library's code
+// object, one copy per GPU, held until the process ends.  Host code never
+// passes `scratch` itself to a kernel (on the host it only names the symbol):
+// it uses the device address hipGetSymbolAddress returns for the current GPU.
+static __device__ __align__(256) unsigned char scratch[Q2_LINEAR_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current GPU's copy of `scratch`, looked up on the
+// first call on that GPU.
+static q2_status noalloc_scratch(void** out) {
+  int dev = 0;
+  Q2_HIP(hipGetDevice(&dev));
+  Q2_CHECK(dev >= 0 && dev < kMaxDevices, Q2_EINVAL, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    Q2_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    Q2_CHECK(p != nullptr, Q2_EHIP, "hipGetSymbolAddress returned a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return Q2_OK;
+}
+
+extern "C" q2_status q2_linear_noalloc(const q2_tensor* out, const q2_tensor* in, const q2_tensor* weight,
+                                       const q2_tensor* bias, void* stream) {
+  clear_error();
+  GemmArgs a{};
+  int32_t dt = 0;
+  Q2_TRY(linear_args(out, in, weight, bias, &a, &dt));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dt == Q2_F32) return gemm_f32(a, s);
+  const size_t need = linear_partial_bytes(dt, a.M, a.N, a.K);
+  Q2_CHECK(need <= Q2_LINEAR_NOALLOC_SCRATCH_BYTES, Q2_ESHAPE,
+           "q2_linear_noalloc: %d x %d x %d needs %zu bytes of split-K partials, more than its %zu-byte "
+           "scratch (use q2_linear with a workspace)",
+           a.M, a.N, a.K, need, static_cast<size_t>(Q2_LINEAR_NOALLOC_SCRATCH_BYTES));
+  if (need) {
+    Q2_TRY(noalloc_scratch(&a.scratch));
+    a.scratch_bytes = Q2_LINEAR_NOALLOC_SCRATCH_BYTES;
+  }
+  // the same plan as q2_linear with a workspace of at least `need` bytes
   return gemm_bf16(a, s);
 }
 
