@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=50)
     ap.add_argument("--only-kernel", action="store_true",
                     help="time only the dominant kernel (for profiler counter runs) and print its record")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
+                    help="KV cache: bf16 (the workloads' definition) or FP8 E4M3 blocks with per-block scales")
     return ap.parse_args()
 
 
@@ -66,14 +68,18 @@ def weight_bytes(sh, es=2):
     return sh.nlayer * per_layer + V * H * es + H * es
 
 
-def kv_bytes_per_token(sh, es=2):
-    """K and V bytes of one cached position across all layers (Day-0 article, step 7)."""
-    return 2 * sh.nlayer * sh.nkv * sh.dh * es
+def kv_bytes_per_token(sh, kv_fp8=False):
+    """K and V bytes of one cached position across all layers (Day-0 article,
+    step 7); the FP8 cache stores one byte per element plus a float32 scale
+    per 128-element block."""
+    if kv_fp8:
+        return 2 * sh.nlayer * sh.nkv * (sh.dh + 4 * (sh.dh // 128))
+    return 2 * sh.nlayer * sh.nkv * sh.dh * 2
 
 
-def decode_step_bytes(sh, batch, ctx):
+def decode_step_bytes(sh, batch, ctx, kv_fp8=False):
     """Algorithmic HBM bytes of one decode step at context ctx (keys incl. the new one)."""
-    return weight_bytes(sh) + batch * (ctx * kv_bytes_per_token(sh) + sh.hidden * 2)
+    return weight_bytes(sh) + batch * (ctx * kv_bytes_per_token(sh, kv_fp8) + sh.hidden * 2)
 
 
 def prefill_flops(sh, batch, T):
@@ -100,78 +106,72 @@ def time_launches(fn, reps, stream):
     return e0.elapsed_time(e1) / reps * 1e-3   # seconds per launch
 
 
-# Weight buffers the dominant-kernel timing cycles through: together they are
-# several times the 256 MB last-level (Infinity) cache, so every launch streams
-# its operand from HBM as it does inside a decode step.
-CYCLE_BYTES = 1 << 30
 CALIB_COPY_BYTES = 512 << 20   # plain device copy, the reference for the HBM byte counters
 
+STAGE_NAMES = {0: "QKV", 1: "attention", 2: "o_proj", 3: "gate/up", 4: "down"}
 
-def dominant_kernel(wl, reps):
-    """Time the dominant kernel at its in-step shape through the C ABI."""
+
+def in_step_kernel(model, wl, prompt, reps, kv_fp8):
+    """Time the dominant kernel of the step as the step launches it: the
+    model replays that product (q2_model_replay_stage: the same kernels and
+    arguments as the forward, on the model's own weights and buffers) for
+    layers 0, 1, ... in turn, `reps` launches between two HIP events on the
+    launch stream.  Cycling the 28 layers keeps every launch streaming its
+    weights (or KV rows) from HBM, as in the step.  The model is reset
+    afterwards."""
     import torch
     import qwen2_decoder_forward_amd as q2
     sh = wl.shape
     dev = "cuda:0"
     stream = torch.cuda.current_stream()
-    g = torch.Generator(device=dev).manual_seed(0)
-    # a copy of known size, so that profiler byte counters can be scaled
+    # a copy of known size first, so that profiler byte counters can be scaled
     src = torch.empty(CALIB_COPY_BYTES // 4, device=dev, dtype=torch.float32).fill_(1.0)
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    if wl.key in ("B", "E"):
-        # decode GEMV/skinny GEMM over the packed gate/up weight [2I, H]
-        M, N, K = wl.batch, 2 * sh.inter, sh.hidden
-        nbuf = max(2, -(-CYCLE_BYTES // (N * K * 2)))
-        Ws = [(torch.randn(N, K, device=dev, generator=g) * 0.02).to(torch.bfloat16) for _ in range(nbuf)]
-        X = torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16)
-        out = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
-        ws = q2.workspace(q2.q2_linear_workspace_bytes(M, N, K))
-        it = [0]
-
-        def launch():
-            q2.q2_linear(out, X, Ws[it[0] % nbuf], None, ws)
-            it[0] += 1
-        dt = time_launches(launch, reps, stream)
-        traffic = N * K * 2 + M * K * 2 + M * N * 2
-        return {"kernel": "gemv_kernel (q2_linear, bf16, M=%d N=%d K=%d, %d weight buffers cycled)" % (M, N, K, nbuf),
-                "bound": "hbm", "achieved": traffic / dt / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "bytes_per_launch": traffic, "avg_launch_us": dt * 1e6}
+    model.reset()
+    B, H, I = wl.batch, sh.hidden, sh.inter
     if wl.key == "C":
-        M, N, K = wl.prompt, 2 * sh.inter, sh.hidden
-        W = (torch.randn(N, K, device=dev, generator=g) * 0.02).to(torch.bfloat16)
-        X = torch.randn(M, K, device=dev, generator=g).to(torch.bfloat16)
-        out = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
-        dt = time_launches(lambda: q2.q2_linear(out, X, W), reps, stream)
-        flops = 2 * M * N * K
-        return {"kernel": "gemm_dtl_mix_kernel (q2_linear, bf16, M=%d N=%d K=%d)" % (M, N, K),
-                "bound": "mfma", "achieved": flops / dt / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "flops_per_launch": flops, "avg_launch_us": dt * 1e6}
-    # D: split-KV decode attention over a 4097-key cache for 64 sequences
-    B, S = wl.batch, wl.prompt + 1
-    kv_bytes = 2 * B * S * sh.nkv * sh.dh * 2
-    nbuf = max(2, -(-CYCLE_BYTES // kv_bytes))
-    q = torch.randn(B, 1, sh.nh, sh.dh, device=dev, generator=g).to(torch.bfloat16)
-    kvs = [(torch.randn(B, S, sh.nkv, sh.dh, device=dev, generator=g).to(torch.bfloat16),
-            torch.randn(B, S, sh.nkv, sh.dh, device=dev, generator=g).to(torch.bfloat16)) for _ in range(nbuf)]
-    o = torch.empty_like(q)
-    ws = q2.workspace(q2.q2_self_attention_workspace_bytes(B, 1, S, sh.nh, sh.nkv, sh.dh))
-    it = [0]
+        stage, tokens = q2.STAGE_GATE_UP, wl.prompt          # the prefill product at length 0
+    else:
+        nxt = torch.empty(B, dtype=torch.int64, device=dev)
+        q2.q2_model_prefill(model.handle, prompt, nxt)        # decode products at length = prompt
+        stage = q2.STAGE_ATTN if wl.key == "D" else q2.STAGE_GATE_UP
+        tokens = 1
 
-    def launch():
-        k, v = kvs[it[0] % nbuf]
-        q2.q2_self_attention(o, q, k, v, sh.dh ** -0.5, ws)
-        it[0] += 1
-    dt = time_launches(launch, reps, stream)
-    traffic = kv_bytes + 2 * q.numel() * 2
-    return {"kernel": "attn_decode_kernel + attn_combine_kernel (q2_self_attention, B=%d S=%d, %d caches cycled)"
-            % (B, S, nbuf), "bound": "hbm", "achieved": traffic / dt / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "bytes_per_launch": traffic, "avg_launch_us": dt * 1e6}
+    def launch(n):
+        q2.q2_model_replay_stage(model.handle, stage, B, tokens, n)
+    launch(sh.nlayer)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    launch(reps)
+    e1.record(stream)
+    e1.synchronize()
+    dt = e0.elapsed_time(e1) / reps * 1e-3
+    model.reset()
+    name = f"{STAGE_NAMES[stage]} product of the step (q2_model_replay_stage, {B} x {tokens} rows, layers cycled)"
+    if wl.key == "C":
+        flops = 2 * wl.prompt * 2 * I * H
+        return {"kernel": "gemm_dtl_mix_kernel, " + name, "bound": "mfma", "achieved": flops / dt / 1e12,
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "flops_per_launch": flops, "avg_launch_us": dt * 1e6}
+    if wl.key == "D":
+        keys = wl.prompt + 1
+        per_key = sh.nkv * (sh.dh * (1 if kv_fp8 else 2) + (4 if kv_fp8 else 0))
+        traffic = 2 * B * keys * per_key + B * sh.nh * sh.dh * 2
+        kern = "attn_decode_kernel<%s>" % ("fp8" if kv_fp8 else "bf16")
+        return {"kernel": kern + ", " + name, "bound": "hbm", "achieved": traffic / dt / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "bytes_per_launch": traffic, "avg_launch_us": dt * 1e6}
+    # weights, norm weight, residual rows and their sums of squares, SwiGLU output
+    traffic = 2 * I * H * 2 + H * 2 + B * H * 2 + B * (H // 16) * 4 + B * I * 2
+    return {"kernel": "gemv_kernel (norm prologue, SwiGLU epilogue), " + name, "bound": "hbm",
+            "achieved": traffic / dt / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": traffic,
+            "avg_launch_us": dt * 1e6}
 
 
-def measured_traffic(wl):
+def measured_traffic(wl, kv="bf16"):
     """HBM bytes per launch of the dominant kernel from the committed profiler
     counter runs, or None when they are absent or the kernel source changed
     since they were taken."""
@@ -179,7 +179,7 @@ def measured_traffic(wl):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f).get(wl.key)
+            rec = json.load(f).get(wl.key if kv == "bf16" else f"{wl.key}-{kv}")
     except (OSError, ValueError):
         return None
     if not rec:
@@ -212,7 +212,7 @@ def blas_threads():
         return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(wl, weights, budget_s):
+def cpu_baseline(wl, weights, budget_s, kv="bf16"):
     """Time the oracle, as it stands, on a bounded sample of the workload.
     Returns (record, reference) where reference holds the oracle's greedy
     tokens and logits when the sample is the whole workload (B), for the
@@ -224,7 +224,7 @@ def cpu_baseline(wl, weights, budget_s):
     if wl.key == "B":
         # the whole workload: prefill of the prompt, then every greedy decode step
         prompt = synth.make_prompt(wl)
-        orc = oracle.OracleModel(sh, weights, "bf16", 1, wl.prompt + wl.steps)
+        orc = oracle.OracleModel(sh, weights, "bf16", 1, wl.prompt + wl.steps, kv="fp8" if kv == "fp8" else "model")
         t0 = time.perf_counter()
         logits, nxt = orc.forward(prompt)
         t_pre = time.perf_counter() - t0
@@ -276,7 +276,8 @@ def parity_record(model, wl, weights, ref):
     import oracle
     from oracle import parity
     orc, prompt, toks, ref_logits = ref
-    orc64 = oracle.OracleModel(wl.shape, weights, "bf16", 1, wl.prompt + wl.steps, accum="f64", share_from=orc)
+    orc64 = oracle.OracleModel(wl.shape, weights, "bf16", 1, wl.prompt + wl.steps, accum="f64", share_from=orc,
+                               kv=orc.kv)
     _, l64 = orc64.generate(prompt, wl.steps, teacher=toks)
     spread = max(float(np.abs(oracle.bf16_round(a) - oracle.bf16_round(b)).max()) for a, b in zip(ref_logits, l64))
     del orc64
@@ -314,19 +315,21 @@ def main():
     sh = wl.shape
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    if args.only_kernel:
-        dk = dominant_kernel(wl, args.kernel_reps)
-        print(json.dumps({"workload": wl.key, "dominant_kernel": dk}), flush=True)
-        return
+    kv_fp8 = args.kv == "fp8"
     t0 = time.perf_counter()
     weights = synth.make_weights(wl)
     t_gen = time.perf_counter() - t0
     max_seq = wl.prompt + wl.steps
     t0 = time.perf_counter()
-    model = q2.load_model(sh, weights, max_seq, wl.batch)
+    model = q2.load_model(sh, weights, max_seq, wl.batch, kv_fp8=kv_fp8)
     torch.cuda.synchronize()
     t_load = time.perf_counter() - t0
     prompt = torch.from_numpy(synth.make_prompt(wl)).to(dev)
+    if args.only_kernel:
+        dk = in_step_kernel(model, wl, prompt, args.kernel_reps, kv_fp8)
+        print(json.dumps({"workload": wl.key, "kv": args.kv, "dominant_kernel": dk}), flush=True)
+        model.close()
+        return
     nxt = torch.empty(wl.batch, dtype=torch.int64, device=dev)
     out = torch.empty(wl.batch, max(wl.steps, 1), dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
@@ -363,17 +366,17 @@ def main():
     prefill_tok_s = wl.batch * wl.prompt / pre_s
     decode_tok_s = wl.batch * wl.steps / dec_s if wl.steps else None
 
-    dk = dominant_kernel(wl, args.kernel_reps)
+    dk = in_step_kernel(model, wl, prompt, args.kernel_reps, kv_fp8)
     roofline = {"bound": dk["bound"], "achieved": round(dk["achieved"], 2), "peak": dk["peak"], "unit": dk["unit"],
-                "frac": round(dk["achieved"] / dk["peak"], 4), "traffic": measured_traffic(wl), "kernel": dk["kernel"],
-                "avg_launch_us": round(dk["avg_launch_us"], 2)}
+                "frac": round(dk["achieved"] / dk["peak"], 4), "traffic": measured_traffic(wl, args.kv),
+                "kernel": dk["kernel"], "avg_launch_us": round(dk["avg_launch_us"], 2)}
     for key in ("bytes_per_launch", "flops_per_launch"):
         if key in dk:
             roofline[key] = dk[key]
 
     if wl.steps:
         ctxs = range(wl.prompt + 1, wl.prompt + wl.steps + 1)
-        step_bytes = float(np.mean([decode_step_bytes(sh, wl.batch, c) for c in ctxs]))
+        step_bytes = float(np.mean([decode_step_bytes(sh, wl.batch, c, kv_fp8) for c in ctxs]))
         gbs = step_bytes / (dec_s / wl.steps) / 1e9
         step_roof = {"what": "decode step", "bound": "hbm", "bytes_per_step": step_bytes, "achieved": round(gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
@@ -385,7 +388,7 @@ def main():
 
     cpu = par = None
     if not args.no_cpu:
-        cpu, ref = cpu_baseline(wl, weights, args.cpu_seconds)
+        cpu, ref = cpu_baseline(wl, weights, args.cpu_seconds, args.kv)
         if ref is not None:
             par = parity_record(model, wl, weights, ref)
 
@@ -398,8 +401,9 @@ def main():
         "value": round(value, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(float(np.mean(step_ms)), 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random-init weights and prompt ids)",
-        "config": {"workload": f"{wl.key}: {wl.description}", "shape": sh.name, "batch": wl.batch,
-                   "prompt": wl.prompt, "decode_steps": wl.steps, "parallelism": "single GPU"},
+        "config": {"workload": f"{wl.key}: {wl.description}" + (" (FP8 KV cache)" if kv_fp8 else ""),
+                   "shape": sh.name, "batch": wl.batch, "prompt": wl.prompt, "decode_steps": wl.steps,
+                   "kv_cache": args.kv, "parallelism": "single GPU"},
         "prefill_tok_s": round(prefill_tok_s, 1),
         "decode_tok_s": round(decode_tok_s, 2) if decode_tok_s else None,
         "prefill_ms": round(pre_s * 1e3, 3), "decode_ms": round(dec_s * 1e3, 3),

@@ -53,7 +53,8 @@ typedef enum {
   Q2_ESTATE = -7   /* model state does not allow the call (capacity, batch) */
 } q2_status;
 
-typedef enum { Q2_F32 = 0, Q2_BF16 = 1, Q2_I64 = 2 } q2_dtype;
+/* Q2_U8: bytes (FP8 KV-cache codes). */
+typedef enum { Q2_F32 = 0, Q2_BF16 = 1, Q2_I64 = 2, Q2_U8 = 3 } q2_dtype;
 
 #define Q2_MAX_DIMS 5
 
@@ -176,6 +177,20 @@ q2_status q2_argmax(const q2_tensor* max_idx, const q2_tensor* max_val, const q2
  * overlapping in/out is undefined. */
 q2_status q2_rearrange(const q2_tensor* out, const q2_tensor* in, void* stream);
 
+/* FP8 KV-cache codec ("新一代大模型Day0推理适配与性能调优教程", step 5: the KV
+ * cache quantised to FP8 per token x per head x block of 128 elements, with
+ * high-precision accumulation).  One block = one row of 128 values.
+ *   amax = max |x_i|; scale = amax / 448 in float32 (0 for an all-zero row);
+ *   code_i = E4M3(x_i / scale): OCP FP8 E4M3 (bias 7, no infinities, max 448),
+ *   round to nearest even, magnitude saturated at 448, sign of x_i kept
+ *   (so -0 codes as 0x80).
+ * q2_kv_quantize: x [N, 128] bf16 -> codes [N, 128] u8, scales [N] f32.
+ * q2_kv_dequantize: x_i = bf16(value(code_i) * scale) (float32 product, then
+ * round to nearest even).  Rows 16-byte aligned; scales contiguous.  Codes
+ * and dequantised values are bit-exact functions of their inputs. */
+q2_status q2_kv_quantize(const q2_tensor* codes, const q2_tensor* scales, const q2_tensor* x, void* stream);
+q2_status q2_kv_dequantize(const q2_tensor* x, const q2_tensor* codes, const q2_tensor* scales, void* stream);
+
 /* ------------------------------------------------------------------------
  * Model driver (section 3.2, fourth layer; section 3.3 item 4: per-device
  * handles and intermediate buffers are created once and reused).
@@ -196,6 +211,10 @@ typedef struct {
   int32_t max_batch;    /* sequences per call, at most */
   float eps;            /* RMSNorm epsilon */
   float theta;          /* RoPE base */
+  int32_t kv_fp8;       /* 0: KV cache in the model dtype; 1 (bf16 models): FP8
+                           E4M3 codes with one float32 scale per token, KV head
+                           and 128-element block ("新一代大模型Day0推理适配与性能调优
+                           教程", step 5), see q2_kv_quantize */
 } q2_config;
 
 /* Create a model on `device`: allocates the packed weights, the KV cache
@@ -264,8 +283,26 @@ q2_status q2_model_generate(q2_model* m, const q2_tensor* prompt, int32_t steps,
 q2_status q2_model_continue(q2_model* m, int32_t steps, const q2_tensor* out_ids, void* stream);
 
 /* Describe layer `layer`'s cache as tensors k, v of shape
- * [max_batch, max_seq, nkv, dh] (strided views of the [B][nkv][S][d] layout). */
+ * [max_batch, max_seq, nkv, dh] (strided views of the [B][nkv][S][d] layout;
+ * Q2_U8 codes for an FP8 cache). */
 q2_status q2_model_kv_view(q2_model* m, int32_t layer, q2_tensor* k, q2_tensor* v);
+
+/* FP8 cache only: layer `layer`'s scales as f32 tensors [max_batch, max_seq,
+ * nkv] (Q2_ESTATE for a cache in the model dtype). */
+q2_status q2_model_kv_scale_view(q2_model* m, int32_t layer, q2_tensor* k_scale, q2_tensor* v_scale);
+
+/* Measurement hook: launch, `reps` times on `stream`, the kernels of one
+ * product of a forward of `batch` sequences x `tokens` new tokens at the
+ * current cached length, for layers 0, 1, ..., nlayer - 1, 0, ... in turn:
+ * stage 0 QKV (with its fused norm and cache write), 1 attention, 2 o_proj,
+ * 3 gate/up, 4 down.  The kernels and arguments are those the forward (or
+ * the captured decode step) launches, reading the model's own weights and
+ * buffers.  The activations, the residual stream and the cache rows at the
+ * replayed positions are left undefined: reset before the next forward.
+ * Needs batch * tokens within the activation arena and len + tokens <=
+ * max_seq. */
+q2_status q2_model_replay_stage(q2_model* m, int32_t stage, int32_t batch, int32_t tokens, int32_t reps,
+                                void* stream);
 
 /* Cached length (positions per sequence). */
 q2_status q2_model_length(const q2_model* m, int32_t* len);

@@ -63,14 +63,21 @@ class OracleModel:
     F64_CACHE_BYTES = 16 << 30
 
     def __init__(self, shape, weights, storage: str, batch: int, max_seq: int, accum: str = "f32",
-                 share_from: "OracleModel | None" = None, cache_f64: bool | None = None):
+                 share_from: "OracleModel | None" = None, cache_f64: bool | None = None, kv: str = "model"):
         """``share_from``: another oracle of the same shape whose float32
         weight copies this one reuses (read-only) instead of widening its own.
         ``cache_f64`` (accum "f64"): keep float64 copies of the matrices
         instead of widening them at every product; None keeps them while they
-        take at most F64_CACHE_BYTES."""
-        if storage not in ("bf16", "fp32") or accum not in ("f32", "f64"):
-            raise ValueError((storage, accum))
+        take at most F64_CACHE_BYTES.
+        ``kv``: "model" keeps the KV cache in the storage type; "fp8" stores
+        every new k / v row as FP8 E4M3 blocks of 128 with a float32 scale
+        (ops.kv_quantize) and attention reads them back dequantised to bf16
+        ("新一代大模型Day0推理适配与性能调优教程", step 5)."""
+        if storage not in ("bf16", "fp32") or accum not in ("f32", "f64") or kv not in ("model", "fp8"):
+            raise ValueError((storage, accum, kv))
+        if kv == "fp8" and (storage != "bf16" or shape.dh != 128):
+            raise ValueError("the FP8 KV cache needs bf16 storage and head_dim 128")
+        self.kv = kv
         self.shape = shape
         self.storage = storage
         self.accum = accum
@@ -166,8 +173,12 @@ class OracleModel:
             for b in range(B):
                 qb = st(ops.rope(q[b], pos, sh.theta), "q_rope")
                 kb = st(ops.rope(k[b], pos, sh.theta), "k_rope")
+                vb = v[b]
+                if self.kv == "fp8":
+                    kb = ops.kv_dequantize(*ops.kv_quantize(kb))
+                    vb = ops.kv_dequantize(*ops.kv_quantize(vb))
                 self.k_cache[l][b, :, P:P + T, :] = kb.transpose(1, 0, 2)
-                self.v_cache[l][b, :, P:P + T, :] = v[b].transpose(1, 0, 2)
+                self.v_cache[l][b, :, P:P + T, :] = vb.transpose(1, 0, 2)
                 kc = self.k_cache[l][b, :, :P + T, :].transpose(1, 0, 2)
                 vc = self.v_cache[l][b, :, :P + T, :].transpose(1, 0, 2)
                 o[b] = st(ops.attention(qb, kc, vc, scale), "attn")

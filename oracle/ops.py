@@ -220,3 +220,83 @@ def rearrange(x: np.ndarray) -> np.ndarray:
     stride-aware copy).  Pinned by: element-wise equality with the source.
     """
     return np.array(x, copy=True, order="C")
+
+
+# ----------------------------------------------------------------------------- FP8 KV cache
+
+def e4m3_values() -> np.ndarray:
+    """Magnitudes of the FP8 E4M3 codes 0x00 .. 0x7E (float64, increasing).
+
+    OCP FP8 E4M3 ("FN", no infinities): 4 exponent bits with bias 7, 3
+    mantissa bits; exponent field 0 holds the subnormals m * 2^-9, fields
+    1..15 hold (1 + m/8) * 2^(e-7); 0x7F is NaN, so 0x7E = 448 is the largest
+    finite value.  The KV-cache quantisation of "新一代大模型Day0推理适配与性能调优教程"
+    (step 5) stores FP8 codes; the pages do not name the FP8 variant, and E4M3
+    (more mantissa, range 448) is the one used for stored tensors.
+
+    Pinned by: 1.0 = 0x38, 448 = 0x7E, the smallest subnormal 2^-9 = 0x01,
+    the values strictly increase, and a loop-written enumeration of the bit
+    fields in tests/_brute.py gives the same table.
+    """
+    codes = np.arange(0x7F)
+    e = codes >> 3
+    m = (codes & 7).astype(np.float64)
+    return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.power(2.0, e - 7))
+
+
+def e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 codes (uint8) of the float32 values y: round to the nearest
+    code, ties to the even code (mantissa LSB 0), magnitudes above 448
+    saturated to 448, sign bit = sign bit of y (so -0 -> 0x80).
+
+    Pinned by: every table value round-trips, brute-force nearest search on a
+    loop-written table, closed-form ties, saturation, signed zero.
+    """
+    y = np.asarray(y, F32)
+    vals = e4m3_values()
+    a = np.abs(y).astype(np.float64)
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, len(vals) - 1)   # vals[hi] >= a (or top)
+    lo = np.clip(hi - 1, 0, len(vals) - 1)
+    dlo = a - vals[lo]
+    dhi = vals[hi] - a
+    take_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo)
+    code = np.where(a >= vals[-1], len(vals) - 1, code)
+    code = np.where(a == 0, 0, code)
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """float32 values of FP8 E4M3 codes (0x7F / 0xFF, NaN, are never written)."""
+    codes = np.asarray(codes, np.uint8)
+    mag = e4m3_values()[np.minimum(codes & 0x7F, 0x7E)]
+    return np.where(codes & 0x80, -mag, mag).astype(F32)
+
+
+def kv_quantize(x: np.ndarray):
+    """Blocks of 128 values (last axis) -> (codes uint8, scales float32).
+
+    "新一代大模型Day0推理适配与性能调优教程", step 5: the KV cache is stored in FP8
+    with one scale per token x head x 128-element block, so a block's error
+    stays inside the block.  Reading (the pages do not give the scale rule):
+    absmax scaling in float32, scale = max|x| / 448, code = E4M3(x / scale);
+    an all-zero block has scale 0 and zero codes.
+
+    Pinned by: the largest element of a block codes to +-448, the round trip
+    error is within half an E4M3 step of each value (plus the bf16 write-back),
+    zero blocks, and the brute-force encode pins.
+    """
+    x = np.asarray(x, F32)
+    amax = np.max(np.abs(x), axis=-1, keepdims=True)
+    zero = amax == 0
+    scale = np.where(zero, F32(1), amax / F32(448.0)).astype(F32)
+    y = np.where(zero, x, x / scale).astype(F32)
+    return e4m3_encode(y), np.where(zero, F32(0), scale)[..., 0].astype(F32)
+
+
+def kv_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """bf16 values (as float32) of quantised blocks: round(value(code) * scale)
+    with a float32 product, rounded to bf16 (the storage type the attention
+    reads).  Pinned by: the kv_quantize pins (round trip)."""
+    v = e4m3_decode(codes) * np.asarray(scales, F32)[..., None]
+    return bf16_round(v.astype(F32))

@@ -18,8 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq2.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "q2.h")
 
-Q2_F32, Q2_BF16, Q2_I64 = 0, 1, 2
-_DTYPES = {torch.float32: Q2_F32, torch.bfloat16: Q2_BF16, torch.int64: Q2_I64}
+Q2_F32, Q2_BF16, Q2_I64, Q2_U8 = 0, 1, 2, 3
+_DTYPES = {torch.float32: Q2_F32, torch.bfloat16: Q2_BF16, torch.int64: Q2_I64, torch.uint8: Q2_U8}
 STATUS = {0: "Q2_OK", -1: "Q2_EINVAL", -2: "Q2_EDTYPE", -3: "Q2_ESHAPE", -4: "Q2_ESTRIDE",
           -5: "Q2_ENOMEM", -6: "Q2_EHIP", -7: "Q2_ESTATE"}
 MAX_DIMS = 5
@@ -34,7 +34,8 @@ class Q2Config(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("nlayer", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("nh", ctypes.c_int32), ("nkv", ctypes.c_int32), ("dh", ctypes.c_int32),
                 ("inter", ctypes.c_int32), ("vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32),
-                ("max_batch", ctypes.c_int32), ("eps", ctypes.c_float), ("theta", ctypes.c_float)]
+                ("max_batch", ctypes.c_int32), ("eps", ctypes.c_float), ("theta", ctypes.c_float),
+                ("kv_fp8", ctypes.c_int32)]
 
 
 class Q2Error(RuntimeError):
@@ -77,6 +78,10 @@ _SIGS = {
     "q2_model_generate": ([ctypes.c_void_p, _P, ctypes.c_int32, _P, _S], ctypes.c_int),
     "q2_model_continue": ([ctypes.c_void_p, ctypes.c_int32, _P, _S], ctypes.c_int),
     "q2_model_kv_view": ([ctypes.c_void_p, ctypes.c_int32, _P, _P], ctypes.c_int),
+    "q2_model_kv_scale_view": ([ctypes.c_void_p, ctypes.c_int32, _P, _P], ctypes.c_int),
+    "q2_model_replay_stage": ([ctypes.c_void_p] + [ctypes.c_int32] * 4 + [_S], ctypes.c_int),
+    "q2_kv_quantize": ([_P, _P, _P, _S], ctypes.c_int),
+    "q2_kv_dequantize": ([_P, _P, _P, _S], ctypes.c_int),
     "q2_model_length": ([ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
     "q2_model_reset": ([ctypes.c_void_p], ctypes.c_int),
     "q2_model_set_decode_path": ([ctypes.c_void_p, ctypes.c_int32], ctypes.c_int),
@@ -217,6 +222,16 @@ def q2_rearrange(out, inp, stream=None):
     return out
 
 
+def q2_kv_quantize(codes, scales, x, stream=None):
+    _check(lib.q2_kv_quantize(_ref(desc(codes)), _ref(desc(scales)), _ref(desc(x)), _stream(stream)))
+    return codes, scales
+
+
+def q2_kv_dequantize(x, codes, scales, stream=None):
+    _check(lib.q2_kv_dequantize(_ref(desc(x)), _ref(desc(codes)), _ref(desc(scales)), _stream(stream)))
+    return x
+
+
 # ------------------------------------------------------------------ model driver
 
 def q2_model_create(cfg: Q2Config, device: int = 0) -> ctypes.c_void_p:
@@ -266,6 +281,19 @@ def q2_model_kv_view(h, layer: int):
     k, v = Q2Tensor(), Q2Tensor()
     _check(lib.q2_model_kv_view(h, int(layer), ctypes.byref(k), ctypes.byref(v)))
     return k, v
+
+
+def q2_model_kv_scale_view(h, layer: int):
+    k, v = Q2Tensor(), Q2Tensor()
+    _check(lib.q2_model_kv_scale_view(h, int(layer), ctypes.byref(k), ctypes.byref(v)))
+    return k, v
+
+
+STAGE_QKV, STAGE_ATTN, STAGE_O, STAGE_GATE_UP, STAGE_DOWN = 0, 1, 2, 3, 4
+
+
+def q2_model_replay_stage(h, stage: int, batch: int, tokens: int, reps: int, stream=None):
+    _check(lib.q2_model_replay_stage(h, int(stage), int(batch), int(tokens), int(reps), _stream(stream)))
 
 
 def q2_model_length(h) -> int:

@@ -24,6 +24,7 @@
 #include <algorithm>
 
 #include "attention.hpp"
+#include "kvcache.hpp"
 
 namespace q2 {
 
@@ -132,6 +133,10 @@ __device__ __forceinline__ void dec_block(const uint4 (&kf)[4], const uint4 (&vf
   wave_lds_sync();
 }
 
+// FP8: K / V rows are E4M3 codes with a scale per key, dequantised to bf16
+// in registers just before their block's products (the loads in flight stay
+// at half the bytes).
+template <bool FP8>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk, int nsplit,
                                                           float* __restrict__ part_o, float2* __restrict__ part_ml) {
   // the V^T tiles of the key loop and the merge buffers of the four waves
@@ -168,8 +173,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qf[kk] = rvalid ? ld16(qp + 32 * kk + 8 * G) : z;
 
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_bs + g * a.k_hs;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.v_bs + g * a.v_hs;
   uint16_t* vt = sVt[wave];
 
   float m_run = NEG_INF, l_run = 0.f;
@@ -177,6 +180,49 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
+  int j0 = j_begin + 16 * wave;
+  if constexpr (FP8) {
+  // as below, with 8-byte code loads and each key's scale
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + b * a.k_bs + g * a.k_hs;
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + b * a.v_bs + g * a.v_hs;
+  const float* ksb = a.ks + b * a.s_bs + g * a.s_hs;
+  const float* vsb = a.vs + b * a.s_bs + g * a.s_hs;
+#define Q2_DEC_LOAD8(KR_, VR_, KS_, VS_, J0_)                                                         \
+  {                                                                                                  \
+    const int key_ = max(min((J0_) + col, j_end - 1), 0);                                           \
+    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) KR_[kk] =                                       \
+        *reinterpret_cast<const uint2*>(kbase + static_cast<int64_t>(key_) * a.k_ss + 32 * kk + 8 * G); \
+    KS_ = ksb[key_];                                                                                 \
+    _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) {                                               \
+      const int vk_ = max(min((J0_) + 4 * G + s_, j_end - 1), 0);                                    \
+      VR_[s_] = *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(vk_) * a.v_ss + 8 * col); \
+      VS_[s_] = vsb[vk_];                                                                            \
+    }                                                                                                \
+  }
+#define Q2_DEC_BLOCK8(KR_, VR_, KS_, VS_, J0_)                                                        \
+  {                                                                                                  \
+    uint4 kf_[4], vf_[4];                                                                            \
+    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) kf_[kk] = e4m3_dequant8(KR_[kk], KS_);          \
+    _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) vf_[s_] = e4m3_dequant8(VR_[s_], VS_[s_]);      \
+    dec_block(kf_, vf_, qf, vt, (J0_), j_end, lim, a.scale, col, G, oacc, m_run, l_run);             \
+  }
+  uint2 kr0[4], vr0[4], kr1[4], vr1[4];
+  float ks0, vs0[4], ks1, vs1[4];
+  Q2_DEC_LOAD8(kr0, vr0, ks0, vs0, j0)
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) settle(qf[kk]);
+  for (; j0 < j_end; j0 += 128) {
+    Q2_DEC_LOAD8(kr1, vr1, ks1, vs1, j0 + 64)
+    Q2_DEC_BLOCK8(kr0, vr0, ks0, vs0, j0)
+    if (j0 + 64 >= j_end) break;
+    Q2_DEC_LOAD8(kr0, vr0, ks0, vs0, j0 + 128)
+    Q2_DEC_BLOCK8(kr1, vr1, ks1, vs1, j0 + 64)
+  }
+#undef Q2_DEC_LOAD8
+#undef Q2_DEC_BLOCK8
+  } else {
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_bs + g * a.k_hs;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.v_bs + g * a.v_hs;
   // K rows j0 + col: 4 x 16 B (d = 32kk + 8G .. +8); V rows j0 + 4G + s,
   // d-chunk 8*col.  Loads are unconditional (keys past the split read its
   // last key: their scores are masked and their probabilities exactly 0), so
@@ -197,7 +243,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
   // key): with a load count that does not depend on the path, the compiler
   // waits for the older set only.
   uint4 kf0[4], vf0[4], kf1[4], vf1[4];
-  int j0 = j_begin + 16 * wave;
   Q2_DEC_LOAD(kf0, vf0, j0)
   // the query fragments were loaded before the first block: mark them
   // arrived here, so that their wait does not hold back the block's loads
@@ -211,6 +256,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
     dec_block(kf1, vf1, qf, vt, j0 + 64, j_end, lim, a.scale, col, G, oacc, m_run, l_run);
   }
 #undef Q2_DEC_LOAD
+  }
   __syncthreads();  // every wave is done with its V^T tile before sO reuses the region
 
   // merge the four waves
@@ -789,8 +835,12 @@ q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
       part_o = static_cast<float*>(a.scratch);
       part_ml = reinterpret_cast<float2*>(part_o + slots * D);
     }
-    hipLaunchKernelGGL(attn_decode_kernel, dim3(p.nsplit, a.B * a.nkv), dim3(256), 0, s, a, p.chunk, p.nsplit,
-                       part_o, part_ml);
+    if (a.kv_fp8)
+      hipLaunchKernelGGL(attn_decode_kernel<true>, dim3(p.nsplit, a.B * a.nkv), dim3(256), 0, s, a, p.chunk,
+                         p.nsplit, part_o, part_ml);
+    else
+      hipLaunchKernelGGL(attn_decode_kernel<false>, dim3(p.nsplit, a.B * a.nkv), dim3(256), 0, s, a, p.chunk,
+                         p.nsplit, part_o, part_ml);
     Q2_TRY(check_launch("attn_decode"));
     if (p.nsplit > 1 && !a.leave_partials) {
       if (p.nsplit <= 8)
@@ -801,6 +851,7 @@ q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
     }
     return Q2_OK;
   }
+  Q2_CHECK(!a.kv_fp8, Q2_EINVAL, "FP8 K/V: the prefill kernel reads bf16 (expand the cache first)");
   // the prefill kernel's buffer loads address a head's keys with 32-bit
   // byte offsets
   const int64_t max_keys = a.d_len ? a.s_max : a.S;

@@ -39,8 +39,10 @@ q2_status check_launch(const char* what);
 
 // ---------------------------------------------------------------- tensors
 
-inline int64_t dtype_size(int32_t dt) { return dt == Q2_F32 ? 4 : dt == Q2_BF16 ? 2 : dt == Q2_I64 ? 8 : 0; }
-inline bool dtype_valid(int32_t dt) { return dt == Q2_F32 || dt == Q2_BF16 || dt == Q2_I64; }
+inline int64_t dtype_size(int32_t dt) {
+  return dt == Q2_F32 ? 4 : dt == Q2_BF16 ? 2 : dt == Q2_I64 ? 8 : dt == Q2_U8 ? 1 : 0;
+}
+inline bool dtype_valid(int32_t dt) { return dt == Q2_F32 || dt == Q2_BF16 || dt == Q2_I64 || dt == Q2_U8; }
 inline bool is_float(int32_t dt) { return dt == Q2_F32 || dt == Q2_BF16; }
 
 inline int64_t numel(const q2_tensor& t) {

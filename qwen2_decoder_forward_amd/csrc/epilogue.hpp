@@ -40,6 +40,10 @@ struct Epi {
   int T;                  // tokens per sequence in this call (row m = b * T + t)
   const int* d_len;       // device cached length (position of t = 0) or null
   int len0;               // host cached length, used when d_len is null
+  // k / v rows go to row t (this call's token index) of kc / vc instead of
+  // row len + t: a staging buffer [B][nkv][T][d] that a separate kernel
+  // stores into the cache (quantised caches); RoPE still uses len + t
+  int kv_rel;
   const float2* rope;     // [S_max][d/2] (cos, sin)
   // ARGMAX: packed (value, index) keys, KEY_SLOTS per row each on its own
   // 128-byte line (stride KEY_STRIDE), combined with atomicMax: spreading a
@@ -108,13 +112,13 @@ __device__ __forceinline__ void epi_pair(const Epi& e, int m, int n, float v0, f
           dst = static_cast<T*>(e.out) + static_cast<int64_t>(m) * e.ldo + head * d;
         } else {
           dst = static_cast<T*>(e.kc) + bt * e.kv_bstride + (head - e.nh) * e.kv_hstride +
-                static_cast<int64_t>(pos) * d;
+                static_cast<int64_t>(e.kv_rel ? t : pos) * d;
         }
         S::st(dst + p, ra);
         S::st(dst + p + (d >> 1), rb);
       } else {
         T* dst = static_cast<T*>(e.vc) + bt * e.kv_bstride + (head - e.nh - e.nkv) * e.kv_hstride +
-                 static_cast<int64_t>(pos) * d + r;
+                 static_cast<int64_t>(e.kv_rel ? t : pos) * d + r;
         S::st(dst, a);
         S::st(dst + 1, c);
       }

@@ -363,7 +363,7 @@ __device__ __forceinline__ void stg_copy_out(const uint16_t* sh, const Epi& e, i
       } else {
         const int bt = m / e.T;
         const int t = m - bt * e.T;
-        const int64_t pos = len0 + t;
+        const int64_t pos = e.kv_rel ? t : len0 + t;
         const bool isk = head < e.nh + e.nkv;
         uint16_t* base = static_cast<uint16_t*>(isk ? e.kc : e.vc);
         const int hh = isk ? head - e.nh : head - e.nh - e.nkv;

@@ -213,6 +213,7 @@ __device__ __forceinline__ void gemv_epilogue(const Epi& epi, int M, int N, int 
     const int head = n / d;
     const int r = n - head * d;
     const int bt = m / epi.T;
+    const int64_t row = epi.kv_rel ? m - bt * epi.T : pre->pos;
     if (head < epi.nh + epi.nkv) {
       const int q = r >> 1;
       const float ra = round_bf(a * pre->cs.x - c * pre->cs.y);
@@ -221,13 +222,12 @@ __device__ __forceinline__ void gemv_epilogue(const Epi& epi, int M, int N, int 
       if (head < epi.nh)
         dst = static_cast<uint16_t*>(epi.out) + static_cast<int64_t>(m) * epi.ldo + head * d;
       else
-        dst = static_cast<uint16_t*>(epi.kc) + bt * epi.kv_bstride + (head - epi.nh) * epi.kv_hstride +
-              static_cast<int64_t>(pre->pos) * d;
+        dst = static_cast<uint16_t*>(epi.kc) + bt * epi.kv_bstride + (head - epi.nh) * epi.kv_hstride + row * d;
       dst[q] = f2bf(ra);
       dst[q + (d >> 1)] = f2bf(rb);
     } else {
       uint16_t* dst = static_cast<uint16_t*>(epi.vc) + bt * epi.kv_bstride + (head - epi.nh - epi.nkv) * epi.kv_hstride +
-                      static_cast<int64_t>(pre->pos) * d + r;
+                      row * d + r;
       dst[0] = f2bf(a);
       dst[1] = f2bf(c);
     }

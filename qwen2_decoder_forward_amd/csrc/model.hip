@@ -32,6 +32,7 @@
 #include "attention.hpp"
 #include "decode_mk.hpp"
 #include "epilogue.hpp"
+#include "kvcache.hpp"
 #include "simple.hpp"
 
 using namespace q2;
@@ -59,6 +60,19 @@ struct q2_model {
   void* kc = nullptr;
   void* vc = nullptr;
   int64_t kv_lstride = 0, kv_bstride = 0, kv_hstride = 0;
+  // FP8 cache (cfg.kv_fp8): kc / vc hold E4M3 codes (same layout, 1 byte per
+  // element) and ks / vs one float32 scale per (layer, sequence, head,
+  // position); new k / v rows are staged as bf16 in kstage / vstage
+  // [B][nkv][T][d] and quantised by kv_store_fp8; the prefill attention reads
+  // the positions it needs expanded to bf16 in kexp / vexp [B][nkv][S][d]
+  bool fp8 = false;
+  float* ks = nullptr;
+  float* vs = nullptr;
+  int64_t ks_lstride = 0;
+  void* kstage = nullptr;
+  void* vstage = nullptr;
+  void* kexp = nullptr;
+  void* vexp = nullptr;
   float2* rope = nullptr;
   // arena
   void *x = nullptr, *h = nullptr, *q = nullptr, *att = nullptr, *act = nullptr, *xl = nullptr;
@@ -167,6 +181,19 @@ __global__ void copy_logits_kernel(float* out, int64_t ld_out, const float* src,
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
+KvFp8 fp8_layer(const q2_model* m, int l) {
+  KvFp8 c{};
+  c.kc = static_cast<uint8_t*>(m->kc) + l * m->kv_lstride;
+  c.vc = static_cast<uint8_t*>(m->vc) + l * m->kv_lstride;
+  c.ks = m->ks + l * m->ks_lstride;
+  c.vs = m->vs + l * m->ks_lstride;
+  c.c_bs = m->kv_bstride;
+  c.c_hs = m->kv_hstride;
+  c.s_hs = m->cfg.max_seq;
+  c.s_bs = int64_t(m->cfg.max_seq) * m->cfg.nkv;
+  return c;
+}
+
 q2_status gemm(const q2_model* m, const GemmArgs& a, hipStream_t s) {
   return m->cfg.dtype == Q2_BF16 ? gemm_bf16(a, s) : gemm_f32(a, s);
 }
@@ -204,8 +231,15 @@ Path path_for(const q2_model* m, int M) {
 // Transformer layers for B sequences x Tc new tokens whose ids are already
 // embedded in x.  Positions start at the device length; with `advance` the
 // device length moves on by Tc at the end.
+// Products of a layer, for measurement (q2_model_replay_stage).
+enum Stage : int { STAGE_QKV = 0, STAGE_ATTN = 1, STAGE_O = 2, STAGE_GATE_UP = 3, STAGE_DOWN = 4, STAGE_HEAD = 5 };
+
+// only_stage >= 0: launch nothing but that stage of layer only_layer (the
+// launch decisions of every other stage are still taken, so the launched
+// kernels and their arguments are those of the full forward).
 template <typename T>
-q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
+q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s, int only_stage = -1,
+                     int only_layer = -1) {
   const q2_config& c = m->cfg;
   const int M = B * Tc;
   const int H = c.hidden, d = c.dh, qd = c.nh * c.dh;
@@ -221,10 +255,12 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
   // (written by the previous residual product's split-K reduction)
   bool h_ready = false;
   for (int l = 0; l < c.nlayer; ++l) {
+    auto want = [&](int st) { return only_stage < 0 || (only_stage == st && only_layer == l); };
     const q2_model::Layer& L = m->layers[l];
-    void* kc = static_cast<char*>(m->kc) + l * m->kv_lstride * m->esize;
-    void* vc = static_cast<char*>(m->vc) + l * m->kv_lstride * m->esize;
-    if (!path.fused_norm && !h_ready)
+    const int kv_es = m->fp8 ? 1 : m->esize;
+    void* kc = static_cast<char*>(m->kc) + l * m->kv_lstride * kv_es;
+    void* vc = static_cast<char*>(m->vc) + l * m->kv_lstride * kv_es;
+    if (!path.fused_norm && !h_ready && want(STAGE_QKV))
       Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->h), H, static_cast<const T*>(m->x), H,
                                static_cast<const T*>(L.w_in), M, H, c.eps, s));
     h_ready = false;
@@ -247,19 +283,23 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
       a.epi.out = m->q;
       a.epi.ldo = qd;
       a.epi.bias = L.b_qkv;
-      a.epi.kc = kc;
-      a.epi.vc = vc;
-      a.epi.kv_bstride = m->kv_bstride;
-      a.epi.kv_hstride = m->kv_hstride;
+      a.epi.kc = m->fp8 ? m->kstage : kc;
+      a.epi.vc = m->fp8 ? m->vstage : vc;
+      a.epi.kv_bstride = m->fp8 ? int64_t(c.nkv) * Tc * d : m->kv_bstride;
+      a.epi.kv_hstride = m->fp8 ? int64_t(Tc) * d : m->kv_hstride;
+      a.epi.kv_rel = m->fp8 ? 1 : 0;
       a.epi.nh = c.nh;
       a.epi.nkv = c.nkv;
       a.epi.dh = d;
       a.epi.T = Tc;
       a.epi.d_len = m->d_len;
       a.epi.rope = m->rope;
-      Q2_TRY(gemm(m, a, s));
+      if (want(STAGE_QKV)) Q2_TRY(gemm(m, a, s));
       cur = nxt;
       pend_splits = 0;
+      if (m->fp8 && want(STAGE_QKV))
+        Q2_TRY(launch_kv_store_fp8(fp8_layer(m, l), static_cast<const uint16_t*>(m->kstage),
+                                   static_cast<const uint16_t*>(m->vstage), B, c.nkv, Tc, m->d_len, m->len, s));
     }
     // with one query per sequence and split-KV partials, o_proj merges them
     // itself -- when there are few: every o_proj workgroup merges all rows of
@@ -294,7 +334,26 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
       a.s_max = c.max_seq;
       a.scratch = m->ascratch;
       a.scratch_bytes = m->ascratch_bytes;
-      Q2_TRY(c.dtype == Q2_BF16 ? attention_bf16(a, s) : attention_f32(a, s));
+      if (m->fp8) {
+        const KvFp8 f = fp8_layer(m, l);
+        if (Tc * (c.nh / c.nkv) <= 16) {
+          // decode kernel: reads the codes and scales itself (byte strides)
+          a.kv_fp8 = true;
+          a.ks = f.ks;
+          a.vs = f.vs;
+          a.s_bs = f.s_bs;
+          a.s_hs = f.s_hs;
+        } else {
+          // prefill kernel: positions [0, len + Tc) expanded to bf16 first
+          if (want(STAGE_ATTN)) Q2_TRY(launch_kv_expand_fp8(static_cast<uint16_t*>(m->kexp), static_cast<uint16_t*>(m->vexp), c.max_seq, f, B,
+                                      c.nkv, m->len + Tc, s));
+          a.k = m->kexp;
+          a.v = m->vexp;
+          a.k_hs = a.v_hs = int64_t(c.max_seq) * d;
+          a.k_bs = a.v_bs = a.k_hs * c.nkv;
+        }
+      }
+      if (want(STAGE_ATTN)) Q2_TRY(c.dtype == Q2_BF16 ? attention_bf16(a, s) : attention_f32(a, s));
     }
     {
       GemmArgs a = gemm_args(m, L.w_o, qd, m->att, qd, M, H, qd);
@@ -317,9 +376,9 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
         a.post_eps = c.eps;
         h_ready = gemm_post_norm(a);
       }
-      Q2_TRY(gemm(m, a, s));
+      if (want(STAGE_O)) Q2_TRY(gemm(m, a, s));
     }
-    if (!path.fused_norm && !h_ready)
+    if (!path.fused_norm && !h_ready && want(STAGE_GATE_UP))
       Q2_TRY(launch_rmsnorm<T>(static_cast<T*>(m->h), H, static_cast<const T*>(m->x), H,
                                static_cast<const T*>(L.w_post), M, H, c.eps, s));
     h_ready = false;
@@ -334,7 +393,7 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
       a.epi.kind = EPI_SWIGLU;
       a.epi.out = m->act;
       a.epi.ldo = c.inter;
-      Q2_TRY(gemm(m, a, s));
+      if (want(STAGE_GATE_UP)) Q2_TRY(gemm(m, a, s));
     }
     {
       GemmArgs a = gemm_args(m, L.w_d, c.inter, m->act, c.inter, M, H, c.inter);
@@ -356,9 +415,10 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s) {
         a.post_eps = c.eps;
         h_ready = gemm_post_norm(a);
       }
-      Q2_TRY(gemm(m, a, s));
+      if (want(STAGE_DOWN)) Q2_TRY(gemm(m, a, s));
     }
   }
+  if (only_stage >= 0) return Q2_OK;
   m->xcur = cur;
   if (!advance) return Q2_OK;
   hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(1), 0, s, m->d_len, Tc);
@@ -577,7 +637,7 @@ q2_status find_slot(q2_model* m, const std::string& name, int layer, WeightSlot*
 static q2_status setup_persistent(q2_model* m) {
   const q2_config& c = m->cfg;
   if (c.dtype != Q2_BF16 || c.dh != 128 || c.max_batch > MK_MAX_BATCH || c.hidden % 16 != 0 ||
-      c.inter % 16 != 0)
+      c.inter % 16 != 0 || m->fp8)
     return Q2_OK;
   // the norm prologue spreads a row over 8 / B waves (one wave per row from
   // batch 8 on), each lane holding at most MK_NORM_CHUNKS 16-byte chunks
@@ -692,6 +752,9 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
   Q2_CHECK(c.dh % 2 == 0, Q2_ESHAPE, "head dim must be even");
   Q2_CHECK(c.max_batch <= 64, Q2_ESHAPE, "max_batch must be <= 64");
   Q2_CHECK(c.eps >= 0.f && c.theta > 0.f, Q2_EINVAL, "bad eps / theta");
+  Q2_CHECK(c.kv_fp8 == 0 || c.kv_fp8 == 1, Q2_EINVAL, "kv_fp8 must be 0 or 1");
+  Q2_CHECK(!c.kv_fp8 || c.dtype == Q2_BF16, Q2_EDTYPE, "the FP8 KV cache needs a bf16 model");
+  Q2_CHECK(!c.kv_fp8 || c.nh / c.nkv <= 16, Q2_ESHAPE, "the FP8 KV cache needs at most 16 query heads per KV head");
   if (c.dtype == Q2_BF16) {
     Q2_CHECK(c.dh == 128, Q2_ESHAPE, "bf16 model needs head_dim 128");
     Q2_CHECK(c.hidden % 32 == 0 && c.inter % 32 == 0, Q2_ESHAPE, "bf16 model needs hidden and inter multiples of 32");
@@ -708,6 +771,7 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
   m->cfg = c;
   m->device = device;
   m->esize = c.dtype == Q2_BF16 ? 2 : 4;
+  m->fp8 = c.kv_fp8 != 0;
   m->qkv_out = (c.nh + 2 * c.nkv) * c.dh;
   const size_t es = m->esize;
   const size_t H = c.hidden, I = c.inter, V = c.vocab, qd = size_t(c.nh) * c.dh;
@@ -737,8 +801,10 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
   m->kv_hstride = int64_t(c.max_seq) * c.dh;
   m->kv_bstride = m->kv_hstride * c.nkv;
   m->kv_lstride = m->kv_bstride * c.max_batch;
-  const size_t kv_one = size_t(m->kv_lstride) * c.nlayer * es;
-  m->kvbytes = 2 * align256(kv_one);
+  const size_t kv_one = size_t(m->kv_lstride) * c.nlayer * (m->fp8 ? 1 : es);
+  m->ks_lstride = int64_t(c.max_batch) * c.nkv * c.max_seq;
+  const size_t ks_one = m->fp8 ? size_t(m->ks_lstride) * c.nlayer * sizeof(float) : 0;
+  m->kvbytes = 2 * align256(kv_one) + 2 * align256(ks_one);
 
   // arena
   const int64_t bs = int64_t(c.max_batch) * c.max_seq;
@@ -782,6 +848,9 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
     }
   m->ascratch_bytes = as;
   const size_t a_as = take(as);
+  const size_t stage_b = m->fp8 ? mt * c.nkv * c.dh * es : 0;
+  const size_t exp_b = m->fp8 ? size_t(c.max_batch) * c.nkv * c.max_seq * c.dh * es : 0;
+  const size_t a_ks = take(stage_b), a_vs = take(stage_b), a_ke = take(exp_b), a_ve = take(exp_b);
   m->abytes = off;
 
   auto cleanup = [&](q2_status st) {
@@ -808,6 +877,14 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
   }
   m->kc = m->kvmem;
   m->vc = m->kvmem + align256(kv_one);
+  if (m->fp8) {
+    m->ks = reinterpret_cast<float*>(m->kvmem + 2 * align256(kv_one));
+    m->vs = reinterpret_cast<float*>(m->kvmem + 2 * align256(kv_one) + align256(ks_one));
+    m->kstage = m->amem + a_ks;
+    m->vstage = m->amem + a_vs;
+    m->kexp = m->amem + a_ke;
+    m->vexp = m->amem + a_ve;
+  }
   m->rope = reinterpret_cast<float2*>(m->amem + a_rope);
   m->x = m->amem + a_x;
   m->h = m->amem + a_h;
@@ -1046,8 +1123,8 @@ extern "C" q2_status q2_model_kv_view(q2_model* m, int32_t layer, q2_tensor* k, 
   for (int i = 0; i < 2; ++i) {
     q2_tensor* t = i ? v : k;
     memset(t, 0, sizeof *t);
-    t->data = static_cast<char*>(i ? m->vc : m->kc) + int64_t(layer) * m->kv_lstride * m->esize;
-    t->dtype = m->cfg.dtype;
+    t->data = static_cast<char*>(i ? m->vc : m->kc) + int64_t(layer) * m->kv_lstride * (m->fp8 ? 1 : m->esize);
+    t->dtype = m->fp8 ? Q2_U8 : m->cfg.dtype;
     t->ndim = 4;
     t->shape[0] = m->cfg.max_batch;
     t->shape[1] = m->cfg.max_seq;
@@ -1057,6 +1134,49 @@ extern "C" q2_status q2_model_kv_view(q2_model* m, int32_t layer, q2_tensor* k, 
     t->stride[1] = m->cfg.dh;
     t->stride[2] = m->kv_hstride;
     t->stride[3] = 1;
+  }
+  return Q2_OK;
+}
+
+extern "C" q2_status q2_model_replay_stage(q2_model* m, int32_t stage, int32_t batch, int32_t tokens, int32_t reps,
+                                          void* stream) {
+  clear_error();
+  Q2_CHECK(m, Q2_EINVAL, "null model");
+  Q2_CHECK(stage >= STAGE_QKV && stage <= STAGE_DOWN, Q2_EINVAL, "stage %d not in [0, 4]", stage);
+  Q2_CHECK(batch >= 1 && batch <= m->cfg.max_batch, Q2_ESHAPE, "batch %d not in [1, %d]", batch, m->cfg.max_batch);
+  Q2_CHECK(tokens >= 1 && reps >= 0, Q2_ESHAPE, "tokens must be positive and reps non-negative");
+  Q2_CHECK(int64_t(batch) * tokens <= m->max_tok, Q2_ESHAPE, "%d x %d rows exceed the activation arena (%d)", batch,
+           tokens, m->max_tok);
+  Q2_CHECK(static_cast<int64_t>(m->len) + tokens <= m->cfg.max_seq, Q2_ESTATE,
+           "replay at length %d + %d tokens exceeds the cache (%d)", m->len, tokens, m->cfg.max_seq);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Q2_TRY(sync_len(m, s));
+  for (int i = 0; i < reps; ++i) {
+    const int l = i % m->cfg.nlayer;
+    Q2_TRY(m->cfg.dtype == Q2_BF16 ? run_layers<uint16_t>(m, batch, tokens, false, s, stage, l)
+                                   : run_layers<float>(m, batch, tokens, false, s, stage, l));
+  }
+  return Q2_OK;
+}
+
+extern "C" q2_status q2_model_kv_scale_view(q2_model* m, int32_t layer, q2_tensor* ks, q2_tensor* vs) {
+  clear_error();
+  Q2_CHECK(m && ks && vs, Q2_EINVAL, "null argument");
+  Q2_CHECK(m->fp8, Q2_ESTATE, "the model's KV cache is not FP8");
+  Q2_CHECK(layer >= 0 && layer < m->cfg.nlayer, Q2_EINVAL, "layer out of range");
+  const KvFp8 f = fp8_layer(m, layer);
+  for (int i = 0; i < 2; ++i) {
+    q2_tensor* t = i ? vs : ks;
+    memset(t, 0, sizeof *t);
+    t->data = i ? f.vs : f.ks;
+    t->dtype = Q2_F32;
+    t->ndim = 3;
+    t->shape[0] = m->cfg.max_batch;
+    t->shape[1] = m->cfg.max_seq;
+    t->shape[2] = m->cfg.nkv;
+    t->stride[0] = f.s_bs;
+    t->stride[1] = 1;
+    t->stride[2] = f.s_hs;
   }
   return Q2_OK;
 }

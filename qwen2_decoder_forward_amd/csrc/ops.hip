@@ -3,6 +3,7 @@
 
 #include "attention.hpp"
 #include "epilogue.hpp"
+#include "kvcache.hpp"
 #include "simple.hpp"
 
 namespace q2 {
@@ -808,7 +809,10 @@ extern "C" q2_status q2_rearrange(const q2_tensor* out, const q2_tensor* in, voi
     g.so[i] = out->stride[i];
     g.si[i] = in->stride[i];
   }
-  if (es == 2)
+  if (es == 1)
+    hipLaunchKernelGGL(rearrange_kernel<uint8_t>, dim3(grid_for(n)), dim3(256), 0, s, static_cast<uint8_t*>(out->data),
+                       static_cast<const uint8_t*>(in->data), g, n);
+  else if (es == 2)
     hipLaunchKernelGGL(rearrange_kernel<uint16_t>, dim3(grid_for(n)), dim3(256), 0, s, static_cast<uint16_t*>(out->data),
                        static_cast<const uint16_t*>(in->data), g, n);
   else if (es == 4)
@@ -818,4 +822,49 @@ extern "C" q2_status q2_rearrange(const q2_tensor* out, const q2_tensor* in, voi
     hipLaunchKernelGGL(rearrange_kernel<uint64_t>, dim3(grid_for(n)), dim3(256), 0, s, static_cast<uint64_t*>(out->data),
                        static_cast<const uint64_t*>(in->data), g, n);
   return check_launch("rearrange");
+}
+
+// ------------------------------------------------------------------ FP8 KV-cache codec
+
+// Rows of 128 values as the codec's [N, 128] operand (row stride in elements).
+static q2_status kv_rows(const q2_tensor* t, const char* name, int32_t dtype, Rows* r) {
+  Q2_TRY(as_rows(t, name, r));
+  Q2_CHECK(r->dtype == dtype, Q2_EDTYPE, "%s has the wrong dtype", name);
+  Q2_CHECK(r->cols == KV_BLOCK, Q2_ESHAPE, "%s rows must hold %d elements", name, KV_BLOCK);
+  Q2_CHECK(aligned16(r->data) && (r->rows <= 1 || (r->ld * dtype_size(dtype)) % 16 == 0), Q2_ESTRIDE,
+           "%s rows must be 16-byte aligned", name);
+  return Q2_OK;
+}
+
+static q2_status kv_scales(const q2_tensor* t, int64_t rows) {
+  Q2_TRY(check_desc(t, "scales"));
+  Q2_CHECK(t->dtype == Q2_F32, Q2_EDTYPE, "scales must be f32");
+  Q2_CHECK(numel(*t) == rows && is_contiguous(*t), Q2_ESHAPE, "scales must be %lld contiguous floats",
+           static_cast<long long>(rows));
+  return Q2_OK;
+}
+
+extern "C" q2_status q2_kv_quantize(const q2_tensor* codes, const q2_tensor* scales, const q2_tensor* x,
+                                    void* stream) {
+  clear_error();
+  Rows c, xr;
+  Q2_TRY(kv_rows(codes, "codes", Q2_U8, &c));
+  Q2_TRY(kv_rows(x, "x", Q2_BF16, &xr));
+  Q2_CHECK(c.rows == xr.rows, Q2_ESHAPE, "codes and x row counts differ");
+  Q2_TRY(kv_scales(scales, xr.rows));
+  return launch_kv_quantize(reinterpret_cast<uint8_t*>(c.data), c.ld, static_cast<float*>(scales->data),
+                            reinterpret_cast<const uint16_t*>(xr.data), xr.ld, xr.rows,
+                            static_cast<hipStream_t>(stream));
+}
+
+extern "C" q2_status q2_kv_dequantize(const q2_tensor* x, const q2_tensor* codes, const q2_tensor* scales,
+                                      void* stream) {
+  clear_error();
+  Rows c, xr;
+  Q2_TRY(kv_rows(codes, "codes", Q2_U8, &c));
+  Q2_TRY(kv_rows(x, "x", Q2_BF16, &xr));
+  Q2_CHECK(c.rows == xr.rows, Q2_ESHAPE, "codes and x row counts differ");
+  Q2_TRY(kv_scales(scales, xr.rows));
+  return launch_kv_dequantize(reinterpret_cast<uint16_t*>(xr.data), xr.ld, reinterpret_cast<const uint8_t*>(c.data),
+                              c.ld, static_cast<const float*>(scales->data), xr.rows, static_cast<hipStream_t>(stream));
 }

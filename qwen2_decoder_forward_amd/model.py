@@ -8,10 +8,12 @@ from . import _lib
 from ._lib import Q2Config, Q2_BF16, Q2_F32
 
 
-def make_config(shape, max_seq: int, max_batch: int) -> Q2Config:
+def make_config(shape, max_seq: int, max_batch: int, kv_fp8: bool = False) -> Q2Config:
     """q2_config from any object with the Qwen2 shape attributes
-    (dtype "f32"/"bf16", nlayer, hidden, nh, nkv, dh, inter, vocab, eps, theta)."""
+    (dtype "f32"/"bf16", nlayer, hidden, nh, nkv, dh, inter, vocab, eps, theta);
+    ``kv_fp8`` selects the FP8 KV cache."""
     c = Q2Config()
+    c.kv_fp8 = 1 if kv_fp8 else 0
     c.dtype = Q2_BF16 if shape.dtype == "bf16" else Q2_F32
     c.nlayer, c.hidden, c.nh, c.nkv = shape.nlayer, shape.hidden, shape.nh, shape.nkv
     c.dh, c.inter, c.vocab = shape.dh, shape.inter, shape.vocab
@@ -24,13 +26,14 @@ class Model:
     """Owns one q2_model.  Weights are loaded from device tensors with
     `load_weight(name, layer, tensor)`; all calls run on the current stream."""
 
-    def __init__(self, shape, max_seq: int, max_batch: int, device: int = 0):
+    def __init__(self, shape, max_seq: int, max_batch: int, device: int = 0, kv_fp8: bool = False):
         self.shape = shape
         self.max_seq = max_seq
         self.max_batch = max_batch
         self.device = device
+        self.kv_fp8 = kv_fp8
         self.torch_dtype = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
-        self.handle = _lib.q2_model_create(make_config(shape, max_seq, max_batch), device)
+        self.handle = _lib.q2_model_create(make_config(shape, max_seq, max_batch, kv_fp8), device)
 
     def close(self):
         if self.handle:
@@ -93,6 +96,10 @@ class Model:
         """q2_tensor descriptors (k, v) of layer `layer`'s cache, [max_batch, max_seq, nkv, dh]."""
         return _lib.q2_model_kv_view(self.handle, layer)
 
+    def kv_scale_view(self, layer: int):
+        """q2_tensor descriptors (k, v) of layer `layer`'s FP8 scales, [max_batch, max_seq, nkv]."""
+        return _lib.q2_model_kv_scale_view(self.handle, layer)
+
     def length(self) -> int:
         return _lib.q2_model_length(self.handle)
 
@@ -118,12 +125,12 @@ def weight_tensor(arr, device: int = 0) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(dev)
 
 
-def load_model(shape, weights, max_seq: int, max_batch: int, device: int = 0) -> Model:
+def load_model(shape, weights, max_seq: int, max_batch: int, device: int = 0, kv_fp8: bool = False) -> Model:
     """Create a model and copy every weight of ``weights`` ({(name, layer):
     host array}, Hugging Face Qwen2 names, layer -1 for the global tensors)
     into it, one tensor at a time (each upload is freed once the library has
     packed it)."""
-    m = Model(shape, max_seq, max_batch, device)
+    m = Model(shape, max_seq, max_batch, device, kv_fp8)
     for (name, layer), arr in weights.items():
         t = weight_tensor(arr, device)
         m.load_weight(name, layer, t)

@@ -150,3 +150,32 @@ class BruteModel:
         self.pos += 1
         hf = st("final_norm", rmsnorm(x, self.W[("norm", -1)], sh.eps))
         return matvec(self.W[("lm_head", -1)], hf)
+
+
+def e4m3_table():
+    """(value, code) of every finite non-negative E4M3 code, from the bit
+    fields: code = e << 3 | m; e = 0: m * 2^-9; else (8 + m) * 2^(e - 10);
+    e = 15, m = 7 is NaN."""
+    out = []
+    for e in range(16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue
+            v = math.ldexp(m, -9) if e == 0 else math.ldexp(8 + m, e - 10)
+            out.append((v, (e << 3) | m))
+    return out
+
+
+def e4m3_nearest(y, table):
+    """Code of the table value nearest to |y| (ties: even code), saturating,
+    with the sign bit of y."""
+    a = abs(y)
+    best = None
+    for v, c in table:
+        d = abs(a - v)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    code = best[1]
+    if a >= 448.0:
+        code = 0x7E
+    return code | (0x80 if math.copysign(1.0, y) < 0 else 0)

@@ -425,3 +425,87 @@ def check_bf16_writeback_vs_brute(model_cls, min_equal=0.99, logit_rel=1e-5):
         assert eq >= min_equal, f"{p}: only {eq:.4f} of stored values equal"
         assert float(rel.max()) <= 2 ** -7 + 1e-12, f"{p}: differs by {rel.max():.3e} relative"
     assert np.abs(lg - lr).max() <= logit_rel * np.abs(lr).max(), np.abs(lg - lr).max() / np.abs(lr).max()
+
+
+# ----------------------------------------------------------------------------- FP8 KV cache
+
+def check_e4m3(values, encode, decode):
+    """The E4M3 table and codec against the loop-written enumeration, closed
+    forms and a brute-force nearest search."""
+    table = _brute.e4m3_table()
+    v = values()
+    assert len(v) == 127 and np.array_equal(v, np.array([t[0] for t in table])), "value table"
+    assert v[0x38] == 1.0 and v[0x7E] == 448.0 and v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6
+    # every value round-trips, both signs
+    codes = np.arange(0x7F, dtype=np.uint8)
+    assert np.array_equal(encode(v.astype(np.float32)), codes)
+    assert np.array_equal(encode(-v.astype(np.float32))[1:], codes[1:] | 0x80)
+    assert np.array_equal(decode(codes).astype(np.float64), v)
+    # closed-form ties (to even), saturation, signed zero
+    ys = np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 448.0, 460.0, 1e9, -0.0, 0.0, -2.0 ** -12],
+                  np.float32)
+    assert encode(ys).tolist() == [0x38, 0x3A, 0x00, 0x02, 0x7E, 0x7E, 0x7E, 0x80, 0x00, 0x80]
+    # brute force on random magnitudes spanning the subnormals to saturation
+    r = np.random.default_rng(41)
+    y = (np.exp(r.uniform(np.log(2.0 ** -12), np.log(500.0), 3000)) * r.choice([-1, 1], 3000)).astype(np.float32)
+    # plus exact midpoints between neighbouring codes
+    mids = ((v[1:] + v[:-1]) / 2).astype(np.float32)
+    y = np.concatenate([y, mids[(mids.astype(np.float64) == (v[1:] + v[:-1]) / 2)]])
+    got = encode(y)
+    want = np.array([_brute.e4m3_nearest(float(t), table) for t in y], np.uint8)
+    assert np.array_equal(got, want), np.nonzero(got != want)[0][:5]
+
+
+def check_kv_quant(quantize, dequantize):
+    """Block quantisation: the block maximum codes to +-448, the round trip
+    is within half an E4M3 step of each value plus the bf16 write-back,
+    zero blocks stay zero."""
+    r = np.random.default_rng(42)
+    x = (r.standard_normal((64, 128)) * np.exp(r.uniform(-6, 3, (64, 1)))).astype(np.float32)
+    x = (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)      # bf16 values
+    x[5] = 0.0
+    x[6, :] = -0.0
+    x[7, 3] = 1e-3
+    codes, scales = quantize(x)
+    assert codes.dtype == np.uint8 and codes.shape == (64, 128) and scales.shape == (64,)
+    amax = np.abs(x).max(-1)
+    nz = amax > 0
+    assert np.array_equal(scales[nz], (amax[nz] / np.float32(448)).astype(np.float32))
+    assert np.all(scales[~nz] == 0) and np.all(codes[5] == 0) and np.all(codes[6] == 0x80)
+    top = np.abs(x).argmax(-1)
+    assert np.all((codes[np.arange(64), top][nz] & 0x7F) == 0x7E)
+    d = dequantize(codes, scales).astype(np.float64)
+    assert np.all(d[~nz] == 0)
+    # half a step: 2^-4 relative for normal codes, 2^-10 * scale absolute below 2^-6 * scale
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scales[:, None]) * (1 + 2 ** -7) + np.abs(x) * 2 ** -8
+    assert np.all(np.abs(d - x) <= bound)
+
+
+def check_fp8_cache_values(model_cls):
+    """The FP8-cache model's cache holds, for every new k (after RoPE) and v
+    row, bf16(value(code) * scale) with scale = max|block| / 448 and the code
+    of each element found by brute-force nearest search (tests/_brute.py)."""
+    import synth
+    sh = synth.ModelShape("pin-fp8", "bf16", 2, 256, 4, 2, 128, 256, 64, 10000.0)
+    w = synth.make_weights(sh, seed=33)
+    m = model_cls(sh, w, "bf16", 1, 8, kv="fp8")
+    m.record = {}
+    m.forward(np.array([[1, 5, 9, 2]], np.int64))
+    table = _brute.e4m3_table()
+    value = {c: v for v, c in table}
+    for l in range(sh.nlayer):
+        for name, cache in (("k_rope", m.k_cache[l]), ("v", m.v_cache[l])):
+            src = np.asarray(m.record[name][l], np.float32).reshape(4, sh.nkv, 128)
+            got = cache[0, :, :4, :].transpose(1, 0, 2)
+            for t in range(4):
+                for h in range(sh.nkv):
+                    x = src[t, h]
+                    scale = np.float32(np.abs(x).max()) / np.float32(448)
+                    y = (x / scale).astype(np.float32)
+                    for i in range(0, 128, 7):
+                        c = _brute.e4m3_nearest(float(y[i]), table)
+                        v = value[c & 0x7F] * (-1 if c & 0x80 else 1)
+                        prod = np.float32(np.float32(v) * scale)
+                        want = (np.array([prod], np.float32).view(np.uint32) + 0x7FFF +
+                                ((np.array([prod], np.float32).view(np.uint32) >> 16) & 1)) >> 16 << 16
+                        assert got[t, h, i] == want.astype(np.uint32).view(np.float32)[0], (l, name, t, h, i)

@@ -2,6 +2,7 @@
 declares, and rejects bad arguments with the documented status codes before
 anything reaches a GPU.  Runs without a GPU."""
 import ctypes
+import os
 
 import pytest
 import torch
@@ -19,10 +20,28 @@ def test_library_exports_every_header_function():
     assert q2.version().startswith("q2")
 
 
-def test_descriptor_layout_matches_header():
-    # data, dtype, ndim, shape[5], stride[5]
-    assert ctypes.sizeof(_lib.Q2Tensor) == 8 + 4 + 4 + 40 + 40
-    assert ctypes.sizeof(_lib.Q2Config) == 10 * 4 + 2 * 4
+def test_descriptor_layout_matches_header(tmp_path):
+    """The ctypes structures have the sizes and field offsets the C compiler
+    gives the header's structs."""
+    src = tmp_path / "layout.c"
+    fields = {"q2_tensor": [f for f, _ in _lib.Q2Tensor._fields_],
+              "q2_config": [f for f, _ in _lib.Q2Config._fields_]}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "q2.h"', "int main(void) {"]
+    for st, fs in fields.items():
+        lines.append(f'printf("%zu\\n", sizeof({st}));')
+        lines += [f'printf("%zu\\n", offsetof({st}, {f}));' for f in fs]
+    lines += ["return 0;", "}"]
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    import subprocess
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    want = []
+    for cls in (_lib.Q2Tensor, _lib.Q2Config):
+        want.append(ctypes.sizeof(cls))
+        want += [getattr(cls, f).offset for f, _ in cls._fields_]
+    assert got == want
 
 
 def _err(fn, *args):

@@ -326,3 +326,24 @@ def test_capacity_exceeded_is_state_error_and_changes_nothing():
     with pytest.raises(q2.Q2Error):
         m.decode(torch.zeros(1, dtype=torch.int64, device=DEV))
     m.close()
+
+
+def test_replay_stage_then_reset_leaves_forward_unchanged():
+    """The measurement hook launches each product of the step (decode and a
+    prefill chunk) without error, and a forward after a reset gives the same
+    logits as before the replays."""
+    sh = SMALL_BF16
+    w = synth.make_weights(sh, seed=8)
+    m = build_model(sh, w, 48, 2)
+    ids = torch.from_numpy(np.random.default_rng(2).integers(0, sh.vocab, (2, 20))).to(DEV)
+    before = m.prefill(ids, logits=True)[1].cpu().numpy()
+    for stage in range(5):
+        q2.q2_model_replay_stage(m.handle, stage, 2, 1, 2 * sh.nlayer)
+        q2.q2_model_replay_stage(m.handle, stage, 2, 20, sh.nlayer)
+    with pytest.raises(q2.Q2Error):
+        q2.q2_model_replay_stage(m.handle, 5, 2, 1, 1)
+    torch.cuda.synchronize()
+    m.reset()
+    after = m.prefill(ids, logits=True)[1].cpu().numpy()
+    m.close()
+    assert np.array_equal(before, after)

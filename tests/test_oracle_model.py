@@ -97,3 +97,29 @@ def test_bf16_writeback_matches_loop_forward():
     """The bf16 forward against the loop-written bf16 forward that rounds at
     the same points (float64 sums): same stored values, same logits."""
     pins.check_bf16_writeback_vs_brute(oracle.OracleModel)
+
+
+def test_fp8_cache_holds_quantised_rows():
+    pins.check_fp8_cache_values(oracle.OracleModel)
+
+
+def test_fp8_cache_decode_equals_recompute_and_batch_independence():
+    """With the FP8 cache each row is quantised once, on its own block, so a
+    decode step still equals the recompute of its prefix and a batched
+    sequence equals the same sequence alone."""
+    sh = synth.ModelShape("pin-fp8", "bf16", 2, 256, 4, 2, 128, 256, 64, 10000.0)
+    w = synth.make_weights(sh, seed=34)
+    prompts = np.array([[3, 1, 4, 1, 5], [9, 2, 6, 5, 3]], np.int64)
+    mb = oracle.OracleModel(sh, w, "bf16", 2, 16, kv="fp8")
+    toks, logits = mb.generate(prompts, 4)
+    for b in range(2):
+        ms = oracle.OracleModel(sh, w, "bf16", 1, 16, kv="fp8")
+        ts, ls = ms.generate(prompts[b:b + 1], 4)
+        assert np.array_equal(ts[0], toks[b])
+        # float32 products of a different row count may sum in another order:
+        # a bf16 flip moves a logit by a few 1e-3 at most at this size
+        assert all(np.abs(a[0] - c[b]).max() <= 2e-2 for a, c in zip(ls, logits))
+    full = np.concatenate([prompts[:1], toks[:1, :3]], axis=1)
+    r = oracle.OracleModel(sh, w, "bf16", 1, 16, kv="fp8")
+    lg, _ = r.forward(full)
+    assert np.abs(lg[0] - logits[3][0]).max() <= 2e-2

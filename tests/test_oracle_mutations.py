@@ -257,3 +257,78 @@ def test_bf16_residual_rounded_once_fails_brute(monkeypatch):
     product is not rounded before the add."""
     monkeypatch.setattr(oracle.OracleModel, "_st", _skip_rounding_unrecorded("o_proj"))
     assert _fails(pins.check_bf16_writeback_vs_brute, oracle.OracleModel)
+
+
+# ----------------------------------------------------------------------------- FP8 KV cache
+
+def e4m3_truncating(y):
+    """Rounds toward zero instead of to nearest."""
+    y = np.asarray(y, F32)
+    vals = ops.e4m3_values()
+    a = np.minimum(np.abs(y).astype(np.float64), 448.0)
+    code = np.searchsorted(vals, a, side="right") - 1
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def e4m3_ties_away(y):
+    """Ties away from zero instead of to even."""
+    y = np.asarray(y, F32)
+    vals = ops.e4m3_values()
+    a = np.abs(y).astype(np.float64)
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, len(vals) - 1)
+    lo = np.clip(hi - 1, 0, len(vals) - 1)
+    code = np.where(vals[hi] - a <= a - vals[lo], hi, lo)
+    code = np.where(a >= 448, 0x7E, code)
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def e4m3_values_fnuz():
+    """The bias-8 variant's magnitudes (half of E4M3FN's)."""
+    return ops.e4m3_values() / 2
+
+
+def kv_quantize_wrong_scale(x):
+    x = np.asarray(x, F32)
+    amax = np.max(np.abs(x), axis=-1, keepdims=True)
+    scale = np.where(amax == 0, F32(1), amax / F32(240.0)).astype(F32)
+    return ops.e4m3_encode(x / scale), np.where(amax == 0, F32(0), scale)[..., 0].astype(F32)
+
+
+def kv_quantize_per_tensor(x):
+    x = np.asarray(x, F32)
+    amax = np.max(np.abs(x))
+    scale = F32(amax / F32(448.0))
+    return ops.e4m3_encode(x / scale), np.full(x.shape[:-1], scale, F32)
+
+
+FP8_CASES = [
+    ("e4m3 truncation", lambda: pins.check_e4m3(ops.e4m3_values, e4m3_truncating, ops.e4m3_decode)),
+    ("e4m3 ties away from zero", lambda: pins.check_e4m3(ops.e4m3_values, e4m3_ties_away, ops.e4m3_decode)),
+    ("e4m3 bias-8 table", lambda: pins.check_e4m3(e4m3_values_fnuz, ops.e4m3_encode, ops.e4m3_decode)),
+    ("kv scale max/240", lambda: pins.check_kv_quant(kv_quantize_wrong_scale, ops.kv_dequantize)),
+    ("kv scale per tensor", lambda: pins.check_kv_quant(kv_quantize_per_tensor, ops.kv_dequantize)),
+]
+
+
+@pytest.mark.parametrize("name,case", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_fp8_mutation_is_caught(name, case):
+    assert _fails(case), f"planted mistake not caught: {name}"
+
+
+def test_fp8_model_mutation_v_not_quantised(monkeypatch):
+    """An FP8 cache that quantises k but stores v unquantised."""
+    real = ops.kv_dequantize
+    calls = [0]
+
+    def only_k(codes, scales):
+        calls[0] += 1
+        return real(codes, scales)
+
+    def quant_k_only(x):
+        calls[0] += 1
+        if calls[0] % 2 == 0:      # every second call is the v row
+            x = np.asarray(x, F32)
+            return ops.e4m3_encode(x), np.ones(x.shape[:-1], F32)
+        return ops.kv_quantize(x)
+    monkeypatch.setattr(ops, "kv_quantize", quant_k_only)
+    assert _fails(pins.check_fp8_cache_values, oracle.OracleModel)

@@ -46,3 +46,11 @@ def test_rearrange():
     assert y.flags.c_contiguous and y.shape == x.shape
     for idx in np.ndindex(*x.shape):
         assert y[idx] == x[idx]
+
+
+def test_e4m3_codec():
+    pins.check_e4m3(oracle.e4m3_values, oracle.e4m3_encode, oracle.e4m3_decode)
+
+
+def test_kv_block_quantization():
+    pins.check_kv_quant(oracle.kv_quantize, oracle.kv_dequantize)
