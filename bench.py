@@ -56,6 +56,8 @@ def parse():
                     help="time only the dominant kernel (for profiler counter runs) and print its record")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="KV cache: bf16 (the workloads' definition) or FP8 E4M3 blocks with per-block scales")
+    ap.add_argument("--paged", type=int, default=0,
+                    help="positions per page of a paged KV cache (0: contiguous per-sequence cache)")
     return ap.parse_args()
 
 
@@ -321,7 +323,7 @@ def main():
     t_gen = time.perf_counter() - t0
     max_seq = wl.prompt + wl.steps
     t0 = time.perf_counter()
-    model = q2.load_model(sh, weights, max_seq, wl.batch, kv_fp8=kv_fp8)
+    model = q2.load_model(sh, weights, max_seq, wl.batch, kv_fp8=kv_fp8, page_size=args.paged)
     torch.cuda.synchronize()
     t_load = time.perf_counter() - t0
     prompt = torch.from_numpy(synth.make_prompt(wl)).to(dev)
@@ -403,7 +405,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random-init weights and prompt ids)",
         "config": {"workload": f"{wl.key}: {wl.description}" + (" (FP8 KV cache)" if kv_fp8 else ""),
                    "shape": sh.name, "batch": wl.batch, "prompt": wl.prompt, "decode_steps": wl.steps,
-                   "kv_cache": args.kv, "parallelism": "single GPU"},
+                   "kv_cache": args.kv + (f", paged ({args.paged} positions per page)" if args.paged else ""),
+                   "parallelism": "single GPU"},
         "prefill_tok_s": round(prefill_tok_s, 1),
         "decode_tok_s": round(decode_tok_s, 2) if decode_tok_s else None,
         "prefill_ms": round(pre_s * 1e3, 3), "decode_ms": round(dec_s * 1e3, 3),

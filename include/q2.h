@@ -215,6 +215,15 @@ typedef struct {
                            E4M3 codes with one float32 scale per token, KV head
                            and 128-element block ("新一代大模型Day0推理适配与性能调优
                            教程", step 5), see q2_kv_quantize */
+  int32_t page_size;    /* 0: each sequence owns a contiguous [max_seq] cache
+                           region; > 0 (bf16 models, a multiple of 64): the
+                           cache is a pool of pages of page_size positions,
+                           taken as sequences grow and given back when they
+                           are released ("万亿参数大模型在国产加速卡上的Day-0适配
+                           教程", step 8: paged KV cache, continuous batching);
+                           sequences may then have different lengths */
+  int32_t kv_pages;     /* paged: pages in the pool (0: max_batch * ceil(max_seq
+                           / page_size), room for every sequence at max_seq) */
 } q2_config;
 
 /* Create a model on `device`: allocates the packed weights, the KV cache
@@ -262,6 +271,27 @@ q2_status q2_model_prefill_embeds(q2_model* m, const q2_tensor* embeds, const q2
  * model dtype, row b * T + t for sequence b and token t of that chunk.  Valid
  * until the next call on the model. */
 q2_status q2_model_hidden_view(q2_model* m, q2_tensor* x);
+
+/* Paged cache only (page_size > 0): sequences of different lengths
+ * ("万亿参数大模型在国产加速卡上的Day-0适配教程", step 8: paged KV cache and
+ * continuous batching, new requests joining a running batch).
+ * q2_model_seq_prefill: run ids [T] int64 for sequence `slot` at its
+ * positions len_slot .. len_slot + T - 1 (len_slot = 0 for a new or released
+ * slot), taking pages as needed; next: [1] or NULL, logits: [1, V] f32 or
+ * NULL.  Q2_ESTATE (nothing changed) if the pool has too few free pages or
+ * max_seq would be exceeded.
+ * q2_model_decode / q2_model_continue then step slots 0 .. B - 1 together,
+ * each at its own length (every one of them must hold at least one
+ * position).  q2_model_prefill still takes B sequences of equal length.
+ * q2_model_seq_release: the slot's pages return to the pool and its length
+ * to 0 (asynchronous on `stream`; no step using the slot may still be
+ * pending).  q2_model_seq_length: positions cached for `slot`.
+ * q2_model_free_pages: pages left in the pool. */
+q2_status q2_model_seq_prefill(q2_model* m, int32_t slot, const q2_tensor* ids, const q2_tensor* next,
+                               const q2_tensor* logits, void* stream);
+q2_status q2_model_seq_release(q2_model* m, int32_t slot, void* stream);
+q2_status q2_model_seq_length(const q2_model* m, int32_t slot, int32_t* len);
+q2_status q2_model_free_pages(const q2_model* m, int32_t* pages);
 
 /* One decode step: ids [B] int64 at position len; same outputs as prefill.
  * Replays a HIP graph captured once per batch size. */

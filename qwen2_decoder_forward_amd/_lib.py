@@ -35,7 +35,7 @@ class Q2Config(ctypes.Structure):
                 ("nh", ctypes.c_int32), ("nkv", ctypes.c_int32), ("dh", ctypes.c_int32),
                 ("inter", ctypes.c_int32), ("vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32),
                 ("max_batch", ctypes.c_int32), ("eps", ctypes.c_float), ("theta", ctypes.c_float),
-                ("kv_fp8", ctypes.c_int32)]
+                ("kv_fp8", ctypes.c_int32), ("page_size", ctypes.c_int32), ("kv_pages", ctypes.c_int32)]
 
 
 class Q2Error(RuntimeError):
@@ -79,6 +79,10 @@ _SIGS = {
     "q2_model_continue": ([ctypes.c_void_p, ctypes.c_int32, _P, _S], ctypes.c_int),
     "q2_model_kv_view": ([ctypes.c_void_p, ctypes.c_int32, _P, _P], ctypes.c_int),
     "q2_model_kv_scale_view": ([ctypes.c_void_p, ctypes.c_int32, _P, _P], ctypes.c_int),
+    "q2_model_seq_prefill": ([ctypes.c_void_p, ctypes.c_int32, _P, _P, _P, _S], ctypes.c_int),
+    "q2_model_seq_release": ([ctypes.c_void_p, ctypes.c_int32, _S], ctypes.c_int),
+    "q2_model_seq_length": ([ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
+    "q2_model_free_pages": ([ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
     "q2_model_replay_stage": ([ctypes.c_void_p] + [ctypes.c_int32] * 4 + [_S], ctypes.c_int),
     "q2_kv_quantize": ([_P, _P, _P, _S], ctypes.c_int),
     "q2_kv_dequantize": ([_P, _P, _P, _S], ctypes.c_int),
@@ -287,6 +291,27 @@ def q2_model_kv_scale_view(h, layer: int):
     k, v = Q2Tensor(), Q2Tensor()
     _check(lib.q2_model_kv_scale_view(h, int(layer), ctypes.byref(k), ctypes.byref(v)))
     return k, v
+
+
+def q2_model_seq_prefill(h, slot: int, ids, next_ids=None, logits=None, stream=None):
+    _check(lib.q2_model_seq_prefill(h, int(slot), _ref(desc(ids)), _ref(desc(next_ids)), _ref(desc(logits)),
+                                    _stream(stream)))
+
+
+def q2_model_seq_release(h, slot: int, stream=None):
+    _check(lib.q2_model_seq_release(h, int(slot), _stream(stream)))
+
+
+def q2_model_seq_length(h, slot: int) -> int:
+    n = ctypes.c_int32()
+    _check(lib.q2_model_seq_length(h, int(slot), ctypes.byref(n)))
+    return n.value
+
+
+def q2_model_free_pages(h) -> int:
+    n = ctypes.c_int32()
+    _check(lib.q2_model_free_pages(h, ctypes.byref(n)))
+    return n.value
 
 
 STAGE_QKV, STAGE_ATTN, STAGE_O, STAGE_GATE_UP, STAGE_DOWN = 0, 1, 2, 3, 4

@@ -133,10 +133,15 @@ __device__ __forceinline__ void dec_block(const uint4 (&kf)[4], const uint4 (&vf
   wave_lds_sync();
 }
 
-// FP8: K / V rows are E4M3 codes with a scale per key, dequantised to bf16
-// in registers just before their block's products (the loads in flight stay
-// at half the bytes).
-template <bool FP8>
+// KVM_STRIDED: K / V addressed by the strides of AttnArgs.  KVM_BF16 /
+// KVM_FP8: addressed as rows of the model's cache layout (a.cache: contiguous
+// or paged); FP8 rows are E4M3 codes with a scale per key, dequantised to
+// bf16 in registers just before their block's products (the loads in flight
+// stay at half the bytes).  A 16-key block never straddles a page (pages
+// hold a multiple of 64 positions), so one row lookup serves a block.
+enum KvMode : int { KVM_STRIDED = 0, KVM_BF16 = 1, KVM_FP8 = 2 };
+
+template <int KVM>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk, int nsplit,
                                                           float* __restrict__ part_o, float2* __restrict__ part_ml) {
   // the V^T tiles of the key loop and the merge buffers of the four waves
@@ -153,7 +158,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
   const int g = bg - b * a.nkv;
   const int group = a.nh / a.nkv;
   const int R = a.T * group;
-  const int S = a.d_len ? (*a.d_len + a.T) : a.S;
+  const int S = a.lens ? (a.lens[b] + a.T) : a.d_len ? (*a.d_len + a.T) : a.S;
   const int P = S - a.T;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -181,22 +186,25 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   int j0 = j_begin + 16 * wave;
-  if constexpr (FP8) {
+  // keys past the split's end re-read its last key (jl); a block's rows are
+  // looked up at Jc, the block start clamped likewise
+  const int jl = max(j_end - 1, 0);
+  if constexpr (KVM == KVM_FP8) {
   // as below, with 8-byte code loads and each key's scale
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.k) + b * a.k_bs + g * a.k_hs;
-  const uint8_t* vbase = static_cast<const uint8_t*>(a.v) + b * a.v_bs + g * a.v_hs;
-  const float* ksb = a.ks + b * a.s_bs + g * a.s_hs;
-  const float* vsb = a.vs + b * a.s_bs + g * a.s_hs;
+  const uint8_t* kc8 = static_cast<const uint8_t*>(a.cache.kc);
+  const uint8_t* vc8 = static_cast<const uint8_t*>(a.cache.vc);
 #define Q2_DEC_LOAD8(KR_, VR_, KS_, VS_, J0_)                                                         \
   {                                                                                                  \
-    const int key_ = max(min((J0_) + col, j_end - 1), 0);                                           \
+    const int jc_ = min((J0_), jl & ~15);                                                            \
+    const int64_t r0_ = kv_row(a.cache, b, g, jc_) - jc_;                                            \
+    const int key_ = max(min((J0_) + col, jl), 0);                                                   \
     _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) KR_[kk] =                                       \
-        *reinterpret_cast<const uint2*>(kbase + static_cast<int64_t>(key_) * a.k_ss + 32 * kk + 8 * G); \
-    KS_ = ksb[key_];                                                                                 \
+        *reinterpret_cast<const uint2*>(kc8 + (r0_ + key_) * D + 32 * kk + 8 * G);                   \
+    KS_ = a.cache.ks[r0_ + key_];                                                                    \
     _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) {                                               \
-      const int vk_ = max(min((J0_) + 4 * G + s_, j_end - 1), 0);                                    \
-      VR_[s_] = *reinterpret_cast<const uint2*>(vbase + static_cast<int64_t>(vk_) * a.v_ss + 8 * col); \
-      VS_[s_] = vsb[vk_];                                                                            \
+      const int vk_ = max(min((J0_) + 4 * G + s_, jl), 0);                                           \
+      VR_[s_] = *reinterpret_cast<const uint2*>(vc8 + (r0_ + vk_) * D + 8 * col);                    \
+      VS_[s_] = a.cache.vs[r0_ + vk_];                                                               \
     }                                                                                                \
   }
 #define Q2_DEC_BLOCK8(KR_, VR_, KS_, VS_, J0_)                                                        \
@@ -221,20 +229,31 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
 #undef Q2_DEC_LOAD8
 #undef Q2_DEC_BLOCK8
   } else {
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + b * a.k_bs + g * a.k_hs;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + b * a.v_bs + g * a.v_hs;
+  // strided: row j of this head at base + j * stride; cache layout: rows of
+  // D elements looked up per block
+  const bool lay = KVM == KVM_BF16;
+  const uint16_t* kbase = lay ? static_cast<const uint16_t*>(a.cache.kc)
+                              : static_cast<const uint16_t*>(a.k) + b * a.k_bs + g * a.k_hs;
+  const uint16_t* vbase = lay ? static_cast<const uint16_t*>(a.cache.vc)
+                              : static_cast<const uint16_t*>(a.v) + b * a.v_bs + g * a.v_hs;
+  const int64_t kss = lay ? D : a.k_ss, vss = lay ? D : a.v_ss;
   // K rows j0 + col: 4 x 16 B (d = 32kk + 8G .. +8); V rows j0 + 4G + s,
   // d-chunk 8*col.  Loads are unconditional (keys past the split read its
   // last key: their scores are masked and their probabilities exactly 0), so
   // the compiler can count them and wait for one block only.
 #define Q2_DEC_LOAD(KF_, VF_, J0_)                                                                   \
   {                                                                                                  \
-    const int key_ = max(min((J0_) + col, j_end - 1), 0);                                           \
+    int64_t r0_ = 0;                                                                                 \
+    if (lay) {                                                                                       \
+      const int jc_ = min((J0_), jl & ~15);                                                          \
+      r0_ = kv_row(a.cache, b, g, jc_) - jc_;                                                        \
+    }                                                                                                \
+    const int key_ = max(min((J0_) + col, jl), 0);                                                   \
     _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) KF_[kk] =                                       \
-        ld16(kbase + static_cast<int64_t>(key_) * a.k_ss + 32 * kk + 8 * G);                         \
+        ld16(kbase + (r0_ + key_) * kss + 32 * kk + 8 * G);                                          \
     _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) {                                               \
-      const int vk_ = max(min((J0_) + 4 * G + s_, j_end - 1), 0);                                    \
-      VF_[s_] = ld16(vbase + static_cast<int64_t>(vk_) * a.v_ss + 8 * col);                          \
+      const int vk_ = max(min((J0_) + 4 * G + s_, jl), 0);                                           \
+      VF_[s_] = ld16(vbase + (r0_ + vk_) * vss + 8 * col);                                           \
     }                                                                                                \
   }
   // two register sets, loop unrolled by two: the next block's loads are in
@@ -817,7 +836,7 @@ q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0 || a.T == 0) return Q2_OK;
   const int group = a.nh / a.nkv;
   if (a.T * group <= 16) {
-    const int s_max = a.d_len ? a.s_max : a.S;
+    const int s_max = (a.d_len || a.lens) ? a.s_max : a.S;
     DecodePlan p = plan_decode(a.B, s_max, a.nkv);
     float* part_o = nullptr;
     float2* part_ml = nullptr;
@@ -835,11 +854,14 @@ q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
       part_o = static_cast<float*>(a.scratch);
       part_ml = reinterpret_cast<float2*>(part_o + slots * D);
     }
-    if (a.kv_fp8)
-      hipLaunchKernelGGL(attn_decode_kernel<true>, dim3(p.nsplit, a.B * a.nkv), dim3(256), 0, s, a, p.chunk,
+    if (a.use_cache && a.cache.fp8)
+      hipLaunchKernelGGL(attn_decode_kernel<KVM_FP8>, dim3(p.nsplit, a.B * a.nkv), dim3(256), 0, s, a, p.chunk,
+                         p.nsplit, part_o, part_ml);
+    else if (a.use_cache)
+      hipLaunchKernelGGL(attn_decode_kernel<KVM_BF16>, dim3(p.nsplit, a.B * a.nkv), dim3(256), 0, s, a, p.chunk,
                          p.nsplit, part_o, part_ml);
     else
-      hipLaunchKernelGGL(attn_decode_kernel<false>, dim3(p.nsplit, a.B * a.nkv), dim3(256), 0, s, a, p.chunk,
+      hipLaunchKernelGGL(attn_decode_kernel<KVM_STRIDED>, dim3(p.nsplit, a.B * a.nkv), dim3(256), 0, s, a, p.chunk,
                          p.nsplit, part_o, part_ml);
     Q2_TRY(check_launch("attn_decode"));
     if (p.nsplit > 1 && !a.leave_partials) {
@@ -851,7 +873,8 @@ q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
     }
     return Q2_OK;
   }
-  Q2_CHECK(!a.kv_fp8, Q2_EINVAL, "FP8 K/V: the prefill kernel reads bf16 (expand the cache first)");
+  Q2_CHECK(!a.use_cache && !a.lens, Q2_EINVAL,
+           "prefill attention reads strided bf16 K/V of equal-length sequences (expand the cache first)");
   // the prefill kernel's buffer loads address a head's keys with 32-bit
   // byte offsets
   const int64_t max_keys = a.d_len ? a.s_max : a.S;

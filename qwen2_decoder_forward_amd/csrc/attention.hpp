@@ -2,6 +2,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "kvcache.hpp"
 
 namespace q2 {
 
@@ -28,13 +29,13 @@ struct AttnArgs {
   size_t scratch_bytes;
   bool leave_partials;         // split-KV: skip the merge, the consumer merges the partials
   bool unsplit_if_short;       // run unsplit when the partials exceed scratch_bytes (else fail)
-  // FP8 cache (decode path only): k / v hold E4M3 codes (strides in bytes),
-  // ks / vs one float32 scale per (sequence, kv head, key) at
-  // b * s_bs + g * s_hs + j (kvcache.hpp)
-  bool kv_fp8;
-  const float* ks;
-  const float* vs;
-  int64_t s_bs, s_hs;
+  // decode path only: K / V are rows of the model's cache (bf16 or FP8,
+  // contiguous or paged, kvcache.hpp) instead of the strided k / v above
+  bool use_cache;
+  KvLayout cache;
+  // per-sequence cached lengths (S_b = lens[b] + T; sequences of different
+  // lengths), or null
+  const int* lens;
 };
 
 q2_status attention_bf16(const AttnArgs& a, hipStream_t s);

@@ -44,6 +44,9 @@ struct Epi {
   // row len + t: a staging buffer [B][nkv][T][d] that a separate kernel
   // stores into the cache (quantised caches); RoPE still uses len + t
   int kv_rel;
+  // per-sequence cached lengths (sequence b's token t sits at lens[b] + t),
+  // overriding d_len / len0 when set
+  const int* lens;
   const float2* rope;     // [S_max][d/2] (cos, sin)
   // ARGMAX: packed (value, index) keys, KEY_SLOTS per row each on its own
   // 128-byte line (stride KEY_STRIDE), combined with atomicMax: spreading a
@@ -101,7 +104,7 @@ __device__ __forceinline__ void epi_pair(const Epi& e, int m, int n, float v0, f
       const int r = n - head * d;
       const int bt = m / e.T;
       const int t = m - bt * e.T;
-      const int pos = (e.d_len ? *e.d_len : e.len0) + t;
+      const int pos = (e.lens ? e.lens[bt] : e.d_len ? *e.d_len : e.len0) + t;
       if (head < e.nh + e.nkv) {
         const int p = r >> 1;
         const float2 cs = e.rope[static_cast<int64_t>(pos) * (d >> 1) + p];

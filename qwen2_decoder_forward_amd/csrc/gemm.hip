@@ -309,7 +309,7 @@ __device__ __forceinline__ void stg_put(uint16_t* sh, const Epi& e, int M, int f
       const int p = nl >> 1;
       float2 c0 = make_float2(1.f, 0.f), c1 = c0;
       if (m < M) {
-        const int64_t pos = len0 + m % e.T;
+        const int64_t pos = (e.lens ? e.lens[m / e.T] : len0) + m % e.T;
         const float4 cs = *reinterpret_cast<const float4*>(e.rope + pos * 64 + p);
         c0 = make_float2(cs.x, cs.y);
         c1 = make_float2(cs.z, cs.w);

@@ -148,7 +148,7 @@ __device__ __forceinline__ void epi_preload(const Epi& e, int M, int N, int n0, 
     pre.b1 = bf2f(b[n + 1]);
     const int head = n / e.dh;
     const int t = m % e.T;
-    pre.pos = (e.d_len ? *e.d_len : e.len0) + t;
+    pre.pos = (e.lens ? e.lens[m / e.T] : e.d_len ? *e.d_len : e.len0) + t;
     if (head < e.nh + e.nkv) pre.cs = e.rope[static_cast<int64_t>(pre.pos) * (e.dh >> 1) + ((n - head * e.dh) >> 1)];
   }
 }

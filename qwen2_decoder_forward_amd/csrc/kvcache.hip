@@ -1,7 +1,8 @@
-// FP8 KV-cache kernels: block quantisation and dequantisation (one wave per
+// KV-cache kernels: FP8 block quantisation and dequantisation (one wave per
 // 128-element block: lane l holds elements 2l and 2l + 1), the model's store
-// of new k / v rows into the cache, and the expansion of cached positions to
-// bf16 for the prefill attention.
+// of new k / v rows into its cache (bf16 or FP8, contiguous or paged), and
+// the expansion of cached positions to contiguous bf16 for the prefill
+// attention.
 #include "kvcache.hpp"
 
 namespace q2 {
@@ -45,48 +46,61 @@ __global__ __launch_bounds__(256) void kv_dequantize_kernel(uint16_t* __restrict
 }
 
 // Rows (b, h, t, kind) of the staged k / v, one wave each.
-__global__ __launch_bounds__(256) void kv_store_fp8_kernel(KvFp8 c, const uint16_t* __restrict__ k_stage,
-                                                           const uint16_t* __restrict__ v_stage, int B, int nkv,
-                                                           int T, const int* __restrict__ d_len, int len0) {
-  const int64_t rows = static_cast<int64_t>(B) * nkv * T;
+__global__ __launch_bounds__(256) void kv_store_kernel(KvLayout c, const uint16_t* __restrict__ k_stage,
+                                                       const uint16_t* __restrict__ v_stage, int B, int T,
+                                                       const int* __restrict__ lens, const int* __restrict__ d_len,
+                                                       int len0) {
+  const int64_t rows = static_cast<int64_t>(B) * c.nkv * T;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (r >= 2 * rows) return;
   const bool isv = r >= rows;
   const int64_t i = isv ? r - rows : r;      // (b * nkv + h) * T + t
   const int t = static_cast<int>(i % T);
   const int64_t bh = i / T;
-  const int h = static_cast<int>(bh % nkv);
-  const int b = static_cast<int>(bh / nkv);
-  const int64_t pos = (d_len ? *d_len : len0) + t;
+  const int h = static_cast<int>(bh % c.nkv);
+  const int b = static_cast<int>(bh / c.nkv);
+  const int pos = (lens ? lens[b] : d_len ? *d_len : len0) + t;
+  if (!kv_mapped(c, b, pos)) return;  // whole waves leave together
   const int lane = threadIdx.x & 63;
   const uint16_t* src = (isv ? v_stage : k_stage) + i * KV_BLOCK;
   const uint32_t xw = *reinterpret_cast<const uint32_t*>(src + 2 * lane);
-  uint32_t c2;
-  const float scale = quant_pair(xw, c2);
-  uint8_t* dst = (isv ? c.vc : c.kc) + b * c.c_bs + h * c.c_hs + pos * KV_BLOCK;
-  *reinterpret_cast<uint16_t*>(dst + 2 * lane) = static_cast<uint16_t>(c2);
-  if (lane == 0) (isv ? c.vs : c.ks)[b * c.s_bs + h * c.s_hs + pos] = scale;
+  const int64_t row = kv_row(c, b, h, pos);
+  if (c.fp8) {
+    uint32_t c2;
+    const float scale = quant_pair(xw, c2);
+    uint8_t* dst = static_cast<uint8_t*>(isv ? c.vc : c.kc) + row * KV_BLOCK;
+    *reinterpret_cast<uint16_t*>(dst + 2 * lane) = static_cast<uint16_t>(c2);
+    if (lane == 0) (isv ? c.vs : c.ks)[row] = scale;
+  } else {
+    uint16_t* dst = static_cast<uint16_t*>(isv ? c.vc : c.kc) + row * KV_BLOCK;
+    *reinterpret_cast<uint32_t*>(dst + 2 * lane) = xw;
+  }
 }
 
 // Cache rows (b, h, j < S, kind) -> bf16 [B][nkv][S_cap][128], 16 lanes per
-// row (8 codes each), 16 rows per workgroup.
-__global__ __launch_bounds__(256) void kv_expand_fp8_kernel(uint16_t* __restrict__ out_k, uint16_t* __restrict__ out_v,
-                                                            int64_t S_cap, KvFp8 c, int B, int nkv, int S) {
-  const int64_t rows = static_cast<int64_t>(B) * nkv * S;
+// row (8 elements each), 16 rows per workgroup.
+__global__ __launch_bounds__(256) void kv_expand_kernel(uint16_t* __restrict__ out_k, uint16_t* __restrict__ out_v,
+                                                        int64_t S_cap, KvLayout c, int B, int S) {
+  const int64_t rows = static_cast<int64_t>(B) * c.nkv * S;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   if (r >= 2 * rows) return;
   const bool isv = r >= rows;
   const int64_t i = isv ? r - rows : r;      // (b * nkv + h) * S + j
   const int j = static_cast<int>(i % S);
   const int64_t bh = i / S;
-  const int h = static_cast<int>(bh % nkv);
-  const int b = static_cast<int>(bh / nkv);
+  const int h = static_cast<int>(bh % c.nkv);
+  const int b = static_cast<int>(bh / c.nkv);
   const int q = threadIdx.x & 15;
-  const uint8_t* src = (isv ? c.vc : c.kc) + b * c.c_bs + h * c.c_hs + static_cast<int64_t>(j) * KV_BLOCK + 8 * q;
-  const float sc = (isv ? c.vs : c.ks)[b * c.s_bs + h * c.s_hs + j];
-  const uint2 codes = *reinterpret_cast<const uint2*>(src);
+  const int64_t row = kv_row(c, b, h, j);
   uint16_t* dst = (isv ? out_v : out_k) + (bh * S_cap + j) * KV_BLOCK + 8 * q;
-  *reinterpret_cast<uint4*>(dst) = e4m3_dequant8(codes, sc);
+  if (c.fp8) {
+    const uint2 codes = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(isv ? c.vc : c.kc) +
+                                                        row * KV_BLOCK + 8 * q);
+    *reinterpret_cast<uint4*>(dst) = e4m3_dequant8(codes, (isv ? c.vs : c.ks)[row]);
+  } else {
+    *reinterpret_cast<uint4*>(dst) =
+        *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(isv ? c.vc : c.kc) + row * KV_BLOCK + 8 * q);
+  }
 }
 
 }  // namespace
@@ -107,23 +121,23 @@ q2_status launch_kv_dequantize(uint16_t* x, int64_t ldx, const uint8_t* codes, i
   return check_launch("kv_dequantize");
 }
 
-q2_status launch_kv_store_fp8(const KvFp8& c, const uint16_t* k_stage, const uint16_t* v_stage, int B, int nkv, int T,
-                              const int* d_len, int len0, hipStream_t s) {
-  const int64_t rows = 2 * static_cast<int64_t>(B) * nkv * T;
+q2_status launch_kv_store(const KvLayout& c, const uint16_t* k_stage, const uint16_t* v_stage, int B, int T,
+                          const int* lens, const int* d_len, int len0, hipStream_t s) {
+  const int64_t rows = 2 * static_cast<int64_t>(B) * c.nkv * T;
   if (rows == 0) return Q2_OK;
-  hipLaunchKernelGGL(kv_store_fp8_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s, c, k_stage,
-                     v_stage, B, nkv, T, d_len, len0);
-  return check_launch("kv_store_fp8");
+  hipLaunchKernelGGL(kv_store_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s, c, k_stage, v_stage,
+                     B, T, lens, d_len, len0);
+  return check_launch("kv_store");
 }
 
-q2_status launch_kv_expand_fp8(uint16_t* out_k, uint16_t* out_v, int64_t S_cap, const KvFp8& c, int B, int nkv, int S,
-                               hipStream_t s) {
-  const int64_t rows = 2 * static_cast<int64_t>(B) * nkv * S;
+q2_status launch_kv_expand(uint16_t* out_k, uint16_t* out_v, int64_t S_cap, const KvLayout& c, int B, int S,
+                           hipStream_t s) {
+  const int64_t rows = 2 * static_cast<int64_t>(B) * c.nkv * S;
   if (rows == 0) return Q2_OK;
   Q2_CHECK(S <= S_cap, Q2_ESHAPE, "kv expand: %d positions exceed the buffer's %lld", S, static_cast<long long>(S_cap));
-  hipLaunchKernelGGL(kv_expand_fp8_kernel, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, s, out_k,
-                     out_v, S_cap, c, B, nkv, S);
-  return check_launch("kv_expand_fp8");
+  hipLaunchKernelGGL(kv_expand_kernel, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, s, out_k, out_v,
+                     S_cap, c, B, S);
+  return check_launch("kv_expand");
 }
 
 }  // namespace q2

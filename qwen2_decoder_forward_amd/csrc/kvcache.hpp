@@ -82,26 +82,50 @@ q2_status launch_kv_quantize(uint8_t* codes, int64_t ldc, float* scales, const u
 q2_status launch_kv_dequantize(uint16_t* x, int64_t ldx, const uint8_t* codes, int64_t ldc, const float* scales,
                                int64_t n, hipStream_t s);
 
-// One layer's FP8 cache: codes [B][nkv][S_max][128] bytes and scales
-// [B][nkv][S_max] for K and for V.
-struct KvFp8 {
-  uint8_t* kc;
-  uint8_t* vc;
-  float* ks;
+// One layer's cache as rows of 128 elements: the bf16 values, or the FP8
+// codes (1 byte each) with one float32 scale per row.  Row (b, h, j) --
+// sequence b, KV head h, position j -- is
+//   contiguous: b * bs + h * hs + j
+//   paged:      table[b * tstride + j / P] * nkv * P + h * P + j % P
+// (a page holds P consecutive positions of all KV heads of one sequence,
+// table maps a sequence's page index to a page of the pool).
+struct KvLayout {
+  void* kc;
+  void* vc;
+  float* ks;        // FP8 scales (null for bf16)
   float* vs;
-  int64_t c_bs, c_hs;  // code strides (bytes) between sequences / heads; 128 between positions
-  int64_t s_bs, s_hs;  // scale strides (floats); 1 between positions
+  int fp8;
+  int64_t bs, hs;   // contiguous strides, in rows
+  const int* table; // paged: [max_batch][tstride] page numbers, or null
+  int64_t tstride;
+  int P;            // positions per page (a multiple of 64)
+  int nkv;
 };
 
-// Quantise this call's new k and v rows, staged as bf16 [B][nkv][T][128]
-// (k_stage, v_stage), into the cache at positions len .. len + T - 1 where
-// len = *d_len when d_len is set, else len0.
-q2_status launch_kv_store_fp8(const KvFp8& c, const uint16_t* k_stage, const uint16_t* v_stage, int B, int nkv, int T,
-                              const int* d_len, int len0, hipStream_t s);
+// (The host gives a page to every position a call writes or reads; a
+// position without one, table entry -1, would be a bug: it maps to page 0
+// here rather than outside the pool, and kv_store skips it.)
+__device__ __forceinline__ int64_t kv_row(const KvLayout& c, int b, int h, int j) {
+  if (c.table)
+    return static_cast<int64_t>(max(c.table[b * c.tstride + j / c.P], 0)) * c.nkv * c.P + h * c.P + j % c.P;
+  return b * c.bs + h * c.hs + j;
+}
 
-// Dequantise cache positions [0, S) into bf16 K and V arrays laid out
-// [B][nkv][S_cap][128] (out_k, out_v), for the prefill attention.
-q2_status launch_kv_expand_fp8(uint16_t* out_k, uint16_t* out_v, int64_t S_cap, const KvFp8& c, int B, int nkv, int S,
-                               hipStream_t s);
+__device__ __forceinline__ bool kv_mapped(const KvLayout& c, int b, int j) {
+  return !c.table || c.table[b * c.tstride + j / c.P] >= 0;
+}
+
+// Store this call's new k and v rows, staged as bf16 [B][nkv][T][128]
+// (k_stage, v_stage), at positions pos_b .. pos_b + T - 1 of each sequence
+// b: pos_b = lens[b] when lens is set, else *d_len when set, else len0.
+// bf16 caches copy the rows; FP8 caches quantise them.
+q2_status launch_kv_store(const KvLayout& c, const uint16_t* k_stage, const uint16_t* v_stage, int B, int T,
+                          const int* lens, const int* d_len, int len0, hipStream_t s);
+
+// Positions [0, S) of B sequences as bf16 K and V arrays [B][nkv][S_cap][128]
+// (out_k, out_v), for the prefill attention: a gather of pages and/or the
+// dequantisation of FP8 rows.
+q2_status launch_kv_expand(uint16_t* out_k, uint16_t* out_v, int64_t S_cap, const KvLayout& c, int B, int S,
+                           hipStream_t s);
 
 }  // namespace q2

@@ -62,13 +62,29 @@ struct q2_model {
   int64_t kv_lstride = 0, kv_bstride = 0, kv_hstride = 0;
   // FP8 cache (cfg.kv_fp8): kc / vc hold E4M3 codes (same layout, 1 byte per
   // element) and ks / vs one float32 scale per (layer, sequence, head,
-  // position); new k / v rows are staged as bf16 in kstage / vstage
-  // [B][nkv][T][d] and quantised by kv_store_fp8; the prefill attention reads
-  // the positions it needs expanded to bf16 in kexp / vexp [B][nkv][S][d]
+  // position).  FP8 and paged caches stage new k / v rows as bf16 in kstage /
+  // vstage [B][nkv][T][d], which kv_store writes (or quantises) into the
+  // cache; their prefill attention reads the positions it needs expanded to
+  // contiguous bf16 in kexp / vexp [B][nkv][S][d]
   bool fp8 = false;
   float* ks = nullptr;
   float* vs = nullptr;
   int64_t ks_lstride = 0;
+  // paged cache (cfg.page_size > 0): each layer's K and V pools hold
+  // pages_total pages of [nkv][page][d]; sequence b's positions
+  // [p * page, (p + 1) * page) live in page d_table[b][p] (all layers);
+  // d_lens[b] is sequence b's cached length (sequences may differ).  The host
+  // keeps copies (h_table, h_lens) and the free list; pages are taken as
+  // positions are reached and given back when a sequence is released.
+  int page = 0;
+  int pages_total = 0;
+  int pages_per_seq = 0;
+  int* d_table = nullptr;
+  int* d_lens = nullptr;
+  std::vector<int> h_table;
+  std::vector<int> h_lens;
+  std::vector<int> free_pages;
+  int slot0 = 0;            // first slot of the rows of the current call (paged)
   void* kstage = nullptr;
   void* vstage = nullptr;
   void* kexp = nullptr;
@@ -109,7 +125,24 @@ struct q2_model {
 namespace {
 
 __global__ void set_len_kernel(int* d_len, int v) { *d_len = v; }
-__global__ void advance_len_kernel(int* d_len, int t) { *d_len += t; }
+// The device length, and with lens each of the B sequences' lengths, move on by t.
+__global__ void advance_len_kernel(int* d_len, int t, int* lens, int B) {
+  if (threadIdx.x == 0) *d_len += t;
+  if (lens && static_cast<int>(threadIdx.x) < B) lens[threadIdx.x] += t;
+}
+
+// Paged cache: table[slot * stride + page_idx[i]] = page[i] for i < n, and
+// lens[slot_len] = len_val when slot_len >= 0 (host-side page allocation and
+// sequence release, applied in stream order).
+struct TableEdits {
+  int n;
+  int slot[64], idx[64], page[64];
+};
+__global__ void table_edit_kernel(int* table, int64_t stride, TableEdits e, int* lens, int slot_len, int len_val) {
+  const int i = threadIdx.x;
+  if (i < e.n) table[static_cast<int64_t>(e.slot[i]) * stride + e.idx[i]] = e.page[i];
+  if (i == 0 && slot_len >= 0) lens[slot_len] = len_val;
+}
 
 __global__ void copy_ids_kernel(int64_t* dst, int64_t dst_stride, const int64_t* src, int64_t src_stride, int B) {
   const int b = blockIdx.x * 64 + threadIdx.x;
@@ -122,7 +155,7 @@ __global__ void copy_ids_kernel(int64_t* dst, int64_t dst_stride, const int64_t*
 // `pending` (the positions of this forward not yet counted).  One workgroup.
 __global__ __launch_bounds__(1024) void finalize_kernel(unsigned long long* keys, int64_t* ids_buf, int64_t* hist,
                                                         int64_t hist_ld, int* d_len, int pending, int64_t* next,
-                                                        int64_t next_stride, int B) {
+                                                        int64_t next_stride, int B, int* lens) {
   // one wave per row, FIN_ROWS rows per wave at a time with their slot loads
   // in flight together; lane i takes key slot i
   static_assert(KEY_SLOTS == 64, "one key slot per lane");
@@ -153,7 +186,13 @@ __global__ __launch_bounds__(1024) void finalize_kernel(unsigned long long* keys
         if (b >= B) break;
         const int64_t id = static_cast<int64_t>(argmax_key_index(best[r]));
         ids_buf[b] = id;
-        hist[b * hist_ld + pos] = id;
+        if (lens) {
+          // per-sequence position; this lane alone reads and moves lens[b]
+          hist[b * hist_ld + lens[b] + pending] = id;
+          lens[b] += pending;
+        } else {
+          hist[b * hist_ld + pos] = id;
+        }
         if (next) next[b * next_stride] = id;
       }
     }
@@ -162,13 +201,15 @@ __global__ __launch_bounds__(1024) void finalize_kernel(unsigned long long* keys
   if (threadIdx.x == 0 && pending) *d_len += pending;
 }
 
+// out[b][c] = hist[b][start + c]; with lens, start = lens[b] - back (per
+// sequence, after the steps moved lens on).
 __global__ void copy_hist_kernel(int64_t* out, int64_t ld_out, const int64_t* hist, int64_t hist_ld, int start, int n,
-                                 int B) {
+                                 int B, const int* lens, int back) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= n * B) return;
   const int b = i / n;
   const int c = i - b * n;
-  out[b * ld_out + c] = hist[b * hist_ld + start + c];
+  out[b * ld_out + c] = hist[b * hist_ld + (lens ? lens[b] - back : start) + c];
 }
 
 __global__ void copy_logits_kernel(float* out, int64_t ld_out, const float* src, int64_t ld_src, int V, int B) {
@@ -181,18 +222,33 @@ __global__ void copy_logits_kernel(float* out, int64_t ld_out, const float* src,
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
-KvFp8 fp8_layer(const q2_model* m, int l) {
-  KvFp8 c{};
-  c.kc = static_cast<uint8_t*>(m->kc) + l * m->kv_lstride;
-  c.vc = static_cast<uint8_t*>(m->vc) + l * m->kv_lstride;
-  c.ks = m->ks + l * m->ks_lstride;
-  c.vs = m->vs + l * m->ks_lstride;
-  c.c_bs = m->kv_bstride;
-  c.c_hs = m->kv_hstride;
-  c.s_hs = m->cfg.max_seq;
-  c.s_bs = int64_t(m->cfg.max_seq) * m->cfg.nkv;
+bool staged_kv(const q2_model* m) { return m->fp8 || m->page > 0; }
+
+// Layer l's cache as KvLayout, for the rows of the current call (slot0 on).
+KvLayout cache_layout(const q2_model* m, int l) {
+  KvLayout c{};
+  const int kv_es = m->fp8 ? 1 : m->esize;
+  c.kc = static_cast<char*>(m->kc) + l * m->kv_lstride * kv_es;
+  c.vc = static_cast<char*>(m->vc) + l * m->kv_lstride * kv_es;
+  c.fp8 = m->fp8 ? 1 : 0;
+  if (m->fp8) {
+    c.ks = m->ks + l * m->ks_lstride;
+    c.vs = m->vs + l * m->ks_lstride;
+  }
+  c.nkv = m->cfg.nkv;
+  if (m->page > 0) {
+    c.table = m->d_table + static_cast<int64_t>(m->slot0) * m->pages_per_seq;
+    c.tstride = m->pages_per_seq;
+    c.P = m->page;
+  } else {
+    c.hs = m->cfg.max_seq;
+    c.bs = int64_t(m->cfg.max_seq) * m->cfg.nkv;
+  }
   return c;
 }
+
+// Per-sequence lengths of the current call's rows (paged), else null.
+const int* call_lens(const q2_model* m) { return m->page > 0 ? m->d_lens + m->slot0 : nullptr; }
 
 q2_status gemm(const q2_model* m, const GemmArgs& a, hipStream_t s) {
   return m->cfg.dtype == Q2_BF16 ? gemm_bf16(a, s) : gemm_f32(a, s);
@@ -283,11 +339,13 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s, in
       a.epi.out = m->q;
       a.epi.ldo = qd;
       a.epi.bias = L.b_qkv;
-      a.epi.kc = m->fp8 ? m->kstage : kc;
-      a.epi.vc = m->fp8 ? m->vstage : vc;
-      a.epi.kv_bstride = m->fp8 ? int64_t(c.nkv) * Tc * d : m->kv_bstride;
-      a.epi.kv_hstride = m->fp8 ? int64_t(Tc) * d : m->kv_hstride;
-      a.epi.kv_rel = m->fp8 ? 1 : 0;
+      const bool stg = staged_kv(m);
+      a.epi.kc = stg ? m->kstage : kc;
+      a.epi.vc = stg ? m->vstage : vc;
+      a.epi.kv_bstride = stg ? int64_t(c.nkv) * Tc * d : m->kv_bstride;
+      a.epi.kv_hstride = stg ? int64_t(Tc) * d : m->kv_hstride;
+      a.epi.kv_rel = stg ? 1 : 0;
+      a.epi.lens = call_lens(m);
       a.epi.nh = c.nh;
       a.epi.nkv = c.nkv;
       a.epi.dh = d;
@@ -297,9 +355,9 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s, in
       if (want(STAGE_QKV)) Q2_TRY(gemm(m, a, s));
       cur = nxt;
       pend_splits = 0;
-      if (m->fp8 && want(STAGE_QKV))
-        Q2_TRY(launch_kv_store_fp8(fp8_layer(m, l), static_cast<const uint16_t*>(m->kstage),
-                                   static_cast<const uint16_t*>(m->vstage), B, c.nkv, Tc, m->d_len, m->len, s));
+      if (staged_kv(m) && want(STAGE_QKV))
+        Q2_TRY(launch_kv_store(cache_layout(m, l), static_cast<const uint16_t*>(m->kstage),
+                               static_cast<const uint16_t*>(m->vstage), B, Tc, call_lens(m), m->d_len, m->len, s));
     }
     // with one query per sequence and split-KV partials, o_proj merges them
     // itself -- when there are few: every o_proj workgroup merges all rows of
@@ -334,19 +392,17 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s, in
       a.s_max = c.max_seq;
       a.scratch = m->ascratch;
       a.scratch_bytes = m->ascratch_bytes;
-      if (m->fp8) {
-        const KvFp8 f = fp8_layer(m, l);
+      if (staged_kv(m)) {
         if (Tc * (c.nh / c.nkv) <= 16) {
-          // decode kernel: reads the codes and scales itself (byte strides)
-          a.kv_fp8 = true;
-          a.ks = f.ks;
-          a.vs = f.vs;
-          a.s_bs = f.s_bs;
-          a.s_hs = f.s_hs;
+          // decode kernel: reads the cache rows itself (per-sequence lengths when paged)
+          a.use_cache = true;
+          a.cache = cache_layout(m, l);
+          a.lens = call_lens(m);
         } else {
-          // prefill kernel: positions [0, len + Tc) expanded to bf16 first
-          if (want(STAGE_ATTN)) Q2_TRY(launch_kv_expand_fp8(static_cast<uint16_t*>(m->kexp), static_cast<uint16_t*>(m->vexp), c.max_seq, f, B,
-                                      c.nkv, m->len + Tc, s));
+          // prefill kernel: positions [0, len + Tc) expanded to contiguous bf16 first
+          if (want(STAGE_ATTN))
+            Q2_TRY(launch_kv_expand(static_cast<uint16_t*>(m->kexp), static_cast<uint16_t*>(m->vexp), c.max_seq,
+                                    cache_layout(m, l), B, m->len + Tc, s));
           a.k = m->kexp;
           a.v = m->vexp;
           a.k_hs = a.v_hs = int64_t(c.max_seq) * d;
@@ -421,7 +477,7 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s, in
   if (only_stage >= 0) return Q2_OK;
   m->xcur = cur;
   if (!advance) return Q2_OK;
-  hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(1), 0, s, m->d_len, Tc);
+  hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(64), 0, s, m->d_len, Tc, const_cast<int*>(call_lens(m)), B);
   return check_launch("advance_len");
 }
 
@@ -452,8 +508,9 @@ q2_status run_head(q2_model* m, int B, int Tc, int pending, float* logits, int64
   a.epi.ldo = ld_logits;
   a.epi.keys = m->keys;
   Q2_TRY(gemm(m, a, s));
-  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1024), 0, s, m->keys, m->ids_buf, m->hist,
-                     static_cast<int64_t>(c.max_seq) + 1, m->d_len, pending, next, next_stride, B);
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1024), 0, s, m->keys, m->ids_buf + m->slot0,
+                     m->hist + static_cast<int64_t>(m->slot0) * (c.max_seq + 1), static_cast<int64_t>(c.max_seq) + 1,
+                     m->d_len, pending, next, next_stride, B, const_cast<int*>(call_lens(m)));
   return check_launch("finalize");
 }
 
@@ -637,7 +694,7 @@ q2_status find_slot(q2_model* m, const std::string& name, int layer, WeightSlot*
 static q2_status setup_persistent(q2_model* m) {
   const q2_config& c = m->cfg;
   if (c.dtype != Q2_BF16 || c.dh != 128 || c.max_batch > MK_MAX_BATCH || c.hidden % 16 != 0 ||
-      c.inter % 16 != 0 || m->fp8)
+      c.inter % 16 != 0 || m->fp8 || m->page)
     return Q2_OK;
   // the norm prologue spreads a row over 8 / B waves (one wave per row from
   // batch 8 on), each lane holding at most MK_NORM_CHUNKS 16-byte chunks
@@ -737,6 +794,97 @@ static q2_status persistent_step(q2_model* m, int B, bool want_logits, hipStream
   return Q2_OK;
 }
 
+// ------------------------------------------------------------------ paged cache bookkeeping
+
+// Queue one table entry; flush 64 at a time (and at the end) as a kernel on s.
+static q2_status table_flush(q2_model* m, TableEdits& e, hipStream_t s, int slot_len = -1, int len_val = 0) {
+  if (e.n == 0 && slot_len < 0) return Q2_OK;
+  hipLaunchKernelGGL(table_edit_kernel, dim3(1), dim3(64), 0, s, m->d_table, static_cast<int64_t>(m->pages_per_seq),
+                     e, m->d_lens, slot_len, len_val);
+  e.n = 0;
+  return check_launch("table_edit");
+}
+
+static q2_status table_set(q2_model* m, TableEdits& e, int slot, int idx, int page, hipStream_t s) {
+  m->h_table[static_cast<size_t>(slot) * m->pages_per_seq + idx] = page;
+  e.slot[e.n] = slot;
+  e.idx[e.n] = idx;
+  e.page[e.n] = page;
+  if (++e.n == 64) return table_flush(m, e, s);
+  return Q2_OK;
+}
+
+// Pages for positions [h_lens[b], h_lens[b] + T) of slots slot0 .. slot0 + B - 1
+// (all or nothing: on failure every page taken here goes back and nothing
+// is launched).
+static q2_status paged_reserve(q2_model* m, int slot0, int B, int T, hipStream_t s) {
+  const int P = m->page;
+  std::vector<std::pair<int, int>> taken;  // (slot, page index)
+  for (int b = slot0; b < slot0 + B; ++b) {
+    const int len = m->h_lens[b];
+    Q2_CHECK(static_cast<int64_t>(len) + T <= m->cfg.max_seq, Q2_ESTATE,
+             "sequence %d: %d cached + %d new positions exceed max_seq %d", b, len, T, m->cfg.max_seq);
+    for (int p = len / P; p < cdiv(len + T, P); ++p) {
+      int& e = m->h_table[static_cast<size_t>(b) * m->pages_per_seq + p];
+      if (e >= 0) continue;
+      if (m->free_pages.empty()) {
+        for (auto& t : taken) {
+          int& r = m->h_table[static_cast<size_t>(t.first) * m->pages_per_seq + t.second];
+          m->free_pages.push_back(r);
+          r = -1;
+        }
+        return fail(Q2_ESTATE, "KV cache out of pages (%d pages of %d positions)", m->pages_total, P);
+      }
+      e = m->free_pages.back();
+      m->free_pages.pop_back();
+      taken.emplace_back(b, p);
+    }
+  }
+  TableEdits ed{};
+  for (auto& t : taken)
+    Q2_TRY(table_set(m, ed, t.first, t.second, m->h_table[static_cast<size_t>(t.first) * m->pages_per_seq + t.second],
+                     s));
+  return table_flush(m, ed, s);
+}
+
+// Give slot's pages back and set its length to 0 (host and device).
+static q2_status paged_release(q2_model* m, int slot, hipStream_t s) {
+  TableEdits ed{};
+  for (int p = 0; p < m->pages_per_seq; ++p) {
+    int& e = m->h_table[static_cast<size_t>(slot) * m->pages_per_seq + p];
+    if (e < 0) continue;
+    m->free_pages.push_back(e);
+    Q2_TRY(table_set(m, ed, slot, p, -1, s));
+  }
+  m->h_lens[slot] = 0;
+  return table_flush(m, ed, s, slot, 0);
+}
+
+// Before a call on slots slot0 .. slot0 + B - 1 that adds T positions each:
+// equal lengths when `uniform`, at least `min_len` cached, then the pages.
+static q2_status paged_begin(q2_model* m, int slot0, int B, int T, bool uniform, int min_len, hipStream_t s) {
+  Q2_CHECK(slot0 >= 0 && B >= 1 && slot0 + B <= m->cfg.max_batch, Q2_ESHAPE, "slots %d .. %d not in [0, %d)", slot0,
+           slot0 + B - 1, m->cfg.max_batch);
+  for (int b = slot0; b < slot0 + B; ++b) {
+    Q2_CHECK(m->h_lens[b] >= min_len, Q2_ESTATE, "sequence %d has %d cached positions (needs %d)", b, m->h_lens[b],
+             min_len);
+    Q2_CHECK(!uniform || m->h_lens[b] == m->h_lens[slot0], Q2_ESTATE,
+             "sequences %d and %d have different lengths: prefill them one at a time (q2_model_seq_prefill)", slot0, b);
+  }
+  Q2_TRY(paged_reserve(m, slot0, B, T, s));
+  m->slot0 = slot0;
+  m->len = m->h_lens[slot0];
+  m->len_dirty = true;
+  return sync_len(m, s);
+}
+
+static void paged_end(q2_model* m, int slot0, int B, int T) {
+  for (int b = slot0; b < slot0 + B; ++b) m->h_lens[b] += T;
+  m->slot0 = 0;
+  m->len = m->h_lens[0];
+  m->len_dirty = true;
+}
+
 // ==================================================================== C ABI
 
 extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_model** out) {
@@ -755,6 +903,10 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
   Q2_CHECK(c.kv_fp8 == 0 || c.kv_fp8 == 1, Q2_EINVAL, "kv_fp8 must be 0 or 1");
   Q2_CHECK(!c.kv_fp8 || c.dtype == Q2_BF16, Q2_EDTYPE, "the FP8 KV cache needs a bf16 model");
   Q2_CHECK(!c.kv_fp8 || c.nh / c.nkv <= 16, Q2_ESHAPE, "the FP8 KV cache needs at most 16 query heads per KV head");
+  Q2_CHECK(c.page_size >= 0 && c.page_size % 64 == 0 && c.kv_pages >= 0, Q2_EINVAL,
+           "page_size must be a non-negative multiple of 64 and kv_pages non-negative");
+  Q2_CHECK(c.page_size == 0 || (c.dtype == Q2_BF16 && c.nh / c.nkv <= 16), Q2_EDTYPE,
+           "the paged KV cache needs a bf16 model with at most 16 query heads per KV head");
   if (c.dtype == Q2_BF16) {
     Q2_CHECK(c.dh == 128, Q2_ESHAPE, "bf16 model needs head_dim 128");
     Q2_CHECK(c.hidden % 32 == 0 && c.inter % 32 == 0, Q2_ESHAPE, "bf16 model needs hidden and inter multiples of 32");
@@ -772,6 +924,11 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
   m->device = device;
   m->esize = c.dtype == Q2_BF16 ? 2 : 4;
   m->fp8 = c.kv_fp8 != 0;
+  m->page = c.page_size;
+  if (m->page) {
+    m->pages_per_seq = cdiv(c.max_seq, m->page);
+    m->pages_total = c.kv_pages ? c.kv_pages : c.max_batch * m->pages_per_seq;
+  }
   m->qkv_out = (c.nh + 2 * c.nkv) * c.dh;
   const size_t es = m->esize;
   const size_t H = c.hidden, I = c.inter, V = c.vocab, qd = size_t(c.nh) * c.dh;
@@ -797,12 +954,12 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
   }
   m->wbytes = off;
 
-  // KV cache
+  // KV cache: [L][Bmax][nkv][S][d], or paged [L][pages][nkv][page][d]
   m->kv_hstride = int64_t(c.max_seq) * c.dh;
   m->kv_bstride = m->kv_hstride * c.nkv;
-  m->kv_lstride = m->kv_bstride * c.max_batch;
+  m->kv_lstride = m->page ? int64_t(m->pages_total) * c.nkv * m->page * c.dh : m->kv_bstride * c.max_batch;
   const size_t kv_one = size_t(m->kv_lstride) * c.nlayer * (m->fp8 ? 1 : es);
-  m->ks_lstride = int64_t(c.max_batch) * c.nkv * c.max_seq;
+  m->ks_lstride = m->kv_lstride / c.dh;
   const size_t ks_one = m->fp8 ? size_t(m->ks_lstride) * c.nlayer * sizeof(float) : 0;
   m->kvbytes = 2 * align256(kv_one) + 2 * align256(ks_one);
 
@@ -848,9 +1005,12 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
     }
   m->ascratch_bytes = as;
   const size_t a_as = take(as);
-  const size_t stage_b = m->fp8 ? mt * c.nkv * c.dh * es : 0;
-  const size_t exp_b = m->fp8 ? size_t(c.max_batch) * c.nkv * c.max_seq * c.dh * es : 0;
+  const bool staged = m->fp8 || m->page > 0;
+  const size_t stage_b = staged ? mt * c.nkv * c.dh * es : 0;
+  const size_t exp_b = staged ? size_t(c.max_batch) * c.nkv * c.max_seq * c.dh * es : 0;
   const size_t a_ks = take(stage_b), a_vs = take(stage_b), a_ke = take(exp_b), a_ve = take(exp_b);
+  const size_t tab_n = m->page ? size_t(c.max_batch) * m->pages_per_seq : 0;
+  const size_t a_tab = take(tab_n * sizeof(int)), a_lens = take(m->page ? size_t(c.max_batch) * sizeof(int) : 0);
   m->abytes = off;
 
   auto cleanup = [&](q2_status st) {
@@ -880,10 +1040,22 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
   if (m->fp8) {
     m->ks = reinterpret_cast<float*>(m->kvmem + 2 * align256(kv_one));
     m->vs = reinterpret_cast<float*>(m->kvmem + 2 * align256(kv_one) + align256(ks_one));
+  }
+  if (staged) {
     m->kstage = m->amem + a_ks;
     m->vstage = m->amem + a_vs;
     m->kexp = m->amem + a_ke;
     m->vexp = m->amem + a_ve;
+  }
+  if (m->page) {
+    m->d_table = reinterpret_cast<int*>(m->amem + a_tab);
+    m->d_lens = reinterpret_cast<int*>(m->amem + a_lens);
+    if (hipMemset(m->d_table, 0xFF, tab_n * sizeof(int)) != hipSuccess)  // every entry -1: no page
+      return cleanup(fail(Q2_EHIP, "hipMemset failed"));
+    m->h_table.assign(tab_n, -1);
+    m->h_lens.assign(c.max_batch, 0);
+    m->free_pages.resize(m->pages_total);
+    for (int i = 0; i < m->pages_total; ++i) m->free_pages[i] = m->pages_total - 1 - i;
   }
   m->rope = reinterpret_cast<float2*>(m->amem + a_rope);
   m->x = m->amem + a_x;
@@ -948,18 +1120,73 @@ extern "C" q2_status q2_model_prefill(q2_model* m, const q2_tensor* ids, const q
   int64_t bs = 0, ts = 0, ns = 0;
   Q2_TRY(check_ids_2d(ids, &B, &Tn, &bs, &ts));
   Q2_CHECK(Tn >= 1, Q2_ESHAPE, "prefill needs at least one token");
-  Q2_TRY(check_batch(m, B, Tn));
+  if (!m->page) Q2_TRY(check_batch(m, B, Tn));
   Q2_TRY(check_next(next, B, &ns));
   Rows lg{};
   Q2_TRY(check_logits(m, logits, B, &lg));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  Q2_TRY(sync_len(m, s));
+  if (m->page)
+    Q2_TRY(paged_begin(m, 0, B, Tn, true, 0, s));
+  else
+    Q2_TRY(sync_len(m, s));
   m->cur_batch = B;
   const int64_t* ip = static_cast<const int64_t*>(ids->data);
   int64_t* np = next ? static_cast<int64_t*>(next->data) : nullptr;
   float* lp = logits ? reinterpret_cast<float*>(lg.data) : nullptr;
-  return m->cfg.dtype == Q2_BF16 ? prefill_impl<uint16_t>(m, ip, bs, ts, B, Tn, lp, lg.ld, np, ns, s)
-                                 : prefill_impl<float>(m, ip, bs, ts, B, Tn, lp, lg.ld, np, ns, s);
+  const q2_status st = m->cfg.dtype == Q2_BF16 ? prefill_impl<uint16_t>(m, ip, bs, ts, B, Tn, lp, lg.ld, np, ns, s)
+                                               : prefill_impl<float>(m, ip, bs, ts, B, Tn, lp, lg.ld, np, ns, s);
+  if (m->page) paged_end(m, 0, B, Tn);
+  return st;
+}
+
+extern "C" q2_status q2_model_seq_prefill(q2_model* m, int32_t slot, const q2_tensor* ids, const q2_tensor* next,
+                                          const q2_tensor* logits, void* stream) {
+  clear_error();
+  Q2_CHECK(m, Q2_EINVAL, "null model");
+  Q2_CHECK(m->page > 0, Q2_ESTATE, "q2_model_seq_prefill needs a paged KV cache (page_size > 0)");
+  Q2_TRY(check_desc(ids, "ids"));
+  Q2_CHECK(ids->dtype == Q2_I64, Q2_EDTYPE, "ids must be int64");
+  Q2_CHECK(ids->ndim == 1, Q2_ESHAPE, "ids must be [T]");
+  const int Tn = static_cast<int>(ids->shape[0]);
+  Q2_CHECK(Tn >= 1, Q2_ESHAPE, "prefill needs at least one token");
+  int64_t ns = 0;
+  Q2_TRY(check_next(next, 1, &ns));
+  Rows lg{};
+  Q2_TRY(check_logits(m, logits, 1, &lg));
+  Q2_CHECK(slot >= 0 && slot < m->cfg.max_batch, Q2_ESHAPE, "slot %d not in [0, %d)", slot, m->cfg.max_batch);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Q2_TRY(paged_begin(m, slot, 1, Tn, true, 0, s));
+  const int64_t* ip = static_cast<const int64_t*>(ids->data);
+  int64_t* np = next ? static_cast<int64_t*>(next->data) : nullptr;
+  float* lp = logits ? reinterpret_cast<float*>(lg.data) : nullptr;
+  const q2_status st = prefill_impl<uint16_t>(m, ip, 0, ids->stride[0], 1, Tn, lp, lg.ld, np, ns, s);
+  paged_end(m, slot, 1, Tn);
+  m->cur_batch = std::max(m->cur_batch, static_cast<int>(slot) + 1);
+  return st;
+}
+
+extern "C" q2_status q2_model_seq_release(q2_model* m, int32_t slot, void* stream) {
+  clear_error();
+  Q2_CHECK(m, Q2_EINVAL, "null model");
+  Q2_CHECK(m->page > 0, Q2_ESTATE, "q2_model_seq_release needs a paged KV cache (page_size > 0)");
+  Q2_CHECK(slot >= 0 && slot < m->cfg.max_batch, Q2_ESHAPE, "slot %d not in [0, %d)", slot, m->cfg.max_batch);
+  return paged_release(m, slot, static_cast<hipStream_t>(stream));
+}
+
+extern "C" q2_status q2_model_seq_length(const q2_model* m, int32_t slot, int32_t* len) {
+  clear_error();
+  Q2_CHECK(m && len, Q2_EINVAL, "null argument");
+  Q2_CHECK(slot >= 0 && slot < m->cfg.max_batch, Q2_ESHAPE, "slot %d not in [0, %d)", slot, m->cfg.max_batch);
+  *len = m->page > 0 ? m->h_lens[slot] : m->len;
+  return Q2_OK;
+}
+
+extern "C" q2_status q2_model_free_pages(const q2_model* m, int32_t* pages) {
+  clear_error();
+  Q2_CHECK(m && pages, Q2_EINVAL, "null argument");
+  Q2_CHECK(m->page > 0, Q2_ESTATE, "the KV cache is not paged");
+  *pages = static_cast<int32_t>(m->free_pages.size());
+  return Q2_OK;
 }
 
 extern "C" q2_status q2_model_prefill_embeds(q2_model* m, const q2_tensor* embeds, const q2_tensor* next,
@@ -1012,16 +1239,19 @@ extern "C" q2_status q2_model_decode(q2_model* m, const q2_tensor* ids, const q2
   Q2_CHECK(ids->dtype == Q2_I64, Q2_EDTYPE, "ids must be int64");
   Q2_CHECK(ids->ndim == 1 || (ids->ndim == 2 && ids->shape[1] == 1), Q2_ESHAPE, "ids must be [B] or [B, 1]");
   const int B = static_cast<int>(ids->shape[0]);
-  Q2_TRY(check_batch(m, B, 1));
+  if (!m->page) Q2_TRY(check_batch(m, B, 1));
   int64_t ns = 0;
   Q2_TRY(check_next(next, B, &ns));
   Rows lg{};
   Q2_TRY(check_logits(m, logits, B, &lg));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  Q2_TRY(sync_len(m, s));
   const bool pers = use_persistent(m, B);
   hipGraphExec_t g = nullptr;
   if (!pers) Q2_TRY(get_graph(m, B, logits != nullptr, &g));
+  if (m->page)
+    Q2_TRY(paged_begin(m, 0, B, 1, false, 1, s));
+  else
+    Q2_TRY(sync_len(m, s));
   m->cur_batch = B;
   hipLaunchKernelGGL(copy_ids_kernel, dim3(1), dim3(64), 0, s, m->ids_buf, int64_t(1),
                      static_cast<const int64_t*>(ids->data), ids->stride[0], B);
@@ -1030,7 +1260,10 @@ extern "C" q2_status q2_model_decode(q2_model* m, const q2_tensor* ids, const q2
     Q2_TRY(persistent_step(m, B, logits != nullptr, s));
   else
     Q2_HIP(hipGraphLaunch(g, s));
-  m->len += 1;
+  if (m->page)
+    paged_end(m, 0, B, 1);
+  else
+    m->len += 1;
   m->last_rows = B;
   if (next) {
     hipLaunchKernelGGL(copy_ids_kernel, dim3(1), dim3(64), 0, s, static_cast<int64_t*>(next->data), ns, m->ids_buf,
@@ -1051,6 +1284,7 @@ static q2_status run_steps(q2_model* m, int steps, const q2_tensor* out_ids, int
   const bool pers = use_persistent(m, B);
   hipGraphExec_t g = nullptr;
   if (steps > 0 && !pers) Q2_TRY(get_graph(m, B, false, &g));
+  if (m->page && steps > 0) Q2_TRY(paged_begin(m, 0, B, steps, false, 1, s));
   const int start = m->len;  // the token produced last sits at position `start`
   for (int i = 0; i < steps; ++i) {
     if (pers)
@@ -1058,13 +1292,17 @@ static q2_status run_steps(q2_model* m, int steps, const q2_tensor* out_ids, int
     else
       Q2_HIP(hipGraphLaunch(g, s));
   }
-  m->len += steps;
+  if (m->page)
+    paged_end(m, 0, B, steps);
+  else
+    m->len += steps;
   if (steps > 0) m->last_rows = B;
   if (out_ids) {
     const int n = static_cast<int>(out_ids->shape[1]);
     hipLaunchKernelGGL(copy_hist_kernel, dim3(cdiv(int64_t(n) * B, 256)), dim3(256), 0, s,
                        static_cast<int64_t*>(out_ids->data), out_ids->stride[0], m->hist,
-                       static_cast<int64_t>(m->cfg.max_seq) + 1, start + 1 - first_col, n, B);
+                       static_cast<int64_t>(m->cfg.max_seq) + 1, start + 1 - first_col, n, B,
+                       m->page > 0 ? m->d_lens : nullptr, steps - 1 + first_col);
     Q2_TRY(check_launch("copy_hist"));
   }
   return Q2_OK;
@@ -1088,18 +1326,28 @@ extern "C" q2_status q2_model_generate(q2_model* m, const q2_tensor* prompt, int
   int64_t bs = 0, ts = 0;
   Q2_TRY(check_ids_2d(prompt, &B, &Tn, &bs, &ts));
   Q2_CHECK(Tn >= 1, Q2_ESHAPE, "prompt needs at least one token");
-  Q2_TRY(check_batch(m, B, Tn + steps));
+  if (!m->page) Q2_TRY(check_batch(m, B, Tn + steps));
   Q2_TRY(check_out_ids(out_ids, B, steps + 1));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  Q2_TRY(sync_len(m, s));
   if (steps > 0 && !use_persistent(m, B)) {
     hipGraphExec_t g = nullptr;
     Q2_TRY(get_graph(m, B, false, &g));  // capture before any state changes
   }
+  if (m->page) {
+    for (int b = 0; b < B; ++b)
+      Q2_CHECK(static_cast<int64_t>(m->h_lens[b]) + Tn + steps <= m->cfg.max_seq, Q2_ESTATE,
+               "sequence %d: capacity exceeded", b);
+    Q2_TRY(paged_begin(m, 0, B, Tn, true, 0, s));
+  } else {
+    Q2_TRY(sync_len(m, s));
+  }
   m->cur_batch = B;
   const int64_t* ip = static_cast<const int64_t*>(prompt->data);
-  Q2_TRY(m->cfg.dtype == Q2_BF16 ? prefill_impl<uint16_t>(m, ip, bs, ts, B, Tn, nullptr, 0, nullptr, 0, s)
-                                 : prefill_impl<float>(m, ip, bs, ts, B, Tn, nullptr, 0, nullptr, 0, s));
+  const q2_status st = m->cfg.dtype == Q2_BF16
+                           ? prefill_impl<uint16_t>(m, ip, bs, ts, B, Tn, nullptr, 0, nullptr, 0, s)
+                           : prefill_impl<float>(m, ip, bs, ts, B, Tn, nullptr, 0, nullptr, 0, s);
+  if (m->page) paged_end(m, 0, B, Tn);
+  Q2_TRY(st);
   // out column 0 is the prefill's token (position len), then one per step
   return run_steps(m, steps, out_ids, 1, s);
 }
@@ -1109,10 +1357,10 @@ extern "C" q2_status q2_model_continue(q2_model* m, int32_t steps, const q2_tens
   Q2_CHECK(m, Q2_EINVAL, "null model");
   Q2_CHECK(steps >= 0, Q2_EINVAL, "steps must be >= 0");
   Q2_CHECK(m->len >= 1 && m->cur_batch >= 1, Q2_ESTATE, "continue needs a prefill first");
-  Q2_TRY(check_batch(m, m->cur_batch, steps));
+  if (!m->page) Q2_TRY(check_batch(m, m->cur_batch, steps));
   if (out_ids) Q2_TRY(check_out_ids(out_ids, m->cur_batch, steps));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  Q2_TRY(sync_len(m, s));
+  if (!m->page) Q2_TRY(sync_len(m, s));
   return run_steps(m, steps, out_ids, 0, s);
 }
 
@@ -1120,6 +1368,7 @@ extern "C" q2_status q2_model_kv_view(q2_model* m, int32_t layer, q2_tensor* k, 
   clear_error();
   Q2_CHECK(m && k && v, Q2_EINVAL, "null argument");
   Q2_CHECK(layer >= 0 && layer < m->cfg.nlayer, Q2_EINVAL, "layer out of range");
+  Q2_CHECK(m->page == 0, Q2_ESTATE, "a paged KV cache has no per-sequence view");
   for (int i = 0; i < 2; ++i) {
     q2_tensor* t = i ? v : k;
     memset(t, 0, sizeof *t);
@@ -1147,9 +1396,21 @@ extern "C" q2_status q2_model_replay_stage(q2_model* m, int32_t stage, int32_t b
   Q2_CHECK(tokens >= 1 && reps >= 0, Q2_ESHAPE, "tokens must be positive and reps non-negative");
   Q2_CHECK(int64_t(batch) * tokens <= m->max_tok, Q2_ESHAPE, "%d x %d rows exceed the activation arena (%d)", batch,
            tokens, m->max_tok);
-  Q2_CHECK(static_cast<int64_t>(m->len) + tokens <= m->cfg.max_seq, Q2_ESTATE,
-           "replay at length %d + %d tokens exceeds the cache (%d)", m->len, tokens, m->cfg.max_seq);
+  const int len_now = m->page > 0 ? m->h_lens[0] : m->len;
+  Q2_CHECK(static_cast<int64_t>(len_now) + tokens <= m->cfg.max_seq, Q2_ESTATE,
+           "replay at length %d + %d tokens exceeds the cache (%d)", len_now, tokens, m->cfg.max_seq);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m->page > 0) {
+    // the replayed positions len .. len + tokens - 1 of every replayed
+    // sequence need their pages (the products write and read them); the
+    // lengths themselves do not move
+    for (int b = 0; b < batch; ++b)
+      Q2_CHECK(m->h_lens[b] == m->h_lens[0], Q2_ESTATE, "replay needs sequences of equal length");
+    Q2_TRY(paged_reserve(m, 0, batch, tokens, s));
+    m->slot0 = 0;
+    m->len = m->h_lens[0];
+    m->len_dirty = true;
+  }
   Q2_TRY(sync_len(m, s));
   for (int i = 0; i < reps; ++i) {
     const int l = i % m->cfg.nlayer;
@@ -1162,9 +1423,9 @@ extern "C" q2_status q2_model_replay_stage(q2_model* m, int32_t stage, int32_t b
 extern "C" q2_status q2_model_kv_scale_view(q2_model* m, int32_t layer, q2_tensor* ks, q2_tensor* vs) {
   clear_error();
   Q2_CHECK(m && ks && vs, Q2_EINVAL, "null argument");
-  Q2_CHECK(m->fp8, Q2_ESTATE, "the model's KV cache is not FP8");
+  Q2_CHECK(m->fp8 && m->page == 0, Q2_ESTATE, "the model's KV cache is not a contiguous FP8 cache");
   Q2_CHECK(layer >= 0 && layer < m->cfg.nlayer, Q2_EINVAL, "layer out of range");
-  const KvFp8 f = fp8_layer(m, layer);
+  const KvLayout f = cache_layout(m, layer);
   for (int i = 0; i < 2; ++i) {
     q2_tensor* t = i ? vs : ks;
     memset(t, 0, sizeof *t);
@@ -1174,9 +1435,9 @@ extern "C" q2_status q2_model_kv_scale_view(q2_model* m, int32_t layer, q2_tenso
     t->shape[0] = m->cfg.max_batch;
     t->shape[1] = m->cfg.max_seq;
     t->shape[2] = m->cfg.nkv;
-    t->stride[0] = f.s_bs;
+    t->stride[0] = f.bs;
     t->stride[1] = 1;
-    t->stride[2] = f.s_hs;
+    t->stride[2] = f.hs;
   }
   return Q2_OK;
 }
@@ -1184,13 +1445,15 @@ extern "C" q2_status q2_model_kv_scale_view(q2_model* m, int32_t layer, q2_tenso
 extern "C" q2_status q2_model_length(const q2_model* m, int32_t* len) {
   clear_error();
   Q2_CHECK(m && len, Q2_EINVAL, "null argument");
-  *len = m->len;
+  *len = m->page > 0 ? m->h_lens[0] : m->len;
   return Q2_OK;
 }
 
 extern "C" q2_status q2_model_reset(q2_model* m) {
   clear_error();
   Q2_CHECK(m, Q2_EINVAL, "null model");
+  if (m->page > 0)
+    for (int b = 0; b < m->cfg.max_batch; ++b) Q2_TRY(paged_release(m, b, nullptr));
   m->len = 0;
   m->cur_batch = 0;
   m->len_dirty = true;

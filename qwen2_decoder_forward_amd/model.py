@@ -8,12 +8,15 @@ from . import _lib
 from ._lib import Q2Config, Q2_BF16, Q2_F32
 
 
-def make_config(shape, max_seq: int, max_batch: int, kv_fp8: bool = False) -> Q2Config:
+def make_config(shape, max_seq: int, max_batch: int, kv_fp8: bool = False, page_size: int = 0,
+                kv_pages: int = 0) -> Q2Config:
     """q2_config from any object with the Qwen2 shape attributes
     (dtype "f32"/"bf16", nlayer, hidden, nh, nkv, dh, inter, vocab, eps, theta);
-    ``kv_fp8`` selects the FP8 KV cache."""
+    ``kv_fp8`` selects the FP8 KV cache, ``page_size`` > 0 the paged cache
+    (``kv_pages`` pages, 0 = room for every sequence at max_seq)."""
     c = Q2Config()
     c.kv_fp8 = 1 if kv_fp8 else 0
+    c.page_size, c.kv_pages = page_size, kv_pages
     c.dtype = Q2_BF16 if shape.dtype == "bf16" else Q2_F32
     c.nlayer, c.hidden, c.nh, c.nkv = shape.nlayer, shape.hidden, shape.nh, shape.nkv
     c.dh, c.inter, c.vocab = shape.dh, shape.inter, shape.vocab
@@ -26,14 +29,16 @@ class Model:
     """Owns one q2_model.  Weights are loaded from device tensors with
     `load_weight(name, layer, tensor)`; all calls run on the current stream."""
 
-    def __init__(self, shape, max_seq: int, max_batch: int, device: int = 0, kv_fp8: bool = False):
+    def __init__(self, shape, max_seq: int, max_batch: int, device: int = 0, kv_fp8: bool = False,
+                 page_size: int = 0, kv_pages: int = 0):
         self.shape = shape
         self.max_seq = max_seq
         self.max_batch = max_batch
         self.device = device
         self.kv_fp8 = kv_fp8
+        self.page_size = page_size
         self.torch_dtype = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
-        self.handle = _lib.q2_model_create(make_config(shape, max_seq, max_batch, kv_fp8), device)
+        self.handle = _lib.q2_model_create(make_config(shape, max_seq, max_batch, kv_fp8, page_size, kv_pages), device)
 
     def close(self):
         if self.handle:
@@ -92,6 +97,23 @@ class Model:
         _lib.q2_model_continue(self.handle, steps, out)
         return out
 
+    def seq_prefill(self, slot: int, ids, logits: bool = False):
+        """Prefill the token ids [T] of sequence `slot` (paged cache), after
+        whatever that slot already holds; returns its next token (and logits)."""
+        nxt = torch.empty(1, dtype=torch.int64, device=ids.device)
+        lg = torch.empty(1, self.shape.vocab, dtype=torch.float32, device=ids.device) if logits else None
+        _lib.q2_model_seq_prefill(self.handle, slot, ids, nxt, lg)
+        return (nxt, lg) if logits else nxt
+
+    def seq_release(self, slot: int):
+        _lib.q2_model_seq_release(self.handle, slot)
+
+    def seq_length(self, slot: int) -> int:
+        return _lib.q2_model_seq_length(self.handle, slot)
+
+    def free_pages(self) -> int:
+        return _lib.q2_model_free_pages(self.handle)
+
     def kv_view(self, layer: int):
         """q2_tensor descriptors (k, v) of layer `layer`'s cache, [max_batch, max_seq, nkv, dh]."""
         return _lib.q2_model_kv_view(self.handle, layer)
@@ -125,12 +147,13 @@ def weight_tensor(arr, device: int = 0) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(dev)
 
 
-def load_model(shape, weights, max_seq: int, max_batch: int, device: int = 0, kv_fp8: bool = False) -> Model:
+def load_model(shape, weights, max_seq: int, max_batch: int, device: int = 0, kv_fp8: bool = False,
+               page_size: int = 0, kv_pages: int = 0) -> Model:
     """Create a model and copy every weight of ``weights`` ({(name, layer):
     host array}, Hugging Face Qwen2 names, layer -1 for the global tensors)
     into it, one tensor at a time (each upload is freed once the library has
     packed it)."""
-    m = Model(shape, max_seq, max_batch, device, kv_fp8)
+    m = Model(shape, max_seq, max_batch, device, kv_fp8, page_size, kv_pages)
     for (name, layer), arr in weights.items():
         t = weight_tensor(arr, device)
         m.load_weight(name, layer, t)
