@@ -12,12 +12,15 @@ the library launches on); prefill tokens/s is reported beside it.  Weights
 and prompts are resident in HBM before the timed region.
 
 Also reported:
-  roofline      the dominant kernel of the step, launched through the C ABI at
-                its in-step shape and timed with HIP events on the same stream
-                (bandwidth-bound kernels cycle through operands several times
-                the last-level cache); `traffic` is its HBM bytes per launch
-                from profiler counters (profiles/traffic.json) while the
-                kernel source is unchanged since they were taken.
+  roofline      the dominant kernel of the step, relaunched as the step
+                launches it (q2_model_replay_stage: the forward's kernels and
+                arguments on the model's own weights and buffers, layers
+                cycled so that every launch streams from HBM) and timed with
+                HIP events on the launch stream: B and E the gate/up GEMV, C
+                the prefill gate/up GEMM, D the decode attention kernel;
+                `traffic` is its HBM bytes per launch from profiler counters
+                (profiles/traffic.json) while the kernel source is unchanged
+                since they were taken.
   step_roofline algorithmic bytes (or flops) of a whole decode (prefill) step
                 against the HBM (MFMA) peak.
   cpu_baseline  the oracle (plain NumPy) timed on this host on a bounded
@@ -110,7 +113,8 @@ def time_launches(fn, reps, stream):
 
 CALIB_COPY_BYTES = 512 << 20   # plain device copy, the reference for the HBM byte counters
 
-STAGE_NAMES = {0: "QKV", 1: "attention", 2: "o_proj", 3: "gate/up", 4: "down"}
+STAGE_NAMES = {0: "QKV", 1: "attention", 2: "o_proj", 3: "gate/up", 4: "down",
+               5: "attention (split-KV kernel without its merge)"}
 
 
 def in_step_kernel(model, wl, prompt, reps, kv_fp8):
@@ -139,7 +143,7 @@ def in_step_kernel(model, wl, prompt, reps, kv_fp8):
     else:
         nxt = torch.empty(B, dtype=torch.int64, device=dev)
         q2.q2_model_prefill(model.handle, prompt, nxt)        # decode products at length = prompt
-        stage = q2.STAGE_ATTN if wl.key == "D" else q2.STAGE_GATE_UP
+        stage = q2.STAGE_ATTN_CORE if wl.key == "D" else q2.STAGE_GATE_UP
         tokens = 1
 
     def launch(n):

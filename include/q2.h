@@ -325,7 +325,10 @@ q2_status q2_model_kv_scale_view(q2_model* m, int32_t layer, q2_tensor* k_scale,
  * product of a forward of `batch` sequences x `tokens` new tokens at the
  * current cached length, for layers 0, 1, ..., nlayer - 1, 0, ... in turn:
  * stage 0 QKV (with its fused norm and cache write), 1 attention, 2 o_proj,
- * 3 gate/up, 4 down.  The kernels and arguments are those the forward (or
+ * 3 gate/up, 4 down, 5 the decode attention kernel alone (its split-KV
+ * partials left unmerged, where stage 1 also launches the merge when the
+ * forward does; for more than one token, as stage 1).
+ * The kernels and arguments are those the forward (or
  * the captured decode step) launches, reading the model's own weights and
  * buffers.  The activations, the residual stream and the cache rows at the
  * replayed positions are left undefined: reset before the next forward.

@@ -314,7 +314,7 @@ def q2_model_free_pages(h) -> int:
     return n.value
 
 
-STAGE_QKV, STAGE_ATTN, STAGE_O, STAGE_GATE_UP, STAGE_DOWN = 0, 1, 2, 3, 4
+STAGE_QKV, STAGE_ATTN, STAGE_O, STAGE_GATE_UP, STAGE_DOWN, STAGE_ATTN_CORE = 0, 1, 2, 3, 4, 5
 
 
 def q2_model_replay_stage(h, stage: int, batch: int, tokens: int, reps: int, stream=None):

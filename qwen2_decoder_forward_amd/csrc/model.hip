@@ -288,7 +288,9 @@ Path path_for(const q2_model* m, int M) {
 // embedded in x.  Positions start at the device length; with `advance` the
 // device length moves on by Tc at the end.
 // Products of a layer, for measurement (q2_model_replay_stage).
-enum Stage : int { STAGE_QKV = 0, STAGE_ATTN = 1, STAGE_O = 2, STAGE_GATE_UP = 3, STAGE_DOWN = 4, STAGE_HEAD = 5 };
+// STAGE_ATTN_CORE: the attention kernel alone, leaving its split-KV partials
+// unmerged (the merge launch, or o_proj's merging prologue, is left out).
+enum Stage : int { STAGE_QKV = 0, STAGE_ATTN = 1, STAGE_O = 2, STAGE_GATE_UP = 3, STAGE_DOWN = 4, STAGE_ATTN_CORE = 5 };
 
 // only_stage >= 0: launch nothing but that stage of layer only_layer (the
 // launch decisions of every other stage are still taken, so the launched
@@ -311,7 +313,10 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s, in
   // (written by the previous residual product's split-K reduction)
   bool h_ready = false;
   for (int l = 0; l < c.nlayer; ++l) {
-    auto want = [&](int st) { return only_stage < 0 || (only_stage == st && only_layer == l); };
+    auto want = [&](int st) {
+      if (only_stage == STAGE_ATTN_CORE && st == STAGE_ATTN) st = STAGE_ATTN_CORE;
+      return only_stage < 0 || (only_stage == st && only_layer == l);
+    };
     const q2_model::Layer& L = m->layers[l];
     const int kv_es = m->fp8 ? 1 : m->esize;
     void* kc = static_cast<char*>(m->kc) + l * m->kv_lstride * kv_es;
@@ -367,7 +372,7 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s, in
     const bool merge_in_o = path.fused_norm && Tc == 1 && nsplit > 1 && B * nsplit <= 16;
     {
       AttnArgs a{};
-      a.leave_partials = merge_in_o;
+      a.leave_partials = merge_in_o || only_stage == STAGE_ATTN_CORE;
       a.q = m->q;
       a.q_bs = static_cast<int64_t>(Tc) * qd;
       a.q_ts = qd;
@@ -1391,7 +1396,7 @@ extern "C" q2_status q2_model_replay_stage(q2_model* m, int32_t stage, int32_t b
                                           void* stream) {
   clear_error();
   Q2_CHECK(m, Q2_EINVAL, "null model");
-  Q2_CHECK(stage >= STAGE_QKV && stage <= STAGE_DOWN, Q2_EINVAL, "stage %d not in [0, 4]", stage);
+  Q2_CHECK(stage >= STAGE_QKV && stage <= STAGE_ATTN_CORE, Q2_EINVAL, "stage %d not in [0, 5]", stage);
   Q2_CHECK(batch >= 1 && batch <= m->cfg.max_batch, Q2_ESHAPE, "batch %d not in [1, %d]", batch, m->cfg.max_batch);
   Q2_CHECK(tokens >= 1 && reps >= 0, Q2_ESHAPE, "tokens must be positive and reps non-negative");
   Q2_CHECK(int64_t(batch) * tokens <= m->max_tok, Q2_ESHAPE, "%d x %d rows exceed the activation arena (%d)", batch,

@@ -337,11 +337,11 @@ def test_replay_stage_then_reset_leaves_forward_unchanged():
     m = build_model(sh, w, 48, 2)
     ids = torch.from_numpy(np.random.default_rng(2).integers(0, sh.vocab, (2, 20))).to(DEV)
     before = m.prefill(ids, logits=True)[1].cpu().numpy()
-    for stage in range(5):
+    for stage in range(6):
         q2.q2_model_replay_stage(m.handle, stage, 2, 1, 2 * sh.nlayer)
         q2.q2_model_replay_stage(m.handle, stage, 2, 20, sh.nlayer)
     with pytest.raises(q2.Q2Error):
-        q2.q2_model_replay_stage(m.handle, 5, 2, 1, 1)
+        q2.q2_model_replay_stage(m.handle, 6, 2, 1, 1)
     torch.cuda.synchronize()
     m.reset()
     after = m.prefill(ids, logits=True)[1].cpu().numpy()
