@@ -31,7 +31,12 @@ namespace q2 {
 namespace {
 
 constexpr int D = 128;
-constexpr int VT_DEC = 20;    // bf16 per V^T LDS row in attn_decode: 16 keys + pad (40 B rows)
+// bf16 per V^T LDS row in attn_decode: 16 keys + pad.  Rows of 9 banks (36
+// bytes), so that the fragment reads (16 consecutive rows) fall in distinct
+// banks; the transposed writes (rows 8 apart) are spread by a rotation of
+// each row's key groups (dec_block).  Rows are 4-byte aligned only, so both
+// go as pairs of 32-bit accesses.
+constexpr int VT_DEC = 18;
 constexpr float NEG_INF = -__builtin_huge_valf();
 
 __device__ __forceinline__ short4_t as_short4(uint2 v) {
@@ -62,9 +67,11 @@ __device__ __forceinline__ uint32_t elem16(const uint4& v, int i) {
 }
 
 // Write four keys' 8-element d-chunks transposed: row (d0 + i) gets the 4 keys
-// at column `col` (4 consecutive bf16 = 8 bytes).
+// at column `col` (4 consecutive bf16 = 8 bytes; ALIGN8: 8-byte aligned, else
+// two 4-byte stores).
 // (v_perm_b32 picks the two 16-bit elements: selector bytes 0-3 address its
 // second operand, 4-7 its first.)
+template <bool ALIGN8>
 __device__ __forceinline__ void store_vt4(uint16_t* base, int row_stride, int d0, int col, const uint4 (&v)[4]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -72,7 +79,13 @@ __device__ __forceinline__ void store_vt4(uint16_t* base, int row_stride, int d0
     uint2 w;
     w.x = __builtin_amdgcn_perm((&v[1].x)[i >> 1], (&v[0].x)[i >> 1], sel);
     w.y = __builtin_amdgcn_perm((&v[3].x)[i >> 1], (&v[2].x)[i >> 1], sel);
-    *reinterpret_cast<uint2*>(base + (d0 + i) * row_stride + col) = w;
+    if constexpr (ALIGN8) {
+      *reinterpret_cast<uint2*>(base + (d0 + i) * row_stride + col) = w;
+    } else {
+      uint32_t* p = reinterpret_cast<uint32_t*>(base + (d0 + i) * row_stride + col);
+      p[0] = w.x;
+      p[1] = w.y;
+    }
   }
 }
 
@@ -110,7 +123,10 @@ __device__ __forceinline__ void dec_block(const uint4 (&kf)[4], const uint4 (&vf
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
     sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kk]), as_bf16x8(qf[kk]), sacc, 0, 0, 0);
-  store_vt4(vt, VT_DEC, 8 * col, 4 * G, vf);
+  // rows d hold their four 4-key groups rotated by (d / 32) % 4 places: the
+  // 16 lanes of one transposed write (rows 8 apart) then cover 16 distinct
+  // bank pairs
+  store_vt4<false>(vt, VT_DEC, 8 * col, 4 * ((G + (col >> 2)) & 3), vf);
 
   float s[4];
 #pragma unroll
@@ -127,23 +143,77 @@ __device__ __forceinline__ void dec_block(const uint4 (&kf)[4], const uint4 (&vf
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     oacc[dt][0] *= alpha; oacc[dt][1] *= alpha; oacc[dt][2] *= alpha; oacc[dt][3] *= alpha;
-    const uint2 vv = *reinterpret_cast<const uint2*>(vt + (16 * dt + col) * VT_DEC + 4 * G);
+    const uint32_t* vp =
+        reinterpret_cast<const uint32_t*>(vt + (16 * dt + col) * VT_DEC + 4 * ((G + (dt >> 1)) & 3));
+    const uint2 vv = make_uint2(vp[0], vp[1]);
     oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_short4(vv), pf, oacc[dt], 0, 0, 0);
   }
   wave_lds_sync();
 }
 
 // KVM_STRIDED: K / V addressed by the strides of AttnArgs.  KVM_BF16 /
-// KVM_FP8: addressed as rows of the model's cache layout (a.cache: contiguous
-// or paged); FP8 rows are E4M3 codes with a scale per key, dequantised to
-// bf16 in registers just before their block's products (the loads in flight
-// stay at half the bytes).  A 16-key block never straddles a page (pages
-// hold a multiple of 64 positions), so one row lookup serves a block.
+// KVM_FP8: addressed as rows of the model's cache layout (a.cache, paged
+// when PAGED); FP8 rows are E4M3 codes with a scale per key, dequantised to
+// bf16 in registers just before their block's products.  A 16-key block
+// never straddles a page (pages hold a multiple of 64 positions), so one
+// row lookup serves a block.
 enum KvMode : int { KVM_STRIDED = 0, KVM_BF16 = 1, KVM_FP8 = 2 };
 
-template <int KVM>
-__global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk, int nsplit,
-                                                          float* __restrict__ part_o, float2* __restrict__ part_ml) {
+// Cache row of key jc (a wave-uniform block start) of sequence b, KV head g.
+template <bool PAGED>
+__device__ __forceinline__ int64_t block_row(const KvLayout& c, int b, int g, int jc) {
+  if constexpr (PAGED) {
+    // one page-table entry per block, the same for the whole wave: read
+    // through the constant address space (the table does not change during
+    // the kernel), so it is a scalar load, which the vector loads in flight
+    // do not have to drain before
+    typedef const __attribute__((address_space(4))) int ConstInt;
+    const int e = __builtin_amdgcn_readfirstlane(b * static_cast<int>(c.tstride) + jc / c.P);
+    const int page = ((ConstInt*)(c.table))[e];
+    return static_cast<int64_t>(max(page, 0)) * c.nkv * c.P + g * c.P + jc % c.P;
+  } else {
+    return b * c.bs + g * c.hs + jc;
+  }
+}
+
+// The key loop keeps three register sets of K / V loads: while one block is
+// multiplied, the next two are in flight.  It runs whole groups of three
+// blocks, then the last one or two, with no exit inside a group: with a
+// single path around the loop the compiler's wait counts stay exact (exits
+// in the middle of an unrolled body merge their pending loads into the
+// loop head and make every iteration wait for more than its own block).
+// The scheduling barriers keep each block's loads issued before the
+// previous block's arithmetic.
+#define Q2_DEC_RING(LOAD, BLOCK, S0, S1, S2)                                                          \
+  {                                                                                                  \
+    const int nblk = j0 < j_end ? (j_end - j0 + 63) >> 6 : 0;                                        \
+    LOAD(S0, j0)                                                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+    LOAD(S1, j0 + 64)                                                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                               \
+      settle(qf[kk]);                                                                                \
+      if (!rvalid) qf[kk] = z;                                                                       \
+    }                                                                                                \
+    int it = 0;                                                                                      \
+    for (; it + 3 <= nblk; it += 3, j0 += 192) {                                                     \
+      LOAD(S2, j0 + 128)                                                                             \
+      __builtin_amdgcn_sched_barrier(0);                                                             \
+      BLOCK(S0, j0)                                                                                  \
+      LOAD(S0, j0 + 192)                                                                             \
+      __builtin_amdgcn_sched_barrier(0);                                                             \
+      BLOCK(S1, j0 + 64)                                                                             \
+      LOAD(S1, j0 + 256)                                                                             \
+      __builtin_amdgcn_sched_barrier(0);                                                             \
+      BLOCK(S2, j0 + 128)                                                                            \
+    }                                                                                                \
+    if (it < nblk) BLOCK(S0, j0)                                                                     \
+    if (it + 1 < nblk) BLOCK(S1, j0 + 64)                                                            \
+  }
+
+template <int KVM, bool PAGED>
+__global__ __launch_bounds__(256, 2) void attn_decode_kernel(AttnArgs a, int chunk, int nsplit,
+                                                             float* __restrict__ part_o, float2* __restrict__ part_ml) {
   // the V^T tiles of the key loop and the merge buffers of the four waves
   // are never live together (a barrier separates them): one LDS region
   constexpr int VT_BYTES = 4 * D * VT_DEC * 2, O_BYTES = 4 * D * 17 * 4;
@@ -161,7 +231,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
   const int S = a.lens ? (a.lens[b] + a.T) : a.d_len ? (*a.d_len + a.T) : a.S;
   const int P = S - a.T;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;
   const int G = lane >> 4;
   const int j_begin = split * chunk;
@@ -173,10 +243,19 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
   const int head = g * group + (rvalid ? col - t * group : 0);
   const int lim = rvalid ? P + t : S - 1;
   const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.q_bs + t * a.q_ts + head * a.q_hs;
+  // loaded for every lane (rows past R read a valid head) and zeroed past R
+  // only after the first key blocks' loads are out, so that no wait for them
+  // comes first.  Fragment kk of lane group G holds d = kd(kk, G) .. + 7; the
+  // K fragments use the same order (any order of d gives the same q . k).
+  // bf16 rows: kd = 32 kk + 8 G, so one load instruction covers 64
+  // contiguous bytes of each of 16 rows.  FP8 rows (128 bytes): kd = 64
+  // (kk / 2) + 16 G + 8 (kk % 2), so a lane's four fragments are two 16-byte
+  // loads and one instruction again covers 64 contiguous bytes of each row.
   uint4 qf[4];
   const uint4 z = {0, 0, 0, 0};
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) qf[kk] = rvalid ? ld16(qp + 32 * kk + 8 * G) : z;
+  for (int kk = 0; kk < 4; ++kk)
+    qf[kk] = ld16(qp + (KVM == KVM_FP8 ? 64 * (kk >> 1) + 16 * G + 8 * (kk & 1) : 32 * kk + 8 * G));
 
   uint16_t* vt = sVt[wave];
 
@@ -186,96 +265,83 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int chunk,
   for (int dt = 0; dt < 8; ++dt) oacc[dt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   int j0 = j_begin + 16 * wave;
-  // keys past the split's end re-read its last key (jl); a block's rows are
-  // looked up at Jc, the block start clamped likewise
+  // Loads are unconditional: keys past the split's end re-read its last key
+  // jl (their scores are masked and their probabilities exactly 0), and a
+  // block's rows are looked up at its start clamped likewise.
   const int jl = max(j_end - 1, 0);
   if constexpr (KVM == KVM_FP8) {
-  // as below, with 8-byte code loads and each key's scale
+  // K codes: two 16-byte loads per lane (the fragment order above); V:
+  // 8-byte code loads; each key's scale
   const uint8_t* kc8 = static_cast<const uint8_t*>(a.cache.kc);
   const uint8_t* vc8 = static_cast<const uint8_t*>(a.cache.vc);
-#define Q2_DEC_LOAD8(KR_, VR_, KS_, VS_, J0_)                                                         \
+  struct Set8 {
+    uint4 kr[2];
+    uint2 vr[4];
+    float ks, vs[4];
+  };
+#define Q2_DEC_LOAD8(S_, J0_)                                                                         \
   {                                                                                                  \
     const int jc_ = min((J0_), jl & ~15);                                                            \
-    const int64_t r0_ = kv_row(a.cache, b, g, jc_) - jc_;                                            \
+    const int64_t r0_ = block_row<PAGED>(a.cache, b, g, jc_) - jc_;                                  \
     const int key_ = max(min((J0_) + col, jl), 0);                                                   \
-    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) KR_[kk] =                                       \
-        *reinterpret_cast<const uint2*>(kc8 + (r0_ + key_) * D + 32 * kk + 8 * G);                   \
-    KS_ = a.cache.ks[r0_ + key_];                                                                    \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h) S_.kr[h] =                                         \
+        *reinterpret_cast<const uint4*>(kc8 + (r0_ + key_) * D + 64 * h + 16 * G);                   \
+    S_.ks = a.cache.ks[r0_ + key_];                                                                  \
     _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) {                                               \
       const int vk_ = max(min((J0_) + 4 * G + s_, jl), 0);                                           \
-      VR_[s_] = *reinterpret_cast<const uint2*>(vc8 + (r0_ + vk_) * D + 8 * col);                    \
-      VS_[s_] = a.cache.vs[r0_ + vk_];                                                               \
+      S_.vr[s_] = *reinterpret_cast<const uint2*>(vc8 + (r0_ + vk_) * D + 8 * col);                  \
+      S_.vs[s_] = a.cache.vs[r0_ + vk_];                                                             \
     }                                                                                                \
   }
-#define Q2_DEC_BLOCK8(KR_, VR_, KS_, VS_, J0_)                                                        \
+#define Q2_DEC_BLOCK8(S_, J0_)                                                                        \
   {                                                                                                  \
     uint4 kf_[4], vf_[4];                                                                            \
-    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) kf_[kk] = e4m3_dequant8(KR_[kk], KS_);          \
-    _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) vf_[s_] = e4m3_dequant8(VR_[s_], VS_[s_]);      \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                                  \
+      kf_[2 * h] = e4m3_dequant8(make_uint2(S_.kr[h].x, S_.kr[h].y), S_.ks);                         \
+      kf_[2 * h + 1] = e4m3_dequant8(make_uint2(S_.kr[h].z, S_.kr[h].w), S_.ks);                     \
+    }                                                                                                \
+    _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) vf_[s_] = e4m3_dequant8(S_.vr[s_], S_.vs[s_]);  \
     dec_block(kf_, vf_, qf, vt, (J0_), j_end, lim, a.scale, col, G, oacc, m_run, l_run);             \
   }
-  uint2 kr0[4], vr0[4], kr1[4], vr1[4];
-  float ks0, vs0[4], ks1, vs1[4];
-  Q2_DEC_LOAD8(kr0, vr0, ks0, vs0, j0)
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) settle(qf[kk]);
-  for (; j0 < j_end; j0 += 128) {
-    Q2_DEC_LOAD8(kr1, vr1, ks1, vs1, j0 + 64)
-    Q2_DEC_BLOCK8(kr0, vr0, ks0, vs0, j0)
-    if (j0 + 64 >= j_end) break;
-    Q2_DEC_LOAD8(kr0, vr0, ks0, vs0, j0 + 128)
-    Q2_DEC_BLOCK8(kr1, vr1, ks1, vs1, j0 + 64)
-  }
+  Set8 s0, s1, s2;
+  Q2_DEC_RING(Q2_DEC_LOAD8, Q2_DEC_BLOCK8, s0, s1, s2)
 #undef Q2_DEC_LOAD8
 #undef Q2_DEC_BLOCK8
   } else {
   // strided: row j of this head at base + j * stride; cache layout: rows of
-  // D elements looked up per block
+  // D elements looked up per block.  K rows j0 + col: 4 x 16 B (d = 32kk +
+  // 8G .. +8); V rows j0 + 4G + s, d-chunk 8*col.
   const bool lay = KVM == KVM_BF16;
   const uint16_t* kbase = lay ? static_cast<const uint16_t*>(a.cache.kc)
                               : static_cast<const uint16_t*>(a.k) + b * a.k_bs + g * a.k_hs;
   const uint16_t* vbase = lay ? static_cast<const uint16_t*>(a.cache.vc)
                               : static_cast<const uint16_t*>(a.v) + b * a.v_bs + g * a.v_hs;
   const int64_t kss = lay ? D : a.k_ss, vss = lay ? D : a.v_ss;
-  // K rows j0 + col: 4 x 16 B (d = 32kk + 8G .. +8); V rows j0 + 4G + s,
-  // d-chunk 8*col.  Loads are unconditional (keys past the split read its
-  // last key: their scores are masked and their probabilities exactly 0), so
-  // the compiler can count them and wait for one block only.
-#define Q2_DEC_LOAD(KF_, VF_, J0_)                                                                   \
+  struct Set16 {
+    uint4 kf[4], vf[4];
+  };
+#define Q2_DEC_LOAD(S_, J0_)                                                                         \
   {                                                                                                  \
     int64_t r0_ = 0;                                                                                 \
     if (lay) {                                                                                       \
       const int jc_ = min((J0_), jl & ~15);                                                          \
-      r0_ = kv_row(a.cache, b, g, jc_) - jc_;                                                        \
+      r0_ = block_row<PAGED>(a.cache, b, g, jc_) - jc_;                                              \
     }                                                                                                \
     const int key_ = max(min((J0_) + col, jl), 0);                                                   \
-    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) KF_[kk] =                                       \
+    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) S_.kf[kk] =                                     \
         ld16(kbase + (r0_ + key_) * kss + 32 * kk + 8 * G);                                          \
     _Pragma("unroll") for (int s_ = 0; s_ < 4; ++s_) {                                               \
       const int vk_ = max(min((J0_) + 4 * G + s_, jl), 0);                                           \
-      VF_[s_] = ld16(vbase + (r0_ + vk_) * vss + 8 * col);                                           \
+      S_.vf[s_] = ld16(vbase + (r0_ + vk_) * vss + 8 * col);                                         \
     }                                                                                                \
   }
-  // two register sets, loop unrolled by two: the next block's loads are in
-  // flight while this block is multiplied
-  // Every load is issued unconditionally (past the end it rereads a valid
-  // key): with a load count that does not depend on the path, the compiler
-  // waits for the older set only.
-  uint4 kf0[4], vf0[4], kf1[4], vf1[4];
-  Q2_DEC_LOAD(kf0, vf0, j0)
-  // the query fragments were loaded before the first block: mark them
-  // arrived here, so that their wait does not hold back the block's loads
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) settle(qf[kk]);
-  for (; j0 < j_end; j0 += 128) {
-    Q2_DEC_LOAD(kf1, vf1, j0 + 64)
-    dec_block(kf0, vf0, qf, vt, j0, j_end, lim, a.scale, col, G, oacc, m_run, l_run);
-    if (j0 + 64 >= j_end) break;
-    Q2_DEC_LOAD(kf0, vf0, j0 + 128)
-    dec_block(kf1, vf1, qf, vt, j0 + 64, j_end, lim, a.scale, col, G, oacc, m_run, l_run);
-  }
+#define Q2_DEC_BLOCK(S_, J0_) dec_block(S_.kf, S_.vf, qf, vt, (J0_), j_end, lim, a.scale, col, G, oacc, m_run, l_run);
+  Set16 s0, s1, s2;
+  Q2_DEC_RING(Q2_DEC_LOAD, Q2_DEC_BLOCK, s0, s1, s2)
 #undef Q2_DEC_LOAD
+#undef Q2_DEC_BLOCK
   }
+#undef Q2_DEC_RING
   __syncthreads();  // every wave is done with its V^T tile before sO reuses the region
 
   // merge the four waves
@@ -639,7 +705,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(AttnArgs a, int ns
       const int r_ = q_ >> 4;                                                                        \
       sK[BUF_][r_ * PF_KR + (q_ & 15)] = RK_[i];                                                     \
     }                                                                                                \
-    store_vt4(sVt[BUF_], PF_VT, 8 * vc, pf_keyperm(4 * vg) ^ (((vc >> 1) & 7) << 3), RV_);           \
+    store_vt4<true>(sVt[BUF_], PF_VT, 8 * vc, pf_keyperm(4 * vg) ^ (((vc >> 1) & 7) << 3), RV_);           \
   }
 
   float m_run = NEG_INF, l_run = 0.f;
@@ -854,15 +920,23 @@ q2_status attention_bf16(const AttnArgs& a, hipStream_t s) {
       part_o = static_cast<float*>(a.scratch);
       part_ml = reinterpret_cast<float2*>(part_o + slots * D);
     }
-    if (a.use_cache && a.cache.fp8)
-      hipLaunchKernelGGL(attn_decode_kernel<KVM_FP8>, dim3(p.nsplit, a.B * a.nkv), dim3(256), 0, s, a, p.chunk,
-                         p.nsplit, part_o, part_ml);
+    const dim3 grid(p.nsplit, a.B * a.nkv);
+    const bool paged = a.use_cache && a.cache.table;
+    if (a.use_cache && a.cache.fp8 && paged)
+      hipLaunchKernelGGL((attn_decode_kernel<KVM_FP8, true>), grid, dim3(256), 0, s, a, p.chunk, p.nsplit, part_o,
+                         part_ml);
+    else if (a.use_cache && a.cache.fp8)
+      hipLaunchKernelGGL((attn_decode_kernel<KVM_FP8, false>), grid, dim3(256), 0, s, a, p.chunk, p.nsplit, part_o,
+                         part_ml);
+    else if (paged)
+      hipLaunchKernelGGL((attn_decode_kernel<KVM_BF16, true>), grid, dim3(256), 0, s, a, p.chunk, p.nsplit, part_o,
+                         part_ml);
     else if (a.use_cache)
-      hipLaunchKernelGGL(attn_decode_kernel<KVM_BF16>, dim3(p.nsplit, a.B * a.nkv), dim3(256), 0, s, a, p.chunk,
-                         p.nsplit, part_o, part_ml);
+      hipLaunchKernelGGL((attn_decode_kernel<KVM_BF16, false>), grid, dim3(256), 0, s, a, p.chunk, p.nsplit, part_o,
+                         part_ml);
     else
-      hipLaunchKernelGGL(attn_decode_kernel<KVM_STRIDED>, dim3(p.nsplit, a.B * a.nkv), dim3(256), 0, s, a, p.chunk,
-                         p.nsplit, part_o, part_ml);
+      hipLaunchKernelGGL((attn_decode_kernel<KVM_STRIDED, false>), grid, dim3(256), 0, s, a, p.chunk, p.nsplit,
+                         part_o, part_ml);
     Q2_TRY(check_launch("attn_decode"));
     if (p.nsplit > 1 && !a.leave_partials) {
       if (p.nsplit <= 8)
