@@ -557,25 +557,25 @@ __global__ __launch_bounds__(256) void reduce_resid_norm_kernel(const float* __r
   uint16_t* xr = x + static_cast<int64_t>(m) * ldx;
   for (int i = threadIdx.x; i < nch; i += 256) {
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    // four splits' loads in flight at a time
-    for (int s0 = 0; s0 < splits; s0 += 4) {
-      float4 p0[4], p1[4];
+    const uint4 xv = *reinterpret_cast<const uint4*>(xr + 8 * i);  // with the first partials
+    // sixteen splits' loads in flight at a time
+    for (int s0 = 0; s0 < splits; s0 += 16) {
+      float4 p0[16], p1[16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 16; ++j) {
         const int sp = min(s0 + j, splits - 1);
         const float4* q = reinterpret_cast<const float4*>(partial + (static_cast<int64_t>(sp) * M + m) * N + 8 * i);
         p0[j] = q[0];
         p1[j] = q[1];
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 16; ++j) {
         if (s0 + j < splits) {
           a[0] += p0[j].x; a[1] += p0[j].y; a[2] += p0[j].z; a[3] += p0[j].w;
           a[4] += p1[j].x; a[5] += p1[j].y; a[6] += p1[j].z; a[7] += p1[j].w;
         }
       }
     }
-    const uint4 xv = *reinterpret_cast<const uint4*>(xr + 8 * i);
     const uint32_t* xs = &xv.x;
     uint4 xn;
     uint32_t* ns = &xn.x;
