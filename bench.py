@@ -308,8 +308,8 @@ def parity_record(model, wl, weights, ref):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the forward is single-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the forward runs on one GPU and exchanges nothing between GPUs)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
