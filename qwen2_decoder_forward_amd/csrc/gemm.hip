@@ -281,7 +281,8 @@ __device__ __forceinline__ int stg_idx(int r, int col) {
 // 8-byte load and the two RoPE (cos, sin) pairs as one 16-byte load.
 template <int EK>
 __device__ __forceinline__ void stg_put(uint16_t* sh, const Epi& e, int M, int fb0, int tb0, int r, int nl,
-                                        int len0, float x0, float x1, float x2, float x3) {
+                                        int len0, float x0, float x1, float x2, float x3,
+                                        const uint2* pre_bias = nullptr, const float4* pre_cs = nullptr) {
   const uint16_t* bias = static_cast<const uint16_t*>(e.bias);
   if constexpr (EK == EPI_STORE || EK == EPI_RESID) {
     if (EK == EPI_STORE && bias) {
@@ -300,7 +301,7 @@ __device__ __forceinline__ void stg_put(uint16_t* sh, const Epi& e, int M, int f
   } else if constexpr (EK == EPI_QKV) {
     // the block is one head (d = 128); q and k heads hold rotate-half pairs
     // in adjacent rows (2p: original p, 2p+1: original p + 64)
-    const uint2 bb = *reinterpret_cast<const uint2*>(bias + fb0 + nl);
+    const uint2 bb = pre_bias ? *pre_bias : *reinterpret_cast<const uint2*>(bias + fb0 + nl);
     const float a0 = round_bf(x0 + bf_lo(bb.x)), a1 = round_bf(x1 + bf_hi(bb.x));
     const float a2 = round_bf(x2 + bf_lo(bb.y)), a3 = round_bf(x3 + bf_hi(bb.y));
     const int head = fb0 >> 7;
@@ -308,7 +309,10 @@ __device__ __forceinline__ void stg_put(uint16_t* sh, const Epi& e, int M, int f
       const int m = tb0 + r;
       const int p = nl >> 1;
       float2 c0 = make_float2(1.f, 0.f), c1 = c0;
-      if (m < M) {
+      if (pre_cs) {
+        c0 = make_float2(pre_cs->x, pre_cs->y);
+        c1 = make_float2(pre_cs->z, pre_cs->w);
+      } else if (m < M) {
         const int64_t pos = (e.lens ? e.lens[m / e.T] : len0) + m % e.T;
         const float4 cs = *reinterpret_cast<const float4*>(e.rope + pos * 64 + p);
         c0 = make_float2(cs.x, cs.y);
@@ -325,11 +329,31 @@ __device__ __forceinline__ void stg_put(uint16_t* sh, const Epi& e, int M, int f
   }
 }
 
+// Residual chunks a lane adds in stg_copy_out, loaded before the epilogue's
+// LDS staging (up to RES_PRE per lane; iterations past them load their own).
+constexpr int RES_PRE = 8;
+
+template <int ROWS>
+__device__ __forceinline__ void res_preload(const Epi& e, int M, int N, int fb0, int tb0, int lane,
+                                            uint4 (&pre)[RES_PRE]) {
+#pragma unroll
+  for (int it = 0; it < RES_PRE && it < ROWS * 16 / 64; ++it) {
+    // unconditional loads at a clamped in-range address (chunks outside the
+    // product are never stored), so none of them waits for another
+    const int q = it * 64 + lane;
+    const int r = q / 16, c = q % 16;
+    const int m = min(tb0 + r, M - 1);
+    const int f = min(fb0 + c * 8, N - 8);
+    pre[it] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(e.out) + static_cast<int64_t>(m) * e.ldo + f);
+  }
+}
+
 template <int EK, int ROWS>
 __device__ __forceinline__ void stg_copy_out(const uint16_t* sh, const Epi& e, int M, int N, int fb0, int tb0,
-                                             int lane, int len0) {
+                                             int lane, int len0, const uint4 (&res)[RES_PRE]) {
   constexpr int CPR = EK == EPI_SWIGLU ? 8 : 16;  // 16-byte chunks per row of the block
-#pragma unroll 4
+  // fully unrolled, so that res[] stays in registers
+#pragma unroll
   for (int it = 0; it < ROWS * CPR / 64; ++it) {
     const int q = it * 64 + lane;
     const int r = q / CPR, c = q % CPR;
@@ -343,7 +367,7 @@ __device__ __forceinline__ void stg_copy_out(const uint16_t* sh, const Epi& e, i
       if (fb0 + c * 8 >= N) continue;
       uint4* dst =
           reinterpret_cast<uint4*>(static_cast<uint16_t*>(e.out) + static_cast<int64_t>(m) * e.ldo + fb0 + c * 8);
-      const uint4 o = *dst;
+      const uint4 o = it < RES_PRE ? res[it] : *dst;
       const uint32_t* os = &o.x;
       const uint32_t* vs = &v.x;
       uint4 w;
@@ -559,7 +583,37 @@ __device__ __forceinline__ void dtl_tile(const uint16_t* __restrict__ W, int64_t
       if (lane < 32 && m < M) atomicMax(epi.keys + m * KEY_ROW + (blockIdx.x % KEY_SLOTS) * KEY_STRIDE, key);
     }
   } else if constexpr (STAGED) {
-    __syncthreads();  // every wave has finished reading the stages reused below
+    // the residual rows this lane adds are loaded before the staging, so
+    // their latency overlaps it
+    uint4 res[RES_PRE];
+    if constexpr (EK == EPI_RESID) res_preload<TM>(epi, M, N, fb0, tb0, lane, res);
+    // QKV (one token row per lane): every bias quad and RoPE (cos, sin) pair
+    // pair of the lane's features, loaded together at clamped in-range
+    // addresses (rows past M and value heads ignore theirs)
+    constexpr bool QPRE = EK == EPI_QKV && FM == 1;
+    uint2 qb[QPRE ? FN : 1][4];
+    float4 qcs[QPRE ? FN : 1][4];
+    if constexpr (QPRE) {
+      // the position first (its load, if any, is then the only one waited
+      // for), then all the loads that need it
+      const int m = min(tb0 + (lane & 31), M - 1);
+      const int len0q = epi.d_len ? *epi.d_len : epi.len0;
+      const int64_t pos = (epi.lens ? epi.lens[m / epi.T] : len0q) + m % epi.T;
+      const uint16_t* bias = static_cast<const uint16_t*>(epi.bias);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int nl = 32 * i + 8 * v + 4 * (lane >> 5);
+          qcs[i][v] = *reinterpret_cast<const float4*>(epi.rope + pos * 64 + (nl >> 1));
+          qb[i][v] = *reinterpret_cast<const uint2*>(bias + fb0 + nl);
+        }
+    }
+    // every wave has finished reading the stages reused below (an LDS-only
+    // barrier: the residual loads stay in flight across it)
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
     uint16_t* sh = reinterpret_cast<uint16_t*>(dsm) + wave * (TM * 128);
     const int len0 = EK == EPI_QKV ? (epi.d_len ? *epi.d_len : epi.len0) : 0;
 #pragma unroll
@@ -569,8 +623,9 @@ __device__ __forceinline__ void dtl_tile(const uint16_t* __restrict__ W, int64_t
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           stg_put<EK>(sh, epi, M, fb0, tb0, 32 * j + (lane & 31), 32 * i + 8 * v + 4 * (lane >> 5), len0,
-                      acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]);
-    stg_copy_out<EK, TM>(sh, epi, M, N, fb0, tb0, lane, len0);
+                      acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3],
+                      QPRE ? &qb[QPRE ? i : 0][v] : nullptr, QPRE ? &qcs[QPRE ? i : 0][v] : nullptr);
+    stg_copy_out<EK, TM>(sh, epi, M, N, fb0, tb0, lane, len0, res);
   } else {
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
