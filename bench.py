@@ -74,9 +74,10 @@ def weight_bytes(sh, es=2):
 
 
 def kv_bytes_per_token(sh, kv_fp8=False):
-    """K and V bytes of one cached position across all layers (Day-0 article,
-    step 7); the FP8 cache stores one byte per element plus a float32 scale
-    per 128-element block."""
+    """K and V bytes of one cached position across all layers ("万亿参数大模型
+    在国产加速卡上的Day-0适配教程", step 7, KV-cache memory estimate); the FP8
+    cache stores one byte per element plus a float32 scale per 128-element
+    block."""
     if kv_fp8:
         return 2 * sh.nlayer * sh.nkv * (sh.dh + 4 * (sh.dh // 128))
     return 2 * sh.nlayer * sh.nkv * sh.dh * 2

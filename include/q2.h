@@ -135,8 +135,8 @@ q2_status q2_rope(const q2_tensor* out, const q2_tensor* in, const q2_tensor* po
                   void* stream);
 
 /* Causal grouped-query attention (section 3.2, self_attention; the scaled
- * Q K^T -> causal mask -> stable softmax -> times V sequence of the Day-0
- * adaptation article, step 5).
+ * Q K^T -> causal mask -> stable softmax -> times V sequence of
+ * "万亿参数大模型在国产加速卡上的Day-0适配教程", step 5).
  * q: [T, nh, d] or [B, T, nh, d]; k, v: [S, nkv, d] or [B, S, nkv, d] with
  * S >= T; out: same shape as q.  Query t (absolute position S - T + t) sees
  * keys j <= S - T + t.  Query head h reads KV head h / (nh / nkv).

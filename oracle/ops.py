@@ -71,8 +71,8 @@ def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
     """y = x / sqrt(mean(x^2) + eps) * w over the last axis, in float32.
 
     Reading: the epsilon sits inside the square root, added to the mean square
-    (the Day-0 article, step 5, names the epsilon position as an error-prone
-    spot; this is the Qwen2 convention).  The output is rounded once by the
+    ("万亿参数大模型在国产加速卡上的Day-0适配教程", step 5, names the epsilon
+    position as an error-prone spot; this is the Qwen2 convention).  The output is rounded once by the
     caller (no intermediate rounding of x / rms before the weight multiply).
 
     Pinned by: closed form on a constant vector, output RMS = sqrt(ms/(ms+eps))
@@ -142,7 +142,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.n
     q [T, nh, d]; k, v [S, nkv, d] with S >= T (the first S - T keys are the
     cached past).  Query t sits at absolute position S - T + t and sees keys
     j <= S - T + t.  Query head h reads KV head h // (nh / nkv) (contiguous
-    groups).  Per the Day-0 article, step 5: scores = q k^T * scale, causal
+    groups).  Per "万亿参数大模型在国产加速卡上的Day-0适配教程", step 5: scores = q k^T * scale, causal
     mask, max-subtracted softmax in float32, probabilities times v.  Masked
     keys get probability exactly 0.
 
