@@ -20,6 +20,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "kvcache.hpp"
 
 namespace q2 {
 
@@ -181,6 +182,15 @@ struct GemmArgs {
   void* post_out;
   const void* post_w;
   float post_eps;
+  // QKV product (bf16, d = 128) whose split-K reduction runs as a kernel of
+  // its own: with qkv_cache set (a paged and/or FP8 cache), that kernel also
+  // writes the k and v rows straight into the cache (positions as the
+  // epilogue's; FP8 rows quantised) and sets *qkv_cache_done, so that no
+  // separate store of the staged rows is needed.  Without a split-K
+  // reduction the epilogue writes epi.kc / epi.vc as usual and
+  // *qkv_cache_done stays false.
+  const KvLayout* qkv_cache;
+  bool* qkv_cache_done;
 };
 
 q2_status gemm_bf16(const GemmArgs& a, hipStream_t s);

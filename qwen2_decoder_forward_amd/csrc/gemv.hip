@@ -716,6 +716,7 @@ q2_status launch_gemv(const GemmArgs& a, const GemvPlan& p, hipStream_t s) {
       Q2_TRY((launch_gemv2<MT, NW, EK, SRC, false>(a, p, 0, s)));
   }
   if (p.splits == 1 || a.defer_reduce) return Q2_OK;
+  if (EK == EPI_QKV && a.qkv_cache) return split_reduce(a, p.splits, s);
   const int pairs = a.M * cdiv(a.N, 16);
   hipLaunchKernelGGL((gemv_reduce_kernel<EK>), dim3(cdiv(pairs, 32)), dim3(256), 0, s,
                      static_cast<const float*>(a.scratch), p.splits, a.M, a.N, a.epi);
@@ -747,7 +748,97 @@ bool gemv_can_defer(int M, int K) {
   return gemv_can_fuse(M, K) && M <= 2 && K / 8 <= 16 * 64;
 }
 
+namespace {
+
+// Split-K reduction of the QKV product straight into a staged-layout cache
+// (paged and/or FP8): one wave per (token row m, head).  Lane l owns features
+// 2l, 2l + 1 of the head -- for q and k heads the rotate-half pair (l, l + 64),
+// as the packed weight rows put them -- and sums their partials in split order
+// (as gemv_reduce_kernel), then applies the QKV epilogue (bias, RoPE,
+// rounding).  q rows go to e.out; k and v rows go to the cache rows of their
+// positions: bf16 values, or FP8 codes quantised as whole 128-element blocks
+// (kv_store_kernel's quantisation, so the same codes and scales).
+template <bool FP8>
+__global__ __launch_bounds__(256) void qkv_reduce_cache_kernel(const float* __restrict__ partial, int splits, int M,
+                                                               int N, Epi e, KvLayout c) {
+  const int nht = e.nh + 2 * e.nkv;
+  const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (idx >= M * nht) return;  // whole waves leave together
+  const int lane = threadIdx.x & 63;
+  const int m = idx / nht;
+  const int head = idx - m * nht;
+  const int n = head * 128 + 2 * lane;
+  float v0 = 0.f, v1 = 0.f;
+#pragma unroll 8
+  for (int sp = 0; sp < splits; ++sp) {
+    const float2 q = *reinterpret_cast<const float2*>(partial + (static_cast<int64_t>(sp) * M + m) * N + n);
+    v0 += q.x;
+    v1 += q.y;
+  }
+  const uint16_t* bias = static_cast<const uint16_t*>(e.bias);
+  const float a = round_bf(v0 + bf2f(bias[n]));
+  const float b = round_bf(v1 + bf2f(bias[n + 1]));
+  const int bt = m / e.T;
+  const int t = m - bt * e.T;
+  const int pos = (e.lens ? e.lens[bt] : e.d_len ? *e.d_len : e.len0) + t;
+  float x0 = a, x1 = b;  // the block elements this lane holds
+  if (head < e.nh + e.nkv) {
+    const float2 cs = e.rope[static_cast<int64_t>(pos) * 64 + lane];
+    x0 = round_bf(a * cs.x - b * cs.y);  // element lane
+    x1 = round_bf(b * cs.x + a * cs.y);  // element lane + 64
+    if (head < e.nh) {
+      uint16_t* dst = static_cast<uint16_t*>(e.out) + static_cast<int64_t>(m) * e.ldo + head * 128;
+      dst[lane] = f2bf(x0);
+      dst[lane + 64] = f2bf(x1);
+      return;
+    }
+  }
+  if (!kv_mapped(c, bt, pos)) return;  // whole waves leave together
+  const bool isv = head >= e.nh + e.nkv;
+  const bool rot = !isv;  // k: elements lane, lane + 64; v: 2 lane, 2 lane + 1
+  const int hh = isv ? head - e.nh - e.nkv : head - e.nh;
+  const int64_t row = kv_row(c, bt, hh, pos);
+  if constexpr (FP8) {
+    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+    const float scale = amax / 448.0f;
+    const uint32_t c0 = e4m3_encode(amax == 0.f ? x0 : x0 / scale);
+    const uint32_t c1 = e4m3_encode(amax == 0.f ? x1 : x1 / scale);
+    uint8_t* dst = static_cast<uint8_t*>(isv ? c.vc : c.kc) + row * KV_BLOCK;
+    if (rot) {
+      dst[lane] = static_cast<uint8_t>(c0);
+      dst[lane + 64] = static_cast<uint8_t>(c1);
+    } else {
+      *reinterpret_cast<uint16_t*>(dst + 2 * lane) = static_cast<uint16_t>(c0 | (c1 << 8));
+    }
+    if (lane == 0) (isv ? c.vs : c.ks)[row] = amax == 0.f ? 0.f : scale;
+  } else {
+    uint16_t* dst = static_cast<uint16_t*>(isv ? c.vc : c.kc) + row * KV_BLOCK;
+    if (rot) {
+      dst[lane] = f2bf(x0);
+      dst[lane + 64] = f2bf(x1);
+    } else {
+      *reinterpret_cast<uint32_t*>(dst + 2 * lane) = pack_bf2(x0, x1);
+    }
+  }
+}
+
+}  // namespace
+
 q2_status split_reduce(const GemmArgs& a, int splits, hipStream_t s) {
+  if (a.epi.kind == EPI_QKV && a.qkv_cache) {
+    Q2_CHECK(a.epi.dh == 128 && a.N == (a.epi.nh + 2 * a.epi.nkv) * 128 && a.epi.bias, Q2_EINVAL,
+             "split reduce: the fused cache store needs head_dim 128 and a bias");
+    const int waves = a.M * (a.epi.nh + 2 * a.epi.nkv);
+    if (a.qkv_cache->fp8)
+      hipLaunchKernelGGL(qkv_reduce_cache_kernel<true>, dim3(cdiv(waves, 4)), dim3(256), 0, s,
+                         static_cast<const float*>(a.scratch), splits, a.M, a.N, a.epi, *a.qkv_cache);
+    else
+      hipLaunchKernelGGL(qkv_reduce_cache_kernel<false>, dim3(cdiv(waves, 4)), dim3(256), 0, s,
+                         static_cast<const float*>(a.scratch), splits, a.M, a.N, a.epi, *a.qkv_cache);
+    Q2_TRY(check_launch("split_reduce_qkv_cache"));
+    if (a.qkv_cache_done) *a.qkv_cache_done = true;
+    return Q2_OK;
+  }
   if (a.epi.kind == EPI_RESID && a.post_out) {
     Q2_CHECK(a.N % 8 == 0 && a.epi.ldo % 8 == 0, Q2_EINVAL, "split reduce: fused norm needs N %% 8 == 0");
     hipLaunchKernelGGL(reduce_resid_norm_kernel, dim3(a.M), dim3(256), static_cast<size_t>(a.N) * 2, s,

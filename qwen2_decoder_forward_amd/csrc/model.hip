@@ -357,11 +357,19 @@ q2_status run_layers(q2_model* m, int B, int Tc, bool advance, hipStream_t s, in
       a.epi.T = Tc;
       a.epi.d_len = m->d_len;
       a.epi.rope = m->rope;
+      // a paged and/or FP8 cache: a split-K reduction of this product stores
+      // the k / v rows itself, else kv_store does from the staged rows
+      const KvLayout lay = cache_layout(m, l);
+      bool stored = false;
+      if (stg && m->cfg.dtype == Q2_BF16) {
+        a.qkv_cache = &lay;
+        a.qkv_cache_done = &stored;
+      }
       if (want(STAGE_QKV)) Q2_TRY(gemm(m, a, s));
       cur = nxt;
       pend_splits = 0;
-      if (staged_kv(m) && want(STAGE_QKV))
-        Q2_TRY(launch_kv_store(cache_layout(m, l), static_cast<const uint16_t*>(m->kstage),
+      if (staged_kv(m) && !stored && want(STAGE_QKV))
+        Q2_TRY(launch_kv_store(lay, static_cast<const uint16_t*>(m->kstage),
                                static_cast<const uint16_t*>(m->vstage), B, Tc, call_lens(m), m->d_len, m->len, s));
     }
     // with one query per sequence and split-KV partials, o_proj merges them

@@ -80,40 +80,48 @@ def _fp8_run(shape, batch, prompt_len, steps, seed=1234):
     return r, model, orc, w, prompt
 
 
-def test_fp8_model_small_teacher_forced():
-    r, model, orc, _, _ = _fp8_run(SMALL_BF16, 3, 40, 12)
-    print(f"\n[fp8 small] {r.summary()}", flush=True)
-    # the first layer's cache: GPU codes and scales, dequantised, against the oracle's
+def _check_layer0_cache(model, orc, batch, nkv, tag):
+    """The first layer's cache -- GPU codes and scales, dequantised -- against
+    the oracle's, over every cached position (prompt rows from the prefill's
+    store, the rest from the decode steps' QKV reductions)."""
     k, v = model.kv_view(0)
     ks, vs = model.kv_scale_view(0)
     L0 = orc.length
-    for cdesc, sdesc, ref in ((k, ks, orc.k_cache[0]), (v, vs, orc.v_cache[0])):
-        codes = torch.empty(3, L0, SMALL_BF16.nkv, 128, dtype=torch.uint8, device=DEV)
+    for name, cdesc, sdesc, ref in (("k", k, ks, orc.k_cache[0]), ("v", v, vs, orc.v_cache[0])):
+        codes = torch.empty(batch, L0, nkv, 128, dtype=torch.uint8, device=DEV)
         c2 = q2.Q2Tensor.from_buffer_copy(cdesc)
-        c2.shape[0], c2.shape[1] = 3, L0
+        c2.shape[0], c2.shape[1] = batch, L0
         q2.q2_rearrange(codes, c2)
-        sc = torch.empty(3, L0, SMALL_BF16.nkv, dtype=torch.float32, device=DEV)
+        sc = torch.empty(batch, L0, nkv, dtype=torch.float32, device=DEV)
         s2 = q2.Q2Tensor.from_buffer_copy(sdesc)
-        s2.shape[0], s2.shape[1] = 3, L0
+        s2.shape[0], s2.shape[1] = batch, L0
         q2.q2_rearrange(sc, s2)
-        deq = torch.empty(3 * L0 * SMALL_BF16.nkv, 128, dtype=torch.bfloat16, device=DEV)
+        deq = torch.empty(batch * L0 * nkv, 128, dtype=torch.bfloat16, device=DEV)
         q2.q2_kv_dequantize(deq, codes.view(-1, 128), sc.view(-1))
-        got = down(deq).reshape(3, L0, SMALL_BF16.nkv, 128).transpose(0, 2, 1, 3)
+        got = down(deq).reshape(batch, L0, nkv, 128).transpose(0, 2, 1, 3)
         want = ref[:, :, :L0, :]
         eq = float(np.mean(got == want))
-        print(f"  layer-0 cache rows equal to the oracle's: {eq:.4f}", flush=True)
+        print(f"  [{tag}] layer-0 {name} cache rows equal to the oracle's: {eq:.4f}", flush=True)
         assert eq >= 0.99
+
+
+def test_fp8_model_small_teacher_forced():
+    r, model, orc, _, _ = _fp8_run(SMALL_BF16, 3, 40, 12)
+    print(f"\n[fp8 small] {r.summary()}", flush=True)
+    _check_layer0_cache(model, orc, 3, SMALL_BF16.nkv, "fp8 small")
     model.close()
     assert r.ok(), r.summary()
 
 
 def test_fp8_model_batched_decode_1p5b_width():
     """1.5B layer shapes with 4 layers, 64 sequences, 96-token prompts, 4
-    batched decode steps (the 64-sequence decode path with an FP8 cache)."""
+    batched decode steps (the 64-sequence decode path with an FP8 cache,
+    whose QKV split-K reduction quantises the new k / v rows itself)."""
     sh = dataclasses.replace(synth.SHAPES["1.5b"], nlayer=4)
-    r, model, _, _, _ = _fp8_run(sh, 64, 96, 4)
-    model.close()
+    r, model, orc, _, _ = _fp8_run(sh, 64, 96, 4)
     print(f"\n[fp8 1.5B width, batch 64] {r.summary()}", flush=True)
+    _check_layer0_cache(model, orc, 64, sh.nkv, "fp8 batch 64")
+    model.close()
     assert r.ok(), r.summary()
 
 
