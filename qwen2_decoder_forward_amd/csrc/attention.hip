@@ -139,10 +139,17 @@ __device__ __forceinline__ void dec_block(const uint4 (&kf)[4], const uint4 (&vf
   pw.x = pack_bf2(s[0], s[1]);
   pw.y = pack_bf2(s[2], s[3]);
   const short4_t pf = as_short4(pw);
+  // a running max that did not move leaves alpha exactly 1: skip the rescale
+  // (after the first blocks it rarely moves)
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      oacc[dt][0] *= alpha; oacc[dt][1] *= alpha; oacc[dt][2] *= alpha; oacc[dt][3] *= alpha;
+    }
+  }
   wave_lds_sync();
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
-    oacc[dt][0] *= alpha; oacc[dt][1] *= alpha; oacc[dt][2] *= alpha; oacc[dt][3] *= alpha;
     const uint32_t* vp =
         reinterpret_cast<const uint32_t*>(vt + (16 * dt + col) * VT_DEC + 4 * ((G + (dt >> 1)) & 3));
     const uint2 vv = make_uint2(vp[0], vp[1]);
