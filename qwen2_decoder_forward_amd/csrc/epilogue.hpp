@@ -191,6 +191,12 @@ struct GemmArgs {
   // *qkv_cache_done stays false.
   const KvLayout* qkv_cache;
   bool* qkv_cache_done;
+  // Stream-K workspace (stream_k_bytes, zeroed once before its first use;
+  // the kernels leave it zeroed): prefill products with fewer tiles than CUs
+  // then share tiles between workgroups instead of leaving CUs idle.  Null:
+  // plain tiles.
+  void* sk_ws;
+  size_t sk_ws_bytes;
 };
 
 q2_status gemm_bf16(const GemmArgs& a, hipStream_t s);
@@ -216,5 +222,9 @@ size_t gemm_scratch_bytes(int M, int N, int K);
 q2_status split_reduce(const GemmArgs& a, int splits, hipStream_t s);
 // Whether gemm_bf16(a) writes a.post_out itself (else the caller norms).
 bool gemm_post_norm(const GemmArgs& a);
+// Bytes of the stream-K workspace for device `device` (GemmArgs::sk_ws), and
+// the offset of its error word (non-zero after a hand-over wait timed out).
+size_t stream_k_bytes(int device);
+size_t stream_k_err_offset();
 
 }  // namespace q2

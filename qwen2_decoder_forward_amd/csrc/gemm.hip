@@ -13,6 +13,7 @@
 // tokens the B operand, so a lane's accumulators hold runs of four
 // consecutive features of one token -- the adjacent feature pairs the QKV
 // (rotate-half) and SwiGLU epilogues need are in the same lane.
+#include <algorithm>
 #include <type_traits>
 
 #include "epilogue.hpp"
@@ -416,14 +417,48 @@ __device__ __forceinline__ void xcd_tile(int t, int T, int tiles_m, int& tn, int
   tn = r / gs;
 }
 
+// Stream-K hand-over between the two workgroups that share a tile: the
+// partial tile and the flag are written and read at agent scope (the L2s of
+// the XCDs are not coherent with each other), the flag only after every
+// store of the partial has completed.
+__device__ __forceinline__ void sk_st64(float* p, float x, float y) {
+  const uint64_t v = static_cast<uint64_t>(__float_as_uint(x)) | (static_cast<uint64_t>(__float_as_uint(y)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 sk_ld64(const float* p) {
+  const uint64_t v =
+      __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(static_cast<uint32_t>(v >> 32)));
+}
+__device__ __forceinline__ void sk_st32(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned sk_ld32(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// polls of a stream-K flag before the finisher gives up and reports it
+constexpr long SK_SPIN_MAX = 1L << 22;
+
+// Stream-K roles of dtl_tile (template argument SK):
+enum SkRole : int { SK_NONE = 0, SK_PRODUCE = 1, SK_FINISH = 2 };
+struct SkPart {
+  int kt0, nkt;       // K slices [kt0, kt0 + nkt) of the tile
+  float* part;        // the tile's float32 hand-over buffer (NT x 64 floats, thread-major)
+  unsigned* flag;     // 0: empty, 1: written; the finisher resets it
+  unsigned* err;      // set when a finisher's wait times out
+};
+
 // One BN x BM output tile at features n0.., tokens m0...
 // With SPLIT, blockIdx.y takes slices [y * kt_split, (y + 1) * kt_split) of
 // K and the float32 tile goes to partial[y][m][n] (a second kernel sums the
 // splits in order and applies the epilogue).
-template <int EK, int BN, int BM, int WN, int WM, bool STAGED, bool SPLIT>
+// With SK, the K slices are sk.kt0 .. + sk.nkt: SK_PRODUCE hands its float32
+// tile over to the finisher and returns; SK_FINISH adds the hand-over
+// (earlier slices first: p + acc) and applies the epilogue.
+template <int EK, int BN, int BM, int WN, int WM, bool STAGED, bool SPLIT, int SK = SK_NONE>
 __device__ __forceinline__ void dtl_tile(const uint16_t* __restrict__ W, int64_t ldw, const uint16_t* __restrict__ X,
                                          int64_t ldx, int N, int M, int K, int n0, int m0, int kt_split,
-                                         float* __restrict__ partial, const Epi& epi) {
+                                         float* __restrict__ partial, const Epi& epi, const SkPart& sk = SkPart{}) {
   using C = Dtl<BN, BM, WN, WM>;
   constexpr int FN = C::FN, FM = C::FM, TN = C::TN, TM = C::TM, NT = C::NT, LD = C::LD;
   extern __shared__ uint4 dsm[];
@@ -443,7 +478,8 @@ __device__ __forceinline__ void dtl_tile(const uint16_t* __restrict__ W, int64_t
     const bool isw = slot < BN * 4;
     const int ls = isw ? slot : slot - BN * 4;
     const int r = ls >> 2;
-    const int c = dtl_swz(r, ls & 3) + (SPLIT ? blockIdx.y * kt_split * (C::BK / 8) : 0);
+    const int c = dtl_swz(r, ls & 3) +
+                  (SPLIT ? blockIdx.y * kt_split * (C::BK / 8) : SK != SK_NONE ? sk.kt0 * (C::BK / 8) : 0);
     if (isw) {
       const int row = min(n0 + r, N - 1);
       src[i] = W + static_cast<int64_t>(row) * ldw + 8 * c;
@@ -452,7 +488,8 @@ __device__ __forceinline__ void dtl_tile(const uint16_t* __restrict__ W, int64_t
       src[i] = X + static_cast<int64_t>(row) * ldx + 8 * c;
     }
   }
-  const int nk = SPLIT ? min(kt_split, K / C::BK - static_cast<int>(blockIdx.y) * kt_split) : K / C::BK;
+  const int nk = SPLIT ? min(kt_split, K / C::BK - static_cast<int>(blockIdx.y) * kt_split)
+                 : SK != SK_NONE ? sk.nkt : K / C::BK;
 #define Q2_DTL_ISSUE(S_, KT_)                                                                        \
   {                                                                                                  \
     const int kt_ = (KT_);                                                                           \
@@ -532,6 +569,46 @@ __device__ __forceinline__ void dtl_tile(const uint16_t* __restrict__ W, int64_t
   // no load into LDS may still be in flight when the stages are reused or
   // the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (SK == SK_PRODUCE) {
+    // hand the float32 tile over (thread-major: a store instruction covers
+    // 512 contiguous bytes per wave), then raise the flag once every
+    // thread's stores have completed
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sk_st64(sk.part + 2 * (static_cast<int64_t>((i * FM + j) * 8 + e) * NT + tid), acc[i][j][2 * e],
+                  acc[i][j][2 * e + 1]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) sk_st32(sk.flag, 1u);
+    return;
+  }
+  if constexpr (SK == SK_FINISH) {
+    if (tid == 0) {
+      long spins = 0;
+      while (sk_ld32(sk.flag) == 0u) {
+        if (++spins > SK_SPIN_MAX) {
+          sk_st32(sk.err, 1u);
+          break;
+        }
+      }
+      sk_st32(sk.flag, 0u);  // ready for the next launch
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 q = sk_ld64(sk.part + 2 * (static_cast<int64_t>((i * FM + j) * 8 + e) * NT + tid));
+          acc[i][j][2 * e] = q.x + acc[i][j][2 * e];
+          acc[i][j][2 * e + 1] = q.y + acc[i][j][2 * e + 1];
+        }
+  }
 #undef Q2_DTL_ISSUE
 #undef Q2_DTL_WAIT_BARRIER
 #undef Q2_DTL_READ
@@ -677,6 +754,70 @@ __global__ __launch_bounds__(512) void gemm_dtl_mix_kernel(const uint16_t* __res
     dtl_tile<EK, 128, 256, 1, 8, STAGED, false>(W, ldw, X, ldx, N, M, K, n_main + tn * 128, tm * 256, 0, nullptr,
                                                epi);
   }
+}
+
+// Stream-K for long-K products with fewer 128-feature x 256-token tiles than
+// CUs (down at hidden 1536 and 4096 tokens: 192 tiles, K = 8960): each
+// tile's K is cut into four quarters (whole 128-wide groups) and every
+// workgroup takes three consecutive quarters, so 4/3 as many workgroups as
+// tiles (256 for 192) each do three quarters of a tile.  A tile is then shared by at most two workgroups: the
+// one with its first quarters hands its float32 partial over (SK_PRODUCE),
+// the one with its last quarters adds it and applies the epilogue
+// (SK_FINISH).  Every workgroup produces before it finishes, so the hand-over
+// it waits for was (nearly always) written long before.  All workgroups must
+// be resident together (one per CU; the host launches this only when the
+// grid fits the CUs); a wait that times out sets the error word instead of
+// hanging.  Workgroups are numbered XCD-major, so that consecutive ones (which
+// share tiles) sit on one XCD.
+// sk: [flags: SK_MAX_TILES words][err word, padded to 1 KB][partials].
+constexpr int SK_MAX_TILES = 256;
+constexpr size_t SK_PART_OFF = SK_MAX_TILES * sizeof(unsigned) + 1024;
+constexpr size_t SK_TILE_FLOATS = 128 * 256;
+
+template <int EK, bool STAGED, int SK>
+__device__ __forceinline__ void sk_segment(const uint16_t* __restrict__ W, int64_t ldw,
+                                           const uint16_t* __restrict__ X, int64_t ldx, int N, int M, int K,
+                                           int tiles_m, int tiles, int t, int q0, int q1, unsigned char* skw,
+                                           const Epi& epi) {
+  // tile t: groups of 4 token tiles x all weight tiles (as xcd_tile)
+  const int tiles_n = tiles / tiles_m;
+  const int fm = t / (4 * tiles_n) * 4;
+  const int gs = min(tiles_m - fm, 4);
+  const int r = t - fm * tiles_n;
+  const int tm = fm + r % gs, tn = r / gs;
+  // quarter q starts at K group round(q * G4 / 4) of G4 128-wide groups: the
+  // main loop takes 32-wide slices four at a time, so a segment must be
+  // whole groups (quarters of 280 slices: 72, 68, 72, 68)
+  const int G4 = K / 128;
+  const int g0 = (2 * q0 * G4 + 4) / 8, g1 = (2 * q1 * G4 + 4) / 8;
+  unsigned* flags = reinterpret_cast<unsigned*>(skw);
+  SkPart sk;
+  sk.kt0 = 4 * g0;
+  sk.nkt = 4 * (g1 - g0);
+  sk.part = reinterpret_cast<float*>(skw + SK_PART_OFF) + static_cast<int64_t>(t) * SK_TILE_FLOATS;
+  sk.flag = flags + t;
+  sk.err = flags + SK_MAX_TILES;
+  dtl_tile<EK, 128, 256, 1, 8, STAGED, false, SK>(W, ldw, X, ldx, N, M, K, tn * 128, tm * 256, 0, nullptr, epi, sk);
+}
+
+template <int EK, bool STAGED>
+__global__ __launch_bounds__(512) void gemm_dtl_sk_kernel(const uint16_t* __restrict__ W, int64_t ldw,
+                                                          const uint16_t* __restrict__ X, int64_t ldx, int N, int M,
+                                                          int K, int tiles_m, int tiles, unsigned char* skw, Epi epi) {
+  const int G = gridDim.x;
+  const int L = G % 8 == 0 ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int s0 = 3 * L, s1 = s0 + 3;  // quarters [s0, s1) of the tile sequence
+  const int t0 = s0 >> 2, t1 = (s1 - 1) >> 2;
+  if (t1 > t0) {
+    // the first quarters of tile t1, handed over
+    sk_segment<EK, STAGED, SK_PRODUCE>(W, ldw, X, ldx, N, M, K, tiles_m, tiles, t1, 0, s1 - 4 * t1, skw, epi);
+    __syncthreads();  // every wave is done with the LDS ring before it is refilled
+  }
+  const int a = s0 - 4 * t0, b = min(s1, 4 * t0 + 4) - 4 * t0;
+  if (a == 0)
+    sk_segment<EK, STAGED, SK_PRODUCE>(W, ldw, X, ldx, N, M, K, tiles_m, tiles, t0, 0, b, skw, epi);
+  else
+    sk_segment<EK, STAGED, SK_FINISH>(W, ldw, X, ldx, N, M, K, tiles_m, tiles, t0, a, 4, skw, epi);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -853,6 +994,48 @@ q2_status launch_dtl_mix(const GemmArgs& a, int main_tiles, hipStream_t s) {
   return check_launch("gemm_dtl_mix");
 }
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Stream-K applies to a 128 x 256 tiling of `tiles` tiles when its 4/3 as
+// many workgroups fit the CUs at once (one each) and the workspace holds the
+// hand-over tiles.
+bool sk_fits(const GemmArgs& a, int tiles) {
+  if (!a.sk_ws || a.epi.kind == EPI_ARGMAX || tiles % 3 != 0 || tiles > SK_MAX_TILES) return false;
+  // long K only: the hand-over (a 128 KB partial tile written and read back)
+  // costs a short product more than its idle CUs do (o_proj at K = 1536:
+  // 30 -> 38 us); every quarter is at least one 128-wide group
+  if (a.K % 128 != 0 || a.K < 4096) return false;
+  const int grid = tiles / 3 * 4;
+  if (grid > cu_count()) return false;
+  return a.sk_ws_bytes >= SK_PART_OFF + static_cast<size_t>(tiles) * SK_TILE_FLOATS * sizeof(float);
+}
+
+template <int EK>
+q2_status launch_dtl_sk(const GemmArgs& a, int tiles, hipStream_t s) {
+  const int tiles_m = cdiv(a.M, 256);
+  const size_t lds = Dtl<128, 256, 1, 8>::LDS_BYTES;
+  unsigned char* skw = static_cast<unsigned char*>(a.sk_ws);
+  const dim3 grid(tiles / 3 * 4);
+  if (staged_ok(a))
+    hipLaunchKernelGGL((gemm_dtl_sk_kernel<EK, true>), grid, dim3(512), lds, s, static_cast<const uint16_t*>(a.W),
+                       a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M, a.K, tiles_m, tiles, skw, a.epi);
+  else
+    hipLaunchKernelGGL((gemm_dtl_sk_kernel<EK, false>), grid, dim3(512), lds, s, static_cast<const uint16_t*>(a.W),
+                       a.ldw, static_cast<const uint16_t*>(a.X), a.ldx, a.N, a.M, a.K, tiles_m, tiles, skw, a.epi);
+  return check_launch("gemm_dtl_sk");
+}
+
 template <int EK>
 q2_status launch_dtl(const GemmArgs& a, hipStream_t s) {
   const int big_tiles = cdiv(a.M, 256) * cdiv(a.N, 256);
@@ -861,7 +1044,13 @@ q2_status launch_dtl(const GemmArgs& a, hipStream_t s) {
     if (main_tiles > 0) return launch_dtl_mix<EK>(a, main_tiles, s);
     return launch_dtl_cfg<EK, 256, 256, 2, 4>(a, s);
   }
-  if (a.M >= 512) return launch_dtl_cfg<EK, 128, 256, 1, 8>(a, s);
+  if (a.M >= 512) {
+    if constexpr (EK != EPI_ARGMAX) {
+      const int tiles = cdiv(a.M, 256) * cdiv(a.N, 128);
+      if (sk_fits(a, tiles)) return launch_dtl_sk<EK>(a, tiles, s);
+    }
+    return launch_dtl_cfg<EK, 128, 256, 1, 8>(a, s);
+  }
   return launch_dtl_cfg<EK, 128, 128, 1, 4>(a, s);
 }
 
@@ -931,6 +1120,15 @@ size_t gemm_scratch_bytes(int M, int N, int K) {
   }
   return b;
 }
+
+size_t stream_k_bytes(int device) {
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) n = 0;
+  const int tiles = std::min(SK_MAX_TILES, n / 4 * 3);
+  return SK_PART_OFF + static_cast<size_t>(tiles) * SK_TILE_FLOATS * sizeof(float);
+}
+
+size_t stream_k_err_offset() { return SK_MAX_TILES * sizeof(unsigned); }
 
 bool gemm_post_norm(const GemmArgs& a) {
   // the skinny path's split-K reduction of a residual product (rows of 16-byte

@@ -102,6 +102,9 @@ struct q2_model {
   int* d_len = nullptr;
   void* gscratch = nullptr;
   size_t gscratch_bytes = 0;
+  // stream-K workspace of the prefill products (zeroed with the arena)
+  void* skws = nullptr;
+  size_t sk_bytes = 0;
   void* ascratch = nullptr;
   size_t ascratch_bytes = 0;
   float* sq = nullptr;            // [max_tok][hidden / 16] row sums of squares (decode path)
@@ -265,6 +268,8 @@ GemmArgs gemm_args(const q2_model* m, const void* W, int64_t ldw, const void* X,
   a.K = K;
   a.scratch = m->gscratch;
   a.scratch_bytes = m->gscratch_bytes;
+  a.sk_ws = m->skws;
+  a.sk_ws_bytes = m->sk_bytes;
   return a;
 }
 
@@ -1001,6 +1006,8 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
   }
   m->gscratch_bytes = gs;
   const size_t a_gs = take(gs);
+  m->sk_bytes = (c.dtype == Q2_BF16 && m->max_tok >= 512) ? stream_k_bytes(m->device) : 0;
+  const size_t a_sk = take(m->sk_bytes);
   size_t as = 0;
   if (c.dtype == Q2_BF16)
     for (int b = 1; b <= c.max_batch; ++b) {
@@ -1084,6 +1091,7 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
   m->hist = reinterpret_cast<int64_t*>(m->amem + a_hist);
   m->d_len = reinterpret_cast<int*>(m->amem + a_len);
   m->gscratch = gs ? m->amem + a_gs : nullptr;
+  m->skws = m->sk_bytes ? m->amem + a_sk : nullptr;
   m->ascratch = as ? m->amem + a_as : nullptr;
   m->sq = reinterpret_cast<float*>(m->amem + a_sq);
   if (hipStreamCreateWithFlags(&m->cap, hipStreamNonBlocking) != hipSuccess)
@@ -1497,6 +1505,11 @@ extern "C" q2_status q2_model_check(q2_model* m) {
     unsigned err = 0;
     Q2_HIP(hipMemcpy(&err, m->mk.err, sizeof err, hipMemcpyDeviceToHost));
     Q2_CHECK(err == 0, Q2_EHIP, "a grid barrier of the persistent decode step timed out");
+  }
+  if (m->skws) {
+    unsigned err = 0;
+    Q2_HIP(hipMemcpy(&err, static_cast<char*>(m->skws) + stream_k_err_offset(), sizeof err, hipMemcpyDeviceToHost));
+    Q2_CHECK(err == 0, Q2_EHIP, "a stream-K hand-over wait of a prefill product timed out");
   }
   return Q2_OK;
 }

@@ -37,6 +37,12 @@ from tests.model_util import DEV, build_model, reduced_shape, teacher_forced
 pytestmark = pytest.mark.gpu
 
 SMALL_BF16 = synth.ModelShape("small-bf16", "bf16", 3, 256, 4, 2, 128, 512, 1000, 10000.0)
+# one such layer with a long down projection (K = 4096), whose prefill tiles
+# are shared between workgroups (stream-K) when there are fewer tiles than
+# CUs; one layer, so that the hidden state shows that product's own rounding
+# (a bf16 flip of a layer's output changes the next layer's RMSNorm of every
+# feature, and three layers of that reach two steps at the largest value)
+SMALL_LONGK = synth.ModelShape("small-bf16-longk", "bf16", 1, 256, 4, 2, 128, 4096, 1000, 10000.0)
 
 
 def _run(shape, batch, prompt_len, steps, seed=1234, prompt_seed=5678):
@@ -207,22 +213,29 @@ def test_chunked_prefill_equals_one_shot_small_bf16():
     assert np.abs(one - two).max() <= 2e-2
 
 
-@pytest.mark.parametrize("T", [7, 40])
+@pytest.mark.parametrize("T", [7, 40, 768])
 def test_fused_model_equals_unfused_operator_chain(T):
     """The model's fused kernels against the chain of standalone operators
     (embedding, rms_norm, linear, rope, rearrange into the KV cache,
     self_attention, linear, add, swiglu, argmax) on the same input.  7 tokens
     take the GEMV path with its fused norms; 40 take the skinny split-K
-    products, whose residual reductions also write the following RMSNorm.
+    products, whose residual reductions also write the following RMSNorm;
+    768 take the prefill tiles, and with a 4096-wide intermediate layer (one
+    layer) the down projection's 3 x 2 tiles of 128 x 256 are each shared
+    between two workgroups (stream-K: the model passes the hand-over
+    workspace, the standalone operator does not).
     At 7 tokens every product sums K in the same order on both sides, so the
     K and V caches of every layer, the final hidden state and the logits are
     bit-equal (the fused epilogues and prologues round exactly where the
-    operators do).  At 40 tokens the fused products split K differently from
-    the standalone ones (float32 sums in another order, and from layer 1 on
-    an input that differs by those flips), so the caches are held to two
-    bf16 steps of their largest value, the hidden state to one bf16 step of
-    its largest value and the logits to 1e-2, with the same argmax."""
-    sh = SMALL_BF16
+    operators do).  At 40 tokens the fused products split K differently
+    from the standalone ones (float32 sums in another order, and from layer 1 on
+    an input that differs by those flips); at 768 the first layer's K and V
+    cache rows are still bit-equal, but the products after the attention need
+    not sum in the operators' order (the stream-K down projection among them).
+    So the caches are held to two bf16 steps of their largest value, the
+    hidden state to one bf16 step of its largest value and the logits to
+    1e-2, with the same argmax."""
+    sh = SMALL_LONGK if T == 768 else SMALL_BF16
     w = synth.make_weights(sh, seed=6)
     if T == 7:
         ids = np.array([[1, 2, 3, 500, 999, 0, 42]], np.int64)
@@ -295,6 +308,7 @@ def test_fused_model_equals_unfused_operator_chain(T):
     val = torch.empty(1, dtype=torch.float32, device=DEV)
     q2.q2_argmax(idx, val, logits)
     hid = m.hidden().float()
+    m.check()  # no stream-K hand-over wait timed out
     m.close()
     xf = x.float()
     dh = float((hid - xf).abs().max())
