@@ -358,7 +358,11 @@ q2_status q2_model_decode_path(const q2_model* m, int32_t batch, int32_t* persis
 
 /* Synchronises the device and reports failures recorded on it by earlier
  * asynchronous calls: Q2_EHIP if a grid barrier of the persistent decode
- * kernel timed out (the step's results are then invalid). */
+ * kernel timed out, or if a prefill product whose tiles are shared between
+ * two workgroups (stream-K: long-K products with fewer tiles than CUs)
+ * waited past its bound for the other workgroup's partial tile -- which
+ * happens only if the device could not hold all of that launch's
+ * workgroups at once.  The affected results are then invalid. */
 q2_status q2_model_check(q2_model* m);
 
 
