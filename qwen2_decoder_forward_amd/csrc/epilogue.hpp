@@ -197,6 +197,7 @@ struct GemmArgs {
   // plain tiles.
   void* sk_ws;
   size_t sk_ws_bytes;
+  int sk_cus;  // compute units of the device the product runs on
 };
 
 q2_status gemm_bf16(const GemmArgs& a, hipStream_t s);
@@ -222,9 +223,11 @@ size_t gemm_scratch_bytes(int M, int N, int K);
 q2_status split_reduce(const GemmArgs& a, int splits, hipStream_t s);
 // Whether gemm_bf16(a) writes a.post_out itself (else the caller norms).
 bool gemm_post_norm(const GemmArgs& a);
-// Bytes of the stream-K workspace for device `device` (GemmArgs::sk_ws), and
-// the offset of its error word (non-zero after a hand-over wait timed out).
-size_t stream_k_bytes(int device);
+// Compute units of device `device` (0 if unknown); bytes of the stream-K
+// workspace for a device of `cus` compute units (GemmArgs::sk_ws), and the
+// offset of its error word (non-zero after a hand-over wait timed out).
+int device_cus(int device);
+size_t stream_k_bytes(int cus);
 size_t stream_k_err_offset();
 
 }  // namespace q2

@@ -994,19 +994,6 @@ q2_status launch_dtl_mix(const GemmArgs& a, int main_tiles, hipStream_t s) {
   return check_launch("gemm_dtl_mix");
 }
 
-// Compute units of the current device (cached per device).
-int cu_count() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 // Stream-K applies to a 128 x 256 tiling of `tiles` tiles when its 4/3 as
 // many workgroups fit the CUs at once (one each) and the workspace holds the
 // hand-over tiles.
@@ -1017,7 +1004,7 @@ bool sk_fits(const GemmArgs& a, int tiles) {
   // 30 -> 38 us); every quarter is at least one 128-wide group
   if (a.K % 128 != 0 || a.K < 4096) return false;
   const int grid = tiles / 3 * 4;
-  if (grid > cu_count()) return false;
+  if (grid > a.sk_cus) return false;
   return a.sk_ws_bytes >= SK_PART_OFF + static_cast<size_t>(tiles) * SK_TILE_FLOATS * sizeof(float);
 }
 
@@ -1121,11 +1108,15 @@ size_t gemm_scratch_bytes(int M, int N, int K) {
   return b;
 }
 
-size_t stream_k_bytes(int device) {
+int device_cus(int device) {
   int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) n = 0;
-  const int tiles = std::min(SK_MAX_TILES, n / 4 * 3);
-  return SK_PART_OFF + static_cast<size_t>(tiles) * SK_TILE_FLOATS * sizeof(float);
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return 0;
+  return n;
+}
+
+size_t stream_k_bytes(int cus) {
+  const int tiles = std::min(SK_MAX_TILES, cus / 4 * 3);
+  return tiles > 0 ? SK_PART_OFF + static_cast<size_t>(tiles) * SK_TILE_FLOATS * sizeof(float) : 0;
 }
 
 size_t stream_k_err_offset() { return SK_MAX_TILES * sizeof(unsigned); }

@@ -105,6 +105,7 @@ struct q2_model {
   // stream-K workspace of the prefill products (zeroed with the arena)
   void* skws = nullptr;
   size_t sk_bytes = 0;
+  int cus = 0;
   void* ascratch = nullptr;
   size_t ascratch_bytes = 0;
   float* sq = nullptr;            // [max_tok][hidden / 16] row sums of squares (decode path)
@@ -270,6 +271,7 @@ GemmArgs gemm_args(const q2_model* m, const void* W, int64_t ldw, const void* X,
   a.scratch_bytes = m->gscratch_bytes;
   a.sk_ws = m->skws;
   a.sk_ws_bytes = m->sk_bytes;
+  a.sk_cus = m->cus;
   return a;
 }
 
@@ -1006,7 +1008,8 @@ extern "C" q2_status q2_model_create(const q2_config* cfg, int32_t device, q2_mo
   }
   m->gscratch_bytes = gs;
   const size_t a_gs = take(gs);
-  m->sk_bytes = (c.dtype == Q2_BF16 && m->max_tok >= 512) ? stream_k_bytes(m->device) : 0;
+  m->cus = device_cus(m->device);
+  m->sk_bytes = (c.dtype == Q2_BF16 && m->max_tok >= 512) ? stream_k_bytes(m->cus) : 0;
   const size_t a_sk = take(m->sk_bytes);
   size_t as = 0;
   if (c.dtype == Q2_BF16)
