@@ -2,6 +2,7 @@
 """Benchmark of the Qwen2 decoder forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload B|C|D|E] [--no-cpu]
+                    [--also C,D] [--kv bf16|fp8] [--paged N]
 
 Default workload B: Qwen2-1.5B shape, bf16, random-init weights, batch 1,
 64-token random prompt, 128 greedy decode steps.  One "step" is one pass of
@@ -30,6 +31,10 @@ Also reported:
                 tokens, its logits against the oracle's at every position
                 (raw max abs error, raw and decisive top-1 agreement, the
                 oracle's own float32/float64 spread and the derived bound).
+  also          (B, unless --also says otherwise) workloads C and D on the
+                same weights, after the main one: value, step time,
+                dominant-kernel and step rooflines of each, as measured by
+                this same run (they do not enter `value`).
 """
 from __future__ import annotations
 
@@ -59,6 +64,10 @@ def parse():
                     help="time only the dominant kernel (for profiler counter runs) and print its record")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="KV cache: bf16 (the workloads' definition) or FP8 E4M3 blocks with per-block scales")
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads of the same model shape timed after the main one, each "
+                         "reported as a compact record under `also` (default: C,D after B; '' for none)")
+    ap.add_argument("--also-steps", type=int, default=3, help="timed passes of each --also workload")
     ap.add_argument("--paged", type=int, default=0,
                     help="positions per page of a paged KV cache (0: contiguous per-sequence cache)")
     return ap.parse_args()
@@ -306,37 +315,27 @@ def parity_record(model, wl, weights, ref):
 
 # ----------------------------------------------------------------------------- main
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the forward runs on one GPU and exchanges nothing between GPUs)", file=sys.stderr)
-        sys.exit(2)
+def measure(wl, weights, steps, warmup, kv="bf16", paged=0, kernel_reps=50, only_kernel=False):
+    """Load the model of workload `wl`, run `warmup` untimed and `steps` timed
+    passes of the hot path (prefill of the prompt, then the greedy decode
+    steps with the argmax fed back on the device), and time the dominant
+    kernel in the step.  Returns (record, model); the caller closes the model."""
     import numpy as np
     import torch
-
     import synth
     import qwen2_decoder_forward_amd as q2
 
-    wl = synth.WORKLOADS[args.workload]
     sh = wl.shape
     dev = "cuda:0"
-    torch.cuda.set_device(0)
-    kv_fp8 = args.kv == "fp8"
-    t0 = time.perf_counter()
-    weights = synth.make_weights(wl)
-    t_gen = time.perf_counter() - t0
+    kv_fp8 = kv == "fp8"
     max_seq = wl.prompt + wl.steps
     t0 = time.perf_counter()
-    model = q2.load_model(sh, weights, max_seq, wl.batch, kv_fp8=kv_fp8, page_size=args.paged)
+    model = q2.load_model(sh, weights, max_seq, wl.batch, kv_fp8=kv_fp8, page_size=paged)
     torch.cuda.synchronize()
     t_load = time.perf_counter() - t0
     prompt = torch.from_numpy(synth.make_prompt(wl)).to(dev)
-    if args.only_kernel:
-        dk = in_step_kernel(model, wl, prompt, args.kernel_reps, kv_fp8)
-        print(json.dumps({"workload": wl.key, "kv": args.kv, "dominant_kernel": dk}), flush=True)
-        model.close()
-        return
+    if only_kernel:
+        return {"dominant_kernel": in_step_kernel(model, wl, prompt, kernel_reps, kv_fp8)}, model
     nxt = torch.empty(wl.batch, dtype=torch.int64, device=dev)
     out = torch.empty(wl.batch, max(wl.steps, 1), dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
@@ -359,11 +358,11 @@ def main():
             dec_ms.append(e1.elapsed_time(e2))
             step_ms.append(e0.elapsed_time(e2))
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         one_step(False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         one_step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -373,9 +372,9 @@ def main():
     prefill_tok_s = wl.batch * wl.prompt / pre_s
     decode_tok_s = wl.batch * wl.steps / dec_s if wl.steps else None
 
-    dk = in_step_kernel(model, wl, prompt, args.kernel_reps, kv_fp8)
+    dk = in_step_kernel(model, wl, prompt, kernel_reps, kv_fp8)
     roofline = {"bound": dk["bound"], "achieved": round(dk["achieved"], 2), "peak": dk["peak"], "unit": dk["unit"],
-                "frac": round(dk["achieved"] / dk["peak"], 4), "traffic": measured_traffic(wl, args.kv),
+                "frac": round(dk["achieved"] / dk["peak"], 4), "traffic": measured_traffic(wl, kv),
                 "kernel": dk["kernel"], "avg_launch_us": round(dk["avg_launch_us"], 2)}
     for key in ("bytes_per_launch", "flops_per_launch"):
         if key in dk:
@@ -393,33 +392,95 @@ def main():
         step_roof = {"what": "prefill", "bound": "mfma", "flops": fl, "achieved": round(tf, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
 
-    cpu = par = None
-    if not args.no_cpu:
-        cpu, ref = cpu_baseline(wl, weights, args.cpu_seconds, args.kv)
-        if ref is not None:
-            par = parity_record(model, wl, weights, ref)
-
     if wl.steps:
         metric, value = "decode tok/s", decode_tok_s
     else:
         metric, value = "prefill tok/s", prefill_tok_s
     rec = {
         "metric": metric + " (Qwen2 decoder forward, 1 GPU) + % HBM/MFMA roofline",
-        "value": round(value, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(float(np.mean(step_ms)), 3), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random-init weights and prompt ids)",
-        "config": {"workload": f"{wl.key}: {wl.description}" + (" (FP8 KV cache)" if kv_fp8 else ""),
-                   "shape": sh.name, "batch": wl.batch, "prompt": wl.prompt, "decode_steps": wl.steps,
-                   "kv_cache": args.kv + (f", paged ({args.paged} positions per page)" if args.paged else ""),
-                   "parallelism": "single GPU"},
+        "value": round(value, 2), "unit": "tok/s", "steps": steps, "warmup": warmup,
+        "ms_per_step": round(float(np.mean(step_ms)), 3),
+        "workload": f"{wl.key}: {wl.description}" + (" (FP8 KV cache)" if kv_fp8 else ""),
+        "kv_cache": kv + (f", paged ({paged} positions per page)" if paged else ""),
         "prefill_tok_s": round(prefill_tok_s, 1),
         "decode_tok_s": round(decode_tok_s, 2) if decode_tok_s else None,
         "prefill_ms": round(pre_s * 1e3, 3), "decode_ms": round(dec_s * 1e3, 3),
-        "roofline": roofline, "step_roofline": step_roof, "cpu_baseline": cpu, "parity": par,
-        "wall_s_timed": round(wall, 3), "weight_gen_s": round(t_gen, 1), "load_s": round(t_load, 2),
+        "roofline": roofline, "step_roofline": step_roof,
+        "wall_s_timed": round(wall, 3), "load_s": round(t_load, 2),
+    }
+    return rec, model
+
+
+# workloads timed after B when --also is not given (same 1.5B weights): C
+# (4096-token prefill) and D (64 x 4096 batched decode)
+ALSO_DEFAULT = "C,D"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the forward runs on one GPU and exchanges nothing between GPUs)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    import qwen2_decoder_forward_amd as q2
+
+    wl = synth.WORKLOADS[args.workload]
+    sh = wl.shape
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    weights = synth.make_weights(wl)
+    t_gen = time.perf_counter() - t0
+    if args.only_kernel:
+        r, model = measure(wl, weights, 0, 0, args.kv, args.paged, args.kernel_reps, only_kernel=True)
+        model.close()
+        print(json.dumps({"workload": wl.key, "kv": args.kv, **r}), flush=True)
+        return
+    r, model = measure(wl, weights, args.steps, args.warmup, args.kv, args.paged, args.kernel_reps)
+
+    cpu = par = None
+    if not args.no_cpu:
+        cpu, ref = cpu_baseline(wl, weights, args.cpu_seconds, args.kv)
+        if ref is not None:
+            par = parity_record(model, wl, weights, ref)
+    model.close()
+    del model
+    torch.cuda.empty_cache()
+
+    # the other workloads of the same model shape, each a compact record of
+    # its own (not part of `value`)
+    also = {}
+    keys = (ALSO_DEFAULT if wl.key == "B" else "") if args.also is None else args.also
+    for key in [k for k in keys.split(",") if k and k != wl.key]:
+        wk = synth.WORKLOADS[key]
+        if wk.shape.name != sh.name:
+            raise SystemExit(f"--also {key}: workload {key} has another model shape than {wl.key}")
+        print(f"[bench] timing workload {key}", file=sys.stderr, flush=True)
+        ra, ma = measure(wk, weights, args.also_steps, 1, args.kv, args.paged, args.kernel_reps)
+        ma.close()
+        del ma
+        torch.cuda.empty_cache()
+        also[key] = {k: ra[k] for k in ("workload", "metric", "value", "unit", "steps", "warmup", "ms_per_step",
+                                        "prefill_tok_s", "decode_tok_s")}
+        also[key]["roofline"] = {k: ra["roofline"][k] for k in ("kernel", "bound", "achieved", "peak", "unit",
+                                                                 "frac", "avg_launch_us")}
+        also[key]["step_roofline"] = {k: ra["step_roofline"][k] for k in ("what", "achieved", "unit", "frac")}
+
+    rec = {
+        "metric": r["metric"], "value": r["value"], "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random-init weights and prompt ids)",
+        "config": {"workload": r["workload"], "shape": sh.name, "batch": wl.batch, "prompt": wl.prompt,
+                   "decode_steps": wl.steps, "kv_cache": r["kv_cache"], "parallelism": "single GPU"},
+        "prefill_tok_s": r["prefill_tok_s"], "decode_tok_s": r["decode_tok_s"],
+        "prefill_ms": r["prefill_ms"], "decode_ms": r["decode_ms"],
+        "roofline": r["roofline"], "step_roofline": r["step_roofline"], "cpu_baseline": cpu, "parity": par,
+        "also": also or None,
+        "wall_s_timed": r["wall_s_timed"], "weight_gen_s": round(t_gen, 1), "load_s": r["load_s"],
         "library": q2.version(),
     }
-    model.close()
     print(json.dumps(rec), flush=True)
 
 

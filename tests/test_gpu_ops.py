@@ -208,6 +208,12 @@ def _attn_case(seed, B, T, S, nh, nkv, d, dtype, cache_layout=False, smax=None, 
     (1, 1024, 1024, 12, 2),  # causal prefill whose last query blocks are split over two workgroups
     (2, 1024, 1024, 28, 4),  # the same with groups of 7 query heads and two sequences
     (2, 200, 3000, 12, 2),   # long cached past: every query block split, ragged last block
+    # split prefill blocks with one or two heads, a cached past with a ragged
+    # last block, and groups of 7 with two sequences and a ragged last block
+    (1, 512, 512, 1, 1),
+    (1, 512, 512, 2, 1),
+    (1, 1500, 2600, 12, 2),
+    (2, 1000, 1100, 28, 4),
 ])
 def test_attention_bf16(B, T, S, nh, nkv):
     _attn_case(B * 7 + T * 13 + S, B, T, S, nh, nkv, 128, BF)
