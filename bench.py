@@ -21,7 +21,10 @@ Also reported:
                 the prefill gate/up GEMM, D the decode attention kernel;
                 `traffic` is its HBM bytes per launch from profiler counters
                 (profiles/traffic.json) while the kernel source is unchanged
-                since they were taken.
+                since they were taken; `achievable` is what plain library
+                code reaches on the box (a device copy for HBM, torch.matmul
+                on the prefill gate/up shape for MFMA) and the kernel's
+                fraction of it.
   step_roofline algorithmic bytes (or flops) of a whole decode (prefill) step
                 against the HBM (MFMA) peak.
   cpu_baseline  the oracle (plain NumPy) timed on this host on a bounded
@@ -185,6 +188,30 @@ def in_step_kernel(model, wl, prompt, reps, kv_fp8):
     return {"kernel": "gemv_kernel (norm prologue, SwiGLU epilogue), " + name, "bound": "hbm",
             "achieved": traffic / dt / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": traffic,
             "avg_launch_us": dt * 1e6}
+
+
+def achievable(bound, sh, reps=20):
+    """What plain library code reaches on this machine, beside the published
+    peak: for an HBM-bound kernel a device-to-device copy of 512 MiB (read +
+    write bytes over its time); for an MFMA-bound one torch.matmul
+    (hipBLASLt) on the prefill gate/up shape [4096, H] x [H, 2 I] in bf16."""
+    import torch
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    if bound == "hbm":
+        src = torch.empty(CALIB_COPY_BYTES // 4, device=dev, dtype=torch.float32).fill_(1.0)
+        dst = torch.empty_like(src)
+        dt = time_launches(lambda: dst.copy_(src), reps, stream)
+        del src, dst
+        return {"what": "device copy of 512 MiB (torch)", "value": round(2 * CALIB_COPY_BYTES / dt / 1e9, 1),
+                "unit": "GB/s"}
+    g = torch.Generator(device=dev).manual_seed(0)
+    x = torch.randn(4096, sh.hidden, device=dev, generator=g).to(torch.bfloat16)
+    w = torch.randn(sh.hidden, 2 * sh.inter, device=dev, generator=g).to(torch.bfloat16)
+    dt = time_launches(lambda: torch.matmul(x, w), reps, stream)
+    del x, w
+    return {"what": f"torch.matmul bf16 [4096, {sh.hidden}] x [{sh.hidden}, {2 * sh.inter}]",
+            "value": round(2 * 4096 * sh.hidden * 2 * sh.inter / dt / 1e12, 1), "unit": "TFLOP/s"}
 
 
 def measured_traffic(wl, kv="bf16"):
@@ -379,6 +406,9 @@ def measure(wl, weights, steps, warmup, kv="bf16", paged=0, kernel_reps=50, only
     for key in ("bytes_per_launch", "flops_per_launch"):
         if key in dk:
             roofline[key] = dk[key]
+    ach = achievable(dk["bound"], sh)
+    ach["frac"] = round(dk["achieved"] / ach["value"], 4)
+    roofline["achievable"] = ach
 
     if wl.steps:
         ctxs = range(wl.prompt + 1, wl.prompt + wl.steps + 1)
@@ -465,7 +495,7 @@ def main():
         also[key] = {k: ra[k] for k in ("workload", "metric", "value", "unit", "steps", "warmup", "ms_per_step",
                                         "prefill_tok_s", "decode_tok_s")}
         also[key]["roofline"] = {k: ra["roofline"][k] for k in ("kernel", "bound", "achieved", "peak", "unit",
-                                                                 "frac", "avg_launch_us")}
+                                                                 "frac", "avg_launch_us", "achievable")}
         also[key]["step_roofline"] = {k: ra["step_roofline"][k] for k in ("what", "achieved", "unit", "frac")}
 
     rec = {
