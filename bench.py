@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=50)
     ap.add_argument("--only-kernel", action="store_true",
                     help="time only the dominant kernel (for profiler counter runs) and print its record")
+    ap.add_argument("--stage", default=None, choices=sorted(PREFILL_STAGES),
+                    help="with --only-kernel and workload C: the prefill product (or the attention) to replay "
+                         "instead of gate/up")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="KV cache: bf16 (the workloads' definition) or FP8 E4M3 blocks with per-block scales")
     ap.add_argument("--also", default=None,
@@ -130,7 +133,17 @@ STAGE_NAMES = {0: "QKV", 1: "attention", 2: "o_proj", 3: "gate/up", 4: "down",
                5: "attention (split-KV kernel without its merge)"}
 
 
-def in_step_kernel(model, wl, prompt, reps, kv_fp8):
+PREFILL_STAGES = {"qkv": 0, "attn": 1, "o": 2, "gate_up": 3, "down": 4}
+
+
+def prefill_stage_flops(sh, T, stage):
+    """Algorithmic flops of one prefill product (or causal attention) over T tokens."""
+    H, I, qd = sh.hidden, sh.inter, sh.nh * sh.dh
+    return {"qkv": 2 * T * H * sh.qkv_out, "o": 2 * T * qd * H, "gate_up": 2 * T * 2 * I * H,
+            "down": 2 * T * I * H, "attn": 4 * sh.dh * sh.nh * T * (T + 1) // 2}[stage]
+
+
+def in_step_kernel(model, wl, prompt, reps, kv_fp8, stage_name=None):
     """Time the dominant kernel of the step as the step launches it: the
     model replays that product (q2_model_replay_stage: the same kernels and
     arguments as the forward, on the model's own weights and buffers) for
@@ -152,7 +165,8 @@ def in_step_kernel(model, wl, prompt, reps, kv_fp8):
     model.reset()
     B, H, I = wl.batch, sh.hidden, sh.inter
     if wl.key == "C":
-        stage, tokens = q2.STAGE_GATE_UP, wl.prompt          # the prefill product at length 0
+        # the prefill product at length 0 (gate/up unless another is asked for)
+        stage, tokens = PREFILL_STAGES[stage_name or "gate_up"], wl.prompt
     else:
         nxt = torch.empty(B, dtype=torch.int64, device=dev)
         q2.q2_model_prefill(model.handle, prompt, nxt)        # decode products at length = prompt
@@ -173,8 +187,10 @@ def in_step_kernel(model, wl, prompt, reps, kv_fp8):
     model.reset()
     name = f"{STAGE_NAMES[stage]} product of the step (q2_model_replay_stage, {B} x {tokens} rows, layers cycled)"
     if wl.key == "C":
-        flops = 2 * wl.prompt * 2 * I * H
-        return {"kernel": "gemm_dtl_mix_kernel, " + name, "bound": "mfma", "achieved": flops / dt / 1e12,
+        flops = prefill_stage_flops(sh, wl.prompt, stage_name or "gate_up")
+        kern = {"gate_up": "gemm_dtl_mix_kernel", "down": "gemm_dtl_sk_kernel", "attn": "attn_prefill_kernel",
+                "qkv": "gemm_dtl_kernel", "o": "gemm_dtl_kernel"}[stage_name or "gate_up"]
+        return {"kernel": kern + ", " + name, "bound": "mfma", "achieved": flops / dt / 1e12,
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "flops_per_launch": flops, "avg_launch_us": dt * 1e6}
     if wl.key == "D":
         keys = wl.prompt + 1
@@ -342,7 +358,7 @@ def parity_record(model, wl, weights, ref):
 
 # ----------------------------------------------------------------------------- main
 
-def measure(wl, weights, steps, warmup, kv="bf16", paged=0, kernel_reps=50, only_kernel=False):
+def measure(wl, weights, steps, warmup, kv="bf16", paged=0, kernel_reps=50, only_kernel=False, stage=None):
     """Load the model of workload `wl`, run `warmup` untimed and `steps` timed
     passes of the hot path (prefill of the prompt, then the greedy decode
     steps with the argmax fed back on the device), and time the dominant
@@ -362,7 +378,7 @@ def measure(wl, weights, steps, warmup, kv="bf16", paged=0, kernel_reps=50, only
     t_load = time.perf_counter() - t0
     prompt = torch.from_numpy(synth.make_prompt(wl)).to(dev)
     if only_kernel:
-        return {"dominant_kernel": in_step_kernel(model, wl, prompt, kernel_reps, kv_fp8)}, model
+        return {"dominant_kernel": in_step_kernel(model, wl, prompt, kernel_reps, kv_fp8, stage)}, model
     nxt = torch.empty(wl.batch, dtype=torch.int64, device=dev)
     out = torch.empty(wl.batch, max(wl.steps, 1), dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
@@ -452,6 +468,8 @@ def main():
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the forward runs on one GPU and exchanges nothing between GPUs)", file=sys.stderr)
         sys.exit(2)
+    if args.stage and (not args.only_kernel or args.workload != "C"):
+        raise SystemExit("--stage applies to --only-kernel runs of workload C")
     import torch
 
     import synth
@@ -464,7 +482,8 @@ def main():
     weights = synth.make_weights(wl)
     t_gen = time.perf_counter() - t0
     if args.only_kernel:
-        r, model = measure(wl, weights, 0, 0, args.kv, args.paged, args.kernel_reps, only_kernel=True)
+        r, model = measure(wl, weights, 0, 0, args.kv, args.paged, args.kernel_reps, only_kernel=True,
+                           stage=args.stage)
         model.close()
         print(json.dumps({"workload": wl.key, "kv": args.kv, **r}), flush=True)
         return
