@@ -87,12 +87,15 @@ __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(uint16_t* __restrict__
   if (row >= rows) return;
   const int nch = H >> 3;
   const uint16_t* x = in + static_cast<int64_t>(row) * ldi;
-  uint4 v[CH];
+  // the norm weight does not depend on the row: its loads go out with the
+  // row's, so the row costs a single memory round trip
+  uint4 v[CH], wv[CH];
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int i = lane + 64 * c;
     v[c] = i < nch ? *reinterpret_cast<const uint4*>(x + 8 * i) : uint4{0, 0, 0, 0};
+    wv[c] = i < nch ? *reinterpret_cast<const uint4*>(w + 8 * i) : uint4{0, 0, 0, 0};
   }
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
@@ -111,9 +114,8 @@ __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(uint16_t* __restrict__
   for (int c = 0; c < CH; ++c) {
     const int i = lane + 64 * c;
     if (i < nch) {
-      const uint4 wv = *reinterpret_cast<const uint4*>(w + 8 * i);
       const uint32_t* e = &v[c].x;
-      const uint32_t* we = &wv.x;
+      const uint32_t* we = &wv[c].x;
       uint4 r;
       uint32_t* re = &r.x;
 #pragma unroll
