@@ -119,6 +119,18 @@ def test_e_shape_2_layers_batch8():
     assert r.ok(), r.summary()
 
 
+@pytest.mark.parametrize("batch", [2, 16, 17, 33, 48])
+def test_decode_batch_sizes_small_bf16(batch):
+    """Decode batches at the edges of the product paths: 2 (the GEMV whose
+    prologue adds the pending split-K residual), 16 (the largest GEMV batch
+    with fused norms), 17 (the smallest skinny split-K batch, 32-row token
+    tiles), 33 and 48 (64-row token tiles, partly filled), against the
+    oracle under teacher forcing."""
+    r = _run(SMALL_BF16, batch, 20, 4, seed=40 + batch)
+    _print(f"small-bf16 batch {batch}", r)
+    assert r.ok(), r.summary()
+
+
 def _layerwise(shape, prompt_len, seed=1234):
     """Each layer of the GPU model (a one-layer model holding that layer's
     weights) fed the oracle's input hidden state; returns per-layer
