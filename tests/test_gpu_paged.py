@@ -63,30 +63,31 @@ def _oracle_alone(sh, w, prompt, steps, max_seq, kv="model"):
     return parity.reference(orc, prompt[None, :], steps, orc64)
 
 
-def _ragged(kv_fp8):
+def _ragged(kv_fp8, lens=(5, 70, 130), steps=8):
     sh = SMALL_BF16
     w = synth.make_weights(sh, seed=42)
-    lens, steps, max_seq = [5, 70, 130], 8, 160
+    lens, max_seq = list(lens), max(lens) + steps + 22
+    B = len(lens)
     prompts = [_prompt(10 + i, n, sh.vocab) for i, n in enumerate(lens)]
     refs = [_oracle_alone(sh, w, p, steps, max_seq, "fp8" if kv_fp8 else "model") for p in prompts]
-    m = q2.load_model(sh, w, max_seq, 3, kv_fp8=kv_fp8, page_size=64)
+    m = q2.load_model(sh, w, max_seq, B, kv_fp8=kv_fp8, page_size=64)
     got_l = [[] for _ in lens]
     got_t = [[] for _ in lens]
     for b, p in enumerate(prompts):
         nxt, lg = m.seq_prefill(b, torch.from_numpy(p).to(DEV), logits=True)
         got_l[b].append(lg.cpu().numpy())
         got_t[b].append(nxt.cpu().numpy())
-    assert [m.seq_length(b) for b in range(3)] == lens
+    assert [m.seq_length(b) for b in range(B)] == lens
     for s in range(1, steps + 1):
-        feed = torch.tensor([int(refs[b][0][0, s - 1]) for b in range(3)], dtype=torch.int64, device=DEV)
+        feed = torch.tensor([int(refs[b][0][0, s - 1]) for b in range(B)], dtype=torch.int64, device=DEV)
         nxt, lg = m.decode(feed, logits=True)
         lg, nxt = lg.cpu().numpy(), nxt.cpu().numpy()
-        for b in range(3):
+        for b in range(B):
             got_l[b].append(lg[b:b + 1])
             got_t[b].append(nxt[b:b + 1])
-    assert [m.seq_length(b) for b in range(3)] == [n + steps for n in lens]
+    assert [m.seq_length(b) for b in range(B)] == [n + steps for n in lens]
     m.close()
-    for b in range(3):
+    for b in range(B):
         toks, ref_logits, spread = refs[b]
         r = parity.compare(got_l[b], np.stack(got_t[b], axis=1), ref_logits, toks, spread, True)
         print(f"\n[paged{' fp8' if kv_fp8 else ''} ragged, sequence {b} (prompt {lens[b]})] {r.summary()}", flush=True)
@@ -99,6 +100,17 @@ def test_paged_ragged_batch_matches_each_sequence_alone():
 
 def test_paged_fp8_ragged_batch_matches_each_sequence_alone():
     _ragged(True)
+
+
+# 20 sequences of 3 to 193 cached positions (one to four pages): the decode
+# products take the skinny split-K path, whose QKV reduction writes each new
+# k / v row into its own sequence's page (and, FP8, quantises it there)
+RAGGED_20 = tuple(3 + 10 * i for i in range(20))
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_paged_ragged_batch_20_matches_each_sequence_alone(kv_fp8):
+    _ragged(kv_fp8, RAGGED_20, steps=5)
 
 
 def test_paged_continuous_batching_release_and_join():
