@@ -4,8 +4,11 @@ checked against independent derivations: the tensor inventory of the model
 count of the causal (query, key) pairs, and the per-step totals of the
 workloads (3.091 GB for the 1.5B batch-1 decode, 1.2177e13 flop for the
 4096-token prefill, 10.63 GB for the 64 x 4096 decode, 14.67 GB for the 7B
-batch-8 decode).  No GPU."""
+batch-8 decode); and the command line's refusals.  No GPU."""
 import math
+import os
+import subprocess
+import sys
 
 import numpy as np
 
@@ -70,3 +73,21 @@ def test_prefill_stage_flops_sum_to_the_layer():
     stages = sum(bench.prefill_stage_flops(sh, T, s) for s in bench.PREFILL_STAGES)
     per_layer = (bench.prefill_flops(sh, 1, T) - 2 * sh.hidden * sh.vocab) // sh.nlayer
     assert stages == per_layer
+
+
+def _bench(*args):
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    return subprocess.run([sys.executable, os.path.join(root, "bench.py"), *args], capture_output=True, text=True,
+                          timeout=120)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """One GPU only: --gpus 2 exits with status 2 and says so, before touching
+    any device."""
+    r = _bench("--gpus", "2")
+    assert r.returncode == 2 and "one GPU" in r.stderr, (r.returncode, r.stderr)
+
+
+def test_bench_stage_only_for_prefill_kernel_runs():
+    r = _bench("--stage", "down")
+    assert r.returncode != 0 and "--stage applies to --only-kernel runs of workload C" in r.stderr, r.stderr
