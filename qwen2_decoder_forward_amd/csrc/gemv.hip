@@ -1,8 +1,8 @@
 // Decode-path linear layers: Y[M, N] = X[M, K] W[N, K]^T for M <= 64 rows.
 //
 // Bound by reading W once from HBM.  A workgroup owns a tile of 16 weight
-// rows; its four waves share that tile's K range, each taking 128-wide K
-// blocks in turn.  A lane (row r = lane % 16, group g = lane / 16) loads four
+// rows; its waves (12 or 16) share that tile's K range, each taking 128-wide
+// K blocks in turn.  A lane (row r = lane % 16, group g = lane / 16) loads four
 // 16-byte pieces of row r per block (all issued before any math); load u of
 // the four lane groups covers 64 contiguous bytes of each of the 16 rows.
 // They feed four 16x16x32 bf16 MFMAs with the weight rows as the A operand;
@@ -31,7 +31,7 @@ namespace q2 {
 namespace {
 
 constexpr int KB = 128;  // K per block
-constexpr int GEMV_WGS = 256;  // workgroups the tile loops aim at (one 16-wave workgroup per CU)
+constexpr int GEMV_WGS = 256;  // workgroups the tile loops aim at (one 12- or 16-wave workgroup per CU)
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
@@ -242,7 +242,7 @@ __device__ __forceinline__ void gemv_epilogue(const Epi& epi, int M, int N, int 
 // With STAGE the X rows of this workgroup's K range are built in dynamic
 // LDS first (required for the NORM and ATTN sources).  Every wave streams
 // weights: handing the staging to a few dedicated waves lowers the loads in
-// flight more than it saves.  The occupancy bound keeps two 16-wave
+// flight more than it saves.  The occupancy bound keeps two 12- or 16-wave
 // workgroups resident per CU (at most 64 VGPRs): one more register halves the
 // workgroups in flight and costs a third of the bandwidth on the long
 // LM-head pass.
@@ -684,7 +684,7 @@ q2_status launch_gemv2(const GemmArgs& a, const GemvPlan& p, size_t lds, hipStre
   const GemvSrc src{static_cast<const uint16_t*>(a.norm_w), a.norm_sq, a.norm_sq_ld, a.norm_eps, a.att_o, a.att_ml,
                     a.att_nsplit, a.att_group, a.att_nkv, a.resid_part, a.resid_splits,
                     static_cast<uint16_t*>(a.resid_out)};
-  // at most two rounds of 16-wave workgroups on the chip; each loops over
+  // at most two rounds of 12- or 16-wave workgroups on the chip; each loops over
   // its tiles with the next tile's weights in flight
   // (the residual epilogue needs whole 16-row tiles; the others may give a
   // workgroup fewer rows, down to 8, when there are fewer tiles than slots)
@@ -723,12 +723,28 @@ q2_status launch_gemv(const GemmArgs& a, const GemvPlan& p, hipStream_t s) {
   return check_launch("gemv_reduce");
 }
 
+// Waves per workgroup for up to 16 token rows: 12 when a split's K range is
+// at most 12 blocks (hidden 1536: every wave streams one block of each tile
+// and none waits idle at the cross-wave reduction; batch-1 decode +1 %), 16
+// otherwise (the 7B products' 28 blocks: 12 waves would leave a third of
+// them with a second round of loads).  The pending-residual prologue covers
+// a row with one pass of the threads, so there 12 waves also need
+// K <= 8 x 768.
+constexpr int GEMV_NW_SHORT = 12;
+
+template <int EK, int SRC>
+q2_status gemv_mt1(const GemmArgs& a, const GemvPlan& p, hipStream_t s) {
+  if (p.bps <= GEMV_NW_SHORT && (SRC != XSRC_NORMR || a.K <= 8 * 64 * GEMV_NW_SHORT))
+    return launch_gemv<1, GEMV_NW_SHORT, EK, SRC>(a, p, s);
+  return launch_gemv<1, 16, EK, SRC>(a, p, s);
+}
+
 template <int EK>
 q2_status gemv_ek(const GemmArgs& a, const GemvPlan& p, hipStream_t s) {
-  if (a.norm_w && a.resid_part) return launch_gemv<1, 16, EK, XSRC_NORMR>(a, p, s);
-  if (a.norm_w) return launch_gemv<1, 16, EK, XSRC_NORM>(a, p, s);
-  if (a.att_o) return launch_gemv<1, 16, EK, XSRC_ATTN>(a, p, s);
-  if (p.mt == 1) return launch_gemv<1, 16, EK, XSRC_RAW>(a, p, s);
+  if (a.norm_w && a.resid_part) return gemv_mt1<EK, XSRC_NORMR>(a, p, s);
+  if (a.norm_w) return gemv_mt1<EK, XSRC_NORM>(a, p, s);
+  if (a.att_o) return gemv_mt1<EK, XSRC_ATTN>(a, p, s);
+  if (p.mt == 1) return gemv_mt1<EK, XSRC_RAW>(a, p, s);
   if (p.mt == 2) return launch_gemv<2, 16, EK, XSRC_RAW>(a, p, s);
   return launch_gemv<4, 8, EK, XSRC_RAW>(a, p, s);
 }
