@@ -201,7 +201,8 @@ def _attn_case(seed, B, T, S, nh, nkv, d, dtype, cache_layout=False, smax=None, 
     (64, 1, 1000, 12, 2),    # decode batch: several 16-key blocks per wave (double-buffered loads)
     (64, 1, 4097, 12, 2),    # the 64-sequence decode at its full cache length: 4 splits of 1088 keys
     (4, 1, 5000, 28, 4),     # long splits with a ragged last one (more than 16 splits)
-    (8, 1, 1280, 28, 4),     # the 7B batch-8 decode at its last step: 10 splits (the 16-split merge)
+    (8, 1, 1280, 28, 4),     # the 7B batch-8 decode at its last step: 7 splits (at most 8 once they fill the CUs)
+    (4, 1, 800, 28, 4),      # 13 splits: the 16-split merge
     (1, 64, 64, 12, 2),      # one full prefill block
     (1, 100, 300, 12, 2),    # prefill with a cached past, ragged
     (2, 130, 130, 28, 4),    # several query blocks, batch 2
