@@ -121,3 +121,21 @@ def test_valid_model_without_gpu_is_an_error_not_a_crash():
     import synth
     cfg = make_config(synth.SHAPES["tiny"], 32, 1)
     assert _err(q2.q2_model_create, cfg) in ("Q2_EINVAL", "Q2_EHIP")
+
+
+def test_decode_attention_split_plan_without_gpu():
+    """The split-KV plan of the decode attention, seen through the workspace
+    it asks for (float32 partials [B * nkv][splits][16][128] plus a (max, sum)
+    pair per row): keys in chunks of whole 64-key blocks, at most two
+    workgroups per CU (512), and at most 8 splits once 8 already give every
+    CU a workgroup (B * nkv >= 32)."""
+    per_split = 16 * (128 * 4 + 8)
+
+    def splits(B, S, nh, nkv):
+        return q2.q2_self_attention_workspace_bytes(B, 1, S, nh, nkv, 128) // (B * nkv * per_split)
+
+    assert splits(1, 192, 12, 2) == 3      # batch-1 decode at its last step: 3 x 64 keys
+    assert splits(64, 4097, 12, 2) == 4    # 64 x 4097: 128 (sequence, KV head) pairs, 4 splits each
+    assert splits(8, 1280, 28, 4) == 7     # 7B batch 8: capped at 8 -> 7 x 192 keys
+    assert splits(4, 800, 28, 4) == 13     # 16 pairs: 13 x 64 keys (8 would leave CUs idle)
+    assert q2.q2_self_attention_workspace_bytes(1, 1, 64, 12, 2, 128) == 0   # one split, no partials
